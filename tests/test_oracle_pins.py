@@ -1,0 +1,451 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, not against the oracle itself.
+
+Sources: Qin, "Is 2:4 Sparsity Still Worth It?" — paper-daily.com English
+summary §2 (equal bits), §3 (formats), §4 (energy loss, additivity, predicted
+R), §6 (pairwise 4:8). Hand-worked examples live in tests/golden/.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from conftest import GOLDEN
+
+HAND = json.load(open(os.path.join(GOLDEN, "hand_examples.json")))
+PAGES = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+
+
+def bf16(vals):
+    """bf16 bit patterns of exactly representable values (sign of zero kept)."""
+    a = np.asarray(vals, dtype=np.float64)
+    bits = W.to_bf16_bits(a)
+    back = W.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.array_equal(back, a), "hand example must be bf16-exact"
+    bits[(a == 0) & np.signbit(a)] = 0x8000
+    return bits
+
+
+def hexs(xs):
+    return np.array([int(h, 16) for h in xs], dtype=np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked layouts and codes
+# ---------------------------------------------------------------------------
+
+
+def test_meta_layout_hand_example():
+    ex = HAND["meta_layout"]
+    raw = bf16([ex["row"]])
+    vals, meta = O.prune_compress(raw, O.BF16)
+    assert np.array_equal(O.decode_input(vals, O.BF16)[0], ex["kept"])
+    assert np.array_equal(meta[0], hexs(ex["meta_bytes"]))
+
+
+def test_tie_groups_hand_example():
+    ex = HAND["tie_groups"]
+    raw = bf16([sum(ex["groups"], [])])
+    idx = O.select_2of4(O.score_values(O.decode_input(raw, O.BF16)))
+    assert idx[0].tolist() == ex["kept_positions"]
+
+
+def test_int4_row_hand_example():
+    ex = HAND["int4_row"]
+    codes, s = O.quantize_rows(bf16([ex["row"]]), O.BF16, O.QSpec("int", ex["bits"]))
+    assert codes[0].tolist() == ex["codes"]
+    assert int(s.view(np.uint32)[0]) == int(ex["scale_hex"], 16)
+
+
+def test_fp8_row_hand_example():
+    ex = HAND["fp8_row"]
+    raw = bf16([ex["row"]])
+    codes, s = O.quantize_rows(raw, O.BF16, O.QSpec("fp8"))
+    assert np.array_equal(codes[0], hexs(ex["dense_codes"]))
+    assert s[0] == ex["dense_scale"]
+    pc, meta, ps = O.prune_quantize(raw, O.BF16, O.QSpec("fp8"))
+    assert np.array_equal(meta[0], hexs(ex["pruned_meta_bytes"]))
+    assert np.array_equal(pc[0], hexs(ex["pruned_codes"]))
+    assert ps[0] == ex["pruned_scale"]
+
+
+def test_mxfp4_hand_example():
+    ex = HAND["mxfp4_row"]
+    row = np.zeros(128)
+    exp_codes = np.zeros(128, dtype=np.int64)
+    for b, (vals, cods) in enumerate(zip(ex["row_blocks"], ex["block_codes"])):
+        row[b * 32:b * 32 + len(vals)] = vals
+        exp_codes[b * 32:b * 32 + len(cods)] = cods
+    raw = bf16([row.tolist()])
+    packed, sc = O.quantize_mxfp4(raw, O.BF16)
+    assert sc[0].tolist() == ex["scale_codes"]
+    got = np.empty(128, dtype=np.int64)
+    got[0::2] = packed[0] & 0xF
+    got[1::2] = packed[0] >> 4
+    assert got.tolist() == exp_codes.tolist()
+
+
+def test_nvfp4_hand_example():
+    ex = HAND["nvfp4_tensor"]
+    raw = bf16(ex["rows"])
+    packed, bs, s_t = O.quantize_nvfp4(raw, O.BF16)
+    assert float(s_t) == ex["tensor_scale"]
+    assert np.array_equal(bs[:, 0], hexs(ex["block_scales"]))
+    for r in range(2):
+        assert np.array_equal(packed[r], hexs(ex["packed"][r]))
+
+
+def test_predict_R_hand_example():
+    ex = HAND["predict_R_row"]
+    raw = bf16([ex["row"]])
+    e = O.error_energy(raw, O.BF16, O.QSpec("none"), O.QSpec("int", 4))
+    assert e[0, 0] == ex["sum_x2"] and e[0, 1] == ex["sum_dropped"] and e[0, 2] == 0.0
+    r = O.predict_R(raw, O.BF16, [O.QSpec("none")], [O.QSpec("int", 4)])[0, 0]
+    assert r[0] == pytest.approx(ex["E_prune"], rel=1e-15)
+    assert r[1] == 0.0
+    assert r[2] == pytest.approx(ex["E_prune"], rel=1e-15)
+    assert r[3] == pytest.approx(ex["E_dense_approx"], rel=1e-6)
+    assert r[4] == pytest.approx(ex["R_approx"], rel=1e-6)
+    ek = O.error_energy(raw, O.BF16, O.QSpec("int", 4), O.QSpec("int", 4))
+    assert ek[0, 2] == pytest.approx(ex["kept_int4_sum_err2_approx"], rel=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# P2: brute force over all six masks of a group
+# ---------------------------------------------------------------------------
+
+PAIRS = list(itertools.combinations(range(4), 2))   # lexicographic order
+
+
+def brute_keep(scores):
+    """Pair with the largest kept score sum; among equal sums the
+    lexicographically smallest pair (exact rational arithmetic)."""
+    best = None
+    for p in PAIRS:
+        v = scores[p[0]] + scores[p[1]]
+        if best is None or v > best[0]:
+            best = (v, p)
+    return list(best[1])
+
+
+def test_all_tie_patterns_small_alphabet():
+    alphabet = [0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0]
+    groups = list(itertools.product(alphabet, repeat=4))
+    raw = bf16([sum((list(g) for g in groups), [])])
+    idx = O.select_2of4(O.score_values(O.decode_input(raw, O.BF16)))[0]
+    for g, got in zip(groups, idx.tolist()):
+        want = brute_keep([Fraction(abs(v)) ** 2 for v in g])
+        assert got == want, (g, got, want)
+
+
+def test_bruteforce_random_magnitude_and_wanda():
+    rng = np.random.default_rng(7)
+    rows, k = 64, 64
+    # small integer values make ties frequent; scaling keeps them exact
+    w = rng.integers(-4, 5, size=(rows, k)) * 0.25
+    raw = bf16(w)
+    norm = (rng.integers(0, 4, size=k) * 0.5).astype(np.float32)
+    x = O.decode_input(raw, O.BF16)
+    for score in ("magnitude", "wanda"):
+        idx = O.select_2of4(O.score_values(x, score, norm))
+        for r in range(rows):
+            for g in range(k // 4):
+                vals = [Fraction(float(v)) for v in x[r, 4 * g:4 * g + 4]]
+                if score == "magnitude":
+                    sc = [v * v for v in vals]
+                else:
+                    sc = [abs(v) * Fraction(float(norm[4 * g + i])) for i, v in enumerate(vals)]
+                assert idx[r, g].tolist() == brute_keep(sc)
+
+
+# ---------------------------------------------------------------------------
+# P3: additivity of prune and kept-quantization error ([PD §4])
+# ---------------------------------------------------------------------------
+
+
+def test_additivity_exact_rational():
+    rng = np.random.default_rng(3)
+    raw = W.to_bf16_bits(rng.standard_normal((8, 32)))
+    x = O.decode_input(raw, O.BF16)
+    for q in (O.QSpec("int", 4), O.QSpec("int", 8), O.QSpec("fp8")):
+        codes, meta, s = O.prune_quantize(raw, O.BF16, q)
+        xhat = O.dequantize_pruned(codes, meta, q, s)
+        mask = O.decompress(np.ones_like(codes, dtype=np.uint8), meta).astype(bool)
+        e = O.error_energy(raw, O.BF16, q, O.QSpec("int", 8))
+        total = Fraction(0)
+        dropped = Fraction(0)
+        kept = Fraction(0)
+        for r in range(x.shape[0]):
+            for j in range(x.shape[1]):
+                xv = Fraction(float(x[r, j]))
+                hv = Fraction(float(xhat[r, j]))
+                total += (xv - hv) ** 2
+                if mask[r, j]:
+                    kept += (xv - hv) ** 2
+                else:
+                    dropped += xv ** 2
+        assert total == dropped + kept                      # exact
+        assert float(dropped) == pytest.approx(e[0, 1], rel=1e-12)
+        assert float(kept) == pytest.approx(e[0, 2], rel=1e-12)
+
+
+def test_additivity_full_size_fp64():
+    raw = W.gaussian_f32(11, 256, 1024)
+    q = O.QSpec("int", 6)
+    codes, meta, s = O.prune_quantize(raw, O.F32, q)
+    xhat = O.dequantize_pruned(codes, meta, q, s)
+    x = O.decode_input(raw, O.F32)
+    e = O.error_energy(raw, O.F32, q, O.QSpec("int", 4))
+    assert np.sum((x - xhat) ** 2) == pytest.approx(e[0, 1] + e[0, 2], rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P1 / P7: the pages' Gaussian figures ([PD §4])
+# ---------------------------------------------------------------------------
+
+
+def gaussian_energy_loss_closed_form():
+    """E[Y(1)^2 + Y(2)^2] / 4 for the two smallest of four iid |N(0,1)|,
+    from the order-statistic densities (numerical integration)."""
+    from scipy import integrate, stats
+
+    def moment(k):
+        f = lambda y: y * y * 4 * math.comb(3, k - 1) * (stats.halfnorm.cdf(y) ** (k - 1)) * \
+            (stats.halfnorm.sf(y) ** (4 - k)) * stats.halfnorm.pdf(y)
+        return integrate.quad(f, 0, np.inf, epsabs=1e-13)[0]
+    return (moment(1) + moment(2)) / 4
+
+
+def test_gaussian_energy_loss_closed_form_matches_pages():
+    cf = gaussian_energy_loss_closed_form()
+    assert cf == pytest.approx(0.1324474, abs=2e-7)
+    assert round(cf, 3) == PAGES["gaussian_24_energy_loss"]["value"]
+
+
+def test_gaussian_energy_loss_of_oracle():
+    cf = gaussian_energy_loss_closed_form()
+    raw = W.gaussian_f32(0, 256, 1024)
+    e = O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", 8))
+    loss = e[0, 1] / e[0, 0]
+    assert 0.1309 < loss < 0.1339                 # 3 sd of the seed spread at this shape
+    big = W.gaussian_f32(1, 2048, 2048)
+    e = O.error_energy(big, O.F32, O.QSpec("none"), O.QSpec("int", 8))
+    # sd of the estimate at 4M elements is about 1.3e-4
+    assert abs(e[0, 1] / e[0, 0] - cf) < 6e-4
+
+
+def test_gaussian_relative_errors_match_pages():
+    raw = W.gaussian_f32(5, 4096, 128)            # 128-element scale vectors
+    dense = {b: O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", b)) for b in (3, 8)}
+    rel = {b: math.sqrt(d[0, 3] / d[0, 0]) for b, d in dense.items()}
+    assert rel[3] == pytest.approx(PAGES["gaussian_dense_int3_relative_error"]["value"], abs=0.004)
+    assert rel[8] == pytest.approx(PAGES["gaussian_dense_int8_relative_error"]["value"], abs=0.001)
+    lo, hi = (PAGES["gaussian_24_side_relative_error"][k] for k in ("low", "high"))
+    for m in (3, 4, 6, 8):
+        r = O.predict_R(raw, O.F32, [O.QSpec("int", 2 * m)], [O.QSpec("int", m + 1)])[0, 0]
+        assert lo - 0.005 <= math.sqrt(r[2]) <= hi + 0.01
+    # the curves cross only below 3 bits: R > 1 at m = 2 (INT4 kept vs INT3)
+    r = O.predict_R(raw, O.F32, [O.QSpec("int", 4)], [O.QSpec("int", 3)])[0, 0]
+    assert r[4] > 1.0
+
+
+def test_each_added_bit_quarters_dense_error_energy():
+    raw = W.gaussian_f32(9, 1024, 256)
+    # the uniform-noise picture holds once the grid is fine (from about 5 bits)
+    e = [O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", b))[0, 3] for b in range(5, 13)]
+    ratios = np.array(e[:-1]) / np.array(e[1:])
+    assert np.all((ratios > 3.6) & (ratios < 4.4))
+    # E_2:4 tends to the energy loss as kept bits grow ([PD §4])
+    r = O.predict_R(raw, O.F32, [O.QSpec("int", 16)], [O.QSpec("int", 9)])[0, 0]
+    assert r[1] < 1e-8 and r[2] == pytest.approx(r[0], rel=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# P4: the equal-bits accounting ([PD §2])
+# ---------------------------------------------------------------------------
+
+
+def test_equal_bits_accounting():
+    for m in range(1, 9):
+        assert O.bits_per_element(O.QSpec("int", 2 * m), sparse24=True, row_len=4096) == \
+            O.bits_per_element(O.QSpec("int", m + 1), row_len=4096)
+    for a, ab, b, bb in PAGES["equal_bits"]["pairs"]:
+        assert O.bits_per_element(O.QSpec(a, ab), sparse24=True) == O.bits_per_element(O.QSpec(b, bb))
+    assert O.bits_per_element(O.QSpec("none"), sparse24=True, value_bits=16) > \
+        O.bits_per_element(O.QSpec("fp8"))
+    m = PAGES["equal_bits"]["eight_bit_budget_kept_bits"] // 2
+    assert O.bits_per_element(O.QSpec("int", 2 * m), sparse24=True) == 8.0
+    assert O.bits_per_element(O.QSpec("mxfp4")) == 4.25
+    assert O.bits_per_element(O.QSpec("nvfp4")) == 4.5
+
+
+# ---------------------------------------------------------------------------
+# P5: invariants
+# ---------------------------------------------------------------------------
+
+
+def test_mask_invariants_and_roundtrip():
+    rng = np.random.default_rng(12)
+    raw = W.to_bf16_bits(rng.standard_normal((33, 72)) * np.exp(rng.standard_normal((33, 1))))
+    vals, meta = O.prune_compress(raw, O.BF16)
+    idx = O.indices_from_meta(meta)
+    assert np.all(idx[..., 0] < idx[..., 1])
+    dense = O.decompress(vals, meta)
+    x = O.decode_input(raw, O.BF16)
+    mask = O.decompress(np.ones_like(vals), meta).astype(bool)
+    assert np.array_equal(O.decode_input(dense, O.BF16), np.where(mask, x, 0.0))
+    assert np.all(mask.reshape(33, -1, 4).sum(-1) == 2)
+    # magnitude keeps every group's maximum, so kept amax == row amax
+    assert np.array_equal(np.abs(O.decode_input(vals, O.BF16)).max(1), np.abs(x).max(1))
+
+
+def test_energy_loss_bounds():
+    # at most two non-zeros per group -> nothing dropped
+    x = np.zeros((4, 16))
+    x[:, 0::4] = 1.0
+    x[:, 2::4] = -3.0
+    e = O.error_energy(bf16(x), O.BF16, O.QSpec("none"), O.QSpec("int", 8))
+    assert e[0, 1] == 0.0
+    # all magnitudes equal in every group -> exactly half dropped
+    y = np.where(np.arange(16) % 3 == 0, 2.0, -2.0) * np.ones((4, 1))
+    e = O.error_energy(bf16(y), O.BF16, O.QSpec("none"), O.QSpec("int", 8))
+    assert e[0, 1] / e[0, 0] == 0.5
+
+
+def test_energy_loss_independent_of_bits():
+    raw = W.activation_x(2, 64, 512)
+    el = {O.error_energy(raw, O.BF16, O.QSpec("int", b), O.QSpec("int", b))[0, 1] for b in (2, 5, 8, 16)}
+    assert len(el) == 1
+
+
+def test_blocks_partition_the_sums():
+    raw = W.student_t_x(4, 384, 256)
+    whole = O.error_energy(raw, O.BF16, O.QSpec("fp8"), O.QSpec("nvfp4"))
+    blk = O.error_energy(raw, O.BF16, O.QSpec("fp8"), O.QSpec("nvfp4"), rows_per_block=128)
+    assert blk.shape == (3, 4)
+    assert np.allclose(blk.sum(0), whole[0], rtol=1e-12)
+
+
+def test_degenerate_R():
+    z = np.zeros((1, 8), dtype=np.uint16)
+    r = O.predict_R(z, O.BF16, [O.QSpec("fp8")], [O.QSpec("int", 8)])[0, 0]
+    assert np.all(np.isnan(r))
+    # exactly representable row: dense error 0, 2:4 error > 0 -> R = inf
+    raw = bf16([[1, 3, -1, 3, 2, 1, 3, -3]])          # amax 3 = qmax of INT3: scale 1
+    r = O.predict_R(raw, O.BF16, [O.QSpec("none")], [O.QSpec("int", 3)])[0, 0]
+    assert r[3] == 0.0 and r[4] == np.inf
+
+
+# ---------------------------------------------------------------------------
+# P6: encoders against library routines and exact brute force
+# ---------------------------------------------------------------------------
+
+
+def all_finite_bf16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = W.bf16_bits_to_f32(bits)
+    return v[np.isfinite(v)]
+
+
+def test_e4m3_matches_torch_cast_on_all_bf16_and_random_fp32():
+    import torch
+
+    v = all_finite_bf16().astype(np.float32)
+    rng = np.random.default_rng(0)
+    r = (rng.standard_normal(200000) * np.exp2(rng.integers(-14, 10, 200000))).astype(np.float32)
+    for y in (v, r):
+        clamped = np.clip(y, -448.0, 448.0)
+        want = torch.from_numpy(clamped).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = O.e4m3_encode(y)
+        # torch keeps the sign of -0 as 0x80 as well
+        assert np.array_equal(got, want)
+
+
+def exact_nearest(grid, a):
+    """Brute force over a grid with Fractions; ties go to the even index."""
+    a = Fraction(a)
+    best = None
+    for i, g in enumerate(grid):
+        d = abs(a - Fraction(g))
+        if best is None or d < best[0] or (d == best[0] and i % 2 == 0):
+            best = (d, i)
+    return best[1]
+
+
+def test_e2m1_brute_force_on_all_bf16_in_range():
+    v = all_finite_bf16()
+    v = v[np.abs(v) <= 8.0]
+    got = O.e2m1_encode(v)
+    for x, c in zip(v.tolist(), got.tolist()):
+        assert c & 7 == exact_nearest([0, 0.5, 1, 1.5, 2, 3, 4, 6], abs(x))
+        assert (c >> 3) == (1 if math.copysign(1.0, x) < 0 else 0)
+    assert np.all(O.e2m1_encode(np.array([7.0, 100.0, -1e30])) & 7 == 7)
+
+
+def test_e2m1_midpoints_from_definition():
+    mids = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for y, c in mids.items():
+        assert O.e2m1_encode(np.array([y]))[0] == c
+        assert O.e2m1_encode(np.array([-y]))[0] == c | 8
+
+
+def test_e4m3_grid_definition():
+    g = O.E4M3_GRID
+    assert g[0x7E] == 448.0 and g[0x08] == 2.0 ** -6 and g[0x01] == 2.0 ** -9 and g[0x38] == 1.0
+    assert np.all(np.diff(g) > 0)
+    codes = np.arange(0x7F)
+    assert np.array_equal(O.e4m3_encode(g), codes)              # idempotent on the grid
+    assert np.array_equal(O.e4m3_encode(-g), codes | 0x80)
+
+
+def test_int_rtn_brute_force():
+    rng = np.random.default_rng(1)
+    y = np.concatenate([np.arange(-20, 20.5, 0.5), rng.standard_normal(2000) * 10])
+    for b in (2, 3, 4, 8):
+        qmax = 2 ** (b - 1) - 1
+        got = O.int_rtn_codes(y, b)
+        for yy, c in zip(y.tolist(), got.tolist()):
+            grid = list(range(-qmax, qmax + 1))
+            # nearest integer in range, ties to the even integer
+            f = Fraction(yy)
+            best = min(grid, key=lambda q: (abs(f - q), q % 2))
+            assert c == best
+
+
+def test_mxfp4_scale_rule():
+    # power-of-two scale: amax in [2^(e+2), 2^(e+3)) gives code e + 127
+    for e in (-10, -1, 0, 3, 20):
+        for frac in (1.0, 1.5, 1.9921875):
+            row = np.zeros(32)
+            row[5] = frac * 2.0 ** (e + 2)
+            _, sc = O.quantize_mxfp4(bf16([row.tolist()]), O.BF16)
+            assert sc[0, 0] == e + 127
+
+
+def test_tiny_rows_zero_coded():
+    t = 2.0 ** -130                                    # subnormal bf16, amax < 2^-64
+    raw = bf16([[t, -t, 0, 0, 0, 0, 0, 2.0 ** -70]])
+    c, s = O.quantize_rows(raw, O.BF16, O.QSpec("int", 8))
+    assert np.all(c == 0) and s[0] == 0.0
+    c, s = O.quantize_rows(raw, O.BF16, O.QSpec("fp8"))
+    assert np.array_equal(c[0], hexs(["0x00", "0x80", "0x00", "0x00", "0x00", "0x00", "0x00", "0x00"]))
+
+
+def test_col_l2norm_closed_form():
+    # columns built so the norm is known exactly: 3-4-5 and constant columns
+    x = np.zeros((16, 8))
+    x[0, 0], x[1, 0] = 3.0, 4.0
+    x[:, 1] = 0.5
+    x[:, 2] = -2.0
+    x[::2, 3] = 1.0
+    raw = bf16(x)
+    n = O.col_l2norm(raw, O.BF16)
+    assert n.dtype == np.float32
+    assert n[0] == 5.0 and n[1] == 2.0 and n[2] == 8.0 and n[4] == 0.0
+    assert n[3] == np.float32(math.sqrt(8.0))
