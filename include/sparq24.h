@@ -1,0 +1,212 @@
+/*
+ * sparq24 — online 2:4 prune-and-compress, dense quantizers and the energy
+ * reductions that compare them, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow Xiuyi Qin, "Is 2:4 Sparsity Still Worth It?
+ * Semi-Structured Sparsity versus Quantization in LLM Inference"
+ * (arXiv 2610.28947) as summarised on the paper-daily.com English page,
+ * cited below as [PD §n] (n = the section number on that page).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ * Operand.  A sparq24_tensor describes B x R vectors of length K along the
+ *   GEMM reduction axis ("rows"); the hardware forms its groups of four along
+ *   that axis [PD §1].  Element (b, r, k) lives at
+ *   data + b*batch_stride + r*row_stride + k*k_stride   (strides in elements).
+ *   Two layouts are accepted:
+ *     K-contiguous: k_stride == 1 (e.g. X [tokens, hidden], W [out, in],
+ *                   Q/K [heads*seq, head_dim], P [heads*q, keys]);
+ *     transposed:   row_stride == 1 and k_stride >= R (e.g. V [heads, seq,
+ *                   head_dim] pruned along seq: B = heads, R = head_dim,
+ *                   K = seq, k_stride = head_dim).  Only
+ *                   sparq24_prune_compress accepts it; the other calls
+ *                   return SPARQ24_ERR_UNSUPPORTED for it.
+ *   K must be a multiple of 8 (two groups fill one metadata byte).
+ * Outputs.  Always dense and K-contiguous, row-major over (b, r):
+ *   kept values / kept codes [B][R][K/2], metadata [B][R][K/8],
+ *   per-row scales [B][R], dense codes [B][R][K] (or [B][R][K/2] packed).
+ * Memory.  Every array pointer is DEVICE memory owned by the caller, which
+ *   must keep it alive until the stream work completes.  Inputs and outputs
+ *   must not overlap.  The library allocates nothing and keeps no state
+ *   between calls; calls are safe from several host threads.
+ * Alignment.  data, outputs and workspace must be 16-byte aligned, and
+ *   batch_stride/row_stride (K-contiguous) or k_stride/batch_stride
+ *   (transposed) times the element size must be multiples of 16 bytes
+ *   whenever that dimension has more than one entry.
+ * Streams.  Work is enqueued on `stream` (NULL = the default stream) and the
+ *   call returns without synchronising.  A fault during execution surfaces at
+ *   the caller's next synchronisation.
+ * Workspace.  Calls taking (ws, ws_bytes): with ws == NULL the call stores
+ *   the bytes it needs in *ws_bytes, returns SPARQ24_OK and enqueues
+ *   nothing; otherwise *ws_bytes must be at least that many.
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ *   on any error nothing is enqueued.  No call aborts or throws.
+ * Rounding.  Every fp32 step named below is one IEEE-754 single-precision
+ *   operation (round to nearest even, subnormals kept).
+ */
+#ifndef SPARQ24_H
+#define SPARQ24_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARQ24_OK = 0,
+  SPARQ24_ERR_INVALID = 1,     /* null pointer, negative size, unknown enum value */
+  SPARQ24_ERR_UNSUPPORTED = 2, /* dtype / format / bits / layout not offered by this call */
+  SPARQ24_ERR_SHAPE = 3,       /* K % 8 (K % 32 for MXFP4, K % 16 for NVFP4), K too large, bad block size */
+  SPARQ24_ERR_ALIGN = 4,       /* 16-byte alignment of a pointer or stride */
+  SPARQ24_ERR_WORKSPACE = 5,   /* *ws_bytes smaller than required, or ws_bytes == NULL */
+  SPARQ24_ERR_DEVICE = 6,      /* no usable HIP device */
+  SPARQ24_ERR_LAUNCH = 7       /* the HIP runtime rejected a kernel launch */
+} sparq24_status;
+
+typedef enum { SPARQ24_F32 = 0, SPARQ24_BF16 = 1, SPARQ24_F16 = 2 } sparq24_dtype;
+
+typedef struct {
+  const void* data;
+  int32_t dtype; /* sparq24_dtype */
+  int64_t batch, rows, k;
+  int64_t batch_stride, row_stride, k_stride; /* in elements */
+} sparq24_tensor;
+
+/* Pruning score [PD §2, the 2:4 side's pruners]: magnitude |x|, or Wanda
+ * |w| * n_k with n_k the L2 norm of input channel k (an fp32 array of K
+ * entries supplied by the caller, e.g. from sparq24_col_l2norm).  The Wanda
+ * product is formed exactly (in fp64). */
+typedef enum { SPARQ24_SCORE_MAGNITUDE = 0, SPARQ24_SCORE_WANDA = 1 } sparq24_score;
+
+/* Quantization formats [PD §2-§3]:
+ *  NONE  keep the storage type (the 2:4 side at 16 bits);
+ *  INT   symmetric b-bit round-to-nearest-even, one scale per row,
+ *        qmax = 2^(b-1)-1, s = fp32(amax/qmax), code = clamp(rne(fp32(x *
+ *        fp32(qmax/amax))), -qmax, qmax); codes int8 for b <= 8, int16 above;
+ *  FP8   OCP e4m3 of fp32(x * fp32(448/amax)), RNE, saturating at 448, sign
+ *        copied; one fp32 scale s = fp32(amax/448) per row; uint8 codes;
+ *  MXFP4 E2M1 codes with one E8M0 scale per 32 elements, 2^e with
+ *        e = floor(log2 amax_blk) - 2 clamped to [-127,127];
+ *  NVFP4 E2M1 codes with one e4m3 scale per 16 elements plus an fp32 tensor
+ *        scale s_t = fp32(T/2688), T the tensor's absolute maximum; block
+ *        code = e4m3(fp32(amax_blk * fp32(448/T))), elements are E2M1 of
+ *        fp32(x * fp32(1/fp32(bval*s_t))).
+ * E2M1 is RNE and saturating at 6 with the sign copied; two codes per byte,
+ * element 2j in the low nibble.  A row (INT/FP8) or tensor (NVFP4) whose
+ * absolute maximum is below 2^-64 gets scale 0 and zero codes. */
+typedef enum {
+  SPARQ24_Q_NONE = 0,
+  SPARQ24_Q_INT = 1,
+  SPARQ24_Q_FP8_E4M3 = 2,
+  SPARQ24_Q_MXFP4 = 3,
+  SPARQ24_Q_NVFP4 = 4
+} sparq24_qfmt;
+
+typedef struct {
+  int32_t fmt;                 /* sparq24_qfmt */
+  int32_t bits;                /* INT: 2..16; ignored otherwise */
+  const float* tensor_amax_in; /* NVFP4: device pointer to T, or NULL to compute T */
+} sparq24_qspec;
+
+/* Largest K accepted by the calls that need a whole row at once
+ * (prune_quantize, quantize INT/FP8, error_energy, predict_R). */
+#define SPARQ24_MAX_ROW_K 32768
+/* Largest number of quantizer pairs of one sparq24_predict_R call. */
+#define SPARQ24_MAX_PAIRS 16
+
+/* Online 2:4 prune-and-compress [PD §3, the fused online kernel; PD intro:
+ * two of every four kept along the reduction axis].
+ * In every aligned group of four along K, keep the two elements with the
+ * largest score (ties keep the lower position).  values [B][R][K/2] receives
+ * the kept elements in the input's storage type, in position order;
+ * meta [B][R][K/8] receives per group the nibble (i0 | i1 << 2), group 2j in
+ * the low nibble of byte j.  col_norm: NULL for magnitude, [K] fp32 for
+ * Wanda.  Reads the operand once and writes each output once. */
+sparq24_status sparq24_prune_compress(const sparq24_tensor* x, int32_t score,
+                                      const float* col_norm, void* values,
+                                      uint8_t* meta, hipStream_t stream);
+
+/* Dense online quantization [PD §2: the quantized side pays its online
+ * quantization; PD §3: INT8 with one scale per row, FP8, MXFP4, NVFP4].
+ * INT/FP8: codes [B][R][K], scales fp32 [B][R].
+ * MXFP4:   codes uint8 [B][R][K/2], scales uint8 E8M0 [B][R][K/32].
+ * NVFP4:   codes uint8 [B][R][K/2], scales uint8 e4m3 [B][R][K/16], and
+ *          tensor_scale_out (device, 1 fp32) receives s_t.
+ * Workspace: NVFP4 without tensor_amax_in needs a few KB; others need none. */
+sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
+                                void* codes, void* scales, float* tensor_scale_out,
+                                void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* Fused online prune + compress + quantize of the kept values [PD §4: the
+ * 2:4 side quantizes its kept values to 2m bits; PD §5: 2:4 stacked on FP8].
+ * Same selection and metadata as sparq24_prune_compress; the kept values of
+ * each row are quantized (INT or FP8) with one scale per row taken from the
+ * absolute maximum of that row's kept values.  codes [B][R][K/2],
+ * meta [B][R][K/8], scales fp32 [B][R].  One read, one write per output.
+ * Needs no workspace (ws may be NULL with *ws_bytes set to 0 by a query). */
+sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score,
+                                      const float* col_norm, const sparq24_qspec* q,
+                                      void* codes, uint8_t* meta, float* scales,
+                                      void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* Error energies of both sides [PD §4].
+ * For each block of rows_per_block consecutive rows (flattened over (b, r);
+ * 0 = the whole operand; the last block may be shorter), out[blk][4] fp64 =
+ *   { sum x^2, sum of dropped x^2, sum over kept elements of (x - xhat)^2
+ *     under kept_q, sum over all elements of (x - xhat)^2 under dense_q }.
+ * kept_q: NONE, INT or FP8.  dense_q: INT, FP8, MXFP4 or NVFP4 (NVFP4's T is
+ * over the whole operand).  Sums are accumulated in fp64 in a fixed order,
+ * so repeated calls give identical bits. */
+sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score,
+                                    const float* col_norm, const sparq24_qspec* kept_q,
+                                    const sparq24_qspec* dense_q, int64_t rows_per_block,
+                                    double* out, void* ws, size_t* ws_bytes,
+                                    hipStream_t stream);
+
+/* Predicted R [PD §4]: for every block and pair p (kept_q[p] vs dense_q[p]),
+ * out[blk][p][5] fp64 = { E_prune, E_qkept, E_2:4, E_dense, R } with
+ * E_prune = dropped energy / total, E_qkept = kept error / total,
+ * E_2:4 = E_prune + E_qkept (disjoint elements, so the energies add),
+ * E_dense = dense error / total and R = sqrt(E_2:4 / E_dense); IEEE fp64
+ * division (0/0 = NaN, x/0 = inf).  1 <= npairs <= SPARQ24_MAX_PAIRS.
+ * Equal quantizers appearing in several pairs are evaluated once. */
+sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score,
+                                 const float* col_norm, const sparq24_qspec* kept_q,
+                                 const sparq24_qspec* dense_q, int32_t npairs,
+                                 int64_t rows_per_block, double* out, void* ws,
+                                 size_t* ws_bytes, hipStream_t stream);
+
+/* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
+ * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in
+ * fp64, then rounded once.  x is an activation [tokens, channels] given with
+ * rows = tokens and k = channels (K-contiguous).  Workspace: a few hundred KB. */
+sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
+                                  size_t* ws_bytes, hipStream_t stream);
+
+/* Plain device copy of `bytes` bytes (16-byte aligned, bytes % 16 == 0): the
+ * read-once/write-once bandwidth baseline the prune kernels are compared to. */
+sparq24_status sparq24_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Storage bits per original element [PD §2: values, position indices and
+ * scales are all charged].  Host-only arithmetic; no device needed.
+ * sparse24 = 0: dense q; = 1: 2:4 with kept values in q.  row_len: elements
+ * sharing one per-row scale (INT/FP8), 0 to leave scales out.  value_bits:
+ * width for SPARQ24_Q_NONE.  tensor_elems: NVFP4 tensor size, 0 to leave its
+ * scale out.  Returns a negative value for an invalid spec. */
+double sparq24_bits_per_element(const sparq24_qspec* q, int32_t sparse24, int64_t row_len,
+                                int32_t value_bits, int64_t tensor_elems);
+
+/* Static text for a status code. */
+const char* sparq24_status_string(sparq24_status s);
+
+/* Library version as "major.minor.patch". */
+const char* sparq24_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARQ24_H */

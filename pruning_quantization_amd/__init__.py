@@ -1,0 +1,23 @@
+"""sparq24 for MI355X: online 2:4 prune-and-compress, dense quantizers and the
+energy reductions that score them (Qin, "Is 2:4 Sparsity Still Worth It?").
+
+The compute lives in ``libsparq24.so`` (HIP kernels for gfx950 behind a C
+ABI, see ``include/sparq24.h``); :mod:`.binding` marshals torch tensors into
+it.  Build with ``python -m pruning_quantization_amd.build``.
+"""
+from .binding import (  # noqa: F401
+    Sparq24Error,
+    SYMBOLS,
+    bits_per_element,
+    col_l2norm,
+    copy,
+    describe,
+    error_energy,
+    lib,
+    predict_R,
+    prune_compress,
+    prune_quantize,
+    qspec,
+    quantize,
+    version,
+)

@@ -1,0 +1,440 @@
+// C-ABI entry points of libsparq24: argument validation (pure host code, run
+// before any HIP call), variant selection, workspace sizing and launches on
+// the caller's stream.  The operations are those of Qin, "Is 2:4 Sparsity
+// Still Worth It?" (paper-daily.com English summary, sections 2-4); see
+// include/sparq24.h for the contract of each call.
+#include "sparq24.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+using namespace sparq24;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(int dtype) { return dtype == SPARQ24_F32 ? 4 : 2; }
+
+// Structural checks of an operand; fills the kernel view (strides in bytes,
+// back-to-back batches folded into rows).
+sparq24_status check_tensor(const sparq24_tensor* x, bool allow_transposed, RowDesc& d) {
+  if (!x) return SPARQ24_ERR_INVALID;
+  if (x->dtype != SPARQ24_F32 && x->dtype != SPARQ24_BF16 && x->dtype != SPARQ24_F16)
+    return SPARQ24_ERR_INVALID;
+  if (x->batch < 0 || x->rows < 0 || x->k < 0) return SPARQ24_ERR_INVALID;
+  if (x->batch_stride < 0 || x->row_stride < 0 || x->k_stride < 0) return SPARQ24_ERR_INVALID;
+  if (x->k % 8 != 0) return SPARQ24_ERR_SHAPE;
+  const int es = esize(x->dtype);
+  d.x = (const char*)x->data;
+  d.dtype = x->dtype;
+  d.B = x->batch;
+  d.R = x->rows;
+  d.K = x->k;
+  if (d.B * d.R * d.K == 0) {  // empty: nothing to read
+    d.kcontig = true;
+    d.flat = true;
+    d.bs = d.rs = d.ks = 0;
+    return SPARQ24_OK;
+  }
+  if (!x->data) return SPARQ24_ERR_INVALID;
+  if (!aligned16(x->data)) return SPARQ24_ERR_ALIGN;
+  if (x->k_stride == 1 || x->k == 1) {
+    d.kcontig = true;
+    if (d.R > 1 && x->row_stride < d.K) return SPARQ24_ERR_UNSUPPORTED;
+    if (d.B > 1 && x->batch_stride < (d.R - 1) * x->row_stride + d.K) return SPARQ24_ERR_UNSUPPORTED;
+    if (d.R > 1 && (x->row_stride * es) % 16) return SPARQ24_ERR_ALIGN;
+    if (d.B > 1 && (x->batch_stride * es) % 16) return SPARQ24_ERR_ALIGN;
+    int64_t rs = d.R > 1 ? x->row_stride : d.K;
+    int64_t bs = d.B > 1 ? x->batch_stride : d.R * rs;
+    if (d.B > 1 && bs == d.R * rs) {  // batches back to back: fold into rows
+      d.R *= d.B;
+      d.B = 1;
+      bs = d.R * rs;
+    }
+    d.rs = rs * es;
+    d.bs = bs * es;
+    d.ks = es;
+    d.flat = (rs == d.K) && d.B == 1;
+  } else if (x->row_stride == 1 || d.R == 1) {
+    if (!allow_transposed) return SPARQ24_ERR_UNSUPPORTED;
+    if (x->k_stride < d.R) return SPARQ24_ERR_UNSUPPORTED;
+    if (d.B > 1 && x->batch_stride < (d.K - 1) * x->k_stride + d.R) return SPARQ24_ERR_UNSUPPORTED;
+    if ((x->k_stride * es) % 16) return SPARQ24_ERR_ALIGN;
+    if (d.B > 1 && (x->batch_stride * es) % 16) return SPARQ24_ERR_ALIGN;
+    d.kcontig = false;
+    d.flat = false;
+    d.rs = es;
+    d.ks = x->k_stride * es;
+    d.bs = (d.B > 1 ? x->batch_stride : d.K * x->k_stride) * es;
+  } else {
+    return SPARQ24_ERR_UNSUPPORTED;
+  }
+  if (d.B > 65535) return SPARQ24_ERR_UNSUPPORTED;
+  return SPARQ24_OK;
+}
+
+sparq24_status check_score(int32_t score, const float* col_norm) {
+  if (score != SPARQ24_SCORE_MAGNITUDE && score != SPARQ24_SCORE_WANDA) return SPARQ24_ERR_INVALID;
+  if (score == SPARQ24_SCORE_WANDA) {
+    if (!col_norm) return SPARQ24_ERR_INVALID;
+    if (!aligned16(col_norm)) return SPARQ24_ERR_ALIGN;
+  }
+  return SPARQ24_OK;
+}
+
+// Quantizer spec -> code container and qmax.  `allowed` is a bit set of
+// sparq24_qfmt values the call accepts.
+sparq24_status check_q(const sparq24_qspec* q, unsigned allowed, int& cfmt, float& qmax) {
+  if (!q) return SPARQ24_ERR_INVALID;
+  if (q->fmt < SPARQ24_Q_NONE || q->fmt > SPARQ24_Q_NVFP4) return SPARQ24_ERR_INVALID;
+  if (!(allowed & (1u << q->fmt))) return SPARQ24_ERR_UNSUPPORTED;
+  switch (q->fmt) {
+    case SPARQ24_Q_NONE: cfmt = CF_NONE; qmax = 0.f; break;
+    case SPARQ24_Q_INT:
+      if (q->bits < 2 || q->bits > 16) return SPARQ24_ERR_UNSUPPORTED;
+      cfmt = q->bits <= 8 ? CF_INT8 : CF_INT16;
+      qmax = (float)((1 << (q->bits - 1)) - 1);
+      break;
+    case SPARQ24_Q_FP8_E4M3: cfmt = CF_FP8; qmax = 448.f; break;
+    case SPARQ24_Q_MXFP4: cfmt = CF_MX; qmax = 6.f; break;
+    case SPARQ24_Q_NVFP4:
+      cfmt = CF_NV; qmax = 6.f;
+      if (q->tensor_amax_in && ((uintptr_t)q->tensor_amax_in & 3u)) return SPARQ24_ERR_ALIGN;
+      break;
+  }
+  return SPARQ24_OK;
+}
+
+// Workspace protocol shared by the calls.
+sparq24_status workspace(void* ws, size_t* ws_bytes, size_t need, bool& query) {
+  if (!ws_bytes) return SPARQ24_ERR_WORKSPACE;
+  if (!ws) {
+    *ws_bytes = need;
+    query = true;
+    return SPARQ24_OK;
+  }
+  query = false;
+  if (*ws_bytes < need) return SPARQ24_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SPARQ24_ERR_ALIGN;
+  return SPARQ24_OK;
+}
+
+sparq24_status device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SPARQ24_ERR_DEVICE;
+  }
+  return SPARQ24_OK;
+}
+
+sparq24_status launched(hipError_t e) {
+  if (e == hipSuccess) return SPARQ24_OK;
+  (void)hipGetLastError();
+  return SPARQ24_ERR_LAUNCH;
+}
+
+#define CHECK(expr)                              \
+  do {                                           \
+    sparq24_status _st = (expr);                 \
+    if (_st != SPARQ24_OK) return _st;           \
+  } while (0)
+
+// Energy-call planning: unique kept/dense quantizers, pair columns, workspace.
+struct EnergyPlan {
+  EnergyParams p;
+  FinalizeParams f;
+  const float* nv_in = nullptr;
+  bool need_nv_partials = false;
+  int nparts = 0;
+  int64_t nrows = 0, rpb = 0, nblk = 0;
+  size_t off_rowpart = 0, off_parts = 0, need = 0;
+};
+
+sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
+                           const sparq24_qspec* dense_q, int npairs, int64_t rows_per_block,
+                           EnergyPlan& pl) {
+  memset(&pl.p, 0, sizeof(pl.p));
+  memset(&pl.f, 0, sizeof(pl.f));
+  const sparq24_qspec* kept_u[kMaxQ];
+  const sparq24_qspec* dense_u[kMaxQ];
+  int nk = 0, nd = 0;
+  const unsigned kept_ok = (1u << SPARQ24_Q_NONE) | (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3);
+  const unsigned dense_ok = kept_ok | (1u << SPARQ24_Q_MXFP4) | (1u << SPARQ24_Q_NVFP4);
+  auto same = [](const sparq24_qspec* a, const sparq24_qspec* b) {
+    return a->fmt == b->fmt && (a->fmt != SPARQ24_Q_INT || a->bits == b->bits) &&
+           (a->fmt != SPARQ24_Q_NVFP4 || a->tensor_amax_in == b->tensor_amax_in);
+  };
+  for (int i = 0; i < npairs; ++i) {
+    int cf;
+    float qm;
+    CHECK(check_q(&kept_q[i], kept_ok, cf, qm));
+    CHECK(check_q(&dense_q[i], dense_ok, cf, qm));
+    if (dense_q[i].fmt == SPARQ24_Q_MXFP4 && d.K % 32) return SPARQ24_ERR_SHAPE;
+    if (dense_q[i].fmt == SPARQ24_Q_NVFP4 && d.K % 16) return SPARQ24_ERR_SHAPE;
+  }
+  for (int i = 0; i < npairs; ++i) {
+    int ki = -1, di = -1;
+    for (int j = 0; j < nk; ++j)
+      if (same(kept_u[j], &kept_q[i])) ki = j;
+    if (ki < 0) { kept_u[nk] = &kept_q[i]; ki = nk++; }
+    for (int j = 0; j < nd; ++j)
+      if (same(dense_u[j], &dense_q[i])) di = j;
+    if (di < 0) { dense_u[nd] = &dense_q[i]; di = nd++; }
+    pl.f.kcol[i] = 2 + ki;
+    pl.f.dcol[i] = di;  // fixed up below once nk is known
+  }
+  int n_nv = 0;
+  for (int j = 0; j < nk; ++j) {
+    float qm;
+    int cf;
+    check_q(kept_u[j], kept_ok, cf, qm);
+    pl.p.kept.fmt[j] = cf;
+    pl.p.kept.qmax[j] = qm;
+  }
+  for (int j = 0; j < nd; ++j) {
+    float qm;
+    int cf;
+    check_q(dense_u[j], dense_ok, cf, qm);
+    pl.p.dense.fmt[j] = cf;
+    pl.p.dense.qmax[j] = qm;
+    if (cf == CF_NV) {
+      ++n_nv;
+      pl.nv_in = dense_u[j]->tensor_amax_in;
+    }
+  }
+  if (n_nv > 1) return SPARQ24_ERR_UNSUPPORTED;
+  pl.p.kept.n = nk;
+  pl.p.dense.n = nd;
+  for (int i = 0; i < npairs; ++i) pl.f.dcol[i] += 2 + nk;
+  pl.f.ncols = 2 + nk + nd;
+  pl.f.npairs = npairs;
+  pl.nrows = d.B * d.R;
+  pl.rpb = rows_per_block == 0 ? pl.nrows : rows_per_block;
+  pl.nblk = (pl.nrows + pl.rpb - 1) / pl.rpb;
+  pl.need_nv_partials = n_nv == 1 && pl.nv_in == nullptr;
+  pl.nparts = pl.need_nv_partials ? absmax_partial_count(d) : 0;
+  const size_t rowpart = (size_t)pl.f.ncols * (size_t)pl.nrows * sizeof(double);
+  const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk * sizeof(double);
+  pl.off_rowpart = 0;
+  pl.off_parts = round_up(rowpart + sums, kAlign);
+  pl.need = pl.off_parts + round_up((size_t)pl.nparts * sizeof(uint32_t), kAlign);
+  return SPARQ24_OK;
+}
+
+sparq24_status run_energy(const RowDesc& d, int32_t score, const float* col_norm, EnergyPlan& pl,
+                          double* out, void* ws, hipStream_t stream) {
+  char* w = (char*)ws;
+  double* rowpart = (double*)(w + pl.off_rowpart);
+  uint32_t* parts = (uint32_t*)(w + pl.off_parts);
+  if (pl.need_nv_partials) {
+    CHECK(launched(launch_absmax_partials(d, parts, stream)));
+    pl.p.nv_partials = parts;
+    pl.p.n_partials = pl.nparts;
+  }
+  pl.p.nv_tamax = pl.nv_in;
+  CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart, stream)));
+  return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, out, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+sparq24_status sparq24_prune_compress(const sparq24_tensor* x, int32_t score, const float* col_norm,
+                                      void* values, uint8_t* meta, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, true, d));
+  CHECK(check_score(score, col_norm));
+  if (d.B * d.R * d.K == 0) return SPARQ24_OK;
+  if (!values || !meta) return SPARQ24_ERR_INVALID;
+  if (!aligned16(values) || !aligned16(meta)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_prune_compress(d, score == SPARQ24_SCORE_WANDA, col_norm, values, meta, stream));
+}
+
+sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q, void* codes,
+                                void* scales, float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  int cfmt;
+  float qmax;
+  CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
+                       (1u << SPARQ24_Q_NVFP4),
+                cfmt, qmax));
+  if (cfmt == CF_MX && d.K % 32) return SPARQ24_ERR_SHAPE;
+  if (cfmt == CF_NV && d.K % 16) return SPARQ24_ERR_SHAPE;
+  if ((cfmt == CF_INT8 || cfmt == CF_INT16 || cfmt == CF_FP8) && d.K / 8 > kMaxRowUnits)
+    return SPARQ24_ERR_SHAPE;
+  const bool nv_parts = cfmt == CF_NV && q->tensor_amax_in == nullptr;
+  const int nparts = nv_parts ? absmax_partial_count(d) : 0;
+  const size_t need = round_up((size_t)nparts * sizeof(uint32_t), kAlign);
+  bool query;
+  CHECK(workspace(ws, ws_bytes, need, query));
+  if (query) return SPARQ24_OK;
+  if (d.B * d.R * d.K == 0) return SPARQ24_OK;
+  if (!codes || !scales) return SPARQ24_ERR_INVALID;
+  if (cfmt == CF_NV && !tensor_scale_out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(codes) || !aligned16(scales)) return SPARQ24_ERR_ALIGN;
+  if (cfmt == CF_NV && ((uintptr_t)tensor_scale_out & 3u)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  if (cfmt == CF_MX) return launched(launch_quant_mx(d, codes, (uint8_t*)scales, stream));
+  if (cfmt == CF_NV) {
+    uint32_t* parts = (uint32_t*)ws;
+    if (nv_parts) CHECK(launched(launch_absmax_partials(d, parts, stream)));
+    return launched(launch_quant_nv(d, q->tensor_amax_in, parts, nparts, codes, (uint8_t*)scales,
+                                    tensor_scale_out, stream));
+  }
+  return launched(launch_quant_rows(d, cfmt, qmax, codes, (float*)scales, stream));
+}
+
+sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, const float* col_norm,
+                                      const sparq24_qspec* q, void* codes, uint8_t* meta,
+                                      float* scales, void* ws, size_t* ws_bytes,
+                                      hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  CHECK(check_score(score, col_norm));
+  int cfmt;
+  float qmax;
+  CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3), cfmt, qmax));
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  bool query;
+  if (ws_bytes || ws) CHECK(workspace(ws, ws_bytes, 0, query));
+  else query = false;
+  if (query) return SPARQ24_OK;
+  if (d.B * d.R * d.K == 0) return SPARQ24_OK;
+  if (!codes || !meta || !scales) return SPARQ24_ERR_INVALID;
+  if (!aligned16(codes) || !aligned16(meta) || !aligned16(scales)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_prune_quantize(d, score == SPARQ24_SCORE_WANDA, col_norm, cfmt, qmax,
+                                        codes, meta, scales, stream));
+}
+
+sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score, const float* col_norm,
+                                    const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
+                                    int64_t rows_per_block, double* out, void* ws,
+                                    size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  CHECK(check_score(score, col_norm));
+  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
+  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
+  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  EnergyPlan pl;
+  CHECK(plan_energy(d, kept_q, dense_q, 1, rows_per_block, pl));
+  pl.f.mode = 0;
+  bool query;
+  CHECK(workspace(ws, ws_bytes, pl.need, query));
+  if (query) return SPARQ24_OK;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return run_energy(d, score, col_norm, pl, out, ws, stream);
+}
+
+sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score, const float* col_norm,
+                                 const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
+                                 int32_t npairs, int64_t rows_per_block, double* out, void* ws,
+                                 size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  CHECK(check_score(score, col_norm));
+  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
+  if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
+  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
+  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  EnergyPlan pl;
+  CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
+  pl.f.mode = 1;
+  bool query;
+  CHECK(workspace(ws, ws_bytes, pl.need, query));
+  if (query) return SPARQ24_OK;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return run_energy(d, score, col_norm, pl, out, ws, stream);
+}
+
+sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
+                                  size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  const size_t need = round_up((size_t)col_strips(d) * (size_t)d.K * sizeof(double), kAlign);
+  bool query;
+  CHECK(workspace(ws, ws_bytes, need, query));
+  if (query) return SPARQ24_OK;
+  if (d.K == 0) return SPARQ24_OK;
+  if (!norms) return SPARQ24_ERR_INVALID;
+  if (!aligned16(norms)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_col_l2norm(d, (double*)ws, norms, stream));
+}
+
+sparq24_status sparq24_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return SPARQ24_OK;
+  if (!src || !dst) return SPARQ24_ERR_INVALID;
+  if (!aligned16(src) || !aligned16(dst) || bytes % 16) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_copy(src, dst, bytes, stream));
+}
+
+double sparq24_bits_per_element(const sparq24_qspec* q, int32_t sparse24, int64_t row_len,
+                                int32_t value_bits, int64_t tensor_elems) {
+  if (!q || row_len < 0 || tensor_elems < 0) return -1.0;
+  double v, scale;
+  switch (q->fmt) {
+    case SPARQ24_Q_INT:
+      if (q->bits < 2 || q->bits > 16) return -1.0;
+      v = q->bits;
+      scale = row_len ? 32.0 / (double)row_len : 0.0;
+      break;
+    case SPARQ24_Q_FP8_E4M3:
+      v = 8;
+      scale = row_len ? 32.0 / (double)row_len : 0.0;
+      break;
+    case SPARQ24_Q_NONE:
+      if (value_bits <= 0) return -1.0;
+      v = value_bits;
+      scale = 0.0;
+      break;
+    case SPARQ24_Q_MXFP4:
+      v = 4;
+      scale = 8.0 / 32.0;
+      break;
+    case SPARQ24_Q_NVFP4:
+      v = 4;
+      scale = 8.0 / 16.0 + (tensor_elems ? 32.0 / (double)tensor_elems : 0.0);
+      break;
+    default:
+      return -1.0;
+  }
+  // 2:4 keeps half the values and spends 2 position bits per kept value
+  return sparse24 ? v / 2.0 + 1.0 + scale : v + scale;
+}
+
+const char* sparq24_status_string(sparq24_status s) {
+  switch (s) {
+    case SPARQ24_OK: return "ok";
+    case SPARQ24_ERR_INVALID: return "invalid argument";
+    case SPARQ24_ERR_UNSUPPORTED: return "unsupported dtype, format, bits or layout";
+    case SPARQ24_ERR_SHAPE: return "unsupported shape";
+    case SPARQ24_ERR_ALIGN: return "misaligned pointer or stride";
+    case SPARQ24_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPARQ24_ERR_DEVICE: return "no usable HIP device";
+    case SPARQ24_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* sparq24_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Compile-time variant dispatch for the row kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sparq24 {
+
+// Storage-type dispatch: f.template operator()<DT>().
+template <class F>
+inline hipError_t with_dtype(int dtype, F&& f) {
+  switch (dtype) {
+    case 0: return f.template operator()<F32T>();
+    case 1: return f.template operator()<BF16T>();
+    case 2: return f.template operator()<F16T>();
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Team shape for kernels that keep a whole row in registers: the smallest
+// (TEAM lanes, UPL units per lane) with TEAM * UPL >= units of the row.
+template <class F>
+inline hipError_t with_row_variant(int64_t nunits, F&& f) {
+  if (nunits <= 16) return f.template operator()<16, 1>();
+  if (nunits <= 32) return f.template operator()<32, 1>();
+  if (nunits <= 64) return f.template operator()<64, 1>();
+  if (nunits <= 128) return f.template operator()<64, 2>();
+  if (nunits <= 256) return f.template operator()<64, 4>();
+  if (nunits <= 512) return f.template operator()<64, 8>();
+  if (nunits <= 1024) return f.template operator()<64, 16>();
+  if (nunits <= 2048) return f.template operator()<256, 8>();
+  if (nunits <= 4096) return f.template operator()<256, 16>();
+  return hipErrorInvalidValue;
+}
+
+// Team shape for kernels that stream a row in chunks (no whole-row state).
+template <class F>
+inline hipError_t with_loop_variant(int64_t nunits, F&& f) {
+  if (nunits <= 16) return f.template operator()<16, 1>();
+  if (nunits <= 32) return f.template operator()<32, 1>();
+  if (nunits <= 64) return f.template operator()<64, 1>();
+  if (nunits <= 128) return f.template operator()<64, 2>();
+  if (nunits <= 256) return f.template operator()<64, 4>();
+  return f.template operator()<64, 8>();
+}
+
+inline dim3 row_grid(const RowDesc& d, int team) {
+  const int64_t rpb = kBlock / team;
+  return dim3((unsigned)((d.R + rpb - 1) / rpb), (unsigned)d.B, 1);
+}
+
+}  // namespace sparq24

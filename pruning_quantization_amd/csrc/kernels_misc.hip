@@ -1,0 +1,90 @@
+// Wanda input-channel norms and the plain-copy bandwidth baseline.
+//
+// Method: Qin, "Is 2:4 Sparsity Still Worth It?" (paper-daily.com English
+// summary), [PD §2]: Wanda ranks a weight by its magnitude times the size of
+// the activation on its input channel; here that size is the L2 norm of the
+// channel over all tokens.
+#include "dispatch.hpp"
+
+namespace sparq24 {
+
+constexpr int kColStrips = 128;
+
+int col_strips(const RowDesc& d) {
+  const int64_t rows = d.B * d.R;
+  return (int)(rows < kColStrips ? (rows > 0 ? rows : 1) : kColStrips);
+}
+
+// Stage 1: partial[strip][k] = sum over the strip's rows of x[row][k]^2 (fp64).
+// A thread owns one 8-column unit and walks the rows of its strip in order.
+template <class DT>
+__global__ __launch_bounds__(kBlock) void k_col_sumsq(const char* __restrict__ x, int64_t R,
+                                                      int64_t nunits, int64_t bs, int64_t rs,
+                                                      int64_t rows_total, int nstrips,
+                                                      double* __restrict__ partial) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int strip = blockIdx.y;
+  if (i >= nunits) return;
+  const int64_t per = (rows_total + nstrips - 1) / nstrips;
+  const int64_t r0 = (int64_t)strip * per;
+  const int64_t r1 = (r0 + per) < rows_total ? (r0 + per) : rows_total;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t row = r0; row < r1; ++row) {
+    const int64_t b = row / R, r = row % R;
+    Unit<DT> u;
+    load_unit(u, x + b * bs + r * rs + i * (8 * DT::ESIZE));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double v = (double)u.f(e);
+      acc[e] = __builtin_fma(v, v, acc[e]);
+    }
+  }
+  double* o = partial + (int64_t)strip * nunits * 8 + i * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = acc[e];
+}
+
+// Stage 2: norms[k] = fp32(sqrt(sum over strips in order)).
+__global__ __launch_bounds__(kBlock) void k_col_norm_final(const double* __restrict__ partial,
+                                                           int64_t K, int nstrips,
+                                                           float* __restrict__ norms) {
+  const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (k >= K) return;
+  double s = 0.0;
+  for (int st = 0; st < nstrips; ++st) s += partial[(int64_t)st * K + k];
+  norms[k] = (float)__builtin_sqrt(s);
+}
+
+hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  const int ns = col_strips(d);
+  hipError_t e = with_dtype(d.dtype, [&]<class DT>() {
+    hipLaunchKernelGGL((k_col_sumsq<DT>), dim3((unsigned)((nunits + kBlock - 1) / kBlock), ns),
+                       dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, d.B * d.R, ns, partial);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_col_norm_final, dim3((unsigned)((d.K + kBlock - 1) / kBlock)), dim3(kBlock),
+                     0, s, partial, d.K, ns, norms);
+  return hipGetLastError();
+}
+
+// Read-once / write-once copy of 16-byte vectors (grid-stride).
+__global__ __launch_bounds__(kBlock) void k_copy(const uint4* __restrict__ src,
+                                                 uint4* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kBlock)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  int64_t blocks = (n + kBlock - 1) / kBlock;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kBlock), 0, s, (const uint4*)src,
+                     (uint4*)dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace sparq24

@@ -1,0 +1,355 @@
+// Online 2:4 prune-and-compress and fused prune + quantize of the kept values.
+//
+// Method: Qin, "Is 2:4 Sparsity Still Worth It?" (paper-daily.com English
+// summary).  [PD §3]: a fused online kernel reads the operand once and writes
+// the kept values and their position indices once.  [PD §4]: the 2:4 side
+// quantizes the kept values (here one scale per row from their absolute
+// maximum).  This file holds the gfx950 kernels; they read 16-byte vectors,
+// select the top two of every four with integer keys in registers, gather
+// the kept pairs with byte permutes and write values, metadata and scales in
+// the same pass.
+#include "dispatch.hpp"
+
+namespace sparq24 {
+
+// ---------------------------------------------------------------------------
+// Shared per-unit work: two group selections and the kept raw values.
+// ---------------------------------------------------------------------------
+template <class DT, bool WANDA>
+__device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restrict__ norm,
+                                       int64_t k0) {
+  float n8[8];
+  if constexpr (WANDA) {
+    const float4* np = reinterpret_cast<const float4*>(norm + k0);
+    float4 a = np[0], b = np[1];
+    n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
+    n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
+  }
+  uint32_t n0 = select_group<DT, WANDA>(u, 0, n8);
+  uint32_t n1 = select_group<DT, WANDA>(u, 1, n8 + 4);
+  return n0 | (n1 << 4);
+}
+
+// Store the 4 kept raw elements of a unit (storage type) at dst.
+template <class DT>
+__device__ inline void store_kept(const Unit<DT>& u, uint32_t mb, char* dst) {
+  const uint32_t n0 = mb & 0xFu, n1 = mb >> 4;
+  if constexpr (DT::ESIZE == 2) {
+    uint2 o;
+    o.x = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(n0));
+    o.y = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(n1));
+    *reinterpret_cast<uint2*>(dst) = o;
+  } else {
+    uint4 o;
+    o.x = kept_raw(u, 0, n0, 0);
+    o.y = kept_raw(u, 0, n0, 1);
+    o.z = kept_raw(u, 1, n1, 0);
+    o.w = kept_raw(u, 1, n1, 1);
+    *reinterpret_cast<uint4*>(dst) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K-contiguous, fully contiguous operand, magnitude score: the whole tensor is
+// one run of units (rows never split a unit because K % 8 == 0, and the
+// outputs of unit i sit at i in both value and metadata arrays).
+// Each workgroup owns UPL consecutive chunks of 256 units.
+// ---------------------------------------------------------------------------
+template <class DT, int UPL>
+__global__ __launch_bounds__(kBlock) void k_prune_compress_flat(
+    const char* __restrict__ x, int64_t nunits, char* __restrict__ vals,
+    uint8_t* __restrict__ meta) {
+  const int64_t base = (int64_t)blockIdx.x * (kBlock * UPL) + threadIdx.x;
+  Unit<DT> u[UPL];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = base + (int64_t)j * kBlock;
+    if (i < nunits) load_unit(u[j], x + i * (8 * DT::ESIZE));
+    else zero_unit(u[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = base + (int64_t)j * kBlock;
+    if (i < nunits) {
+      const uint32_t mb = select_unit<DT, false>(u[j], nullptr, 0);
+      store_kept(u[j], mb, vals + i * (4 * DT::ESIZE));
+      meta[i] = (uint8_t)mb;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K-contiguous rows with arbitrary row/batch strides (or Wanda scores, which
+// need the position along K): a team of TEAM lanes walks one row in chunks of
+// TEAM * UPL units.
+// ---------------------------------------------------------------------------
+template <class DT, int TEAM, int UPL, bool WANDA>
+__global__ __launch_bounds__(kBlock) void k_prune_compress_rows(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    const float* __restrict__ norm, char* __restrict__ vals, uint8_t* __restrict__ meta) {
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  if (r >= R) return;  // no team-wide synchronisation in this kernel
+  const char* xr = x + b * bs + r * rs;
+  const int64_t orow = b * R + r;
+  char* vr = vals + orow * nunits * (4 * DT::ESIZE);
+  uint8_t* mr = meta + orow * nunits;
+  for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+    Unit<DT> u[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+      else zero_unit(u[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (i < nunits) {
+        const uint32_t mb = select_unit<DT, WANDA>(u[j], norm, i * 8);
+        store_kept(u[j], mb, vr + i * (4 * DT::ESIZE));
+        mr[i] = (uint8_t)mb;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed operand (row_stride == 1, the reduction axis strided), e.g. V
+// [heads, seq, head_dim] pruned along seq.  A workgroup stages a tile of
+// KT positions x RT rows through LDS: loads run along the contiguous row
+// axis, each thread then selects within one (row, unit) column, and the
+// compressed tile is written back K-contiguous per row.
+// ---------------------------------------------------------------------------
+constexpr int kT_KT = 128;  // positions along K per tile (16 units)
+constexpr int kT_RT = 64;   // rows per tile
+
+template <class DT, bool WANDA>
+__global__ __launch_bounds__(kBlock) void k_prune_compress_T(
+    const char* __restrict__ x, int64_t R, int64_t K, int64_t bs, int64_t ks,
+    const float* __restrict__ norm, char* __restrict__ vals, uint8_t* __restrict__ meta) {
+  constexpr int E = DT::ESIZE;
+  constexpr int UT = kT_KT / 8;                          // units per tile row
+  constexpr int OUT_ROW = kT_KT / 2 * E;                 // kept bytes per row per tile
+  constexpr int OUT_PAD = OUT_ROW + 16;
+  __shared__ __align__(16) char tile[kT_KT * kT_RT * E];  // [k][r]
+  __shared__ __align__(16) char otile[kT_RT * OUT_PAD];   // [r][kept bytes]
+  __shared__ __align__(16) uint8_t mtile[kT_RT * UT];     // [r][unit]
+
+  const int64_t k0 = (int64_t)blockIdx.x * kT_KT;
+  const int64_t r0 = (int64_t)blockIdx.y * kT_RT;
+  const int64_t b = blockIdx.z;
+  const char* xb = x + b * bs;
+  const int rcount = (int)((R - r0) < kT_RT ? (R - r0) : kT_RT);
+  const int kcount = (int)((K - k0) < kT_KT ? (K - k0) : kT_KT);  // multiple of 8
+
+  // 1) load: each tile line (one k) is rcount contiguous elements
+  for (int e = threadIdx.x; e < kT_KT * kT_RT; e += kBlock) {
+    const int kk = e / kT_RT, rr = e % kT_RT;
+    uint32_t v = 0;
+    if (kk < kcount && rr < rcount) {
+      const char* p = xb + (k0 + kk) * ks + (r0 + rr) * E;
+      if constexpr (E == 2) v = *reinterpret_cast<const uint16_t*>(p);
+      else v = *reinterpret_cast<const uint32_t*>(p);
+    }
+    if constexpr (E == 2) reinterpret_cast<uint16_t*>(tile)[e] = (uint16_t)v;
+    else reinterpret_cast<uint32_t*>(tile)[e] = v;
+  }
+  __syncthreads();
+
+  // 2) select per (row, unit)
+  for (int item = threadIdx.x; item < kT_RT * UT; item += kBlock) {
+    const int rr = item % kT_RT, uu = item / kT_RT;
+    if (rr < rcount && uu * 8 < kcount) {
+      Unit<DT> u;
+#pragma unroll
+      for (int i = 0; i < DT::W; ++i) u.w[i] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = (uu * 8 + i) * kT_RT + rr;
+        uint32_t v;
+        if constexpr (E == 2) {
+          v = reinterpret_cast<const uint16_t*>(tile)[e];
+          u.w[i >> 1] |= v << ((i & 1) * 16);
+        } else {
+          v = reinterpret_cast<const uint32_t*>(tile)[e];
+          u.w[i] = v;
+        }
+      }
+      const uint32_t mb = select_unit<DT, WANDA>(u, norm, k0 + uu * 8);
+      store_kept(u, mb, otile + rr * OUT_PAD + uu * 4 * E);
+      mtile[rr * UT + uu] = (uint8_t)mb;
+    }
+  }
+  __syncthreads();
+
+  // 3) write: per row, kcount/2 kept elements and kcount/8 metadata bytes
+  const int obytes = kcount / 2 * E;
+  constexpr int CH = 8;  // 8-byte chunks
+  const int nch = obytes / CH;
+  for (int item = threadIdx.x; item < kT_RT * (OUT_ROW / CH); item += kBlock) {
+    const int rr = item / (OUT_ROW / CH), c = item % (OUT_ROW / CH);
+    if (rr < rcount && c < nch) {
+      const int64_t orow = b * R + r0 + rr;
+      char* dst = vals + orow * (K / 2 * E) + k0 / 2 * E + c * CH;
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(otile + rr * OUT_PAD + c * CH);
+    }
+  }
+  for (int item = threadIdx.x; item < kT_RT * UT; item += kBlock) {
+    const int rr = item / UT, uu = item % UT;
+    if (rr < rcount && uu * 8 < kcount) {
+      const int64_t orow = b * R + r0 + rr;
+      meta[orow * (K / 8) + k0 / 8 + uu] = mtile[rr * UT + uu];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused prune + compress + quantize of the kept values, one scale per row.
+// A team holds its whole row in registers: one read, then the kept absolute
+// maximum (team reduction), then codes, metadata and the scale are written.
+// ---------------------------------------------------------------------------
+template <class DT, int TEAM, int UPL, bool WANDA>
+__global__ __launch_bounds__(kBlock) void k_prune_quantize(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    const float* __restrict__ norm, int cfmt, float qmax, char* __restrict__ codes,
+    uint8_t* __restrict__ meta, float* __restrict__ scales) {
+  __shared__ uint32_t red[kBlock / 64];
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;
+  const char* xr = x + b * bs + r * rs;
+  const int64_t orow = b * R + r;
+
+  Unit<DT> u[UPL];
+  uint32_t mb[UPL];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+    else zero_unit(u[j]);
+  }
+  uint32_t am = 0;  // largest |kept| as storage bits (orders like the value)
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    mb[j] = 0;
+    if (i < nunits) {
+      mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t nib = (mb[j] >> (4 * g)) & 0xFu;
+        const uint32_t a0 = kept_raw(u[j], g, nib, 0) & DT::ABS;
+        const uint32_t a1 = kept_raw(u[j], g, nib, 1) & DT::ABS;
+        am = am > a0 ? am : a0;
+        am = am > a1 ? am : a1;
+      }
+    }
+  }
+  am = team_max_u32<TEAM>(am, red);
+  if (!active) return;
+  float s, inv;
+  row_scale(DT::to_f32(am), qmax, s, inv);
+
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    if (i < nunits) {
+      float kv[4];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t nib = (mb[j] >> (4 * g)) & 0xFu;
+        kv[2 * g + 0] = DT::to_f32(kept_raw(u[j], g, nib, 0));
+        kv[2 * g + 1] = DT::to_f32(kept_raw(u[j], g, nib, 1));
+      }
+      const int64_t o = orow * nunits + i;  // unit index in the output
+      if (cfmt == CF_FP8) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= enc_e4m3(kv[e] * inv) << (8 * e);
+        reinterpret_cast<uint32_t*>(codes)[o] = w;
+      } else if (cfmt == CF_INT8) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= ((uint32_t)(int)enc_int(kv[e] * inv, qmax) & 0xFFu) << (8 * e);
+        reinterpret_cast<uint32_t*>(codes)[o] = w;
+      } else {  // CF_INT16
+        uint2 w;
+        w.x = ((uint32_t)(int)enc_int(kv[0] * inv, qmax) & 0xFFFFu) |
+              ((uint32_t)(int)enc_int(kv[1] * inv, qmax) << 16);
+        w.y = ((uint32_t)(int)enc_int(kv[2] * inv, qmax) & 0xFFFFu) |
+              ((uint32_t)(int)enc_int(kv[3] * inv, qmax) << 16);
+        reinterpret_cast<uint2*>(codes)[o] = w;
+      }
+      meta[o] = (uint8_t)mb[j];
+    }
+  }
+  if (t == 0) scales[orow] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm, void* vals,
+                                 uint8_t* meta, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  if (!d.kcontig) {
+    return with_dtype(d.dtype, [&]<class DT>() {
+      dim3 grid((unsigned)((d.K + kT_KT - 1) / kT_KT), (unsigned)((d.R + kT_RT - 1) / kT_RT),
+                (unsigned)d.B);
+      if (wanda)
+        hipLaunchKernelGGL((k_prune_compress_T<DT, true>), grid, dim3(kBlock), 0, s, d.x, d.R,
+                           d.K, d.bs, d.ks, norm, (char*)vals, meta);
+      else
+        hipLaunchKernelGGL((k_prune_compress_T<DT, false>), grid, dim3(kBlock), 0, s, d.x, d.R,
+                           d.K, d.bs, d.ks, norm, (char*)vals, meta);
+      return hipGetLastError();
+    });
+  }
+  if (d.flat && !wanda) {
+    return with_dtype(d.dtype, [&]<class DT>() {
+      constexpr int UPL = 4;
+      const int64_t total = d.B * d.R * nunits;
+      const int64_t nblk = (total + kBlock * UPL - 1) / (kBlock * UPL);
+      hipLaunchKernelGGL((k_prune_compress_flat<DT, UPL>), dim3((unsigned)nblk), dim3(kBlock), 0,
+                         s, d.x, total, (char*)vals, meta);
+      return hipGetLastError();
+    });
+  }
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      if (wanda)
+        hipLaunchKernelGGL((k_prune_compress_rows<DT, TEAM, UPL, true>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, (char*)vals,
+                           meta);
+      else
+        hipLaunchKernelGGL((k_prune_compress_rows<DT, TEAM, UPL, false>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, (char*)vals,
+                           meta);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm, int cfmt,
+                                 float qmax, void* codes, uint8_t* meta, float* scales,
+                                 hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+      if (wanda)
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, true>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, cfmt, qmax,
+                           (char*)codes, meta, scales);
+      else
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, false>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, cfmt, qmax,
+                           (char*)codes, meta, scales);
+      return hipGetLastError();
+    });
+  });
+}
+
+}  // namespace sparq24

@@ -1,0 +1,291 @@
+// Dense online quantizers, the rivals of 2:4 at equal bits or equal tier.
+//
+// Method: Qin, "Is 2:4 Sparsity Still Worth It?" (paper-daily.com English
+// summary).  [PD §2]: the quantized side pays for online quantization of
+// operands produced on the fly.  [PD §3]: INT8 with one scale per row, FP8,
+// MXFP4 (one power-of-two scale per 32 elements) and NVFP4 (an FP8 scale per
+// 16 elements plus one per tensor).
+#include "dispatch.hpp"
+
+namespace sparq24 {
+
+// ---------------------------------------------------------------------------
+// Per-row INT-b / FP8: the team holds its row, reduces |x|max, encodes.
+// ---------------------------------------------------------------------------
+template <class DT, int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_quant_rows(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs, int cfmt,
+    float qmax, char* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ uint32_t red[kBlock / 64];
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;
+  const char* xr = x + b * bs + r * rs;
+  const int64_t orow = b * R + r;
+
+  Unit<DT> u[UPL];
+  uint32_t am = 0;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+    else zero_unit(u[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = u[j].absbits(e);
+      am = am > a ? am : a;
+    }
+  am = team_max_u32<TEAM>(am, red);
+  if (!active) return;
+  float s, inv;
+  row_scale(DT::to_f32(am), qmax, s, inv);
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    if (i < nunits) {
+      const int64_t o = orow * nunits + i;
+      if (cfmt == CF_FP8) {
+        uint2 w = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w.x |= enc_e4m3(u[j].f(e) * inv) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w.y |= enc_e4m3(u[j].f(4 + e) * inv) << (8 * e);
+        reinterpret_cast<uint2*>(codes)[o] = w;
+      } else if (cfmt == CF_INT8) {
+        uint2 w = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w.x |= ((uint32_t)(int)enc_int(u[j].f(e) * inv, qmax) & 0xFFu) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w.y |= ((uint32_t)(int)enc_int(u[j].f(4 + e) * inv, qmax) & 0xFFu) << (8 * e);
+        reinterpret_cast<uint2*>(codes)[o] = w;
+      } else {  // CF_INT16
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (uint32_t)(int)enc_int(u[j].f(e) * inv, qmax) & 0xFFFFu;
+        uint4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        reinterpret_cast<uint4*>(codes)[o] = w;
+      }
+    }
+  }
+  if (t == 0) scales[orow] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Tensor absolute maximum, first stage: one fp32 bit pattern per workgroup
+// (a grid-stride walk over rows; max is order-free so the result is exact).
+// ---------------------------------------------------------------------------
+constexpr int kAbsmaxBlocks = 512;
+
+template <class DT, int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_absmax_partial(
+    const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[kBlock / 64];
+  const int t = threadIdx.x % TEAM;
+  constexpr int RPB = kBlock / TEAM;
+  uint32_t am = 0;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TEAM; row < B * R;
+       row += (int64_t)gridDim.x * RPB) {
+    const int64_t b = row / R, r = row % R;
+    const char* xr = x + b * bs + r * rs;
+    for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+      Unit<DT> u[UPL];
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const int64_t i = c0 + j * TEAM + t;
+        if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+        else zero_unit(u[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < UPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = u[j].absbits(e);
+          am = am > a ? am : a;
+        }
+    }
+  }
+  // to fp32 bits so partials of any storage type compare as fp32
+  am = __float_as_uint(DT::to_f32(am));
+  am = team_max_u32<64>(am, red);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = red[0];
+    for (int i = 1; i < kBlock / 64; ++i) m = m > red[i] ? m : red[i];
+    partials[blockIdx.x] = m;
+  }
+}
+
+int absmax_partial_count(const RowDesc& d) {
+  const int64_t rows = d.B * d.R;
+  const int64_t want = (rows + 3) / 4;
+  return (int)(want < kAbsmaxBlocks ? (want > 0 ? want : 1) : kAbsmaxBlocks);
+}
+
+hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  const int nb = absmax_partial_count(d);
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL>), dim3(nb), dim3(kBlock), 0, s, d.x,
+                         d.B, d.R, nunits, d.bs, d.rs, partials);
+      return hipGetLastError();
+    });
+  });
+}
+
+// Reduce the partial maxima in a workgroup (every thread gets T).
+__device__ inline float block_tensor_amax(const float* tamax_in, const uint32_t* partials,
+                                          int nparts, uint32_t* lds) {
+  if (tamax_in) return *tamax_in;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kBlock) m = m > partials[i] ? m : partials[i];
+  m = team_max_u32<64>(m, lds);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kBlock / 64; ++i) r = r > lds[i] ? r : lds[i];
+  return __uint_as_float(r);
+}
+
+// NVFP4 tensor scale and block-scale multiplier from T.
+__device__ inline void nv_tensor_scales(float T, float& s_t, float& g) {
+  if (T >= 0x1p-64f) {
+    s_t = T / 2688.0f;
+    g = 448.0f / T;
+  } else {
+    s_t = 0.0f;
+    g = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 / NVFP4.  Lane t owns units t, t+TEAM, ...; an MX block (32
+// elements) is 4 adjacent lanes, an NV block (16 elements) 2 adjacent lanes,
+// combined with cross-lane xor shuffles.
+// ---------------------------------------------------------------------------
+__device__ inline int mx_exponent(uint32_t amax_bits) {
+  // floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 -> -127
+  if (amax_bits == 0) return -127;
+  int fl;
+  const uint32_t ex = amax_bits >> 23;
+  if (ex) fl = (int)ex - 127;
+  else fl = (31 - __builtin_clz(amax_bits)) - 149;  // fp32 subnormal
+  int e = fl - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <class DT, int TEAM, int UPL, bool NV>
+__global__ __launch_bounds__(kBlock) void k_quant_block(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    const float* __restrict__ tamax_in, const uint32_t* __restrict__ partials, int nparts,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+  __shared__ uint32_t red[kBlock / 64];
+  float s_t = 0.f, g = 0.f;
+  if constexpr (NV) {
+    const float T = block_tensor_amax(tamax_in, partials, nparts, red);
+    nv_tensor_scales(T, s_t, g);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+  }
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;
+  const char* xr = x + b * bs + r * rs;
+  const int64_t orow = b * R + r;
+  // shuffles below need every lane of the wave, so masked lanes run along
+  for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+    Unit<DT> u[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+      else zero_unit(u[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      uint32_t am = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = u[j].absbits(e);
+        am = am > a ? am : a;
+      }
+      am = __float_as_uint(DT::to_f32(am));
+      uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
+      am = am > w ? am : w;
+      if constexpr (!NV) {
+        w = (uint32_t)__shfl_xor((int)am, 2, 64);
+        am = am > w ? am : w;
+        const int e = mx_exponent(am);
+        uint32_t pk = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pk |= enc_e2m1(__builtin_ldexpf(u[j].f(q), -e)) << (4 * q);
+        if (active && i < nunits) {
+          codes[orow * nunits + i] = pk;
+          if ((i & 3) == 0) scales[orow * (nunits / 4) + (i >> 2)] = (uint8_t)(e + 127);
+        }
+      } else {
+        const uint32_t bc = enc_e4m3(__uint_as_float(am) * g);
+        const float d = dec_e4m3(bc) * s_t;
+        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        uint32_t pk = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pk |= enc_e2m1(u[j].f(q) * inv) << (4 * q);
+        if (active && i < nunits) {
+          codes[orow * nunits + i] = pk;
+          if ((i & 1) == 0) scales[orow * (nunits / 2) + (i >> 1)] = (uint8_t)bc;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
+                             hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL>), row_grid(d, TEAM), dim3(kBlock), 0, s,
+                         d.x, d.R, nunits, d.bs, d.rs, cfmt, qmax, (char*)codes, scales);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_quant_mx(const RowDesc& d, void* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, false>), row_grid(d, TEAM), dim3(kBlock), 0,
+                         s, d.x, d.R, nunits, d.bs, d.rs, nullptr, nullptr, 0, (uint32_t*)codes,
+                         scales, nullptr);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32_t* partials,
+                           int nparts, void* codes, uint8_t* scales, float* ts_out,
+                           hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, true>), row_grid(d, TEAM), dim3(kBlock), 0,
+                         s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials, nparts,
+                         (uint32_t*)codes, scales, ts_out);
+      return hipGetLastError();
+    });
+  });
+}
+
+}  // namespace sparq24

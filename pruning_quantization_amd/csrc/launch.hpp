@@ -1,0 +1,71 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sparq24 {
+
+// Code containers of per-row formats.
+enum CodeFmt : int { CF_INT8 = 0, CF_INT16 = 1, CF_FP8 = 2, CF_NONE = 3, CF_MX = 4, CF_NV = 5 };
+
+// One operand as the kernels see it: B x R vectors of K elements.
+struct RowDesc {
+  const char* x;
+  int dtype;            // sparq24_dtype
+  int64_t B, R, K;
+  int64_t bs, rs, ks;   // strides in BYTES
+  bool kcontig;         // ks == element size
+  bool flat;            // fully contiguous: bs == R*rs, rs == K*esize
+};
+
+constexpr int kMaxQ = 16;
+
+struct QList {
+  int n;
+  int fmt[kMaxQ];      // CodeFmt (CF_NONE/CF_INT8/CF_INT16/CF_FP8/CF_MX/CF_NV)
+  float qmax[kMaxQ];
+};
+
+struct EnergyParams {
+  QList kept, dense;
+  const float* nv_tamax;       // device T for NVFP4 (or null -> reduce partials)
+  const uint32_t* nv_partials; // fp32 bit patterns of partial maxima
+  int n_partials;
+};
+
+// Row kernels that hold a whole row in registers support up to this many units.
+constexpr int64_t kMaxRowUnits = 4096;  // K <= 32768
+
+hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm, void* vals,
+                                 uint8_t* meta, hipStream_t s);
+hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm, int cfmt,
+                                 float qmax, void* codes, uint8_t* meta, float* scales,
+                                 hipStream_t s);
+hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
+                             hipStream_t s);
+int absmax_partial_count(const RowDesc& d);
+hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStream_t s);
+hipError_t launch_quant_mx(const RowDesc& d, void* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32_t* partials,
+                           int nparts, void* codes, uint8_t* scales, float* ts_out,
+                           hipStream_t s);
+hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
+                              const EnergyParams& p, double* rowpart, hipStream_t s);
+// mode 0: out[blk][4] raw sums for pair 0; mode 1: out[blk][npairs][5] E's and R
+struct FinalizeParams {
+  int ncols;            // 2 + nkept + ndense
+  int npairs;
+  int kcol[kMaxQ];      // column of the kept error of pair p
+  int dcol[kMaxQ];      // column of the dense error of pair p
+  int mode;
+};
+hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t rows_per_block,
+                                  int64_t nblk, const FinalizeParams& f, double* out,
+                                  hipStream_t s);
+int col_strips(const RowDesc& d);
+hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace sparq24

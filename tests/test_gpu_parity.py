@@ -1,0 +1,287 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle,
+element by element on the same seeded inputs.
+
+Bar: bit-exact masks, metadata, kept values, codes and scales; energies and
+R within 1e-6 relative; Wanda norms within 1 fp32 ulp.  Shapes span several
+tiles/teams and ragged tails; inputs include ties, signed zeros, subnormals,
+all-zero rows and saturating values.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import pruning_quantization_amd as S  # noqa: E402
+from gpu_util import raw_np, random_raw, tie_heavy_raw, to_dev  # noqa: E402
+
+DTYPES = ["bf16", "f16", "f32"]
+# K values: team shapes 16x1 .. 256x16 and ragged unit counts
+KS = [8, 24, 128, 136, 256, 520, 1024, 4096, 4104, 8192, 16384]
+
+
+def inputs(seed, rows, k, dtype, kind):
+    rng = np.random.default_rng(seed)
+    if kind == "ties":
+        return tie_heavy_raw(rng, (rows, k), dtype)
+    raw = random_raw(rng, (rows, k), dtype)
+    return raw
+
+
+def assert_same(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert got.dtype == want.dtype, (what, got.dtype, want.dtype)
+    if got.dtype.kind == "f":           # compare bit patterns (keeps -0 and +0 apart)
+        ui = {2: np.uint16, 4: np.uint32, 8: np.uint64}[got.dtype.itemsize]
+        got, want = got.view(ui), want.view(ui)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: got {got[i]} want {want[i]}")
+
+
+# ---------------------------------------------------------------------------
+# prune_compress
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [8, 24, 128, 520, 4096, 4104])
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_prune_compress_magnitude(dtype, k, kind):
+    rows = 37
+    raw = inputs(k * 7 + len(dtype), rows, k, dtype, kind)
+    x = to_dev(raw, dtype)
+    v, m = S.prune_compress(x)
+    torch.cuda.synchronize()
+    wv, wm = O.prune_compress(raw, dtype)
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(v), wv, "values")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prune_compress_strided_rows(dtype):
+    # rows taken from a wider buffer: row stride > K exercises the row-team path
+    rng = np.random.default_rng(5)
+    full = random_raw(rng, (50, 1024 + 64), dtype)
+    x = to_dev(full, dtype)[:, :1024]
+    v, m = S.prune_compress(x)
+    wv, wm = O.prune_compress(np.ascontiguousarray(full[:, :1024]), dtype)
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(v), wv, "values")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [24, 128, 4096])
+def test_prune_compress_wanda(dtype, k):
+    rng = np.random.default_rng(k)
+    raw = tie_heavy_raw(rng, (29, k), dtype)
+    norm = (rng.integers(0, 5, size=k) * 0.75).astype(np.float32)  # ties and zeros
+    norm[: k // 8] = rng.random(k // 8).astype(np.float32) * 3
+    x = to_dev(raw, dtype)
+    n = torch.from_numpy(norm).cuda()
+    v, m = S.prune_compress(x, score="wanda", col_norm=n)
+    wv, wm = O.prune_compress(raw, dtype, "wanda", norm)
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(v), wv, "values")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(2, 136, 72), (1, 256, 128), (3, 40, 8), (2, 16392, 128)])
+def test_prune_compress_transposed(dtype, shape):
+    # V [heads, seq, dim] pruned along seq (axis 1)
+    rng = np.random.default_rng(sum(shape))
+    raw = random_raw(rng, shape, dtype)
+    x = to_dev(raw, dtype)
+    v, m = S.prune_compress(x, axis=1)
+    assert v.shape == (shape[0], shape[2], shape[1] // 2)
+    rows = np.ascontiguousarray(np.swapaxes(raw, 1, 2)).reshape(-1, shape[1])
+    wv, wm = O.prune_compress(rows, dtype)
+    assert_same(raw_np(m).reshape(-1, shape[1] // 8), wm, "meta")
+    assert_same(raw_np(v).reshape(-1, shape[1] // 2), wv, "values")
+
+
+# ---------------------------------------------------------------------------
+# prune_quantize
+# ---------------------------------------------------------------------------
+
+QS = [("fp8", 0), ("int", 2), ("int", 3), ("int", 4), ("int", 8), ("int", 9), ("int", 16)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", KS)
+def test_prune_quantize_fp8_int8(dtype, k):
+    rows = 21 if k <= 4104 else 5
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 3, rows, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        for fmt, bits in (("fp8", 0), ("int", 8)):
+            c, m, s = S.prune_quantize(x, (fmt, bits))
+            wc, wm, ws = O.prune_quantize(raw, dtype, O.QSpec(fmt, bits))
+            assert_same(raw_np(m), wm, f"meta {fmt}")
+            assert_same(raw_np(s), ws, f"scales {fmt}")
+            assert_same(raw_np(c), wc, f"codes {fmt}")
+
+
+@pytest.mark.parametrize("fmt,bits", QS)
+@pytest.mark.parametrize("score", ["magnitude", "wanda"])
+def test_prune_quantize_formats(fmt, bits, score):
+    rng = np.random.default_rng(bits + 100)
+    k = 1024
+    raw = inputs(bits, 45, k, "bf16", "normal")
+    norm = (rng.random(k) * 2).astype(np.float32)
+    x = to_dev(raw, "bf16")
+    n = torch.from_numpy(norm).cuda() if score == "wanda" else None
+    c, m, s = S.prune_quantize(x, (fmt, bits), score=score, col_norm=n)
+    wc, wm, ws = O.prune_quantize(raw, "bf16", O.QSpec(fmt, bits), score, norm if n is not None else None)
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(s), ws, "scales")
+    assert_same(raw_np(c), wc, "codes")
+
+
+def test_prune_quantize_k32768_and_tiny_rows():
+    rng = np.random.default_rng(9)
+    raw = random_raw(rng, (3, 32768), "bf16")
+    raw[1] = 0x8000                         # all -0
+    raw[2, ::3] = 0x0001                    # subnormals mixed in
+    x = to_dev(raw, "bf16")
+    c, m, s = S.prune_quantize(x, ("fp8", 0))
+    wc, wm, ws = O.prune_quantize(raw, "bf16", O.QSpec("fp8"))
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(s), ws, "scales")
+    assert_same(raw_np(c), wc, "codes")
+
+
+# ---------------------------------------------------------------------------
+# dense quantizers
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [8, 128, 136, 1024, 4096, 16384])
+@pytest.mark.parametrize("fmt,bits", [("fp8", 0), ("int", 3), ("int", 8), ("int", 12)])
+def test_quantize_rows(dtype, k, fmt, bits):
+    rows = 19 if k <= 4096 else 4
+    raw = inputs(k + bits, rows, k, dtype, "ties" if k % 3 else "normal")
+    x = to_dev(raw, dtype)
+    c, s = S.quantize(x, (fmt, bits))
+    wc, ws = O.quantize_rows(raw, dtype, O.QSpec(fmt, bits))
+    assert_same(raw_np(s), ws, "scales")
+    assert_same(raw_np(c), wc, "codes")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [32, 96, 1024, 4096, 4128])
+def test_quantize_mxfp4(dtype, k):
+    for kind in ("normal", "ties"):
+        raw = inputs(k, 23, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        c, s = S.quantize(x, "mxfp4")
+        wc, ws = O.quantize_mxfp4(raw, dtype)
+        assert_same(raw_np(s), ws, "e8m0")
+        assert_same(raw_np(c), wc, "codes")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [16, 48, 1024, 4096, 4112])
+def test_quantize_nvfp4(dtype, k):
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 1, 23, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        c, s, ts = S.quantize(x, "nvfp4")
+        wc, ws, wts = O.quantize_nvfp4(raw, dtype)
+        assert raw_np(ts)[0] == wts
+        assert_same(raw_np(s), ws, "e4m3 block scales")
+        assert_same(raw_np(c), wc, "codes")
+    # caller-supplied tensor maximum
+    t = np.float32(37.5)
+    c, s, ts = S.quantize(x, "nvfp4", tensor_amax=torch.tensor([t], device="cuda"))
+    wc, ws, wts = O.quantize_nvfp4(raw, dtype, tensor_amax=float(t))
+    assert raw_np(ts)[0] == wts
+    assert_same(raw_np(s), ws, "block scales (given T)")
+    assert_same(raw_np(c), wc, "codes (given T)")
+
+
+# ---------------------------------------------------------------------------
+# energies and predicted R
+# ---------------------------------------------------------------------------
+
+PAIRS_C2 = [(("int", 2 * m), ("int", m + 1)) for m in range(2, 9)]
+
+
+def rel_close(got, want, rtol=1e-6):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    same_nonfinite = (np.isnan(got) & np.isnan(want)) | (np.isinf(got) & (got == want))
+    ok = same_nonfinite | (np.abs(got - want) <= rtol * np.abs(want)) | ((want == 0) & (got == 0))
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} differ; first got {got[~ok][:3]} want {want[~ok][:3]}"
+
+
+def qs_oracle(q):
+    return O.QSpec(q) if isinstance(q, str) else O.QSpec(*q)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [32, 128, 1024, 4096, 16384])
+def test_error_energy(dtype, k):
+    rows = 40 if k <= 4096 else 6
+    raw = inputs(k + 11, rows, k, dtype, "normal")
+    x = to_dev(raw, dtype)
+    for kept, dense in [("fp8", ("int", 8)), (("int", 4), "fp8"), ("none", "mxfp4"), ("fp8", "nvfp4")]:
+        got = S.error_energy(x, kept, dense, rows_per_block=16)
+        want = O.error_energy(raw, dtype, qs_oracle(kept), qs_oracle(dense), rows_per_block=16)
+        rel_close(raw_np(got), want)
+
+
+def test_predict_R_sweep_and_wanda():
+    rng = np.random.default_rng(21)
+    k = 4096
+    raw = inputs(21, 33, k, "bf16", "normal")
+    norm = (rng.random(k) * 3).astype(np.float32)
+    x = to_dev(raw, "bf16")
+    kept = [p[0] for p in PAIRS_C2]
+    dense = [p[1] for p in PAIRS_C2]
+    for score in ("magnitude", "wanda"):
+        n = torch.from_numpy(norm).cuda() if score == "wanda" else None
+        got = S.predict_R(x, kept, dense, score=score, col_norm=n)
+        want = O.predict_R(raw, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
+                           score, norm if n is not None else None)
+        rel_close(raw_np(got), want)
+
+
+def test_predict_R_blocks_degenerate_and_deterministic():
+    raw = inputs(5, 300, 256, "bf16", "ties")
+    raw[:128] = 0                                   # first block all zero -> NaN
+    x = to_dev(raw, "bf16")
+    kept = ["fp8", "fp8", "none"]
+    dense = ["mxfp4", "nvfp4", ("int", 8)]
+    a = S.predict_R(x, kept, dense, rows_per_block=128)
+    b = S.predict_R(x, kept, dense, rows_per_block=128)
+    assert torch.equal(a.view(torch.int64), b.view(torch.int64))     # bitwise repeatable
+    want = O.predict_R(raw, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
+                       rows_per_block=128)
+    assert np.isnan(raw_np(a)[0]).all()
+    rel_close(raw_np(a), want)
+
+
+def test_col_l2norm_within_one_ulp():
+    import workloads as W
+    raw = W.activation_x(3, 512, 1024)
+    x = to_dev(raw, "bf16")
+    got = raw_np(S.col_l2norm(x))
+    want = O.col_l2norm(raw, "bf16")
+    assert np.all(np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64)) <= 1)
+
+
+def test_copy_kernel():
+    a = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    S.copy(a, b)
+    assert torch.equal(a, b)
