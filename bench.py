@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the online 2:4 prune-and-compress hot path on one MI355X.
+
+Workload: a linear-layer activation X [4096 tokens, 4096 hidden] in bf16, rows
+N(0,1) with 4 outlier hidden channels (x50), the setting of the paper's 2x/4x
+tier comparisons (Qin, "Is 2:4 Sparsity Still Worth It?", paper-daily.com
+English summary, sections 2-4).
+
+One step = the whole hot path over one batch (one X):
+  1. fused online 2:4 prune + compress + FP8-e4m3 quantization of the kept
+     values with a per-token scale (the call the metric names),
+  2. the dense rivals: per-token FP8-e4m3 and INT8 quantization,
+  3. predicted R for (2:4+FP8 vs FP8) and (2:4+FP8 vs INT8): energy loss,
+     error energies and R in one read of X.
+Inputs and outputs rotate over a pool larger than the 256 MB last-level
+cache, so every step streams from HBM.  Steps are replayed from HIP graphs
+(torch.cuda.graph) to keep host launch cost out of the measurement.
+
+Prints ONE JSON line (see the repository's design notes for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--pool", type=int, default=16, help="X copies rotated (>= 512 MB total)")
+    ap.add_argument("--tokens", type=int, default=4096)
+    ap.add_argument("--hidden", type=int, default=4096)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of X the CPU oracle processes for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of graphs")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the hot path has no "
+                          "cross-GPU step (rows shard independently), so --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import pruning_quantization_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, H = a.tokens, a.hidden
+
+    # ---- inputs: same seeded bytes for GPU and oracle --------------------------------
+    x_bits = W.activation_x(a.seed, T, H)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    pool = [x0] + [x0.clone() for _ in range(a.pool - 1)]
+
+    kept = ["fp8", "fp8"]
+    dense = ["fp8", ("int", 8)]
+
+    def outputs():
+        return {
+            "pq": (torch.empty(T, H // 2, dtype=torch.uint8, device=dev),
+                   torch.empty(T, H // 8, dtype=torch.uint8, device=dev),
+                   torch.empty(T, dtype=torch.float32, device=dev)),
+            "fp8": (torch.empty(T, H, dtype=torch.uint8, device=dev),
+                    torch.empty(T, dtype=torch.float32, device=dev),
+                    torch.empty(1, dtype=torch.float32, device=dev)),
+            "int8": (torch.empty(T, H, dtype=torch.int8, device=dev),
+                     torch.empty(T, dtype=torch.float32, device=dev),
+                     torch.empty(1, dtype=torch.float32, device=dev)),
+            "R": torch.empty(1, 2, 5, dtype=torch.float64, device=dev),
+        }
+
+    outs = [outputs() for _ in range(a.pool)]
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+
+    def call_pq(i):
+        S.prune_quantize(pool[i], "fp8", out=outs[i]["pq"])
+
+    def call_fp8(i):
+        S.quantize(pool[i], "fp8", out=outs[i]["fp8"])
+
+    def call_int8(i):
+        S.quantize(pool[i], ("int", 8), out=outs[i]["int8"])
+
+    def call_R(i):
+        S.predict_R(pool[i], kept, dense, out=outs[i]["R"], workspace=ws)
+
+    calls = {"prune_quantize_fp8": call_pq, "quantize_fp8": call_fp8,
+             "quantize_int8": call_int8, "predict_R": call_R}
+
+    def step(i):
+        for f in calls.values():
+            f(i)
+
+    # algorithmic bytes per call (input read once + every output written once)
+    xb = T * H * 2
+    alg = {
+        "prune_quantize_fp8": xb + T * H // 2 + T * H // 8 + T * 4,
+        "quantize_fp8": xb + T * H + T * 4,
+        "quantize_int8": xb + T * H + T * 4,
+        "predict_R": xb + 2 * 5 * 8,
+    }
+    step_bytes = sum(alg.values())
+
+    # ---- spot parity against the oracle (not timed) ---------------------------------
+    step(0)
+    torch.cuda.synchronize()
+    import oracle as O
+    rows = np.r_[0:8, T - 8:T]
+    wc, wm, wsc = O.prune_quantize(x_bits[rows], "bf16", O.QSpec("fp8"))
+    c, m, s = (t.cpu().numpy() for t in outs[0]["pq"])
+    parity = bool(np.array_equal(c[rows], wc) and np.array_equal(m[rows], wm)
+                  and np.array_equal(s[rows].view(np.uint32), wsc.view(np.uint32)))
+
+    # ---- warmup ----------------------------------------------------------------------
+    for w in range(a.warmup):
+        step(w % a.pool)
+    torch.cuda.synchronize()
+
+    # ---- graphs: one per pool entry (1 step) and one per call over the ring ----------
+    use_graphs = not a.eager
+    step_graphs, call_graphs = [], {}
+    if use_graphs:
+        try:
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                for i in range(a.pool):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap):
+                        step(i)
+                    step_graphs.append(g)
+                for name, f in calls.items():
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap):
+                        for i in range(a.pool):
+                            f(i)
+                    call_graphs[name] = g
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            for g in step_graphs:
+                g.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported -> eager launches
+            print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            use_graphs = False
+
+    # ---- timed region: exactly K steps ------------------------------------------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for k in range(a.steps):
+        if use_graphs:
+            step_graphs[k % a.pool].replay()
+        else:
+            step(k % a.pool)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---- per-call kernel durations (HIP events around ring replays) ------------------
+    per_call = {}
+    reps = max(1, a.steps // a.pool)
+    for name, f in calls.items():
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            if use_graphs:
+                call_graphs[name].replay()
+            else:
+                for i in range(a.pool):
+                    f(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * a.pool)
+        per_call[name] = {"us": round(us, 3), "GBps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+
+    # ---- copy baseline: library copy kernel over the same rotation -------------------
+    src = [p.view(torch.uint8).view(-1) for p in pool]
+    dst = [torch.empty_like(s_) for s_ in src]
+    for i in range(a.pool):
+        S.copy(src[i], dst[i])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        for i in range(a.pool):
+            S.copy(src[i], dst[i])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) * 1e3 / (reps * a.pool)
+    copy_gbps = 2 * xb / (copy_us * 1e-6) / 1e9
+
+    dom = "prune_quantize_fp8"
+    achieved = per_call[dom]["GBps"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "k_prune_quantize<BF16T,64,8,false>",
+                "algorithmic_bytes_per_launch": alg[dom], "avg_launch_us": per_call[dom]["us"]}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same step ---------------
+    cpu = None
+    if not a.no_cpu_baseline:
+        n = min(a.cpu_rows, T)
+        sub = x_bits[:n]
+        t1 = time.perf_counter()
+        O.prune_quantize(sub, "bf16", O.QSpec("fp8"))
+        O.quantize_rows(sub, "bf16", O.QSpec("fp8"))
+        O.quantize_rows(sub, "bf16", O.QSpec("int", 8))
+        O.predict_R(sub, "bf16", [O.QSpec(k) for k in kept],
+                    [O.QSpec("fp8"), O.QSpec("int", 8)])
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(step_bytes * n / T / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "host_cpus": os.cpu_count(), "seconds": round(dt, 2),
+               "sample": f"first {n} of {T} rows of X through all four calls of one step "
+                         "(numpy, single-threaded)"}
+
+    line = {
+        "metric": "fused 2:4 prune+compress+quant GB/s (% of HBM peak); predicted-R tensors/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "linear-layer activation X 4096x4096 bf16, N(0,1) rows with 4 "
+                               "outlier channels x50; step = 2:4 prune+compress+FP8 (per-token), "
+                               "dense FP8 and INT8 (per-token), predicted R for 2 pairs",
+                   "tokens": T, "hidden": H, "pool": a.pool, "graphs": use_graphs},
+        "fused_prune_quant_GBps": achieved,
+        "fused_prune_quant_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "fused_prune_quant_pct_copy": round(100 * achieved / copy_gbps, 2),
+        "predicted_R_tensors_per_s": round(1e6 / per_call["predict_R"]["us"], 1),
+        "step_tensors_per_s": round(1e3 / ms_step, 1),
+        "copy_GBps": round(copy_gbps, 1),
+        "per_call": per_call,
+        "parity_sampled_rows": parity,
+        "wall_s": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -37,9 +37,12 @@
  * Streams.  Work is enqueued on `stream` (NULL = the default stream) and the
  *   call returns without synchronising.  A fault during execution surfaces at
  *   the caller's next synchronisation.
- * Workspace.  Calls taking (ws, ws_bytes): with ws == NULL the call stores
- *   the bytes it needs in *ws_bytes, returns SPARQ24_OK and enqueues
- *   nothing; otherwise *ws_bytes must be at least that many.
+ * Workspace.  Calls taking (ws, ws_bytes): ws == NULL with ws_bytes != NULL
+ *   is a size query: the call stores the bytes it needs in *ws_bytes,
+ *   returns SPARQ24_OK and enqueues nothing.  Any other combination runs the
+ *   call: if it needs workspace, ws must be non-NULL and *ws_bytes at least
+ *   the queried size (else SPARQ24_ERR_WORKSPACE); if it needs none, ws and
+ *   ws_bytes may both be NULL.  Workspace contents need no initialisation.
  * Errors.  Arguments are checked on the host before anything is enqueued;
  *   on any error nothing is enqueued.  No call aborts or throws.
  * Rounding.  Every fp32 step named below is one IEEE-754 single-precision
@@ -147,7 +150,7 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
  * each row are quantized (INT or FP8) with one scale per row taken from the
  * absolute maximum of that row's kept values.  codes [B][R][K/2],
  * meta [B][R][K/8], scales fp32 [B][R].  One read, one write per output.
- * Needs no workspace (ws may be NULL with *ws_bytes set to 0 by a query). */
+ * Needs no workspace: pass ws = ws_bytes = NULL (a query reports 0). */
 sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score,
                                       const float* col_norm, const sparq24_qspec* q,
                                       void* codes, uint8_t* meta, float* scales,

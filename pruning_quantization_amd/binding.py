@@ -186,11 +186,18 @@ def _norm_ptr(score: str, col_norm: Optional[torch.Tensor]):
     return None
 
 
-def _workspace(x: torch.Tensor, query) -> Tuple[Optional[torch.Tensor], c_size_t]:
+def _workspace(x: torch.Tensor, query):
+    """Query the workspace size and allocate it; returns (ws tensor or None,
+    the ws_bytes argument to pass: a c_size_t, or None when none is needed)."""
     n = c_size_t(0)
     query(None, ctypes.byref(n))
-    ws = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=x.device) if n.value else None
-    return ws, n
+    if n.value == 0:
+        return None, None
+    return torch.empty(int(n.value), dtype=torch.uint8, device=x.device), n
+
+
+def _wsarg(n):
+    return ctypes.byref(n) if n is not None else None
 
 
 def _code_dtype(q: CQSpec):
@@ -269,9 +276,9 @@ def quantize(x: torch.Tensor, q: QLike, axis: int = -1,
         ws, n = _workspace(x, lambda w, nb: L.sparq24_quantize(
             ctypes.byref(c), ctypes.byref(qs), None, None, None, w, nb, s))
     else:
-        ws, n = workspace, c_size_t(workspace.numel())
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
     st = L.sparq24_quantize(ctypes.byref(c), ctypes.byref(qs), codes.data_ptr(), scales.data_ptr(),
-                            ts.data_ptr(), _ptr(ws), ctypes.byref(n), s)
+                            ts.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_quantize", st)
     if qs.fmt == Q_NVFP4:
         return codes, scales, ts
@@ -305,10 +312,10 @@ def error_energy(x: torch.Tensor, kept: QLike, dense: QLike, axis: int = -1,
             ctypes.byref(c), _score(score), npt, ctypes.byref(kq), ctypes.byref(dq),
             rows_per_block, None, w, nb, s))
     else:
-        ws, n = workspace, c_size_t(workspace.numel())
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
     st = L.sparq24_error_energy(ctypes.byref(c), _score(score), npt, ctypes.byref(kq),
                                 ctypes.byref(dq), rows_per_block, out.data_ptr(), _ptr(ws),
-                                ctypes.byref(n), s)
+                                _wsarg(n), s)
     _check("sparq24_error_energy", st)
     return out
 
@@ -335,9 +342,9 @@ def predict_R(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QLike], ax
         ws, n = _workspace(x, lambda w, nb: L.sparq24_predict_R(
             ctypes.byref(c), _score(score), npt, ka, da, npairs, rows_per_block, None, w, nb, s))
     else:
-        ws, n = workspace, c_size_t(workspace.numel())
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
     st = L.sparq24_predict_R(ctypes.byref(c), _score(score), npt, ka, da, npairs, rows_per_block,
-                             out.data_ptr(), _ptr(ws), ctypes.byref(n), s)
+                             out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_predict_R", st)
     return out
 
@@ -352,8 +359,8 @@ def col_l2norm(x: torch.Tensor, out: Optional[torch.Tensor] = None, workspace=No
     if workspace is None:
         ws, n = _workspace(x, lambda w, nb: L.sparq24_col_l2norm(ctypes.byref(c), None, w, nb, s))
     else:
-        ws, n = workspace, c_size_t(workspace.numel())
-    st = L.sparq24_col_l2norm(ctypes.byref(c), out.data_ptr(), _ptr(ws), ctypes.byref(n), s)
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_col_l2norm(ctypes.byref(c), out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_col_l2norm", st)
     return out
 

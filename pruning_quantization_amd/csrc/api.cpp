@@ -110,16 +110,18 @@ sparq24_status check_q(const sparq24_qspec* q, unsigned allowed, int& cfmt, floa
   return SPARQ24_OK;
 }
 
-// Workspace protocol shared by the calls.
+// Workspace protocol shared by the calls: (ws == NULL, ws_bytes != NULL) is a
+// size query; otherwise the call runs and needs ws/*ws_bytes only when the
+// required size is non-zero.
 sparq24_status workspace(void* ws, size_t* ws_bytes, size_t need, bool& query) {
-  if (!ws_bytes) return SPARQ24_ERR_WORKSPACE;
-  if (!ws) {
+  if (!ws && ws_bytes) {
     *ws_bytes = need;
     query = true;
     return SPARQ24_OK;
   }
   query = false;
-  if (*ws_bytes < need) return SPARQ24_ERR_WORKSPACE;
+  if (need == 0) return SPARQ24_OK;
+  if (!ws || !ws_bytes || *ws_bytes < need) return SPARQ24_ERR_WORKSPACE;
   if (!aligned16(ws)) return SPARQ24_ERR_ALIGN;
   return SPARQ24_OK;
 }
@@ -153,7 +155,7 @@ struct EnergyPlan {
   bool need_nv_partials = false;
   int nparts = 0;
   int64_t nrows = 0, rpb = 0, nblk = 0;
-  size_t off_rowpart = 0, off_parts = 0, need = 0;
+  size_t off_rowpart = 0, off_csum = 0, off_parts = 0, need = 0;
 };
 
 sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
@@ -220,9 +222,11 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   pl.need_nv_partials = n_nv == 1 && pl.nv_in == nullptr;
   pl.nparts = pl.need_nv_partials ? absmax_partial_count(d) : 0;
   const size_t rowpart = (size_t)pl.f.ncols * (size_t)pl.nrows * sizeof(double);
-  const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk * sizeof(double);
+  const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk *
+                      (size_t)energy_chunks_per_block(pl.rpb) * sizeof(double);
   pl.off_rowpart = 0;
-  pl.off_parts = round_up(rowpart + sums, kAlign);
+  pl.off_csum = round_up(rowpart, kAlign);
+  pl.off_parts = pl.off_csum + round_up(sums, kAlign);
   pl.need = pl.off_parts + round_up((size_t)pl.nparts * sizeof(uint32_t), kAlign);
   return SPARQ24_OK;
 }
@@ -239,7 +243,8 @@ sparq24_status run_energy(const RowDesc& d, int32_t score, const float* col_norm
   }
   pl.p.nv_tamax = pl.nv_in;
   CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart, stream)));
-  return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, out, stream));
+  double* csum = (double*)(w + pl.off_csum);
+  return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, csum, out, stream));
 }
 
 }  // namespace
@@ -306,8 +311,7 @@ sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, co
   CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3), cfmt, qmax));
   if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
   bool query;
-  if (ws_bytes || ws) CHECK(workspace(ws, ws_bytes, 0, query));
-  else query = false;
+  CHECK(workspace(ws, ws_bytes, 0, query));
   if (query) return SPARQ24_OK;
   if (d.B * d.R * d.K == 0) return SPARQ24_OK;
   if (!codes || !meta || !scales) return SPARQ24_ERR_INVALID;

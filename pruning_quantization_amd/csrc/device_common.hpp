@@ -95,11 +95,12 @@ __device__ inline uint32_t nibble_from_j(uint32_t j1, uint32_t j2) {
 template <class DT, bool WANDA>
 __device__ inline uint32_t select_group(const Unit<DT>& u, int g, const float* n4) {
   if constexpr (!WANDA && DT::ESIZE == 2) {
-    uint32_t k[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) k[i] = (u.absbits(4 * g + i) << 2) | (3u - i);
+    // keys = |x| in bits 16..30, (3 - position) in bits 0..1
+    const uint32_t a = u.w[2 * g] & 0x7FFF7FFFu, b = u.w[2 * g + 1] & 0x7FFF7FFFu;
+    const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
+    const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
     uint32_t t1, t2;
-    top2(k[0], k[1], k[2], k[3], t1, t2);
+    top2(k0, k1, k2, k3, t1, t2);
     return nibble_from_j(t1 & 3u, t2 & 3u);
   } else {
     uint64_t k[4];
@@ -128,10 +129,79 @@ __device__ inline uint32_t perm_sel(uint32_t nib) {
   return 0x01000100u + i0 * 0x0202u + i1 * 0x02020000u;
 }
 
+// ---------------------------------------------------------------------------
+// Both group selections of a unit -> metadata byte (group 0 in the low nibble).
+// Wanda reads the 8 channel norms of the unit (k0 = its first position).
+// ---------------------------------------------------------------------------
+template <class DT, bool WANDA>
+__device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restrict__ norm,
+                                       int64_t k0) {
+  float n8[8];
+  if constexpr (WANDA) {
+    const float4* np = reinterpret_cast<const float4*>(norm + k0);
+    float4 a = np[0], b = np[1];
+    n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
+    n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
+  }
+  uint32_t n0 = select_group<DT, WANDA>(u, 0, n8);
+  uint32_t n1 = select_group<DT, WANDA>(u, 1, n8 + 4);
+  return n0 | (n1 << 4);
+}
+
+// The four kept elements of a unit (two per group, in position order) as raw
+// storage bits.  16-bit types: two dwords, each (kept i0 | kept i1 << 16) of
+// one group, gathered with a byte permute.  fp32: four dwords picked with
+// selects.  Nothing is indexed at run time, so the unit stays in registers.
 template <class DT>
-__device__ inline uint32_t kept_raw(const Unit<DT>& u, int g, uint32_t nib, int which) {
-  uint32_t i = which ? (nib >> 2) : (nib & 3u);
-  return u.raw(4 * g + (int)i);
+struct Kept {
+  uint32_t k[DT::ESIZE == 2 ? 2 : 4];
+  __device__ inline uint32_t raw(int e) const {  // e = 0..3, compile-time after unrolling
+    if constexpr (DT::ESIZE == 2) return (k[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+    else return k[e];
+  }
+  __device__ inline float f(int e) const { return DT::to_f32(raw(e)); }
+};
+
+__device__ inline uint32_t pick4(uint32_t i, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = (i & 1u) ? b : a;
+  const uint32_t hi = (i & 1u) ? d : c;
+  return (i & 2u) ? hi : lo;
+}
+
+template <class DT>
+__device__ inline Kept<DT> gather_kept(const Unit<DT>& u, uint32_t mb) {
+  Kept<DT> kp;
+  const uint32_t n0 = mb & 0xFu, n1 = (mb >> 4) & 0xFu;
+  if constexpr (DT::ESIZE == 2) {
+    kp.k[0] = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(n0));
+    kp.k[1] = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(n1));
+  } else {
+    kp.k[0] = pick4(n0 & 3u, u.w[0], u.w[1], u.w[2], u.w[3]);
+    kp.k[1] = pick4(n0 >> 2, u.w[0], u.w[1], u.w[2], u.w[3]);
+    kp.k[2] = pick4(n1 & 3u, u.w[4], u.w[5], u.w[6], u.w[7]);
+    kp.k[3] = pick4(n1 >> 2, u.w[4], u.w[5], u.w[6], u.w[7]);
+  }
+  return kp;
+}
+
+// Largest |kept| of a unit as storage bits (non-negative floats order like
+// their bit patterns).
+template <class DT>
+__device__ inline uint32_t kept_absmax(const Kept<DT>& kp) {
+  if constexpr (DT::ESIZE == 2) {
+    const uint32_t a = kp.k[0] & 0x7FFF7FFFu, b = kp.k[1] & 0x7FFF7FFFu;
+    const uint32_t m = (a & 0xFFFFu) > (b & 0xFFFFu) ? (a & 0xFFFFu) : (b & 0xFFFFu);
+    const uint32_t h = (a >> 16) > (b >> 16) ? (a >> 16) : (b >> 16);
+    return m > h ? m : h;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t a = kp.k[e] & 0x7FFFFFFFu;
+      m = m > a ? m : a;
+    }
+    return m;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -162,6 +232,21 @@ __device__ inline float dec_e4m3(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// Four e4m3 codes packed little-endian in a dword (element 0 in byte 0), with
+// gfx950's v_cvt_pk_fp8_f32 (OCP e4m3, RNE).  Over every finite fp32 with
+// |y| < 464 it returns exactly enc_e4m3(y); every caller's |y| is at most
+// 448 * (1 + 2^-23), so no clamp is needed.
+__device__ inline uint32_t enc_e4m3_x4(float a, float b, float c, float d) {
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+}
+
+// Value of an e4m3 code held in byte SEL of w (gfx950 v_cvt_f32_fp8).
+template <int SEL>
+__device__ inline float dec_e4m3_hw(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
 // E2M1 (values 0, .5, 1, 1.5, 2, 3, 4, 6), 4-bit code with sign in bit 3.
 __device__ inline uint32_t enc_e2m1(float y) {
   uint32_t u = __float_as_uint(y);
@@ -184,6 +269,28 @@ __device__ inline float dec_e2m1(uint32_t c) {
   float v = (float)((0xC8643210u >> ((c & 7u) * 4u)) & 0xFu) * 0.5f;
   return (c & 8u) ? -v : v;
 }
+
+// Eight E2M1 codes packed two per byte (element 2j in the low nibble of byte
+// j) with gfx950's v_cvt_scalef32_pk_fp4_f32 at scale 1; over every finite
+// fp32 it returns exactly enc_e2m1 (RNE, saturating at 6, sign copied).
+__device__ inline uint32_t enc_e2m1_x8(const float* y) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
+}
+
+// Symmetric INT rounding through the fp32 adder: for |y| <= qmax < 2^22,
+// fp32(clamp(y) + 1.5 * 2^23) holds round-half-even(clamp(y)) in its low
+// mantissa bits (the add rounds to nearest even at unit spacing).  Clamping
+// before rounding equals clamping after because qmax is an integer.  The low
+// byte / half of the result's bits is the two's-complement code.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
+__device__ inline float int_round_magic(float y, float qmax) {
+  return __builtin_fminf(__builtin_fmaxf(y, -qmax), qmax) + kRoundMagic;
+}
+// code value as an exact float
+__device__ inline float int_code_value(float magic_sum) { return magic_sum - kRoundMagic; }
 
 // Symmetric INT code as float (exact integer value), clamp to [-qmax, qmax].
 __device__ inline float enc_int(float y, float qmax) {
@@ -239,6 +346,58 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 #pragma unroll
     for (int i = 1; i < TEAM / 64; ++i) r += lds[first + i];
     return r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent row driver.  Rows are flattened over (b, r); team k of the grid
+// takes rows k, k + nteams, k + 2*nteams, ... and keeps two rows in flight:
+// the next row's loads are issued before the current row is processed, so
+// HBM traffic overlaps the selection/encode arithmetic.  The trip count is
+// the same for every team, so team reductions that synchronise a workgroup
+// are reached by all of its threads.
+// ---------------------------------------------------------------------------
+struct RowGeom {
+  const char* x;
+  int64_t R, nrows, nunits, bs, rs;  // strides in bytes
+};
+
+__device__ inline const char* row_ptr(const RowGeom& g, int64_t row) {
+  if (g.bs == g.R * g.rs) return g.x + row * g.rs;
+  const int64_t b = row / g.R;
+  return g.x + b * g.bs + (row - b * g.R) * g.rs;
+}
+
+template <class DT, int TEAM, int UPL>
+__device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t row, int t) {
+  const bool act = row < g.nrows;
+  const char* xr = act ? row_ptr(g, row) : g.x;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int64_t i = (int64_t)j * TEAM + t;
+    if (act && i < g.nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+    else zero_unit(u[j]);
+  }
+}
+
+template <class DT, int TEAM, int UPL, class Body>
+__device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
+  constexpr int TPB = kBlock / TEAM;
+  const int t = threadIdx.x % TEAM;
+  const int64_t first = (int64_t)blockIdx.x * TPB + threadIdx.x / TEAM;
+  const int64_t stride = (int64_t)gridDim.x * TPB;
+  const int64_t iters = (g.nrows + stride - 1) / stride;
+  Unit<DT> A[UPL], B[UPL];
+  load_row<DT, TEAM, UPL>(A, g, first, t);
+  for (int64_t it = 0; it < iters; it += 2) {
+    const int64_t ra = first + it * stride;
+    const int64_t rb = ra + stride;
+    load_row<DT, TEAM, UPL>(B, g, rb, t);
+    body(A, ra, t);
+    if (it + 1 < iters) {
+      load_row<DT, TEAM, UPL>(A, g, rb + stride, t);
+      body(B, rb, t);
+    }
   }
 }
 

@@ -50,4 +50,16 @@ inline dim3 row_grid(const RowDesc& d, int team) {
   return dim3((unsigned)((d.R + rpb - 1) / rpb), (unsigned)d.B, 1);
 }
 
+// Grid of a persistent row kernel: enough workgroups to fill every CU
+// kBlocksPerCU times (at most one team per row).
+constexpr int kBlocksPerCU = 2;
+int device_cu_count();
+inline dim3 persistent_grid(int64_t nrows, int team) {
+  const int64_t rpb = kBlock / team;
+  const int64_t need = (nrows + rpb - 1) / rpb;
+  const int64_t cap = (int64_t)device_cu_count() * kBlocksPerCU;
+  const int64_t n = need < cap ? need : cap;
+  return dim3((unsigned)(n > 0 ? n : 1));
+}
+
 }  // namespace sparq24

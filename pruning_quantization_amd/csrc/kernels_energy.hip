@@ -39,175 +39,190 @@ __device__ inline int mx_exp_e(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+template <class DT>
+__device__ inline uint32_t unit_absmax_e(const Unit<DT>& u) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < DT::W; ++i) {
+    if constexpr (DT::ESIZE == 2) {
+      const uint32_t a = u.w[i] & 0x7FFF7FFFu;
+      const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+      const uint32_t h = lo > hi ? lo : hi;
+      m = m > h ? m : h;
+    } else {
+      const uint32_t a = u.w[i] & 0x7FFFFFFFu;
+      m = m > a ? m : a;
+    }
+  }
+  return m;
+}
+
 // squared fp32 residual accumulated in fp64
 __device__ inline void acc_err(double& acc, float xhat_unit, float scale, float v) {
   const float e = __builtin_fmaf(xhat_unit, scale, -v);  // one rounding of code*s - x
   acc = __builtin_fma((double)e, (double)e, acc);
 }
 
+// Quantize-dequantize of 4 values with a per-row scale: returns the 4 code
+// values (exact floats) in c[].  fmt: CF_FP8 or CF_INT8/CF_INT16.
+__device__ inline void qdq_row4(int fmt, float inv, float qmax, const float* v, float* c) {
+  if (fmt == CF_FP8) {
+    const uint32_t w = enc_e4m3_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    c[0] = dec_e4m3_hw<0>(w);
+    c[1] = dec_e4m3_hw<1>(w);
+    c[2] = dec_e4m3_hw<2>(w);
+    c[3] = dec_e4m3_hw<3>(w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = int_code_value(int_round_magic(v[e] * inv, qmax));
+  }
+}
+
 template <class DT, int TEAM, int UPL, bool WANDA>
-__global__ __launch_bounds__(kBlock) void k_energy_rows(
-    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
-    const float* __restrict__ norm, EnergyParams p, double* __restrict__ rowpart,
-    int64_t nrows_total) {
+__global__ __launch_bounds__(kBlock) void k_energy_rows(RowGeom g, const float* __restrict__ norm,
+                                                        EnergyParams p,
+                                                        double* __restrict__ rowpart) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
-  const int t = threadIdx.x % TEAM;
-  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
-  const int64_t b = blockIdx.y;
-  const bool active = r < R;
-  const char* xr = x + b * bs + r * rs;
-  const int64_t orow = b * R + r;
 
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
-  float s_t = 0.f, g = 0.f;
+  float s_t = 0.f, gnv = 0.f;
   if (any_nv) {
     const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
-    if (T >= 0x1p-64f) { s_t = T / 2688.0f; g = 448.0f / T; }
+    if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
   }
+  const int64_t nrows = g.nrows;
 
-  Unit<DT> u[UPL];
-  uint32_t km[UPL];  // 8-bit kept mask per unit
+  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+    const bool writer = row < nrows && t == 0;
+    uint32_t km[UPL];  // 8-bit kept mask per unit
+    uint32_t mbs[UPL];
+    double x2 = 0.0, drop = 0.0;
+    uint32_t amd = 0, amk = 0;
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
-    else zero_unit(u[j]);
-  }
-  double x2 = 0.0, drop = 0.0;
-  uint32_t amd = 0, amk = 0;
-#pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    km[j] = 0;
-    if (i < nunits) {
-      float n8[8];
-      if constexpr (WANDA) {
-        const float4* np = reinterpret_cast<const float4*>(norm + i * 8);
-        float4 a = np[0], c = np[1];
-        n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
-        n8[4] = c.x; n8[5] = c.y; n8[6] = c.z; n8[7] = c.w;
-      }
-      const uint32_t n0 = select_group<DT, WANDA>(u[j], 0, n8);
-      const uint32_t n1 = select_group<DT, WANDA>(u[j], 1, n8 + 4);
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = (int64_t)j * TEAM + t;
+      mbs[j] = 0;
+      if (i < g.nunits) mbs[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+      const uint32_t n0 = mbs[j] & 0xFu, n1 = mbs[j] >> 4;
       km[j] = (1u << (n0 & 3u)) | (1u << (n0 >> 2)) | (16u << (n1 & 3u)) | (16u << (n1 >> 2));
-    }
+      const uint32_t ad = unit_absmax_e(u[j]);
+      amd = amd > ad ? amd : ad;
+      const uint32_t ak = kept_absmax(gather_kept(u[j], mbs[j]));
+      amk = amk > ak ? amk : ak;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = u[j].f(e);
-      const double v2 = (double)v * (double)v;  // exact
-      x2 += v2;
-      const uint32_t a = u[j].absbits(e);
-      amd = amd > a ? amd : a;
-      if ((km[j] >> e) & 1u) amk = amk > a ? amk : a;
-      else drop += v2;
+      for (int e = 0; e < 8; ++e) {
+        const double dv = (double)u[j].f(e);
+        x2 = __builtin_fma(dv, dv, x2);  // exact square
+        const double dd = ((km[j] >> e) & 1u) ? 0.0 : dv;
+        drop = __builtin_fma(dd, dd, drop);
+      }
     }
-  }
-  amd = team_max_u32<TEAM>(amd, redu);
-  amk = team_max_u32<TEAM>(amk, redu);
-  x2 = team_sum_f64<TEAM>(x2, redd);
-  drop = team_sum_f64<TEAM>(drop, redd);
-  const int ncols = 2 + p.kept.n + p.dense.n;
-  const bool writer = active && t == 0;
-  if (writer) {
-    rowpart[0 * nrows_total + orow] = x2;
-    rowpart[1 * nrows_total + orow] = drop;
-  }
-  const float famk = DT::to_f32(amk), famd = DT::to_f32(amd);
+    amd = team_max_u32<TEAM>(amd, redu);
+    amk = team_max_u32<TEAM>(amk, redu);
+    x2 = team_sum_f64<TEAM>(x2, redd);
+    drop = team_sum_f64<TEAM>(drop, redd);
+    if (writer) {
+      rowpart[0 * nrows + row] = x2;
+      rowpart[1 * nrows + row] = drop;
+    }
+    const float famk = DT::to_f32(amk), famd = DT::to_f32(amd);
 
-  // kept-side quantizers (per-row scale from the kept maximum)
-  for (int q = 0; q < p.kept.n; ++q) {
-    const int fmt = p.kept.fmt[q];
-    const float qmax = p.kept.qmax[q];
-    double acc = 0.0;
-    if (fmt != CF_NONE) {
-      float s, inv;
-      row_scale(famk, qmax, s, inv);
+    // kept-side quantizers: per-row scale from the kept maximum
+    for (int q = 0; q < p.kept.n; ++q) {
+      const int fmt = p.kept.fmt[q];
+      const float qmax = p.kept.qmax[q];
+      double acc = 0.0;
+      if (fmt != CF_NONE) {
+        float s, inv;
+        row_scale(famk, qmax, s, inv);
 #pragma unroll
-      for (int j = 0; j < UPL; ++j)
+        for (int j = 0; j < UPL; ++j) {
+          const Kept<DT> kp = gather_kept(u[j], mbs[j]);
+          float v[4], c[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if ((km[j] >> e) & 1u) {
-            const float v = u[j].f(e);
-            const float y = v * inv;
-            const float c = (fmt == CF_FP8) ? dec_e4m3(enc_e4m3(y)) : enc_int(y, qmax);
-            acc_err(acc, c, s, v);
+          for (int e = 0; e < 4; ++e) v[e] = kp.f(e);
+          qdq_row4(fmt, inv, qmax, v, c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
+        }
+      }
+      acc = team_sum_f64<TEAM>(acc, redd);
+      if (writer) rowpart[(int64_t)(2 + q) * nrows + row] = acc;
+    }
+
+    // dense quantizers
+    for (int q = 0; q < p.dense.n; ++q) {
+      const int fmt = p.dense.fmt[q];
+      const float qmax = p.dense.qmax[q];
+      double acc = 0.0;
+      if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
+        float s, inv;
+        row_scale(famd, qmax, s, inv);
+#pragma unroll
+        for (int j = 0; j < UPL; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float v[4], c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = u[j].f(4 * h + e);
+            qdq_row4(fmt, inv, qmax, v, c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
           }
-    }
-    acc = team_sum_f64<TEAM>(acc, redd);
-    if (writer) rowpart[(int64_t)(2 + q) * nrows_total + orow] = acc;
-  }
-
-  // dense quantizers
-  for (int q = 0; q < p.dense.n; ++q) {
-    const int fmt = p.dense.fmt[q];
-    const float qmax = p.dense.qmax[q];
-    double acc = 0.0;
-    if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
-      float s, inv;
-      row_scale(famd, qmax, s, inv);
+      } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
-      for (int j = 0; j < UPL; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = u[j].f(e);
-          const float y = v * inv;
-          const float c = (fmt == CF_FP8) ? dec_e4m3(enc_e4m3(y)) : enc_int(y, qmax);
-          acc_err(acc, c, s, v);
-        }
-    } else if (fmt == CF_MX || fmt == CF_NV) {
-#pragma unroll
-      for (int j = 0; j < UPL; ++j) {
-        uint32_t am = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a = u[j].absbits(e);
-          am = am > a ? am : a;
-        }
-        am = __float_as_uint(DT::to_f32(am));
-        uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
-        am = am > w ? am : w;
-        if (fmt == CF_MX) {
-          w = (uint32_t)__shfl_xor((int)am, 2, 64);
+        for (int j = 0; j < UPL; ++j) {
+          uint32_t am = __float_as_uint(DT::to_f32(unit_absmax_e(u[j])));
+          uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
           am = am > w ? am : w;
-          const int ex = mx_exp_e(am);
-          const float X = __builtin_ldexpf(1.0f, ex);
+          float y[8], v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = u[j].f(e);
-            const float c = dec_e2m1(enc_e2m1(__builtin_ldexpf(v, -ex)));
-            acc_err(acc, c, X, v);
-          }
-        } else {
-          const uint32_t bc = enc_e4m3(__uint_as_float(am) * g);
-          const float bval = dec_e4m3(bc);
-          const float d = bval * s_t;
-          const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+          for (int e = 0; e < 8; ++e) v[e] = u[j].f(e);
+          if (fmt == CF_MX) {
+            w = (uint32_t)__shfl_xor((int)am, 2, 64);
+            am = am > w ? am : w;
+            const int ex = mx_exp_e(am);
+            const float X = __builtin_ldexpf(1.0f, ex);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = u[j].f(e);
-            const float c = dec_e2m1(enc_e2m1(v * inv));
-            acc_err(acc, c * bval, s_t, v);
+            for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(v[e], -ex);
+            const uint32_t pk = enc_e2m1_x8(y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc_err(acc, dec_e2m1((pk >> (4 * e)) & 0xFu), X, v[e]);
+          } else {
+            const uint32_t bc = enc_e4m3(__uint_as_float(am) * gnv);
+            const float bval = dec_e4m3(bc);
+            const float d = bval * s_t;
+            const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = v[e] * inv;
+            const uint32_t pk = enc_e2m1_x8(y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc_err(acc, dec_e2m1((pk >> (4 * e)) & 0xFu) * bval, s_t, v[e]);
           }
         }
       }
+      acc = team_sum_f64<TEAM>(acc, redd);
+      if (writer) rowpart[(int64_t)(2 + p.kept.n + q) * nrows + row] = acc;
     }
-    acc = team_sum_f64<TEAM>(acc, redd);
-    if (writer) rowpart[(int64_t)(2 + p.kept.n + q) * nrows_total + orow] = acc;
-  }
-  (void)ncols;
+  });
 }
 
-// Sum of rows [blk*rpb, min(nrows, (blk+1)*rpb)) of one column: grid (nblk, ncols).
+// Stage 1: sum of one column over one chunk of at most kChunk rows that lies
+// inside one block of rows: grid (nblk * chunks_per_block, ncols).
+constexpr int64_t kChunk = 2048;
+
 __global__ __launch_bounds__(kBlock) void k_energy_colsum(const double* __restrict__ rowpart,
-                                                          int64_t nrows, int64_t rpb,
-                                                          double* __restrict__ sums, int ncols) {
+                                                          int64_t nrows, int64_t rpb, int64_t cpb,
+                                                          double* __restrict__ csum, int ncols) {
   __shared__ double sh[kBlock];
-  const int64_t blk = blockIdx.x;
+  const int64_t chunk = blockIdx.x;
   const int c = blockIdx.y;
-  const int64_t r0 = blk * rpb;
-  const int64_t r1 = (r0 + rpb) < nrows ? (r0 + rpb) : nrows;
+  const int64_t blk = chunk / cpb, k = chunk % cpb;
+  const int64_t bend = (blk + 1) * rpb < nrows ? (blk + 1) * rpb : nrows;
+  const int64_t r0 = blk * rpb + k * kChunk;
+  const int64_t r1 = (r0 + kChunk) < bend ? (r0 + kChunk) : bend;
   const double* col = rowpart + (int64_t)c * nrows;
   double acc = 0.0;
   for (int64_t r = r0 + threadIdx.x; r < r1; r += kBlock) acc += col[r];
@@ -217,15 +232,22 @@ __global__ __launch_bounds__(kBlock) void k_energy_colsum(const double* __restri
     if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) sums[blk * ncols + c] = sh[0];
+  if (threadIdx.x == 0) csum[chunk * ncols + c] = sh[0];
 }
 
-__global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restrict__ sums,
-                                                           int64_t nblk, FinalizeParams f,
+// Stage 2: per block of rows, add its chunk sums in order and form the outputs.
+__global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restrict__ csum,
+                                                           int64_t nblk, int64_t cpb,
+                                                           FinalizeParams f,
                                                            double* __restrict__ out) {
   const int64_t blk = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (blk >= nblk) return;
-  const double* sb = sums + blk * f.ncols;
+  double sb[2 + 2 * kMaxQ];
+  for (int c = 0; c < f.ncols; ++c) {
+    double a = 0.0;
+    for (int64_t k = 0; k < cpb; ++k) a += csum[(blk * cpb + k) * f.ncols + c];
+    sb[c] = a;
+  }
   if (f.mode == 0) {
     double* o = out + blk * 4;
     o[0] = sb[0];
@@ -252,32 +274,35 @@ __global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restr
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               const EnergyParams& p, double* rowpart, hipStream_t s) {
   const int64_t nunits = d.K / 8;
-  const int64_t nrows = d.B * d.R;
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+      const dim3 grid = persistent_grid(g.nrows, TEAM);
       if (wanda)
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true>), row_grid(d, TEAM), dim3(kBlock),
-                           0, s, d.x, d.R, nunits, d.bs, d.rs, norm, p, rowpart, nrows);
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g, norm,
+                           p, rowpart);
       else
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false>), row_grid(d, TEAM),
-                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, p, rowpart,
-                           nrows);
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
+                           norm, p, rowpart);
       return hipGetLastError();
     });
   });
 }
 
+int64_t energy_chunks_per_block(int64_t rows_per_block) {
+  return (rows_per_block + kChunk - 1) / kChunk;
+}
+
 hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t rows_per_block,
-                                  int64_t nblk, const FinalizeParams& f, double* out,
+                                  int64_t nblk, const FinalizeParams& f, double* csum, double* out,
                                   hipStream_t s) {
-  // the block sums live right after the row partials in the workspace
-  double* sums = const_cast<double*>(rowpart) + (int64_t)f.ncols * nrows;
-  hipLaunchKernelGGL(k_energy_colsum, dim3((unsigned)nblk, (unsigned)f.ncols), dim3(kBlock), 0, s,
-                     rowpart, nrows, rows_per_block, sums, f.ncols);
+  const int64_t cpb = energy_chunks_per_block(rows_per_block);
+  hipLaunchKernelGGL(k_energy_colsum, dim3((unsigned)(nblk * cpb), (unsigned)f.ncols),
+                     dim3(kBlock), 0, s, rowpart, nrows, rows_per_block, cpb, csum, f.ncols);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_energy_combine, dim3((unsigned)((nblk + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, s, sums, nblk, f, out);
+                     dim3(kBlock), 0, s, csum, nblk, cpb, f, out);
   return hipGetLastError();
 }
 

@@ -10,6 +10,20 @@ namespace sparq24 {
 
 constexpr int kColStrips = 128;
 
+// Compute units of the current device, cached per device id.
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 int col_strips(const RowDesc& d) {
   const int64_t rows = d.B * d.R;
   return (int)(rows < kColStrips ? (rows > 0 ? rows : 1) : kColStrips);

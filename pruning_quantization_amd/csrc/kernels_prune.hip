@@ -12,40 +12,14 @@
 
 namespace sparq24 {
 
-// ---------------------------------------------------------------------------
-// Shared per-unit work: two group selections and the kept raw values.
-// ---------------------------------------------------------------------------
-template <class DT, bool WANDA>
-__device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restrict__ norm,
-                                       int64_t k0) {
-  float n8[8];
-  if constexpr (WANDA) {
-    const float4* np = reinterpret_cast<const float4*>(norm + k0);
-    float4 a = np[0], b = np[1];
-    n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
-    n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
-  }
-  uint32_t n0 = select_group<DT, WANDA>(u, 0, n8);
-  uint32_t n1 = select_group<DT, WANDA>(u, 1, n8 + 4);
-  return n0 | (n1 << 4);
-}
-
 // Store the 4 kept raw elements of a unit (storage type) at dst.
 template <class DT>
 __device__ inline void store_kept(const Unit<DT>& u, uint32_t mb, char* dst) {
-  const uint32_t n0 = mb & 0xFu, n1 = mb >> 4;
+  const Kept<DT> kp = gather_kept(u, mb);
   if constexpr (DT::ESIZE == 2) {
-    uint2 o;
-    o.x = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(n0));
-    o.y = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(n1));
-    *reinterpret_cast<uint2*>(dst) = o;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(kp.k[0], kp.k[1]);
   } else {
-    uint4 o;
-    o.x = kept_raw(u, 0, n0, 0);
-    o.y = kept_raw(u, 0, n0, 1);
-    o.z = kept_raw(u, 1, n1, 0);
-    o.w = kept_raw(u, 1, n1, 1);
-    *reinterpret_cast<uint4*>(dst) = o;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(kp.k[0], kp.k[1], kp.k[2], kp.k[3]);
   }
 }
 
@@ -209,84 +183,58 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
 // Fused prune + compress + quantize of the kept values, one scale per row.
 // A team holds its whole row in registers: one read, then the kept absolute
 // maximum (team reduction), then codes, metadata and the scale are written.
+// Teams are persistent and keep the next row's loads in flight.
 // ---------------------------------------------------------------------------
 template <class DT, int TEAM, int UPL, bool WANDA>
 __global__ __launch_bounds__(kBlock) void k_prune_quantize(
-    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
-    const float* __restrict__ norm, int cfmt, float qmax, char* __restrict__ codes,
+    RowGeom g, const float* __restrict__ norm, int cfmt, float qmax, char* __restrict__ codes,
     uint8_t* __restrict__ meta, float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
-  const int t = threadIdx.x % TEAM;
-  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
-  const int64_t b = blockIdx.y;
-  const bool active = r < R;
-  const char* xr = x + b * bs + r * rs;
-  const int64_t orow = b * R + r;
-
-  Unit<DT> u[UPL];
-  uint32_t mb[UPL];
+  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+    const bool active = row < g.nrows;
+    uint32_t mb[UPL];
+    uint32_t am = 0;  // largest |kept| as storage bits (orders like the value)
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
-    else zero_unit(u[j]);
-  }
-  uint32_t am = 0;  // largest |kept| as storage bits (orders like the value)
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = (int64_t)j * TEAM + t;
+      mb[j] = 0;
+      if (i < g.nunits) mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+      const uint32_t a = kept_absmax(gather_kept(u[j], mb[j]));  // zero units gather zeros
+      am = am > a ? am : a;
+    }
+    am = team_max_u32<TEAM>(am, red);
+    if (!active) return;
+    float s, inv;
+    row_scale(DT::to_f32(am), qmax, s, inv);
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    mb[j] = 0;
-    if (i < nunits) {
-      mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = (int64_t)j * TEAM + t;
+      if (i < g.nunits) {
+        const Kept<DT> kp = gather_kept(u[j], mb[j]);
+        const int64_t o = row * g.nunits + i;  // unit index in the output
+        if (cfmt == CF_FP8) {
+          reinterpret_cast<uint32_t*>(codes)[o] =
+              enc_e4m3_x4(kp.f(0) * inv, kp.f(1) * inv, kp.f(2) * inv, kp.f(3) * inv);
+        } else {
+          float r[4];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint32_t nib = (mb[j] >> (4 * g)) & 0xFu;
-        const uint32_t a0 = kept_raw(u[j], g, nib, 0) & DT::ABS;
-        const uint32_t a1 = kept_raw(u[j], g, nib, 1) & DT::ABS;
-        am = am > a0 ? am : a0;
-        am = am > a1 ? am : a1;
+          for (int e = 0; e < 4; ++e) r[e] = int_round_magic(kp.f(e) * inv, qmax);
+          if (cfmt == CF_INT8) {
+            const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(r[1]), __float_as_uint(r[0]), 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(r[3]), __float_as_uint(r[2]), 0x0c0c0400u);
+            reinterpret_cast<uint32_t*>(codes)[o] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          } else {  // CF_INT16
+            uint2 w;
+            w.x = __builtin_amdgcn_perm(__float_as_uint(r[1]), __float_as_uint(r[0]), 0x05040100u);
+            w.y = __builtin_amdgcn_perm(__float_as_uint(r[3]), __float_as_uint(r[2]), 0x05040100u);
+            reinterpret_cast<uint2*>(codes)[o] = w;
+          }
+        }
+        meta[o] = (uint8_t)mb[j];
       }
     }
-  }
-  am = team_max_u32<TEAM>(am, red);
-  if (!active) return;
-  float s, inv;
-  row_scale(DT::to_f32(am), qmax, s, inv);
-
-#pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    if (i < nunits) {
-      float kv[4];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint32_t nib = (mb[j] >> (4 * g)) & 0xFu;
-        kv[2 * g + 0] = DT::to_f32(kept_raw(u[j], g, nib, 0));
-        kv[2 * g + 1] = DT::to_f32(kept_raw(u[j], g, nib, 1));
-      }
-      const int64_t o = orow * nunits + i;  // unit index in the output
-      if (cfmt == CF_FP8) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w |= enc_e4m3(kv[e] * inv) << (8 * e);
-        reinterpret_cast<uint32_t*>(codes)[o] = w;
-      } else if (cfmt == CF_INT8) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w |= ((uint32_t)(int)enc_int(kv[e] * inv, qmax) & 0xFFu) << (8 * e);
-        reinterpret_cast<uint32_t*>(codes)[o] = w;
-      } else {  // CF_INT16
-        uint2 w;
-        w.x = ((uint32_t)(int)enc_int(kv[0] * inv, qmax) & 0xFFFFu) |
-              ((uint32_t)(int)enc_int(kv[1] * inv, qmax) << 16);
-        w.y = ((uint32_t)(int)enc_int(kv[2] * inv, qmax) & 0xFFFFu) |
-              ((uint32_t)(int)enc_int(kv[3] * inv, qmax) << 16);
-        reinterpret_cast<uint2*>(codes)[o] = w;
-      }
-      meta[o] = (uint8_t)mb[j];
-    }
-  }
-  if (t == 0) scales[orow] = s;
+    if (t == 0) scales[row] = s;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -337,16 +285,16 @@ hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm
                                  float qmax, void* codes, uint8_t* meta, float* scales,
                                  hipStream_t s) {
   const int64_t nunits = d.K / 8;
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+      const dim3 grid = persistent_grid(g.nrows, TEAM);
       if (wanda)
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, true>), row_grid(d, TEAM),
-                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, cfmt, qmax,
-                           (char*)codes, meta, scales);
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g,
+                           norm, cfmt, qmax, (char*)codes, meta, scales);
       else
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, false>), row_grid(d, TEAM),
-                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, cfmt, qmax,
-                           (char*)codes, meta, scales);
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
+                           norm, cfmt, qmax, (char*)codes, meta, scales);
       return hipGetLastError();
     });
   });

@@ -11,69 +11,79 @@ namespace sparq24 {
 
 // ---------------------------------------------------------------------------
 // Per-row INT-b / FP8: the team holds its row, reduces |x|max, encodes.
+// Persistent teams keep the next row's loads in flight.
 // ---------------------------------------------------------------------------
-template <class DT, int TEAM, int UPL>
-__global__ __launch_bounds__(kBlock) void k_quant_rows(
-    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs, int cfmt,
-    float qmax, char* __restrict__ codes, float* __restrict__ scales) {
-  __shared__ uint32_t red[kBlock / 64];
-  const int t = threadIdx.x % TEAM;
-  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
-  const int64_t b = blockIdx.y;
-  const bool active = r < R;
-  const char* xr = x + b * bs + r * rs;
-  const int64_t orow = b * R + r;
-
-  Unit<DT> u[UPL];
-  uint32_t am = 0;
+template <class DT>
+__device__ inline uint32_t unit_absmax(const Unit<DT>& u) {
+  if constexpr (DT::ESIZE == 2) {
+    uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
-    else zero_unit(u[j]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = u.w[i] & 0x7FFF7FFFu;
+      const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+      const uint32_t h = lo > hi ? lo : hi;
+      m = m > h ? m : h;
+    }
+    return m;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = u.w[i] & 0x7FFFFFFFu;
+      m = m > a ? m : a;
+    }
+    return m;
   }
+}
+
+template <class DT, int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_quant_rows(RowGeom g, int cfmt, float qmax,
+                                                       char* __restrict__ codes,
+                                                       float* __restrict__ scales) {
+  __shared__ uint32_t red[kBlock / 64];
+  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+    uint32_t am = 0;
 #pragma unroll
-  for (int j = 0; j < UPL; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = u[j].absbits(e);
+    for (int j = 0; j < UPL; ++j) {
+      const uint32_t a = unit_absmax(u[j]);
       am = am > a ? am : a;
     }
-  am = team_max_u32<TEAM>(am, red);
-  if (!active) return;
-  float s, inv;
-  row_scale(DT::to_f32(am), qmax, s, inv);
+    am = team_max_u32<TEAM>(am, red);
+    if (row >= g.nrows) return;
+    float s, inv;
+    row_scale(DT::to_f32(am), qmax, s, inv);
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int64_t i = (int64_t)j * TEAM + t;
-    if (i < nunits) {
-      const int64_t o = orow * nunits + i;
-      if (cfmt == CF_FP8) {
-        uint2 w = {0u, 0u};
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = (int64_t)j * TEAM + t;
+      if (i < g.nunits) {
+        const int64_t o = row * g.nunits + i;
+        float y[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w.x |= enc_e4m3(u[j].f(e) * inv) << (8 * e);
+        for (int e = 0; e < 8; ++e) y[e] = u[j].f(e) * inv;
+        if (cfmt == CF_FP8) {
+          reinterpret_cast<uint2*>(codes)[o] =
+              make_uint2(enc_e4m3_x4(y[0], y[1], y[2], y[3]), enc_e4m3_x4(y[4], y[5], y[6], y[7]));
+        } else {
+          uint32_t r[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w.y |= enc_e4m3(u[j].f(4 + e) * inv) << (8 * e);
-        reinterpret_cast<uint2*>(codes)[o] = w;
-      } else if (cfmt == CF_INT8) {
-        uint2 w = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w.x |= ((uint32_t)(int)enc_int(u[j].f(e) * inv, qmax) & 0xFFu) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w.y |= ((uint32_t)(int)enc_int(u[j].f(4 + e) * inv, qmax) & 0xFFu) << (8 * e);
-        reinterpret_cast<uint2*>(codes)[o] = w;
-      } else {  // CF_INT16
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (uint32_t)(int)enc_int(u[j].f(e) * inv, qmax) & 0xFFFFu;
-        uint4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        reinterpret_cast<uint4*>(codes)[o] = w;
+          for (int e = 0; e < 8; ++e) r[e] = __float_as_uint(int_round_magic(y[e], qmax));
+          if (cfmt == CF_INT8) {
+            const uint32_t a = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+            const uint32_t b = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+            const uint32_t c = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
+            const uint32_t d = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
+            reinterpret_cast<uint2*>(codes)[o] = make_uint2(__builtin_amdgcn_perm(b, a, 0x05040100u),
+                                                            __builtin_amdgcn_perm(d, c, 0x05040100u));
+          } else {  // CF_INT16
+            reinterpret_cast<uint4*>(codes)[o] = make_uint4(
+                __builtin_amdgcn_perm(r[1], r[0], 0x05040100u), __builtin_amdgcn_perm(r[3], r[2], 0x05040100u),
+                __builtin_amdgcn_perm(r[5], r[4], 0x05040100u), __builtin_amdgcn_perm(r[7], r[6], 0x05040100u));
+          }
+        }
       }
     }
-  }
-  if (t == 0) scales[orow] = s;
+    if (t == 0) scales[row] = s;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -227,9 +237,10 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
         w = (uint32_t)__shfl_xor((int)am, 2, 64);
         am = am > w ? am : w;
         const int e = mx_exponent(am);
-        uint32_t pk = 0;
+        float y[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) pk |= enc_e2m1(__builtin_ldexpf(u[j].f(q), -e)) << (4 * q);
+        for (int q = 0; q < 8; ++q) y[q] = __builtin_ldexpf(u[j].f(q), -e);
+        const uint32_t pk = enc_e2m1_x8(y);
         if (active && i < nunits) {
           codes[orow * nunits + i] = pk;
           if ((i & 3) == 0) scales[orow * (nunits / 4) + (i >> 2)] = (uint8_t)(e + 127);
@@ -238,9 +249,10 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
         const uint32_t bc = enc_e4m3(__uint_as_float(am) * g);
         const float d = dec_e4m3(bc) * s_t;
         const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-        uint32_t pk = 0;
+        float y[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) pk |= enc_e2m1(u[j].f(q) * inv) << (4 * q);
+        for (int q = 0; q < 8; ++q) y[q] = u[j].f(q) * inv;
+        const uint32_t pk = enc_e2m1_x8(y);
         if (active && i < nunits) {
           codes[orow * nunits + i] = pk;
           if ((i & 1) == 0) scales[orow * (nunits / 2) + (i >> 1)] = (uint8_t)bc;
@@ -253,10 +265,11 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
 hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
                              hipStream_t s) {
   const int64_t nunits = d.K / 8;
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL>), row_grid(d, TEAM), dim3(kBlock), 0, s,
-                         d.x, d.R, nunits, d.bs, d.rs, cfmt, qmax, (char*)codes, scales);
+      hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL>), persistent_grid(g.nrows, TEAM),
+                         dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
       return hipGetLastError();
     });
   });

@@ -61,8 +61,9 @@ struct FinalizeParams {
   int dcol[kMaxQ];      // column of the dense error of pair p
   int mode;
 };
+int64_t energy_chunks_per_block(int64_t rows_per_block);
 hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t rows_per_block,
-                                  int64_t nblk, const FinalizeParams& f, double* out,
+                                  int64_t nblk, const FinalizeParams& f, double* csum, double* out,
                                   hipStream_t s);
 int col_strips(const RowDesc& d);
 hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s);
