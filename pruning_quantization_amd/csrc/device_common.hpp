@@ -15,6 +15,18 @@ namespace sparq24 {
 
 constexpr int kBlock = 256;  // threads per workgroup for every row kernel
 
+// Occupancy hint for the row kernels (waves per SIMD the register budget
+// must allow); 0 leaves the choice to the compiler.
+#ifndef SPARQ24_WAVES_PER_EU
+#define SPARQ24_WAVES_PER_EU 0
+#endif
+#if SPARQ24_WAVES_PER_EU > 0
+#define SPARQ24_ROW_KERNEL __global__ __launch_bounds__(kBlock) \
+  __attribute__((amdgpu_waves_per_eu(SPARQ24_WAVES_PER_EU)))
+#else
+#define SPARQ24_ROW_KERNEL __global__ __launch_bounds__(kBlock)
+#endif
+
 // ---------------------------------------------------------------------------
 // Storage types.  W = dwords per 8-element unit.
 // ---------------------------------------------------------------------------
@@ -130,6 +142,64 @@ __device__ inline uint32_t perm_sel(uint32_t nib) {
 }
 
 // ---------------------------------------------------------------------------
+// Packed unsigned 16-bit max of two dwords (v_pk_max_u16).
+typedef unsigned short sparq24_u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(sparq24_u16x2, a),
+                                                                __builtin_bit_cast(sparq24_u16x2, b)));
+}
+
+// Largest |x| of a 16-bit unit as storage bits, via packed 16-bit max.
+__device__ inline uint32_t unit_absmax16_packed(const uint32_t* w, uint32_t acc2) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc2 = pk_max_u16(acc2, w[i] & 0x7FFF7FFFu);
+  return acc2;
+}
+__device__ inline uint32_t unpack_max16(uint32_t acc2) {
+  const uint32_t lo = acc2 & 0xFFFFu, hi = acc2 >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// Magnitude selection for a 16-bit unit, everything in 32-bit lanes:
+//  keys  = |x| in bits 16..30, (3 - position) in bits 0..1 (from the pair of
+//          elements in one dword: 3 ops per pair);
+//  top2  = 7-op max/min network;
+//  i0/i1 = 3 - max(j), 3 - min(j) with j the winners' low bits;
+//  kept  = byte permute with selector bytes (2*i0, 2*i0+1, 2*i1, 2*i1+1),
+//          i.e. 0x07060706 - (jmax | jmin << 16) * 0x0202;
+//  amax  = the top key of each group (its high half is the group's |max|,
+//          which magnitude pruning always keeps).
+struct Sel16 {
+  uint32_t mb;      // metadata byte
+  uint32_t k0, k1;  // kept pairs of group 0 and 1 (position order)
+  uint32_t topkey;  // max of the two groups' top keys
+};
+
+__device__ inline void sel16_group(uint32_t w0, uint32_t w1, uint32_t& nib, uint32_t& kept,
+                                   uint32_t& top) {
+  const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
+  const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
+  const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
+  uint32_t t1, t2;
+  top2(k0, k1, k2, k3, t1, t2);
+  const uint32_t j1 = t1 & 3u, j2 = t2 & 3u;
+  const uint32_t jmax = j1 > j2 ? j1 : j2, jmin = j1 > j2 ? j2 : j1;
+  nib = 15u - jmax - 4u * jmin;
+  const uint32_t sel = 0x07060706u - __umul24(jmax | (jmin << 16), 0x0202u);
+  kept = __builtin_amdgcn_perm(w1, w0, sel);
+  top = t1;
+}
+
+__device__ inline Sel16 select16(const uint32_t* w) {
+  Sel16 r;
+  uint32_t n0, n1, t0, t1;
+  sel16_group(w[0], w[1], n0, r.k0, t0);
+  sel16_group(w[2], w[3], n1, r.k1, t1);
+  r.mb = n0 | (n1 << 4);
+  r.topkey = t0 > t1 ? t0 : t1;
+  return r;
+}
+
 // Both group selections of a unit -> metadata byte (group 0 in the low nibble).
 // Wanda reads the 8 channel norms of the unit (k0 = its first position).
 // ---------------------------------------------------------------------------
@@ -287,7 +357,7 @@ __device__ inline uint32_t enc_e2m1_x8(const float* y) {
 // byte / half of the result's bits is the two's-complement code.
 constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
 __device__ inline float int_round_magic(float y, float qmax) {
-  return __builtin_fminf(__builtin_fmaxf(y, -qmax), qmax) + kRoundMagic;
+  return __builtin_amdgcn_fmed3f(y, -qmax, qmax) + kRoundMagic;
 }
 // code value as an exact float
 __device__ inline float int_code_value(float magic_sum) { return magic_sum - kRoundMagic; }
@@ -351,11 +421,12 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 
 // ---------------------------------------------------------------------------
 // Persistent row driver.  Rows are flattened over (b, r); team k of the grid
-// takes rows k, k + nteams, k + 2*nteams, ... and keeps two rows in flight:
-// the next row's loads are issued before the current row is processed, so
-// HBM traffic overlaps the selection/encode arithmetic.  The trip count is
-// the same for every team, so team reductions that synchronise a workgroup
-// are reached by all of its threads.
+// takes rows k, k + nteams, k + 2*nteams, ...  With SPARQ24_PIPELINE=1 a team
+// keeps two rows in flight (the next row's loads are issued before the
+// current row is processed); the default single-buffered form measured
+// faster on MI355X because its lower register count admits more waves per
+// SIMD.  The trip count is the same for every team, so team reductions that
+// synchronise a workgroup are reached by all of its threads.
 // ---------------------------------------------------------------------------
 struct RowGeom {
   const char* x;
@@ -380,6 +451,10 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
   }
 }
 
+#ifndef SPARQ24_PIPELINE
+#define SPARQ24_PIPELINE 0
+#endif
+
 template <class DT, int TEAM, int UPL, class Body>
 __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
   constexpr int TPB = kBlock / TEAM;
@@ -387,6 +462,15 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
   const int64_t first = (int64_t)blockIdx.x * TPB + threadIdx.x / TEAM;
   const int64_t stride = (int64_t)gridDim.x * TPB;
   const int64_t iters = (g.nrows + stride - 1) / stride;
+  if constexpr (!SPARQ24_PIPELINE) {
+    for (int64_t it = 0; it < iters; ++it) {
+      Unit<DT> A[UPL];
+      const int64_t ra = first + it * stride;
+      load_row<DT, TEAM, UPL>(A, g, ra, t);
+      body(A, ra, t);
+    }
+    return;
+  }
   Unit<DT> A[UPL], B[UPL];
   load_row<DT, TEAM, UPL>(A, g, first, t);
   for (int64_t it = 0; it < iters; it += 2) {

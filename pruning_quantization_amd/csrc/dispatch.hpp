@@ -27,7 +27,14 @@ inline hipError_t with_row_variant(int64_t nunits, F&& f) {
   if (nunits <= 64) return f.template operator()<64, 1>();
   if (nunits <= 128) return f.template operator()<64, 2>();
   if (nunits <= 256) return f.template operator()<64, 4>();
-  if (nunits <= 512) return f.template operator()<64, 8>();
+#ifndef SPARQ24_WIDE
+#define SPARQ24_WIDE 0
+#endif
+  if (nunits <= 512) {
+    if constexpr (SPARQ24_WIDE == 1) return f.template operator()<128, 4>();
+    else if constexpr (SPARQ24_WIDE == 2) return f.template operator()<256, 2>();
+    else return f.template operator()<64, 8>();
+  }
   if (nunits <= 1024) return f.template operator()<64, 16>();
   if (nunits <= 2048) return f.template operator()<256, 8>();
   if (nunits <= 4096) return f.template operator()<256, 16>();
@@ -52,7 +59,10 @@ inline dim3 row_grid(const RowDesc& d, int team) {
 
 // Grid of a persistent row kernel: enough workgroups to fill every CU
 // kBlocksPerCU times (at most one team per row).
-constexpr int kBlocksPerCU = 2;
+#ifndef SPARQ24_BLOCKS_PER_CU
+#define SPARQ24_BLOCKS_PER_CU 4
+#endif
+constexpr int kBlocksPerCU = SPARQ24_BLOCKS_PER_CU;
 int device_cu_count();
 inline dim3 persistent_grid(int64_t nrows, int team) {
   const int64_t rpb = kBlock / team;

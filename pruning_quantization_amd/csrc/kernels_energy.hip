@@ -79,7 +79,7 @@ __device__ inline void qdq_row4(int fmt, float inv, float qmax, const float* v, 
 }
 
 template <class DT, int TEAM, int UPL, bool WANDA>
-__global__ __launch_bounds__(kBlock) void k_energy_rows(RowGeom g, const float* __restrict__ norm,
+SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
                                                         EnergyParams p,
                                                         double* __restrict__ rowpart) {
   __shared__ uint32_t redu[kBlock / 64];

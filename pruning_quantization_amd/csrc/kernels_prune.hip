@@ -183,55 +183,89 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
 // Fused prune + compress + quantize of the kept values, one scale per row.
 // A team holds its whole row in registers: one read, then the kept absolute
 // maximum (team reduction), then codes, metadata and the scale are written.
-// Teams are persistent and keep the next row's loads in flight.
+// Teams are persistent and keep the next row's loads in flight.  CF (the
+// code format) is a template parameter so each variant is straight-line code.
 // ---------------------------------------------------------------------------
-template <class DT, int TEAM, int UPL, bool WANDA>
-__global__ __launch_bounds__(kBlock) void k_prune_quantize(
-    RowGeom g, const float* __restrict__ norm, int cfmt, float qmax, char* __restrict__ codes,
-    uint8_t* __restrict__ meta, float* __restrict__ scales) {
+template <int CF>
+__device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
+  if constexpr (CF == CF_FP8) {
+    *reinterpret_cast<uint32_t*>(dst) = enc_e4m3_x4(y[0], y[1], y[2], y[3]);
+  } else {
+    uint32_t r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(int_round_magic(y[e], qmax));
+    if constexpr (CF == CF_INT8) {
+      const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_amdgcn_perm(r[1], r[0], 0x05040100u),
+                                                  __builtin_amdgcn_perm(r[3], r[2], 0x05040100u));
+    }
+  }
+}
+
+template <class DT, int TEAM, int UPL, bool WANDA, int CF>
+SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ norm, float qmax,
+                                         char* __restrict__ codes, uint8_t* __restrict__ meta,
+                                         float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
+  constexpr int CB = CF == CF_INT16 ? 8 : 4;  // code bytes per unit
+  // 16-bit magnitude: the kept maximum of a row equals its plain maximum
+  // (every group keeps its largest element), so the scale comes from one
+  // packed-max pass over the raw row and selection + encode stream unit by
+  // unit afterwards.
+  constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA;
   for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
-    uint32_t mb[UPL];
-    uint32_t am = 0;  // largest |kept| as storage bits (orders like the value)
+    uint32_t am = 0;
+    uint32_t mb[FAST16 ? 1 : UPL];
+    if constexpr (FAST16) {
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const int64_t i = (int64_t)j * TEAM + t;
-      mb[j] = 0;
-      if (i < g.nunits) mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
-      const uint32_t a = kept_absmax(gather_kept(u[j], mb[j]));  // zero units gather zeros
-      am = am > a ? am : a;
+      for (int j = 0; j < UPL; ++j) am = unit_absmax16_packed(u[j].w, am);
+      am = unpack_max16(am);
+    } else {
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const int64_t i = (int64_t)j * TEAM + t;
+        mb[j] = 0;
+        if (i < g.nunits) mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+        const uint32_t a = kept_absmax(gather_kept(u[j], mb[j]));  // zero units gather zeros
+        am = am > a ? am : a;
+      }
     }
     am = team_max_u32<TEAM>(am, red);
     if (!active) return;
     float s, inv;
     row_scale(DT::to_f32(am), qmax, s, inv);
-#pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const int64_t i = (int64_t)j * TEAM + t;
-      if (i < g.nunits) {
-        const Kept<DT> kp = gather_kept(u[j], mb[j]);
-        const int64_t o = row * g.nunits + i;  // unit index in the output
-        if (cfmt == CF_FP8) {
-          reinterpret_cast<uint32_t*>(codes)[o] =
-              enc_e4m3_x4(kp.f(0) * inv, kp.f(1) * inv, kp.f(2) * inv, kp.f(3) * inv);
-        } else {
-          float r[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = int_round_magic(kp.f(e) * inv, qmax);
-          if (cfmt == CF_INT8) {
-            const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(r[1]), __float_as_uint(r[0]), 0x0c0c0400u);
-            const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(r[3]), __float_as_uint(r[2]), 0x0c0c0400u);
-            reinterpret_cast<uint32_t*>(codes)[o] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-          } else {  // CF_INT16
-            uint2 w;
-            w.x = __builtin_amdgcn_perm(__float_as_uint(r[1]), __float_as_uint(r[0]), 0x05040100u);
-            w.y = __builtin_amdgcn_perm(__float_as_uint(r[3]), __float_as_uint(r[2]), 0x05040100u);
-            reinterpret_cast<uint2*>(codes)[o] = w;
-          }
-        }
-        meta[o] = (uint8_t)mb[j];
+    // per-row output bases; unit j of this lane sits at a constant offset
+    char* crow = codes + (row * g.nunits + t) * CB;
+    uint8_t* mrow = meta + row * g.nunits + t;
+    auto emit = [&](int j) {
+      Kept<DT> kp;
+      uint32_t m;
+      if constexpr (FAST16) {
+        const Sel16 r = select16(u[j].w);
+        kp.k[0] = r.k0;
+        kp.k[1] = r.k1;
+        m = r.mb;
+      } else {
+        kp = gather_kept(u[j], mb[j]);
+        m = mb[j];
       }
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = kp.f(e) * inv;
+      store_kept_codes<CF>(crow + j * TEAM * CB, y, qmax);
+      mrow[j * TEAM] = (uint8_t)m;
+    };
+    if ((UPL - 1) * TEAM + t < g.nunits) {  // every unit of this lane exists
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) emit(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < UPL; ++j)
+        if (j * TEAM + t < g.nunits) emit(j);
     }
     if (t == 0) scales[row] = s;
   });
@@ -289,13 +323,19 @@ hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
-      if (wanda)
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g,
-                           norm, cfmt, qmax, (char*)codes, meta, scales);
-      else
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
-                           norm, cfmt, qmax, (char*)codes, meta, scales);
-      return hipGetLastError();
+      auto go = [&]<bool W, int CF>() {
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF>), grid, dim3(kBlock), 0, s, g,
+                           norm, qmax, (char*)codes, meta, scales);
+        return hipGetLastError();
+      };
+      if (wanda) {
+        if (cfmt == CF_FP8) return go.template operator()<true, CF_FP8>();
+        if (cfmt == CF_INT8) return go.template operator()<true, CF_INT8>();
+        return go.template operator()<true, CF_INT16>();
+      }
+      if (cfmt == CF_FP8) return go.template operator()<false, CF_FP8>();
+      if (cfmt == CF_INT8) return go.template operator()<false, CF_INT8>();
+      return go.template operator()<false, CF_INT16>();
     });
   });
 }

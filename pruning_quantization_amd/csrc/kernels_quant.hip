@@ -37,7 +37,7 @@ __device__ inline uint32_t unit_absmax(const Unit<DT>& u) {
 }
 
 template <class DT, int TEAM, int UPL>
-__global__ __launch_bounds__(kBlock) void k_quant_rows(RowGeom g, int cfmt, float qmax,
+SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
                                                        char* __restrict__ codes,
                                                        float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
