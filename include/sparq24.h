@@ -19,9 +19,12 @@
  *                   Q/K [heads*seq, head_dim], P [heads*q, keys]);
  *     transposed:   row_stride == 1 and k_stride >= R (e.g. V [heads, seq,
  *                   head_dim] pruned along seq: B = heads, R = head_dim,
- *                   K = seq, k_stride = head_dim).  Only
- *                   sparq24_prune_compress accepts it; the other calls
- *                   return SPARQ24_ERR_UNSUPPORTED for it.
+ *                   K = seq, k_stride = head_dim).  sparq24_prune_compress
+ *                   reads it directly through an LDS-tiled transpose; the
+ *                   other calls (except sparq24_col_l2norm, which rejects it
+ *                   with SPARQ24_ERR_UNSUPPORTED) first stage it as dense
+ *                   K-contiguous rows in their workspace, which then needs
+ *                   B*R*K elements more.
  *   K must be a multiple of 8 (two groups fill one metadata byte).
  * Outputs.  Always dense and K-contiguous, row-major over (b, r):
  *   kept values / kept codes [B][R][K/2], metadata [B][R][K/8],

@@ -230,21 +230,29 @@ def prune_compress(x: torch.Tensor, axis: int = -1, score: str = "magnitude",
 
 
 def prune_quantize(x: torch.Tensor, q: QLike, axis: int = -1, score: str = "magnitude",
-                   col_norm: Optional[torch.Tensor] = None, out=None):
+                   col_norm: Optional[torch.Tensor] = None, out=None, workspace=None):
     """Fused 2:4 prune + compress + per-row quantization of the kept values ->
     (codes [..., K/2], meta uint8 [..., K/8], scales fp32 [...])."""
     c, lead = describe(x, axis)
     qs = qspec(q)
     k = int(c.k)
+    L = lib()
+    s = _stream(x)
+    npt = _norm_ptr(score, col_norm)
     if out is None:
         codes = torch.empty(*lead, k // 2, dtype=_code_dtype(qs), device=x.device)
         meta = torch.empty(*lead, k // 8, dtype=torch.uint8, device=x.device)
         scales = torch.empty(*lead, dtype=torch.float32, device=x.device)
     else:
         codes, meta, scales = out
-    st = lib().sparq24_prune_quantize(ctypes.byref(c), _score(score), _norm_ptr(score, col_norm),
-                                      ctypes.byref(qs), codes.data_ptr(), meta.data_ptr(),
-                                      scales.data_ptr(), None, None, _stream(x))
+    if workspace is None:
+        ws, n = _workspace(x, lambda w, nb: L.sparq24_prune_quantize(
+            ctypes.byref(c), _score(score), npt, ctypes.byref(qs), None, None, None, w, nb, s))
+    else:
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_prune_quantize(ctypes.byref(c), _score(score), npt, ctypes.byref(qs),
+                                  codes.data_ptr(), meta.data_ptr(), scales.data_ptr(), _ptr(ws),
+                                  _wsarg(n), s)
     _check("sparq24_prune_quantize", st)
     return codes, meta, scales
 

@@ -147,6 +147,9 @@ sparq24_status launched(hipError_t e) {
     if (_st != SPARQ24_OK) return _st;           \
   } while (0)
 
+size_t staging_bytes(const RowDesc& d);
+RowDesc staged_view(const RowDesc& d, void* ws);
+
 // Energy-call planning: unique kept/dense quantizers, pair columns, workspace.
 struct EnergyPlan {
   EnergyParams p;
@@ -224,16 +227,20 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   const size_t rowpart = (size_t)pl.f.ncols * (size_t)pl.nrows * sizeof(double);
   const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk *
                       (size_t)energy_chunks_per_block(pl.rpb) * sizeof(double);
-  pl.off_rowpart = 0;
-  pl.off_csum = round_up(rowpart, kAlign);
+  pl.off_rowpart = staging_bytes(d);
+  pl.off_csum = pl.off_rowpart + round_up(rowpart, kAlign);
   pl.off_parts = pl.off_csum + round_up(sums, kAlign);
   pl.need = pl.off_parts + round_up((size_t)pl.nparts * sizeof(uint32_t), kAlign);
   return SPARQ24_OK;
 }
 
-sparq24_status run_energy(const RowDesc& d, int32_t score, const float* col_norm, EnergyPlan& pl,
+sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, EnergyPlan& pl,
                           double* out, void* ws, hipStream_t stream) {
   char* w = (char*)ws;
+  if (!d.kcontig) {
+    CHECK(launched(launch_transpose_rows(d, ws, stream)));
+    d = staged_view(d, ws);
+  }
   double* rowpart = (double*)(w + pl.off_rowpart);
   uint32_t* parts = (uint32_t*)(w + pl.off_parts);
   if (pl.need_nv_partials) {
@@ -245,6 +252,26 @@ sparq24_status run_energy(const RowDesc& d, int32_t score, const float* col_norm
   CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart, stream)));
   double* csum = (double*)(w + pl.off_csum);
   return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, csum, out, stream));
+}
+
+// Transposed operands are staged as dense K-contiguous rows at the start of
+// the workspace; the calls then run on that copy.
+size_t staging_bytes(const RowDesc& d) {
+  if (d.kcontig) return 0;
+  return round_up((size_t)(d.B * d.R * d.K) * (size_t)esize(d.dtype), kAlign);
+}
+
+RowDesc staged_view(const RowDesc& d, void* ws) {
+  RowDesc v = d;
+  v.x = (const char*)ws;
+  v.R = d.B * d.R;
+  v.B = 1;
+  v.rs = d.K * esize(d.dtype);
+  v.bs = v.R * v.rs;
+  v.ks = esize(d.dtype);
+  v.kcontig = true;
+  v.flat = true;
+  return v;
 }
 
 }  // namespace
@@ -267,7 +294,7 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
                                 void* scales, float* tensor_scale_out, void* ws, size_t* ws_bytes,
                                 hipStream_t stream) {
   RowDesc d;
-  CHECK(check_tensor(x, false, d));
+  CHECK(check_tensor(x, true, d));
   int cfmt;
   float qmax;
   CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
@@ -279,7 +306,8 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
     return SPARQ24_ERR_SHAPE;
   const bool nv_parts = cfmt == CF_NV && q->tensor_amax_in == nullptr;
   const int nparts = nv_parts ? absmax_partial_count(d) : 0;
-  const size_t need = round_up((size_t)nparts * sizeof(uint32_t), kAlign);
+  const size_t stage = staging_bytes(d);
+  const size_t need = stage + round_up((size_t)nparts * sizeof(uint32_t), kAlign);
   bool query;
   CHECK(workspace(ws, ws_bytes, need, query));
   if (query) return SPARQ24_OK;
@@ -289,9 +317,13 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
   if (!aligned16(codes) || !aligned16(scales)) return SPARQ24_ERR_ALIGN;
   if (cfmt == CF_NV && ((uintptr_t)tensor_scale_out & 3u)) return SPARQ24_ERR_ALIGN;
   CHECK(device_ok());
+  if (stage) {
+    CHECK(launched(launch_transpose_rows(d, ws, stream)));
+    d = staged_view(d, ws);
+  }
   if (cfmt == CF_MX) return launched(launch_quant_mx(d, codes, (uint8_t*)scales, stream));
   if (cfmt == CF_NV) {
-    uint32_t* parts = (uint32_t*)ws;
+    uint32_t* parts = (uint32_t*)((char*)ws + stage);
     if (nv_parts) CHECK(launched(launch_absmax_partials(d, parts, stream)));
     return launched(launch_quant_nv(d, q->tensor_amax_in, parts, nparts, codes, (uint8_t*)scales,
                                     tensor_scale_out, stream));
@@ -304,19 +336,24 @@ sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, co
                                       float* scales, void* ws, size_t* ws_bytes,
                                       hipStream_t stream) {
   RowDesc d;
-  CHECK(check_tensor(x, false, d));
+  CHECK(check_tensor(x, true, d));
   CHECK(check_score(score, col_norm));
   int cfmt;
   float qmax;
   CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3), cfmt, qmax));
   if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  const size_t stage = staging_bytes(d);
   bool query;
-  CHECK(workspace(ws, ws_bytes, 0, query));
+  CHECK(workspace(ws, ws_bytes, stage, query));
   if (query) return SPARQ24_OK;
   if (d.B * d.R * d.K == 0) return SPARQ24_OK;
   if (!codes || !meta || !scales) return SPARQ24_ERR_INVALID;
   if (!aligned16(codes) || !aligned16(meta) || !aligned16(scales)) return SPARQ24_ERR_ALIGN;
   CHECK(device_ok());
+  if (stage) {
+    CHECK(launched(launch_transpose_rows(d, ws, stream)));
+    d = staged_view(d, ws);
+  }
   return launched(launch_prune_quantize(d, score == SPARQ24_SCORE_WANDA, col_norm, cfmt, qmax,
                                         codes, meta, scales, stream));
 }
@@ -326,7 +363,7 @@ sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score, cons
                                     int64_t rows_per_block, double* out, void* ws,
                                     size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;
-  CHECK(check_tensor(x, false, d));
+  CHECK(check_tensor(x, true, d));
   CHECK(check_score(score, col_norm));
   if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
   if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
@@ -349,7 +386,7 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score, const f
                                  int32_t npairs, int64_t rows_per_block, double* out, void* ws,
                                  size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;
-  CHECK(check_tensor(x, false, d));
+  CHECK(check_tensor(x, true, d));
   CHECK(check_score(score, col_norm));
   if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
   if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;

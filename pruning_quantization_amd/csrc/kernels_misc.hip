@@ -83,6 +83,40 @@ hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hi
   return hipGetLastError();
 }
 
+// Transposed operand (row_stride == 1, reduction axis strided) -> dense
+// K-contiguous rows [B][R][K] through a 64x64 LDS tile, so both the reads
+// (along R) and the writes (along K) are contiguous.
+template <typename E>
+__global__ __launch_bounds__(kBlock) void k_transpose_rows(const char* __restrict__ x, int64_t R,
+                                                           int64_t K, int64_t bs, int64_t ks,
+                                                           E* __restrict__ out) {
+  __shared__ E tile[64][65];
+  const int64_t k0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64, b = blockIdx.z;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const char* xb = x + b * bs;
+  for (int kk = ty; kk < 64; kk += kBlock / 64) {
+    const int64_t k = k0 + kk, r = r0 + tx;
+    tile[kk][tx] = (k < K && r < R) ? *reinterpret_cast<const E*>(xb + k * ks + r * (int64_t)sizeof(E))
+                                    : E(0);
+  }
+  __syncthreads();
+  for (int rr = ty; rr < 64; rr += kBlock / 64) {
+    const int64_t r = r0 + rr, k = k0 + tx;
+    if (r < R && k < K) out[(b * R + r) * K + k] = tile[tx][rr];
+  }
+}
+
+hipError_t launch_transpose_rows(const RowDesc& d, void* out, hipStream_t s) {
+  const dim3 grid((unsigned)((d.K + 63) / 64), (unsigned)((d.R + 63) / 64), (unsigned)d.B);
+  if (d.dtype == 0)
+    hipLaunchKernelGGL((k_transpose_rows<uint32_t>), grid, dim3(kBlock), 0, s, d.x, d.R, d.K, d.bs,
+                       d.ks, (uint32_t*)out);
+  else
+    hipLaunchKernelGGL((k_transpose_rows<uint16_t>), grid, dim3(kBlock), 0, s, d.x, d.R, d.K, d.bs,
+                       d.ks, (uint16_t*)out);
+  return hipGetLastError();
+}
+
 // Read-once / write-once copy of 16-byte vectors (grid-stride).
 __global__ __launch_bounds__(kBlock) void k_copy(const uint4* __restrict__ src,
                                                  uint4* __restrict__ dst, int64_t n) {

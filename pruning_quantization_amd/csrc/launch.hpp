@@ -68,5 +68,7 @@ hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t 
 int col_strips(const RowDesc& d);
 hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Transposed operand -> dense [B][R][K] copy in `out` (B*R*K elements).
+hipError_t launch_transpose_rows(const RowDesc& d, void* out, hipStream_t s);
 
 }  // namespace sparq24

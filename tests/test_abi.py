@@ -106,8 +106,11 @@ def test_quantize_validation_and_workspace_query(L):
     assert n.value == 0
     big = tensor(k=32768 + 8)
     assert f(ctypes.byref(big), ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None, ctypes.byref(n), None) == SHAPE
+    # transposed operand: staged through the workspace (8 x 128 bf16 = 2 KiB)
     tt = tensor(rows=8, k=128, rs=1, ks=8)
-    assert f(ctypes.byref(tt), ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None, ctypes.byref(n), None) == UNSUPPORTED
+    assert f(ctypes.byref(tt), ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None, ctypes.byref(n), None) == OK
+    assert n.value >= 8 * 128 * 2
+    assert L.sparq24_col_l2norm(ctypes.byref(tt), FAKE, None, ctypes.byref(n), None) == UNSUPPORTED
 
 
 def test_energy_validation(L):

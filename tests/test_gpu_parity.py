@@ -285,3 +285,40 @@ def test_copy_kernel():
     b = torch.empty_like(a)
     S.copy(a, b)
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# transposed operands (V along seq) through every call
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("shape", [(2, 160, 72), (3, 1056, 128), (1, 4128, 24)])
+def test_transposed_quantize_prune_quantize_and_energy(shape):
+    rng = np.random.default_rng(shape[1])
+    raw = random_raw(rng, shape, "bf16")
+    x = to_dev(raw, "bf16")
+    rows = np.ascontiguousarray(np.swapaxes(raw, 1, 2)).reshape(-1, shape[1])
+    nr, k = rows.shape
+    for fmt, bits in (("fp8", 0), ("int", 8)):
+        c, s = S.quantize(x, (fmt, bits), axis=1)
+        wc, ws = O.quantize_rows(rows, "bf16", O.QSpec(fmt, bits))
+        assert_same(raw_np(s).reshape(nr), ws, "scales")
+        assert_same(raw_np(c).reshape(nr, k), wc, "codes")
+        pc, pm, ps = S.prune_quantize(x, (fmt, bits), axis=1)
+        wc, wm, ws = O.prune_quantize(rows, "bf16", O.QSpec(fmt, bits))
+        assert_same(raw_np(pm).reshape(nr, k // 8), wm, "meta")
+        assert_same(raw_np(ps).reshape(nr), ws, "scales")
+        assert_same(raw_np(pc).reshape(nr, k // 2), wc, "codes")
+    c, sc = S.quantize(x, "mxfp4", axis=1)
+    wc, wsc = O.quantize_mxfp4(rows, "bf16")
+    assert_same(raw_np(c).reshape(nr, k // 2), wc, "mx codes")
+    assert_same(raw_np(sc).reshape(nr, k // 32), wsc, "mx scales")
+    c, sc, ts = S.quantize(x, "nvfp4", axis=1)
+    wc, wsc, wts = O.quantize_nvfp4(rows, "bf16")
+    assert raw_np(ts)[0] == wts
+    assert_same(raw_np(c).reshape(nr, k // 2), wc, "nv codes")
+    kept, dense = ["none", "none", "fp8"], ["fp8", ("int", 8), "nvfp4"]
+    got = S.predict_R(x, kept, dense, axis=1, rows_per_block=shape[2])
+    want = O.predict_R(rows, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
+                       rows_per_block=shape[2])
+    rel_close(raw_np(got), want)
