@@ -49,12 +49,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+CHECK_SRC = "check_converts.hip"
+CHECK_BIN = os.path.join(PKG, "check_converts")
+
+
+def _build_check(verbose: bool) -> None:
+    """Stand-alone program that checks gfx950's fp8/fp4 conversion instructions
+    against the exact encoders over every finite fp32 (run by a GPU test)."""
+    cmd = [HIPCC, *COMMON, os.path.join(CSRC, CHECK_SRC), "-o", CHECK_BIN + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for check_converts:\n" + r.stdout + r.stderr)
+    shutil.move(CHECK_BIN + ".tmp", CHECK_BIN)
+
+
 def build(verbose: bool = False) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        chk = ex.submit(_build_check, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        chk.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
