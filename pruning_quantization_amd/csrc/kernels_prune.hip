@@ -17,9 +17,9 @@ template <class DT>
 __device__ inline void store_kept(const Unit<DT>& u, uint32_t mb, char* dst) {
   const Kept<DT> kp = gather_kept(u, mb);
   if constexpr (DT::ESIZE == 2) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(kp.k[0], kp.k[1]);
+    st2(dst, kp.k[0], kp.k[1]);
   } else {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(kp.k[0], kp.k[1], kp.k[2], kp.k[3]);
+    st4(dst, kp.k[0], kp.k[1], kp.k[2], kp.k[3]);
   }
 }
 
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_flat(
     if (i < nunits) {
       const uint32_t mb = select_unit<DT, false>(u[j], nullptr, 0);
       store_kept(u[j], mb, vals + i * (4 * DT::ESIZE));
-      meta[i] = (uint8_t)mb;
+      st(meta + i, (uint8_t)mb);
     }
   }
 }
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_rows(
       if (i < nunits) {
         const uint32_t mb = select_unit<DT, WANDA>(u[j], norm, i * 8);
         store_kept(u[j], mb, vr + i * (4 * DT::ESIZE));
-        mr[i] = (uint8_t)mb;
+        st(mr + i, (uint8_t)mb);
       }
     }
   }
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
 template <int CF>
 __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
   if constexpr (CF == CF_FP8) {
-    *reinterpret_cast<uint32_t*>(dst) = enc_e4m3_x4(y[0], y[1], y[2], y[3]);
+    st(reinterpret_cast<uint32_t*>(dst), enc_e4m3_x4(y[0], y[1], y[2], y[3]));
   } else {
     uint32_t r[4];
 #pragma unroll
@@ -197,10 +197,10 @@ __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
     if constexpr (CF == CF_INT8) {
       const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
       const uint32_t hi = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
-      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      st(reinterpret_cast<uint32_t*>(dst), __builtin_amdgcn_perm(hi, lo, 0x05040100u));
     } else {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_amdgcn_perm(r[1], r[0], 0x05040100u),
-                                                  __builtin_amdgcn_perm(r[3], r[2], 0x05040100u));
+      st2(dst, __builtin_amdgcn_perm(r[1], r[0], 0x05040100u),
+          __builtin_amdgcn_perm(r[3], r[2], 0x05040100u));
     }
   }
 }
@@ -257,7 +257,7 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = kp.f(e) * inv;
       store_kept_codes<CF>(crow + j * TEAM * CB, y, qmax);
-      mrow[j * TEAM] = (uint8_t)m;
+      st(mrow + j * TEAM, (uint8_t)m);
     };
     if ((UPL - 1) * TEAM + t < g.nunits) {  // every unit of this lane exists
 #pragma unroll
@@ -321,7 +321,7 @@ hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       auto go = [&]<bool W, int CF>() {
         hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF>), grid, dim3(kBlock), 0, s, g,

@@ -61,8 +61,7 @@ SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = u[j].f(e) * inv;
         if (cfmt == CF_FP8) {
-          reinterpret_cast<uint2*>(codes)[o] =
-              make_uint2(enc_e4m3_x4(y[0], y[1], y[2], y[3]), enc_e4m3_x4(y[4], y[5], y[6], y[7]));
+          st2(codes + o * 8, enc_e4m3_x4(y[0], y[1], y[2], y[3]), enc_e4m3_x4(y[4], y[5], y[6], y[7]));
         } else {
           uint32_t r[8];
 #pragma unroll
@@ -72,11 +71,9 @@ SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
             const uint32_t b = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
             const uint32_t c = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
             const uint32_t d = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
-            reinterpret_cast<uint2*>(codes)[o] = make_uint2(__builtin_amdgcn_perm(b, a, 0x05040100u),
-                                                            __builtin_amdgcn_perm(d, c, 0x05040100u));
+            st2(codes + o * 8, __builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(d, c, 0x05040100u));
           } else {  // CF_INT16
-            reinterpret_cast<uint4*>(codes)[o] = make_uint4(
-                __builtin_amdgcn_perm(r[1], r[0], 0x05040100u), __builtin_amdgcn_perm(r[3], r[2], 0x05040100u),
+            st4(codes + o * 16, __builtin_amdgcn_perm(r[1], r[0], 0x05040100u), __builtin_amdgcn_perm(r[3], r[2], 0x05040100u),
                 __builtin_amdgcn_perm(r[5], r[4], 0x05040100u), __builtin_amdgcn_perm(r[7], r[6], 0x05040100u));
           }
         }
@@ -242,8 +239,8 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
         for (int q = 0; q < 8; ++q) y[q] = __builtin_ldexpf(u[j].f(q), -e);
         const uint32_t pk = enc_e2m1_x8(y);
         if (active && i < nunits) {
-          codes[orow * nunits + i] = pk;
-          if ((i & 3) == 0) scales[orow * (nunits / 4) + (i >> 2)] = (uint8_t)(e + 127);
+          st(codes + orow * nunits + i, pk);
+          if ((i & 3) == 0) st(scales + orow * (nunits / 4) + (i >> 2), (uint8_t)(e + 127));
         }
       } else {
         const uint32_t bc = enc_e4m3(__uint_as_float(am) * g);
@@ -254,8 +251,8 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
         for (int q = 0; q < 8; ++q) y[q] = u[j].f(q) * inv;
         const uint32_t pk = enc_e2m1_x8(y);
         if (active && i < nunits) {
-          codes[orow * nunits + i] = pk;
-          if ((i & 1) == 0) scales[orow * (nunits / 2) + (i >> 1)] = (uint8_t)bc;
+          st(codes + orow * nunits + i, pk);
+          if ((i & 1) == 0) st(scales + orow * (nunits / 2) + (i >> 1), (uint8_t)bc);
         }
       }
     }
@@ -267,7 +264,7 @@ hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
       hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL>), persistent_grid(g.nrows, TEAM),
                          dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
       return hipGetLastError();
