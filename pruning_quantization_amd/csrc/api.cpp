@@ -224,7 +224,7 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   pl.nblk = (pl.nrows + pl.rpb - 1) / pl.rpb;
   pl.need_nv_partials = n_nv == 1 && pl.nv_in == nullptr;
   pl.nparts = pl.need_nv_partials ? absmax_partial_count(d) : 0;
-  const size_t rowpart = (size_t)pl.f.ncols * (size_t)pl.nrows * sizeof(double);
+  const size_t rowpart = (size_t)pl.f.ncols * (size_t)energy_partial_rows(pl.nrows) * sizeof(double);
   const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk *
                       (size_t)energy_chunks_per_block(pl.rpb) * sizeof(double);
   pl.off_rowpart = staging_bytes(d);
@@ -249,8 +249,12 @@ sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, Energ
     pl.p.n_partials = pl.nparts;
   }
   pl.p.nv_tamax = pl.nv_in;
-  CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart, stream)));
+  int64_t nparts = 0;
+  CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart,
+                                    pl.rpb, &nparts, stream)));
   double* csum = (double*)(w + pl.off_csum);
+  if (pl.rpb >= pl.nrows)  // one block: reduce the per-team partials
+    return launched(launch_energy_finalize(rowpart, nparts, nparts, 1, pl.f, csum, out, stream));
   return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, csum, out, stream));
 }
 

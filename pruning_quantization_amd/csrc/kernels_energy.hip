@@ -12,6 +12,10 @@
 // pass reduces rows per block in a fixed order.
 #include "dispatch.hpp"
 
+#ifndef SPARQ24_WIDE_E
+#define SPARQ24_WIDE_E 0
+#endif
+
 namespace sparq24 {
 
 __device__ inline float block_tensor_amax_e(const float* tamax_in, const uint32_t* partials,
@@ -78,12 +82,251 @@ __device__ inline void qdq_row4(int fmt, float inv, float qmax, const float* v, 
   }
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA>
-SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
-                                                        EnergyParams p,
-                                                        double* __restrict__ rowpart) {
+// ---------------------------------------------------------------------------
+// bf16 + magnitude fast path.  The top-2 network already orders each group's
+// keys; a key's high half is the element's bf16 magnitude, i.e. the fp32 bit
+// pattern of |x|.  So the two kept and the two dropped magnitudes fall out of
+// the network (two extra mins), and because every quantizer here is
+// symmetric in sign (RNE integers, sign-magnitude e4m3/e2m1 with the sign
+// copied), each error energy depends on |x| only.  The group maximum is
+// always kept, so the kept row maximum is also the plain row maximum.
+// Per unit the 8 magnitudes are held as kept (0..3) then dropped (4..7);
+// block quantizers only need a unit's membership, not the order inside it.
+// Squared residuals are summed pairwise in fp32 over a unit (at most three
+// roundings after the single-rounded fp32 residual, < 3.6e-7 relative) and
+// accumulated in fp64.
+// ---------------------------------------------------------------------------
+// Kept and dropped magnitudes of one group as packed bf16 pairs: bits 0..15
+// and 16..31 each hold a |x| bf16 pattern.
+__device__ inline void sel16_mags_packed(uint32_t w0, uint32_t w1, uint32_t& kept, uint32_t& drop,
+                                         uint32_t& top) {
+  const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
+  const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
+  const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
+  const uint32_t m1 = k0 > k1 ? k0 : k1, n1 = k0 > k1 ? k1 : k0;
+  const uint32_t m2 = k2 > k3 ? k2 : k3, n2 = k2 > k3 ? k3 : k2;
+  const uint32_t t1 = m1 > m2 ? m1 : m2, lo = m1 > m2 ? m2 : m1;
+  const uint32_t nn = n1 > n2 ? n1 : n2, d1 = n1 > n2 ? n2 : n1;
+  const uint32_t t2 = lo > nn ? lo : nn, d2 = lo > nn ? nn : lo;
+  kept = __builtin_amdgcn_perm(t2, t1, 0x07060302u);  // t1 high half low, t2 high half high
+  drop = __builtin_amdgcn_perm(d2, d1, 0x07060302u);
+  top = t1;
+}
+__device__ inline float mag_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ inline float mag_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+__device__ inline void sel16_mags(uint32_t w0, uint32_t w1, float* kept2, float* drop2,
+                                  uint32_t& top) {
+  const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
+  const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
+  const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
+  const uint32_t m1 = k0 > k1 ? k0 : k1, n1 = k0 > k1 ? k1 : k0;
+  const uint32_t m2 = k2 > k3 ? k2 : k3, n2 = k2 > k3 ? k3 : k2;
+  const uint32_t t1 = m1 > m2 ? m1 : m2, lo = m1 > m2 ? m2 : m1;
+  const uint32_t nn = n1 > n2 ? n1 : n2, d1 = n1 > n2 ? n2 : n1;
+  const uint32_t t2 = lo > nn ? lo : nn, d2 = lo > nn ? nn : lo;
+  kept2[0] = __uint_as_float(t1 & 0xFFFF0000u);
+  kept2[1] = __uint_as_float(t2 & 0xFFFF0000u);
+  drop2[0] = __uint_as_float(d1 & 0xFFFF0000u);
+  drop2[1] = __uint_as_float(d2 & 0xFFFF0000u);
+  top = t1;
+}
+
+// Sum of squared residuals of N magnitudes under a per-row scale (pairwise fp32).
+template <int N>
+__device__ inline float sq_err_row(int fmt, float s, float inv, float qmax, const float* v) {
+  float e[N];
+  if (fmt == CF_FP8) {
+#pragma unroll
+    for (int q = 0; q < N; q += 4) {
+      const uint32_t w = enc_e4m3_x4(v[q] * inv, v[q + 1] * inv, v[q + 2] * inv, v[q + 3] * inv);
+      e[q + 0] = __builtin_fmaf(dec_e4m3_hw<0>(w), s, -v[q + 0]);
+      e[q + 1] = __builtin_fmaf(dec_e4m3_hw<1>(w), s, -v[q + 1]);
+      e[q + 2] = __builtin_fmaf(dec_e4m3_hw<2>(w), s, -v[q + 2]);
+      e[q + 3] = __builtin_fmaf(dec_e4m3_hw<3>(w), s, -v[q + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float c = __builtin_rintf(__builtin_fminf(v[q] * inv, qmax));
+      e[q] = __builtin_fmaf(c, s, -v[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < N; ++q) e[q] = e[q] * e[q];
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int q = 0; q + w < N; q += 2 * w) e[q] += e[q + w];
+  return e[0];
+}
+
+// Row partial sums go either to rowpart[col][row] (blocked reductions) or,
+// when the whole operand is one block (ACC), into a per-team LDS accumulator
+// that each team writes once, to rowpart[col][team] (nparts = all teams).
+struct PartialSink {
+  double* rowpart;
+  int64_t stride;  // elements per column
+  bool acc;
+};
+
+template <int TEAM>
+__device__ inline void sink_put(const PartialSink& k, double* lacc, int64_t row, int col,
+                                double v) {
+  if (k.acc) lacc[col * (kBlock / TEAM) + threadIdx.x / TEAM] += v;
+  else k.rowpart[(int64_t)col * k.stride + row] = v;
+}
+
+// One partial per workgroup: thread c adds column c over the teams in order.
+template <int TEAM>
+__device__ inline void sink_flush(const PartialSink& k, double* lacc, int ncols) {
+  if (!k.acc) return;
+  constexpr int TPB = kBlock / TEAM;
+  __syncthreads();
+  const int c = threadIdx.x;
+  if (c < ncols) {
+    double a = 0.0;
+    for (int i = 0; i < TPB; ++i) a += lacc[c * TPB + i];
+    k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
+  }
+}
+
+template <int TEAM>
+__device__ inline void sink_init(double* lacc, int ncols) {
+  for (int i = threadIdx.x; i < ncols * (kBlock / TEAM); i += kBlock) lacc[i] = 0.0;
+  __syncthreads();
+}
+
+template <int TEAM, int UPL>
+SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
+  __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
+  const int ncols = 2 + p.kept.n + p.dense.n;
+  sink_init<TEAM>(lacc, ncols);
+  bool any_nv = false;
+  for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
+  float s_t = 0.f, gnv = 0.f;
+  if (any_nv) {
+    const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
+    if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
+  }
+  const int64_t nrows = g.nrows;
+  for_each_row_pipelined<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+    const bool writer = row < nrows && t == 0;
+    uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept g0, kept g1, dropped g0, dropped g1
+    uint32_t umax[UPL];    // unit maximum as a key (|x| in the high half)
+    uint32_t am = 0;
+    double kept2 = 0.0, drop = 0.0;
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      uint32_t t0, t1;
+      sel16_mags_packed(u[j].w[0], u[j].w[1], pk[j][0], pk[j][2], t0);
+      sel16_mags_packed(u[j].w[2], u[j].w[3], pk[j][1], pk[j][3], t1);
+      umax[j] = t0 > t1 ? t0 : t1;
+      am = am > umax[j] ? am : umax[j];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const double k0 = (double)mag_lo(pk[j][h]), k1 = (double)mag_hi(pk[j][h]);
+        const double d0 = (double)mag_lo(pk[j][2 + h]), d1 = (double)mag_hi(pk[j][2 + h]);
+        kept2 = __builtin_fma(k0, k0, kept2);  // exact squares
+        kept2 = __builtin_fma(k1, k1, kept2);
+        drop = __builtin_fma(d0, d0, drop);
+        drop = __builtin_fma(d1, d1, drop);
+      }
+    }
+    am = team_max_u32<TEAM>(am, redu);
+    double x2 = team_sum_f64<TEAM>(kept2 + drop, redd);
+    drop = team_sum_f64<TEAM>(drop, redd);
+    if (writer) {
+      sink_put<TEAM>(sink, lacc, row, 0, x2);
+      sink_put<TEAM>(sink, lacc, row, 1, drop);
+    }
+    const float amax = __uint_as_float(am & 0xFFFF0000u);  // kept max == row max
+    for (int q = 0; q < p.kept.n; ++q) {
+      const int fmt = p.kept.fmt[q];
+      const float qmax = p.kept.qmax[q];
+      double acc = 0.0;
+      if (fmt != CF_NONE) {
+        float s, inv;
+        row_scale(amax, qmax, s, inv);
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+          acc += (double)sq_err_row<4>(fmt, s, inv, qmax, v);
+        }
+      }
+      acc = team_sum_f64<TEAM>(acc, redd);
+      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
+    }
+    for (int q = 0; q < p.dense.n; ++q) {
+      const int fmt = p.dense.fmt[q];
+      const float qmax = p.dense.qmax[q];
+      double acc = 0.0;
+      if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
+        float s, inv;
+        row_scale(amax, qmax, s, inv);
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
+                              mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+          acc += (double)sq_err_row<8>(fmt, s, inv, qmax, v);
+        }
+      } else if (fmt == CF_MX || fmt == CF_NV) {
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          uint32_t bm = umax[j] & 0xFFFF0000u;  // fp32 bits of the unit's |x| max
+          uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
+          bm = bm > w ? bm : w;
+          float e[8];
+          const float vj[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
+                               mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+          if (fmt == CF_MX) {
+            w = (uint32_t)__shfl_xor((int)bm, 2, 64);
+            bm = bm > w ? bm : w;
+            const int ex = mx_exp_e(bm);
+            const float X = __builtin_ldexpf(1.0f, ex);
+            float y[8];
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2) y[q2] = __builtin_ldexpf(vj[q2], -ex);
+            const uint32_t pk = enc_e2m1_x8(y);
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2)
+              e[q2] = __builtin_fmaf(dec_e2m1((pk >> (4 * q2)) & 0xFu), X, -vj[q2]);
+          } else {
+            const uint32_t bc = enc_e4m3(__uint_as_float(bm) * gnv);
+            const float bval = dec_e4m3(bc);
+            const float d = bval * s_t;
+            const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+            float y[8];
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2) y[q2] = vj[q2] * inv;
+            const uint32_t pk = enc_e2m1_x8(y);
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2)
+              e[q2] = __builtin_fmaf(dec_e2m1((pk >> (4 * q2)) & 0xFu) * bval, s_t, -vj[q2]);
+          }
+#pragma unroll
+          for (int q2 = 0; q2 < 8; ++q2) e[q2] = e[q2] * e[q2];
+          const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          acc += (double)s8;
+        }
+      }
+      acc = team_sum_f64<TEAM>(acc, redd);
+      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + q, acc);
+    }
+  });
+  sink_flush<TEAM>(sink, lacc, ncols);
+}
+
+template <class DT, int TEAM, int UPL, bool WANDA>
+SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
+                                                        EnergyParams p, PartialSink sink) {
+  __shared__ uint32_t redu[kBlock / 64];
+  __shared__ double redd[kBlock / 64];
+  __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
+  const int ncols0 = 2 + p.kept.n + p.dense.n;
+  sink_init<TEAM>(lacc, ncols0);
 
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
@@ -124,8 +367,8 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     x2 = team_sum_f64<TEAM>(x2, redd);
     drop = team_sum_f64<TEAM>(drop, redd);
     if (writer) {
-      rowpart[0 * nrows + row] = x2;
-      rowpart[1 * nrows + row] = drop;
+      sink_put<TEAM>(sink, lacc, row, 0, x2);
+      sink_put<TEAM>(sink, lacc, row, 1, drop);
     }
     const float famk = DT::to_f32(amk), famd = DT::to_f32(amd);
 
@@ -149,7 +392,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
         }
       }
       acc = team_sum_f64<TEAM>(acc, redd);
-      if (writer) rowpart[(int64_t)(2 + q) * nrows + row] = acc;
+      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
     }
 
     // dense quantizers
@@ -204,14 +447,15 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
         }
       }
       acc = team_sum_f64<TEAM>(acc, redd);
-      if (writer) rowpart[(int64_t)(2 + p.kept.n + q) * nrows + row] = acc;
+      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + q, acc);
     }
   });
+  sink_flush<TEAM>(sink, lacc, ncols0);
 }
 
 // Stage 1: sum of one column over one chunk of at most kChunk rows that lies
 // inside one block of rows: grid (nblk * chunks_per_block, ncols).
-constexpr int64_t kChunk = 2048;
+constexpr int64_t kChunk = 16384;
 
 __global__ __launch_bounds__(kBlock) void k_energy_colsum(const double* __restrict__ rowpart,
                                                           int64_t nrows, int64_t rpb, int64_t cpb,
@@ -271,23 +515,109 @@ __global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restr
   }
 }
 
+// One-kernel finalize when every block of rows is a single chunk: workgroup
+// b sums each column over its rows (fixed order) and forms the outputs.
+__global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restrict__ rowpart,
+                                                          int64_t nrows, int64_t rpb,
+                                                          FinalizeParams f,
+                                                          double* __restrict__ out) {
+  constexpr int CB = 8;  // columns reduced together: CB independent loads per row
+  __shared__ double sh[CB][kBlock];
+  __shared__ double sb[2 + 2 * kMaxQ];
+  const int64_t blk = blockIdx.x;
+  const int64_t r0 = blk * rpb;
+  const int64_t r1 = (r0 + rpb) < nrows ? (r0 + rpb) : nrows;
+  for (int cb = 0; cb < f.ncols; cb += CB) {
+    double a[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) a[c] = 0.0;
+    // branch-free body: columns past the end re-read the last one (ignored),
+    // so all CB loads of a row can be in flight together
+    const double* colp[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) colp[c] = rowpart + (int64_t)((cb + c) < f.ncols ? cb + c : f.ncols - 1) * nrows;
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += kBlock) {
+      double v[CB];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) v[c] = colp[c][r];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) a[c] += v[c];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] = a[c];
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] += sh[c][threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x < CB && cb + (int)threadIdx.x < f.ncols) sb[cb + threadIdx.x] = sh[threadIdx.x][0];
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  if (f.mode == 0) {
+    double* o = out + blk * 4;
+    o[0] = sb[0];
+    o[1] = sb[1];
+    o[2] = sb[f.kcol[0]];
+    o[3] = sb[f.dcol[0]];
+  } else {
+    const double tot = sb[0];
+    for (int p = 0; p < f.npairs; ++p) {
+      double* o = out + (blk * f.npairs + p) * 5;
+      const double ep = sb[1] / tot;
+      const double eq = sb[f.kcol[p]] / tot;
+      const double e24 = ep + eq;
+      const double ed = sb[f.dcol[p]] / tot;
+      o[0] = ep;
+      o[1] = eq;
+      o[2] = e24;
+      o[3] = ed;
+      o[4] = __builtin_sqrt(e24 / ed);
+    }
+  }
+}
+
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
-                              const EnergyParams& p, double* rowpart, hipStream_t s) {
+                              const EnergyParams& p, double* rowpart, int64_t rows_per_block,
+                              int64_t* nparts, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
+  const bool acc = rows_per_block >= g.nrows;  // one block: per-team partials
+  auto geom = [&](int, dim3 grid, PartialSink& k) {
+    k.rowpart = rowpart;
+    k.acc = acc;
+    k.stride = acc ? (int64_t)grid.x : g.nrows;
+    *nparts = acc ? (int64_t)grid.x : g.nrows;
+  };
+  if (d.dtype == 1 && !wanda) {  // bf16, magnitude
+    return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
+      const dim3 grid = persistent_grid(g.nrows, TEAM);
+      PartialSink k;
+      geom(TEAM, grid, k);
+      hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL>), grid, dim3(kBlock), 0, s, g, p, k);
+      return hipGetLastError();
+    });
+  }
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
+      PartialSink k;
+      geom(TEAM, grid, k);
       if (wanda)
         hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g, norm,
-                           p, rowpart);
+                           p, k);
       else
         hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
-                           norm, p, rowpart);
+                           norm, p, k);
       return hipGetLastError();
     });
   });
 }
+
+// Upper bound of the partial rows launch_energy_rows writes per column.
+int64_t energy_partial_rows(int64_t nrows) { return nrows + kBlock; }
 
 int64_t energy_chunks_per_block(int64_t rows_per_block) {
   return (rows_per_block + kChunk - 1) / kChunk;
@@ -297,6 +627,11 @@ hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t 
                                   int64_t nblk, const FinalizeParams& f, double* csum, double* out,
                                   hipStream_t s) {
   const int64_t cpb = energy_chunks_per_block(rows_per_block);
+  if (cpb == 1) {
+    hipLaunchKernelGGL(k_energy_final1, dim3((unsigned)nblk), dim3(kBlock), 0, s, rowpart, nrows,
+                       rows_per_block, f, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_energy_colsum, dim3((unsigned)(nblk * cpb), (unsigned)f.ncols),
                      dim3(kBlock), 0, s, rowpart, nrows, rows_per_block, cpb, csum, f.ncols);
   hipError_t e = hipGetLastError();

@@ -51,8 +51,12 @@ hipError_t launch_quant_mx(const RowDesc& d, void* codes, uint8_t* scales, hipSt
 hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32_t* partials,
                            int nparts, void* codes, uint8_t* scales, float* ts_out,
                            hipStream_t s);
+// Writes per-row partials rowpart[col][row], or (rows_per_block >= rows)
+// one partial per team; *nparts receives the partial rows per column.
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
-                              const EnergyParams& p, double* rowpart, hipStream_t s);
+                              const EnergyParams& p, double* rowpart, int64_t rows_per_block,
+                              int64_t* nparts, hipStream_t s);
+int64_t energy_partial_rows(int64_t nrows);
 // mode 0: out[blk][4] raw sums for pair 0; mode 1: out[blk][npairs][5] E's and R
 struct FinalizeParams {
   int ncols;            // 2 + nkept + ndense
