@@ -33,6 +33,9 @@ from .reference import (  # noqa: F401
     indices_from_meta,
     prune_compress,
     decompress,
+    pair_scores,
+    select_pairs48,
+    prune_compress_pairs48,
     E4M3_GRID, E2M1_GRID,
     e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
     int_rtn_codes,

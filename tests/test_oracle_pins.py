@@ -449,3 +449,61 @@ def test_col_l2norm_closed_form():
     assert n.dtype == np.float32
     assert n[0] == 5.0 and n[1] == 2.0 and n[2] == 8.0 and n[4] == 0.0
     assert n[3] == np.float32(math.sqrt(8.0))
+
+
+# ---------------------------------------------------------------------------
+# Pairwise 4:8 ([PD §6])
+# ---------------------------------------------------------------------------
+
+
+def test_pairs48_hand_example():
+    ex = HAND["pairs48_row"]
+    raw = bf16([ex["row"]])
+    vals, meta = O.prune_compress_pairs48(raw, O.BF16)
+    assert O.decode_input(vals, O.BF16)[0].tolist() == ex["kept"]
+    assert np.array_equal(meta[0], hexs(ex["meta_bytes"]))
+
+
+def exp_order_stat_mean(k, n, mean):
+    """E[X_(k)] of n iid exponentials: mean * sum_{i<k} 1/(n-i) (exact)."""
+    return Fraction(mean) * sum(Fraction(1, n - i) for i in range(k))
+
+
+def test_pairs48_gaussian_loss_closed_form_and_pages():
+    # a pair's energy a^2 + b^2 of iid N(0,1) is exponential with mean 2;
+    # dropping the two smallest of four loses (E[X(1)] + E[X(2)]) / 8
+    cf = (exp_order_stat_mean(1, 4, 2) + exp_order_stat_mean(2, 4, 2)) / 8
+    assert cf == Fraction(5, 24)
+    assert round(float(cf), 3) == PAGES["pairwise_48_energy_loss"]["value"]
+    raw = W.gaussian_f32(21, 2048, 2048)
+    e = O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", 8), pattern="pairs4:8")
+    loss = e[0, 1] / e[0, 0]
+    assert abs(loss - float(cf)) < 6e-4
+    # ranking pairs by |a| + |b| instead would lose about 21.35%: excluded
+    x = O.decode_input(raw, O.F32)
+    l1 = np.abs(x[:, 0::2]) + np.abs(x[:, 1::2])
+    sel = O.select_pairs48(l1)
+    g = (x * x).reshape(2048, 256, 4, 2).sum(-1)
+    kept = np.take_along_axis(g, sel, axis=-1).sum()
+    assert 1 - kept / (x * x).sum() > float(cf) + 3e-3
+
+
+def test_pairs48_bruteforce_ties():
+    rng = np.random.default_rng(8)
+    w = rng.integers(-2, 3, size=(32, 64)) * 0.5          # many equal pair energies
+    raw = bf16(w)
+    x = O.decode_input(raw, O.BF16)
+    sel = O.select_pairs48(O.pair_scores(x))
+    for r in range(32):
+        for gi in range(8):
+            e = [Fraction(float(x[r, 8 * gi + 2 * p])) ** 2 + Fraction(float(x[r, 8 * gi + 2 * p + 1])) ** 2
+                 for p in range(4)]
+            assert sel[r, gi].tolist() == brute_keep(e)
+
+
+def test_pairs48_energy_loss_exceeds_24():
+    raw = W.gaussian_f32(22, 512, 1024)
+    e24 = O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", 8))
+    e48 = O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", 8), pattern="pairs4:8")
+    assert e48[0, 1] > e24[0, 1]            # pairs cannot each be chosen by size ([PD §6])
+    assert e48[0, 0] == e24[0, 0]
