@@ -186,6 +186,24 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score,
                                  int64_t rows_per_block, double* out, void* ws,
                                  size_t* ws_bytes, hipStream_t stream);
 
+/* Pairwise 4:8 prune-and-compress [PD §6: Blackwell's sparse FP4 splits each
+ * group of eight into four adjacent pairs and keeps two].  In every aligned
+ * group of eight along K the two pairs (2p, 2p+1) with the largest energy
+ * fp64(a^2 + b^2) are kept, ties to the lower pair.  values [B][R][K/2]
+ * receives the kept pairs in pair order; meta [B][R][K/16] receives per group
+ * the nibble (p0 | p1 << 2), group 2j in the low nibble of byte j.
+ * K % 16 == 0; K-contiguous operands only. */
+sparq24_status sparq24_prune_compress_pairs48(const sparq24_tensor* x, void* values,
+                                              uint8_t* meta, hipStream_t stream);
+
+/* Predicted R of pairwise 4:8 against dense quantizers [PD §4, §6]: same
+ * outputs and workspace protocol as sparq24_predict_R, with the pairwise 4:8
+ * selection above in place of element-wise 2:4.  K % 16 == 0. */
+sparq24_status sparq24_predict_R_pairs48(const sparq24_tensor* x, const sparq24_qspec* kept_q,
+                                         const sparq24_qspec* dense_q, int32_t npairs,
+                                         int64_t rows_per_block, double* out, void* ws,
+                                         size_t* ws_bytes, hipStream_t stream);
+
 /* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
  * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in
  * fp64, then rounded once.  x is an activation [tokens, channels] given with

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     lib,
     predict_R,
     prune_compress,
+    prune_compress_pairs48,
+    predict_R_pairs48,
     prune_quantize,
     qspec,
     quantize,

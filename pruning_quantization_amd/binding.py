@@ -48,6 +48,7 @@ class CQSpec(ctypes.Structure):
 #: Every symbol the C header declares.
 SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize",
            "sparq24_error_energy", "sparq24_predict_R", "sparq24_col_l2norm", "sparq24_copy",
+           "sparq24_prune_compress_pairs48", "sparq24_predict_R_pairs48",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -74,6 +75,9 @@ def lib(path: Optional[str] = None):
                               POINTER(c_size_t), c_void_p],
         "sparq24_col_l2norm": [T, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
         "sparq24_copy": [c_void_p, c_void_p, c_size_t, c_void_p],
+        "sparq24_prune_compress_pairs48": [T, c_void_p, c_void_p, c_void_p],
+        "sparq24_predict_R_pairs48": [T, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
+                                      POINTER(c_size_t), c_void_p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -354,6 +358,49 @@ def predict_R(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QLike], ax
     st = L.sparq24_predict_R(ctypes.byref(c), _score(score), npt, ka, da, npairs, rows_per_block,
                              out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_predict_R", st)
+    return out
+
+
+def prune_compress_pairs48(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Pairwise 4:8 prune-and-compress along the last dim -> (values [..., K/2],
+    meta uint8 [..., K/16])."""
+    c, lead = describe(x, -1)
+    k = int(c.k)
+    if out is None:
+        vals = torch.empty(*lead, k // 2, dtype=x.dtype, device=x.device)
+        meta = torch.empty(*lead, k // 16, dtype=torch.uint8, device=x.device)
+    else:
+        vals, meta = out
+    st = lib().sparq24_prune_compress_pairs48(ctypes.byref(c), vals.data_ptr(), meta.data_ptr(),
+                                              _stream(x))
+    _check("sparq24_prune_compress_pairs48", st)
+    return vals, meta
+
+
+def predict_R_pairs48(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QLike],
+                      axis: int = -1, rows_per_block: int = 0,
+                      out: Optional[torch.Tensor] = None, workspace=None):
+    """Predicted R of pairwise 4:8 vs dense quantizers -> fp64 [nblk, npairs, 5]."""
+    if len(kept) != len(dense):
+        raise ValueError("kept and dense must pair up")
+    c, _ = describe(x, axis)
+    ka, da = _qarray(kept), _qarray(dense)
+    L = lib()
+    s = _stream(x)
+    nrows = int(c.batch) * int(c.rows)
+    rpb = rows_per_block or nrows
+    nblk = (nrows + rpb - 1) // rpb
+    npairs = len(kept)
+    if out is None:
+        out = torch.empty(nblk, npairs, 5, dtype=torch.float64, device=x.device)
+    if workspace is None:
+        ws, n = _workspace(x, lambda w, nb: L.sparq24_predict_R_pairs48(
+            ctypes.byref(c), ka, da, npairs, rows_per_block, None, w, nb, s))
+    else:
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_predict_R_pairs48(ctypes.byref(c), ka, da, npairs, rows_per_block,
+                                     out.data_ptr(), _ptr(ws), _wsarg(n), s)
+    _check("sparq24_predict_R_pairs48", st)
     return out
 
 

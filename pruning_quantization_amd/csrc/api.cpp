@@ -409,6 +409,43 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score, const f
   return run_energy(d, score, col_norm, pl, out, ws, stream);
 }
 
+sparq24_status sparq24_prune_compress_pairs48(const sparq24_tensor* x, void* values,
+                                              uint8_t* meta, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, false, d));
+  if (d.K % 16) return SPARQ24_ERR_SHAPE;
+  if (d.B * d.R * d.K == 0) return SPARQ24_OK;
+  if (!values || !meta) return SPARQ24_ERR_INVALID;
+  if (!aligned16(values) || !aligned16(meta)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_prune_compress_pairs48(d, values, meta, stream));
+}
+
+sparq24_status sparq24_predict_R_pairs48(const sparq24_tensor* x, const sparq24_qspec* kept_q,
+                                         const sparq24_qspec* dense_q, int32_t npairs,
+                                         int64_t rows_per_block, double* out, void* ws,
+                                         size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, true, d));
+  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
+  if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
+  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
+  if (d.K % 16) return SPARQ24_ERR_SHAPE;
+  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  EnergyPlan pl;
+  CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
+  pl.p.pairs48 = 1;
+  pl.f.mode = 1;
+  bool query;
+  CHECK(workspace(ws, ws_bytes, pl.need, query));
+  if (query) return SPARQ24_OK;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return run_energy(d, SPARQ24_SCORE_MAGNITUDE, nullptr, pl, out, ws, stream);
+}
+
 sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
                                   size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;

@@ -308,6 +308,52 @@ __device__ inline uint32_t kept_absmax(const Kept<DT>& kp) {
   }
 }
 
+// Pairwise 4:8 [PD §6]: a unit is one group of eight = four adjacent pairs.
+// Pair energy e_p = fp64(a^2 + b^2) (exact squares, one rounding, as
+// fma(b, b, a*a)); the two pairs with the largest energy are kept, ties to
+// the lower pair.  Pair p beats q (p < q) iff e_p >= e_q; with that strict
+// total order exactly two pairs win at least two of their three contests.
+// Returns the nibble p0 | p1 << 2 (p0 < p1).
+template <class DT>
+__device__ inline uint32_t select_pairs48(const Unit<DT>& u) {
+  double e[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const double a = (double)u.f(2 * p), b = (double)u.f(2 * p + 1);
+    e[p] = __builtin_fma(b, b, a * a);
+  }
+  const uint32_t c01 = e[0] >= e[1], c02 = e[0] >= e[2], c03 = e[0] >= e[3];
+  const uint32_t c12 = e[1] >= e[2], c13 = e[1] >= e[3], c23 = e[2] >= e[3];
+  const uint32_t w0 = c01 + c02 + c03, w1 = (1u - c01) + c12 + c13;
+  const uint32_t w2 = (1u - c02) + (1u - c12) + c23, w3 = (1u - c03) + (1u - c13) + (1u - c23);
+  const uint32_t m = (uint32_t)(w0 >= 2) | ((uint32_t)(w1 >= 2) << 1) | ((uint32_t)(w2 >= 2) << 2) |
+                     ((uint32_t)(w3 >= 2) << 3);
+  const uint32_t p0 = (uint32_t)__builtin_ctz(m), p1 = 31u - (uint32_t)__builtin_clz(m);
+  return p0 | (p1 << 2);
+}
+
+// 8-bit element mask of a pairwise-4:8 nibble.
+__device__ inline uint32_t pairs48_mask(uint32_t nib) {
+  return (3u << (2 * (nib & 3u))) | (3u << (2 * (nib >> 2)));
+}
+
+// The two kept pairs of a unit as raw storage bits (pair order).
+template <class DT>
+__device__ inline Kept<DT> gather_pairs48(const Unit<DT>& u, uint32_t nib) {
+  Kept<DT> kp;
+  const uint32_t p0 = nib & 3u, p1 = nib >> 2;
+  if constexpr (DT::ESIZE == 2) {
+    kp.k[0] = pick4(p0, u.w[0], u.w[1], u.w[2], u.w[3]);
+    kp.k[1] = pick4(p1, u.w[0], u.w[1], u.w[2], u.w[3]);
+  } else {
+    kp.k[0] = pick4(p0, u.w[0], u.w[2], u.w[4], u.w[6]);
+    kp.k[1] = pick4(p0, u.w[1], u.w[3], u.w[5], u.w[7]);
+    kp.k[2] = pick4(p1, u.w[0], u.w[2], u.w[4], u.w[6]);
+    kp.k[3] = pick4(p1, u.w[1], u.w[3], u.w[5], u.w[7]);
+  }
+  return kp;
+}
+
 // ---------------------------------------------------------------------------
 // Encoders: exact integer implementations of round-to-nearest-even with
 // saturation, sign copied from the input (so -0 keeps its sign bit).

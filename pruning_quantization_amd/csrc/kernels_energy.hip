@@ -347,13 +347,22 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = (int64_t)j * TEAM + t;
       mbs[j] = 0;
-      if (i < g.nunits) mbs[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
-      const uint32_t n0 = mbs[j] & 0xFu, n1 = mbs[j] >> 4;
-      km[j] = (1u << (n0 & 3u)) | (1u << (n0 >> 2)) | (16u << (n1 & 3u)) | (16u << (n1 >> 2));
+      if (p.pairs48) {
+        // pairwise 4:8 (zero units select pairs 0 and 1 of zeros: harmless)
+        mbs[j] = select_pairs48(u[j]);
+        km[j] = pairs48_mask(mbs[j]);
+      } else {
+        if (i < g.nunits) mbs[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+        const uint32_t n0 = mbs[j] & 0xFu, n1 = mbs[j] >> 4;
+        km[j] = (1u << (n0 & 3u)) | (1u << (n0 >> 2)) | (16u << (n1 & 3u)) | (16u << (n1 >> 2));
+      }
       const uint32_t ad = unit_absmax_e(u[j]);
       amd = amd > ad ? amd : ad;
-      const uint32_t ak = kept_absmax(gather_kept(u[j], mbs[j]));
-      amk = amk > ak ? amk : ak;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = ((km[j] >> e) & 1u) ? u[j].absbits(e) : 0u;
+        amk = amk > a ? amk : a;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const double dv = (double)u[j].f(e);
@@ -381,15 +390,17 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
         float s, inv;
         row_scale(famk, qmax, s, inv);
 #pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const Kept<DT> kp = gather_kept(u[j], mbs[j]);
-          float v[4], c[4];
+        for (int j = 0; j < UPL; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = kp.f(e);
-          qdq_row4(fmt, inv, qmax, v, c);
+          for (int h = 0; h < 2; ++h) {
+            // all 8 elements are evaluated; dropped ones contribute zero
+            float v[4], c[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
-        }
+            for (int e = 0; e < 4; ++e) v[e] = ((km[j] >> (4 * h + e)) & 1u) ? u[j].f(4 * h + e) : 0.0f;
+            qdq_row4(fmt, inv, qmax, v, c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
+          }
       }
       acc = team_sum_f64<TEAM>(acc, redd);
       if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
@@ -591,7 +602,7 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
     k.stride = acc ? (int64_t)grid.x : g.nrows;
     *nparts = acc ? (int64_t)grid.x : g.nrows;
   };
-  if (d.dtype == 1 && !wanda) {  // bf16, magnitude
+  if (d.dtype == 1 && !wanda && !p.pairs48) {  // bf16, magnitude, 2:4
     return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;

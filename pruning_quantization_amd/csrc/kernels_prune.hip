@@ -272,6 +272,46 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
 }
 
 // ---------------------------------------------------------------------------
+// Pairwise 4:8 prune-and-compress [PD §6].  Same team walk as the 2:4 row
+// kernel; one unit is one group of eight, whose nibble (p0 | p1 << 2) is
+// paired with the neighbouring lane's (units 2m and 2m+1) into one byte.
+// ---------------------------------------------------------------------------
+template <class DT, int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_prune_compress_pairs48(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    char* __restrict__ vals, uint8_t* __restrict__ meta) {
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;  // lanes of absent rows stay for the shuffles
+  const char* xr = x + b * bs + (active ? r : 0) * rs;
+  const int64_t orow = b * R + r;
+  char* vr = vals + orow * nunits * (4 * DT::ESIZE);
+  uint8_t* mr = meta + orow * (nunits / 2);
+  for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+    Unit<DT> u[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+      else zero_unit(u[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      const uint32_t nib = select_pairs48(u[j]);
+      const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1, 64);
+      if (active && i < nunits) {
+        const Kept<DT> kp = gather_pairs48(u[j], nib);
+        if constexpr (DT::ESIZE == 2) st2(vr + i * 8, kp.k[0], kp.k[1]);
+        else st4(vr + i * 16, kp.k[0], kp.k[1], kp.k[2], kp.k[3]);
+        if ((i & 1) == 0) st(mr + (i >> 1), (uint8_t)(nib | (other << 4)));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm, void* vals,
@@ -310,6 +350,18 @@ hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm
         hipLaunchKernelGGL((k_prune_compress_rows<DT, TEAM, UPL, false>), row_grid(d, TEAM),
                            dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, (char*)vals,
                            meta);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_prune_compress_pairs48(const RowDesc& d, void* vals, uint8_t* meta,
+                                        hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_prune_compress_pairs48<DT, TEAM, UPL>), row_grid(d, TEAM), dim3(kBlock),
+                         0, s, d.x, d.R, nunits, d.bs, d.rs, (char*)vals, meta);
       return hipGetLastError();
     });
   });

@@ -30,6 +30,7 @@ struct QList {
 
 struct EnergyParams {
   QList kept, dense;
+  int pairs48;                 // 1: pairwise 4:8 selection instead of 2:4
   const float* nv_tamax;       // device T for NVFP4 (or null -> reduce partials)
   const uint32_t* nv_partials; // fp32 bit patterns of partial maxima
   int n_partials;
@@ -40,6 +41,8 @@ constexpr int64_t kMaxRowUnits = 4096;  // K <= 32768
 
 hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm, void* vals,
                                  uint8_t* meta, hipStream_t s);
+hipError_t launch_prune_compress_pairs48(const RowDesc& d, void* vals, uint8_t* meta,
+                                        hipStream_t s);
 hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm, int cfmt,
                                  float qmax, void* codes, uint8_t* meta, float* scales,
                                  hipStream_t s);

@@ -136,6 +136,19 @@ def test_energy_validation(L):
     assert g(ctypes.byref(t), 0, None, None, ctypes.byref(q(B.Q_FP8)), 0, FAKE, None, ctypes.byref(n), None) == INVALID
 
 
+def test_pairs48_validation(L):
+    f = L.sparq24_prune_compress_pairs48
+    assert f(ctypes.byref(tensor(k=24)), FAKE, FAKE, None) == SHAPE        # K % 16
+    assert f(ctypes.byref(tensor(k=32)), None, FAKE, None) == INVALID
+    assert f(ctypes.byref(tensor(rows=8, k=128, rs=1, ks=8)), FAKE, FAKE, None) == UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    g = L.sparq24_predict_R_pairs48
+    arr = (B.CQSpec * 1)(q(B.Q_FP8))
+    assert g(ctypes.byref(tensor(k=24)), arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
+    assert g(ctypes.byref(tensor(k=32)), arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
+    assert n.value > 0
+
+
 def test_copy_validation(L):
     assert L.sparq24_copy(FAKE, FAKE, 0, None) == OK
     assert L.sparq24_copy(FAKE, FAKE, 24, None) == ALIGN

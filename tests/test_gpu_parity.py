@@ -322,3 +322,47 @@ def test_transposed_quantize_prune_quantize_and_energy(shape):
     want = O.predict_R(rows, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
                        rows_per_block=shape[2])
     rel_close(raw_np(got), want)
+
+
+# ---------------------------------------------------------------------------
+# pairwise 4:8 ([PD §6])
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [16, 48, 1024, 4096, 4112])
+def test_prune_compress_pairs48(dtype, k):
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 5, 19, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        v, m = S.prune_compress_pairs48(x)
+        wv, wm = O.prune_compress_pairs48(raw, dtype)
+        assert_same(raw_np(m), wm, "meta")
+        assert_same(raw_np(v), wv, "values")
+
+
+def test_prune_compress_pairs48_strided_rows():
+    rng = np.random.default_rng(48)
+    full = random_raw(rng, (21, 2048 + 32), "bf16")
+    x = to_dev(full, "bf16")[:, 16:16 + 2048]
+    v, m = S.prune_compress_pairs48(x)
+    wv, wm = O.prune_compress_pairs48(np.ascontiguousarray(full[:, 16:16 + 2048]), "bf16")
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(v), wv, "values")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [16, 128, 4096])
+def test_predict_R_pairs48(dtype, k):
+    raw = inputs(k + 9, 37, k, dtype, "normal")
+    x = to_dev(raw, dtype)
+    kept = ["none", "fp8", ("int", 4), "fp8"]
+    dense = ["fp8", ("int", 8), ("int", 3), "nvfp4"]
+    got = S.predict_R_pairs48(x, kept, dense, rows_per_block=8)
+    want = O.predict_R(raw, dtype, [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
+                       rows_per_block=8, pattern="pairs4:8")
+    rel_close(raw_np(got), want)
+    if k % 32 == 0:
+        got = S.predict_R_pairs48(x, ["none"], ["mxfp4"])
+        want = O.predict_R(raw, dtype, [O.QSpec("none")], [O.QSpec("mxfp4")], pattern="pairs4:8")
+        rel_close(raw_np(got), want)
