@@ -36,6 +36,7 @@ from .reference import (  # noqa: F401
     pair_scores,
     select_pairs48,
     prune_compress_pairs48,
+    decompress_pairs48,
     E4M3_GRID, E2M1_GRID,
     e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
     int_rtn_codes,
@@ -44,7 +45,10 @@ from .reference import (  # noqa: F401
     dequantize_rows,
     quantize_mxfp4, dequantize_mxfp4,
     quantize_nvfp4, dequantize_nvfp4,
+    quantize_kept,
+    dequantize_kept,
     prune_quantize,
+    prune_quantize_pairs48,
     dequantize_pruned,
     error_energy,
     predict_R,

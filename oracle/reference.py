@@ -217,6 +217,23 @@ def _mask_pairs48(x: np.ndarray) -> np.ndarray:
     return np.repeat(m.reshape(rows, k // 2), 2, axis=1)
 
 
+def decompress_pairs48(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
+    """Dense [rows, K] from pairwise 4:8 values [rows, K/2] and meta
+    [rows, K/16]; dropped pairs are zero."""
+    rows, half = values.shape
+    k = 2 * half
+    nib = np.empty((rows, k // 8), dtype=np.int64)
+    nib[:, 0::2] = meta & 0xF
+    nib[:, 1::2] = meta >> 4
+    out = np.zeros((rows, k // 8, 4, 2), dtype=values.dtype)
+    v = values.reshape(rows, k // 8, 2, 2)
+    g = np.arange(k // 8)
+    for r in range(rows):
+        out[r, g, nib[r] & 3] = v[r, :, 0]
+        out[r, g, nib[r] >> 2] = v[r, :, 1]
+    return out.reshape(rows, k)
+
+
 # ---------------------------------------------------------------------------
 # Element encoders ([PD §3]: FP8, MXFP4 and NVFP4 as the dense rivals; a
 # reading fixes OCP e4m3 and E2M1 with round-to-nearest-even, saturating)
@@ -465,24 +482,67 @@ def dequantize_nvfp4(packed: np.ndarray, bscales: np.ndarray, s_t) -> np.ndarray
 # ---------------------------------------------------------------------------
 
 
+def quantize_kept(kept_raw: np.ndarray, dtype: str, q: QSpec):
+    """Quantize compressed kept values ``[rows, K/2]`` (stored in ``dtype``).
+
+    INT / FP8: one scale per row from the kept values' absolute maximum,
+    returns ``(codes [rows, K/2], scales fp32 [rows])``.  MXFP4 / NVFP4: the
+    block format applied to the compressed row, so a block covers 32 / 16
+    consecutive kept values; returns what :func:`quantize_mxfp4` /
+    :func:`quantize_nvfp4` return, with the NVFP4 tensor maximum taken over
+    the kept values unless ``q.tensor_amax`` is given (the sparse FP4 format
+    of [PD §6] scales what it stores)."""
+    if q.fmt in ("int", "fp8"):
+        kept = decode_input(kept_raw, dtype).astype(np.float32)
+        amax = np.max(np.abs(kept), axis=1)
+        s, inv = row_scale(amax, _qmax(q))
+        return _encode_scaled(kept, inv, q), s
+    if q.fmt == "mxfp4":
+        return quantize_mxfp4(kept_raw, dtype)
+    if q.fmt == "nvfp4":
+        return quantize_nvfp4(kept_raw, dtype, q.tensor_amax)
+    raise ValueError(q.fmt)
+
+
 def prune_quantize(raw: np.ndarray, dtype: str, q: QSpec, score: str = "magnitude",
                    col_norm: Optional[np.ndarray] = None):
-    """Prune 2:4, then quantize the kept values with one scale per row taken
-    from their absolute maximum.
+    """Prune 2:4, then quantize the kept values (:func:`quantize_kept`).
 
-    Returns ``(codes [rows, K/2], meta [rows, K/8], scales fp32 [rows])``."""
+    Returns ``(codes, meta [rows, K/8], *scales)``: INT/FP8 codes [rows, K/2]
+    with fp32 row scales; MXFP4 packed codes [rows, K/4] with E8M0 scales
+    [rows, K/64]; NVFP4 packed codes [rows, K/4], e4m3 scales [rows, K/32]
+    and the fp32 tensor scale."""
     vals, meta = prune_compress(raw, dtype, score, col_norm)
-    kept = decode_input(vals, dtype).astype(np.float32)
-    amax = np.max(np.abs(kept), axis=1)
-    s, inv = row_scale(amax, _qmax(q))
-    return _encode_scaled(kept, inv, q), meta, s
+    qc = quantize_kept(vals, dtype, q)
+    return (qc[0], meta) + tuple(qc[1:])
 
 
-def dequantize_pruned(codes: np.ndarray, meta: np.ndarray, q: QSpec,
-                      scales: np.ndarray) -> np.ndarray:
+def prune_quantize_pairs48(raw: np.ndarray, dtype: str, q: QSpec):
+    """Pairwise 4:8 prune, then quantize the kept values
+    (:func:`quantize_kept`); with NVFP4 this is the sparse FP4 operand of
+    [PD §6].  Returns ``(codes, meta [rows, K/16], *scales)`` as
+    :func:`prune_quantize`."""
+    vals, meta = prune_compress_pairs48(raw, dtype)
+    qc = quantize_kept(vals, dtype, q)
+    return (qc[0], meta) + tuple(qc[1:])
+
+
+def dequantize_kept(codes: np.ndarray, q: QSpec, *scales) -> np.ndarray:
+    """fp64 kept values [rows, K/2] from :func:`quantize_kept`'s output."""
+    if q.fmt in ("int", "fp8"):
+        return dequantize_rows(codes, q, scales[0])
+    if q.fmt == "mxfp4":
+        return dequantize_mxfp4(codes, scales[0])
+    if q.fmt == "nvfp4":
+        return dequantize_nvfp4(codes, scales[0], scales[1])
+    raise ValueError(q.fmt)
+
+
+def dequantize_pruned(codes: np.ndarray, meta: np.ndarray, q: QSpec, *scales,
+                      pattern: str = "2:4") -> np.ndarray:
     """Dense fp64 reconstruction of a pruned-and-quantized operand."""
-    kept = dequantize_rows(codes, q, scales)
-    return decompress(kept, meta)
+    kept = dequantize_kept(codes, q, *scales)
+    return decompress(kept, meta) if pattern == "2:4" else decompress_pairs48(kept, meta)
 
 
 # ---------------------------------------------------------------------------
@@ -491,13 +551,11 @@ def dequantize_pruned(codes: np.ndarray, meta: np.ndarray, q: QSpec,
 
 
 def _reconstruct_kept(kept_raw: np.ndarray, dtype: str, q: QSpec) -> np.ndarray:
-    """Kept values after the 2:4 side's quantizer, fp64 [rows, K/2]."""
+    """Kept values after the sparse side's quantizer, fp64 [rows, K/2]."""
     if q.fmt == "none":
         return decode_input(kept_raw, dtype)
-    kept = decode_input(kept_raw, dtype).astype(np.float32)
-    amax = np.max(np.abs(kept), axis=1)
-    s, inv = row_scale(amax, _qmax(q))
-    return dequantize_rows(_encode_scaled(kept, inv, q), q, s)
+    codes, *scales = quantize_kept(kept_raw, dtype, q)
+    return dequantize_kept(codes, q, *scales)
 
 
 def _reconstruct_dense(raw: np.ndarray, dtype: str, q: QSpec,
@@ -614,31 +672,41 @@ def col_l2norm(raw: np.ndarray, dtype: str) -> np.ndarray:
 
 def bits_per_element(q: QSpec, sparse24: bool = False, row_len: Optional[int] = None,
                      value_bits: Optional[int] = None,
-                     tensor_elems: Optional[int] = None) -> float:
+                     tensor_elems: Optional[int] = None, pattern: Optional[str] = None) -> float:
     """Storage bits charged per original element ([PD §2]: values, indices
     and scales all count).
 
     Dense: value bits + scale bits amortised over the elements they cover
     (one fp32 per row of ``row_len`` for INT/FP8 rows; 8 bits per 32 for
     MXFP4; 8 bits per 16 plus one fp32 per tensor for NVFP4).
-    2:4: half the elements at the kept value width, plus the 2-bit position
-    of each kept value (1 bit per original element), plus the same per-row
-    scale. ``value_bits`` gives the width for fmt "none" (e.g. 16 for bf16).
+    Sparse (``pattern`` "2:4", or ``sparse24=True``, or "pairs4:8"): half the
+    elements at the kept value width, plus the position bits (2:4: 2 bits per
+    kept value, 1 per original element; pairwise 4:8: 2 bits per kept pair,
+    1/2 per original element), plus the scales: the per-row scale as on the
+    dense side, block scales over kept values (so half as many per original
+    element), the NVFP4 tensor scale once. ``value_bits`` gives the width for
+    fmt "none" (e.g. 16 for bf16).
     """
+    if pattern is None:
+        pattern = "2:4" if sparse24 else "dense"
+    block = 0.0
+    row = 0.0
+    tensor = 0.0
     if q.fmt == "int":
-        v, scale = q.bits, (32.0 / row_len if row_len else 0.0)
+        v, row = q.bits, (32.0 / row_len if row_len else 0.0)
     elif q.fmt == "fp8":
-        v, scale = 8, (32.0 / row_len if row_len else 0.0)
+        v, row = 8, (32.0 / row_len if row_len else 0.0)
     elif q.fmt == "none":
         if value_bits is None:
             raise ValueError("fmt none needs value_bits")
-        v, scale = value_bits, 0.0
+        v = value_bits
     elif q.fmt == "mxfp4":
-        v, scale = 4, 8.0 / 32.0
+        v, block = 4, 8.0 / 32.0
     elif q.fmt == "nvfp4":
-        v, scale = 4, 8.0 / 16.0 + (32.0 / tensor_elems if tensor_elems else 0.0)
+        v, block, tensor = 4, 8.0 / 16.0, (32.0 / tensor_elems if tensor_elems else 0.0)
     else:
         raise ValueError(q.fmt)
-    if sparse24:
-        return v / 2.0 + 1.0 + scale
-    return float(v) + scale
+    if pattern == "dense":
+        return float(v) + row + block + tensor
+    index = {"2:4": 1.0, "pairs4:8": 0.5}[pattern]
+    return v / 2.0 + index + row + block / 2.0 + tensor

@@ -507,3 +507,98 @@ def test_pairs48_energy_loss_exceeds_24():
     e48 = O.error_energy(raw, O.F32, O.QSpec("none"), O.QSpec("int", 8), pattern="pairs4:8")
     assert e48[0, 1] > e24[0, 1]            # pairs cannot each be chosen by size ([PD §6])
     assert e48[0, 0] == e24[0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Sparse FP4 and block formats on kept values ([PD §6]: pairwise 4:8 with
+# NVFP4 values; [PD §3]: MXFP4)
+# ---------------------------------------------------------------------------
+
+
+def test_pairs48_nvfp4_hand_example():
+    ex = HAND["pairs48_nvfp4"]
+    raw = bf16(ex["rows"])
+    codes, meta, bs, st = O.prune_quantize_pairs48(raw, O.BF16, O.QSpec("nvfp4"))
+    assert np.array_equal(meta, np.stack([hexs(m) for m in ex["meta_bytes"]]))
+    assert np.array_equal(codes, np.stack([hexs(p) for p in ex["packed"]]))
+    assert np.array_equal(bs[:, 0], hexs(ex["block_scales"]))
+    assert float(st) == ex["tensor_scale"]
+    vals, _ = O.prune_compress_pairs48(raw, O.BF16)
+    assert np.array_equal(O.decode_input(vals, O.BF16), np.array(ex["kept"], dtype=np.float64))
+
+
+def test_pairs48_kept_amax_hand_example():
+    ex = HAND["pairs48_kept_amax"]
+    raw = bf16([ex["row"]])
+    codes, meta, s = O.prune_quantize_pairs48(raw, O.BF16, O.QSpec("int", ex["bits"]))
+    assert np.array_equal(meta[0], hexs(ex["meta_bytes"]))
+    assert codes[0].tolist() == ex["codes"]
+    assert int(np.float32(s[0]).view(np.uint32)) == int(ex["scale_hex"], 16)
+    r = O.predict_R(raw, O.BF16, [O.QSpec("int", ex["bits"])], [O.QSpec("int", 8)],
+                    pattern="pairs4:8")
+    assert r[0, 0, 0] == ex["sum_dropped"] / ex["sum_x2"]
+    # each kept 4 comes back as 7 * s with s = fp32(4/7): error energy 4 (7s - 4)^2
+    sc = float(np.uint32(int(ex["scale_hex"], 16)).view(np.float32))
+    assert r[0, 0, 1] == pytest.approx(4 * (7 * sc - 4) ** 2 / ex["sum_x2"], rel=1e-12)
+
+
+def test_sparse24_mxfp4_hand_example():
+    ex = HAND["sparse24_mxfp4"]
+    raw = bf16([ex["row"]])
+    assert raw.shape == (1, 64)
+    codes, meta, sc = O.prune_quantize(raw, O.BF16, O.QSpec("mxfp4"))
+    assert np.array_equal(meta[0], hexs(ex["meta_bytes"]))
+    assert sc[0].tolist() == ex["scale_codes"]
+    assert np.array_equal(codes[0], hexs(ex["packed"]))
+    vals, _ = O.prune_compress(raw, O.BF16)
+    assert O.decode_input(vals, O.BF16)[0, :16].tolist() == ex["kept_first16"]
+
+
+def test_decompress_pairs48_places_kept_pairs():
+    rng = np.random.default_rng(7)
+    x = rng.integers(-3, 4, size=(5, 64)).astype(np.float64)
+    raw = bf16(x)
+    vals, meta = O.prune_compress_pairs48(raw, O.BF16)
+    dense = O.decompress_pairs48(O.decode_input(vals, O.BF16), meta)
+    g = x.reshape(5, 8, 4, 2)
+    d = dense.reshape(5, 8, 4, 2)
+    for r in range(5):
+        for q in range(8):
+            kept = [p for p in range(4) if np.any(d[r, q, p] != 0) or False]
+            e = (g[r, q] ** 2).sum(axis=1)
+            nib = (meta[r, q // 2] >> (4 * (q % 2))) & 0xF
+            want = sorted({nib & 3, nib >> 2})
+            assert len(want) == 2
+            for p in range(4):
+                if p in want:
+                    assert np.array_equal(d[r, q, p], g[r, q, p])
+                else:
+                    assert np.all(d[r, q, p] == 0)
+            # the kept pairs carry the two largest energies
+            assert min(e[want]) >= max(e[[p for p in range(4) if p not in want]])
+            assert set(kept) <= set(want)
+
+
+def test_block_scaled_kept_reconstruction_is_exact_on_grid():
+    # kept values already on the E2M1 grid under a power-of-two MX scale come
+    # back unchanged: 2:4 prune then MXFP4 loses only the dropped elements
+    rng = np.random.default_rng(3)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    x = rng.choice(grid, size=(4, 128)) * rng.choice([-1, 1], size=(4, 128))
+    x[:, ::32] = 6.0  # every MX block of kept values reaches 6 -> scale 2^0
+    raw = bf16(x)
+    codes, meta, sc = O.prune_quantize(raw, O.BF16, O.QSpec("mxfp4"))
+    xhat = O.dequantize_pruned(codes, meta, O.QSpec("mxfp4"), sc)
+    vals, _ = O.prune_compress(raw, O.BF16)
+    assert np.array_equal(xhat, O.decompress(O.decode_input(vals, O.BF16), meta))
+
+
+def test_sparse_bits_accounting():
+    # 2:4: v/2 + 1 index bit; pairwise 4:8: v/2 + 1/2; block scales cover kept values
+    assert O.bits_per_element(O.QSpec("nvfp4"), pattern="pairs4:8") == 2 + 0.5 + 0.25
+    assert O.bits_per_element(O.QSpec("mxfp4"), pattern="2:4") == 2 + 1 + 0.125
+    assert O.bits_per_element(O.QSpec("int", 8), pattern="pairs4:8") == 4.5
+    assert O.bits_per_element(O.QSpec("int", 8), pattern="2:4") == \
+        O.bits_per_element(O.QSpec("int", 8), sparse24=True) == 5.0
+    n = 1 << 20
+    assert O.bits_per_element(O.QSpec("nvfp4"), pattern="pairs4:8", tensor_elems=n) == 2.75 + 32 / n
