@@ -121,6 +121,15 @@ def main():
                      torch.empty(T, dtype=torch.float32, device=dev),
                      torch.empty(1, dtype=torch.float32, device=dev)),
             "R": torch.empty(1, 2, 5, dtype=torch.float64, device=dev),
+            "pc": (torch.empty(T, H // 2, dtype=torch.bfloat16, device=dev),
+                   torch.empty(T, H // 8, dtype=torch.uint8, device=dev)),
+            "p48": (torch.empty(T, H // 2, dtype=torch.bfloat16, device=dev),
+                    torch.empty(T, H // 16, dtype=torch.uint8, device=dev)),
+            "R48": torch.empty(1, 2, 5, dtype=torch.float64, device=dev),
+            "sfp4": (torch.empty(T, H // 4, dtype=torch.uint8, device=dev),
+                     torch.empty(T, H // 16, dtype=torch.uint8, device=dev),
+                     torch.empty(T, H // 32, dtype=torch.uint8, device=dev),
+                     torch.empty(1, dtype=torch.float32, device=dev)),
         }
 
     outs = [outputs() for _ in range(a.pool)]
@@ -141,6 +150,23 @@ def main():
     calls = {"prune_quantize_fp8": call_pq, "quantize_fp8": call_fp8,
              "quantize_int8": call_int8, "predict_R": call_R}
 
+    # timed one by one beside the step, not part of it: plain 2:4 compression and
+    # the pairwise 4:8 pattern with its predicted R
+    def call_pc(i):
+        S.prune_compress(pool[i], out=outs[i]["pc"])
+
+    def call_p48(i):
+        S.prune_compress_pairs48(pool[i], out=outs[i]["p48"])
+
+    def call_R48(i):
+        S.predict_R_pairs48(pool[i], kept, dense, out=outs[i]["R48"], workspace=ws)
+
+    def call_sfp4(i):  # sparse FP4: pairwise 4:8 with NVFP4 kept values
+        S.prune_quantize_pairs48(pool[i], "nvfp4", out=outs[i]["sfp4"], workspace=ws)
+
+    side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
+                  "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4}
+
     def step(i):
         for f in calls.values():
             f(i)
@@ -154,9 +180,19 @@ def main():
         "predict_R": xb + 2 * 5 * 8,
     }
     step_bytes = sum(alg.values())
+    alg.update({
+        "prune_compress_2of4": xb + xb // 2 + T * H // 8,
+        "prune_compress_pairs48": xb + xb // 2 + T * H // 16,
+        "predict_R_pairs48": xb + 2 * 5 * 8,
+        # one read of X (the kept-maximum pre-pass reads it a second time)
+        "prune_quantize_pairs48_nvfp4": xb + T * H // 4 + T * H // 16 + T * H // 32 + 4,
+    })
 
     # ---- spot parity against the oracle (not timed) ---------------------------------
     step(0)
+    for f in side_calls.values():
+        for i in range(a.pool):
+            f(i)
     torch.cuda.synchronize()
     import oracle as O
     rows = np.r_[0:8, T - 8:T]
@@ -164,6 +200,11 @@ def main():
     c, m, s = (t.cpu().numpy() for t in outs[0]["pq"])
     parity = bool(np.array_equal(c[rows], wc) and np.array_equal(m[rows], wm)
                   and np.array_equal(s[rows].view(np.uint32), wsc.view(np.uint32)))
+    wv, wm = O.prune_compress_pairs48(x_bits[rows], "bf16")
+    v48, m48 = (t.cpu().view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+                for t in outs[0]["p48"])
+    parity = parity and bool(np.array_equal(m48[rows], wm)
+                             and np.array_equal(v48[rows].view(np.uint16), wv.view(np.uint16)))
 
     # ---- warmup ----------------------------------------------------------------------
     for w in range(a.warmup):
@@ -183,7 +224,7 @@ def main():
                     with torch.cuda.graph(g, stream=cap):
                         step(i)
                     step_graphs.append(g)
-                for name, f in calls.items():
+                for name, f in {**calls, **side_calls}.items():
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.graph(g, stream=cap):
                         for i in range(a.pool):
@@ -218,7 +259,7 @@ def main():
     # ---- per-call kernel durations (HIP events around ring replays) ------------------
     per_call = {}
     reps = max(1, a.steps // a.pool)
-    for name, f in calls.items():
+    for name, f in {**calls, **side_calls}.items():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()

@@ -148,23 +148,37 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
                                 void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /* Fused online prune + compress + quantize of the kept values [PD §4: the
- * 2:4 side quantizes its kept values to 2m bits; PD §5: 2:4 stacked on FP8].
- * Same selection and metadata as sparq24_prune_compress; the kept values of
- * each row are quantized (INT or FP8) with one scale per row taken from the
- * absolute maximum of that row's kept values.  codes [B][R][K/2],
- * meta [B][R][K/8], scales fp32 [B][R].  One read, one write per output.
- * Needs no workspace: pass ws = ws_bytes = NULL (a query reports 0). */
+ * 2:4 side quantizes its kept values to 2m bits; PD §5: 2:4 stacked on FP8;
+ * PD §3: MXFP4 and NVFP4].  Same selection and metadata as
+ * sparq24_prune_compress; the kept values of each row, in compressed order,
+ * are quantized as a row of K/2 values:
+ *   INT/FP8: codes [B][R][K/2] (int8, int16 above 8 bits, or e4m3 bytes) and
+ *            scales fp32 [B][R], one per row from the absolute maximum of
+ *            that row's kept values.
+ *   MXFP4:   codes uint8 [B][R][K/4] (two E2M1 per byte, low nibble first),
+ *            scales E8M0 [B][R][K/64] (one per 32 kept values); K % 64 == 0.
+ *   NVFP4:   codes uint8 [B][R][K/4], scales e4m3 [B][R][K/32] (one per 16
+ *            kept values), tensor_scale_out (device, 1 fp32) receives s_t;
+ *            T is the largest |kept value| of the operand, or
+ *            *q->tensor_amax_in.  K % 32 == 0.
+ * tensor_scale_out is only read for NVFP4 (NULL otherwise).  Workspace:
+ * NVFP4 without tensor_amax_in needs a few KB, a transposed operand its
+ * staging copy, others none (pass ws = ws_bytes = NULL).  One read of the
+ * operand (plus one for the NVFP4 tensor maximum), one write per output. */
 sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score,
                                       const float* col_norm, const sparq24_qspec* q,
-                                      void* codes, uint8_t* meta, float* scales,
-                                      void* ws, size_t* ws_bytes, hipStream_t stream);
+                                      void* codes, uint8_t* meta, void* scales,
+                                      float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                      hipStream_t stream);
 
 /* Error energies of both sides [PD §4].
  * For each block of rows_per_block consecutive rows (flattened over (b, r);
  * 0 = the whole operand; the last block may be shorter), out[blk][4] fp64 =
  *   { sum x^2, sum of dropped x^2, sum over kept elements of (x - xhat)^2
  *     under kept_q, sum over all elements of (x - xhat)^2 under dense_q }.
- * kept_q: NONE, INT or FP8.  dense_q: INT, FP8, MXFP4 or NVFP4 (NVFP4's T is
+ * kept_q: NONE, INT, FP8, MXFP4 (K % 64) or NVFP4 (K % 32; T over the kept
+ * values of the whole operand), blocked over the compressed row as in
+ * sparq24_prune_quantize.  dense_q: INT, FP8, MXFP4 or NVFP4 (NVFP4's T is
  * over the whole operand).  Sums are accumulated in fp64 in a fixed order,
  * so repeated calls give identical bits. */
 sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score,
@@ -196,6 +210,18 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score,
 sparq24_status sparq24_prune_compress_pairs48(const sparq24_tensor* x, void* values,
                                               uint8_t* meta, hipStream_t stream);
 
+/* Pairwise 4:8 prune + quantize of the kept values [PD §6: with NVFP4 this is
+ * Blackwell's sparse FP4 operand].  Selection and meta [B][R][K/16] as
+ * sparq24_prune_compress_pairs48; codes, scales, tensor_scale_out, formats,
+ * workspace and shape rules as sparq24_prune_quantize (kept values blocked
+ * over the compressed row; the INT/FP8 row scale and the NVFP4 tensor
+ * maximum come from the kept values, which need not hold the row's largest
+ * element).  K % 16 == 0. */
+sparq24_status sparq24_prune_quantize_pairs48(const sparq24_tensor* x, const sparq24_qspec* q,
+                                              void* codes, uint8_t* meta, void* scales,
+                                              float* tensor_scale_out, void* ws,
+                                              size_t* ws_bytes, hipStream_t stream);
+
 /* Predicted R of pairwise 4:8 against dense quantizers [PD §4, §6]: same
  * outputs and workspace protocol as sparq24_predict_R, with the pairwise 4:8
  * selection above in place of element-wise 2:4.  K % 16 == 0. */
@@ -217,8 +243,11 @@ sparq24_status sparq24_copy(const void* src, void* dst, size_t bytes, hipStream_
 
 /* Storage bits per original element [PD §2: values, position indices and
  * scales are all charged].  Host-only arithmetic; no device needed.
- * sparse24 = 0: dense q; = 1: 2:4 with kept values in q.  row_len: elements
- * sharing one per-row scale (INT/FP8), 0 to leave scales out.  value_bits:
+ * sparse24 = 0: dense q; = 1: 2:4 with kept values in q (2 position bits per
+ * kept value); = 2: pairwise 4:8 (2 bits per kept pair).  Sparse block
+ * scales cover kept values, so they cost half as much per original element.
+ * row_len: elements sharing one per-row scale (INT/FP8), 0 to leave scales
+ * out.  value_bits:
  * width for SPARQ24_Q_NONE.  tensor_elems: NVFP4 tensor size, 0 to leave its
  * scale out.  Returns a negative value for an invalid spec. */
 double sparq24_bits_per_element(const sparq24_qspec* q, int32_t sparse24, int64_t row_len,

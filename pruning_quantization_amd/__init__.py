@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     prune_compress_pairs48,
     predict_R_pairs48,
     prune_quantize,
+    prune_quantize_pairs48,
     qspec,
     quantize,
     version,

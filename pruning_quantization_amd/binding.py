@@ -48,7 +48,8 @@ class CQSpec(ctypes.Structure):
 #: Every symbol the C header declares.
 SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize",
            "sparq24_error_energy", "sparq24_predict_R", "sparq24_col_l2norm", "sparq24_copy",
-           "sparq24_prune_compress_pairs48", "sparq24_predict_R_pairs48",
+           "sparq24_prune_compress_pairs48", "sparq24_prune_quantize_pairs48",
+           "sparq24_predict_R_pairs48",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -68,7 +69,9 @@ def lib(path: Optional[str] = None):
         "sparq24_prune_compress": [T, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
         "sparq24_quantize": [T, Q, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
         "sparq24_prune_quantize": [T, c_int32, c_void_p, Q, c_void_p, c_void_p, c_void_p, c_void_p,
-                                   POINTER(c_size_t), c_void_p],
+                                   c_void_p, POINTER(c_size_t), c_void_p],
+        "sparq24_prune_quantize_pairs48": [T, Q, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           POINTER(c_size_t), c_void_p],
         "sparq24_error_energy": [T, c_int32, c_void_p, Q, Q, c_int64, c_void_p, c_void_p,
                                  POINTER(c_size_t), c_void_p],
         "sparq24_predict_R": [T, c_int32, c_void_p, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
@@ -233,32 +236,61 @@ def prune_compress(x: torch.Tensor, axis: int = -1, score: str = "magnitude",
     return vals, meta
 
 
-def prune_quantize(x: torch.Tensor, q: QLike, axis: int = -1, score: str = "magnitude",
-                   col_norm: Optional[torch.Tensor] = None, out=None, workspace=None):
-    """Fused 2:4 prune + compress + per-row quantization of the kept values ->
-    (codes [..., K/2], meta uint8 [..., K/8], scales fp32 [...])."""
-    c, lead = describe(x, axis)
-    qs = qspec(q)
+def _pq_outputs(x, lead, k, qs, meta_div):
+    dev = x.device
+    meta = torch.empty(*lead, k // meta_div, dtype=torch.uint8, device=dev)
+    if qs.fmt in (Q_INT, Q_FP8):
+        codes = torch.empty(*lead, k // 2, dtype=_code_dtype(qs), device=dev)
+        return codes, meta, torch.empty(*lead, dtype=torch.float32, device=dev)
+    codes = torch.empty(*lead, k // 4, dtype=torch.uint8, device=dev)
+    if qs.fmt == Q_MXFP4:
+        return codes, meta, torch.empty(*lead, k // 64, dtype=torch.uint8, device=dev)
+    return (codes, meta, torch.empty(*lead, k // 32, dtype=torch.uint8, device=dev),
+            torch.empty(1, dtype=torch.float32, device=dev))
+
+
+def _prune_quantize(name, head, x, lead, c, qs, meta_div, out, workspace):
+    """Shared marshalling of the fused prune + quantize calls; ``head`` are the
+    arguments between the tensor and the qspec."""
     k = int(c.k)
-    L = lib()
+    fn = getattr(lib(), name)
     s = _stream(x)
-    npt = _norm_ptr(score, col_norm)
-    if out is None:
-        codes = torch.empty(*lead, k // 2, dtype=_code_dtype(qs), device=x.device)
-        meta = torch.empty(*lead, k // 8, dtype=torch.uint8, device=x.device)
-        scales = torch.empty(*lead, dtype=torch.float32, device=x.device)
-    else:
-        codes, meta, scales = out
+    outs = _pq_outputs(x, lead, k, qs, meta_div) if out is None else tuple(out)
+    codes, meta, scales = outs[:3]
+    ts = outs[3] if len(outs) > 3 else None
     if workspace is None:
-        ws, n = _workspace(x, lambda w, nb: L.sparq24_prune_quantize(
-            ctypes.byref(c), _score(score), npt, ctypes.byref(qs), None, None, None, w, nb, s))
+        ws, n = _workspace(x, lambda w, nb: fn(ctypes.byref(c), *head, ctypes.byref(qs), None, None,
+                                               None, None, w, nb, s))
     else:
         ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
-    st = L.sparq24_prune_quantize(ctypes.byref(c), _score(score), npt, ctypes.byref(qs),
-                                  codes.data_ptr(), meta.data_ptr(), scales.data_ptr(), _ptr(ws),
-                                  _wsarg(n), s)
-    _check("sparq24_prune_quantize", st)
-    return codes, meta, scales
+    st = fn(ctypes.byref(c), *head, ctypes.byref(qs), codes.data_ptr(), meta.data_ptr(),
+            scales.data_ptr(), _ptr(ts), _ptr(ws), _wsarg(n), s)
+    _check(name, st)
+    return outs
+
+
+def prune_quantize(x: torch.Tensor, q: QLike, axis: int = -1, score: str = "magnitude",
+                   col_norm: Optional[torch.Tensor] = None,
+                   tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
+    """Fused 2:4 prune + compress + quantization of the kept values.
+    INT/FP8 -> (codes [..., K/2], meta uint8 [..., K/8], scales fp32 [...]);
+    MXFP4 -> (codes [..., K/4], meta, e8m0 [..., K/64]); NVFP4 -> (codes
+    [..., K/4], meta, e4m3 [..., K/32], tensor scale fp32 [1])."""
+    c, lead = describe(x, axis)
+    qs = qspec(q, tensor_amax)
+    return _prune_quantize("sparq24_prune_quantize", (_score(score), _norm_ptr(score, col_norm)),
+                           x, lead, c, qs, 8, out, workspace)
+
+
+def prune_quantize_pairs48(x: torch.Tensor, q: QLike, axis: int = -1,
+                           tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
+    """Pairwise 4:8 prune + quantization of the kept values (with NVFP4: the
+    sparse FP4 operand).  Outputs as :func:`prune_quantize` with meta
+    [..., K/16]."""
+    c, lead = describe(x, axis)
+    qs = qspec(q, tensor_amax)
+    return _prune_quantize("sparq24_prune_quantize_pairs48", (), x, lead, c, qs, 16, out,
+                           workspace)
 
 
 def quantize(x: torch.Tensor, q: QLike, axis: int = -1,
@@ -428,10 +460,15 @@ def copy(src: torch.Tensor, dst: torch.Tensor) -> None:
 
 
 def bits_per_element(q: QLike, sparse24: bool = False, row_len: int = 0, value_bits: int = 0,
-                     tensor_elems: int = 0) -> float:
-    """Storage bits charged per original element (host arithmetic in the library)."""
+                     tensor_elems: int = 0, pattern: Optional[str] = None) -> float:
+    """Storage bits charged per original element (host arithmetic in the
+    library).  ``pattern``: "dense", "2:4" or "pairs4:8" (``sparse24=True`` is
+    "2:4")."""
     qs = qspec(q)
-    return lib().sparq24_bits_per_element(ctypes.byref(qs), int(sparse24), row_len, value_bits,
+    if pattern is None:
+        pattern = "2:4" if sparse24 else "dense"
+    code = {"dense": 0, "2:4": 1, "pairs4:8": 2}[pattern]
+    return lib().sparq24_bits_per_element(ctypes.byref(qs), code, row_len, value_bits,
                                           tensor_elems)
 
 

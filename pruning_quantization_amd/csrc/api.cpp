@@ -155,10 +155,11 @@ struct EnergyPlan {
   EnergyParams p;
   FinalizeParams f;
   const float* nv_in = nullptr;
-  bool need_nv_partials = false;
-  int nparts = 0;
+  const float* knv_in = nullptr;  // NVFP4 on kept values
+  bool need_nv_partials = false, need_knv_partials = false;
+  int nparts = 0, nkparts = 0;
   int64_t nrows = 0, rpb = 0, nblk = 0;
-  size_t off_rowpart = 0, off_csum = 0, off_parts = 0, need = 0;
+  size_t off_rowpart = 0, off_csum = 0, off_parts = 0, off_kparts = 0, need = 0;
 };
 
 sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
@@ -169,8 +170,10 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   const sparq24_qspec* kept_u[kMaxQ];
   const sparq24_qspec* dense_u[kMaxQ];
   int nk = 0, nd = 0;
-  const unsigned kept_ok = (1u << SPARQ24_Q_NONE) | (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3);
-  const unsigned dense_ok = kept_ok | (1u << SPARQ24_Q_MXFP4) | (1u << SPARQ24_Q_NVFP4);
+  const unsigned kept_ok = (1u << SPARQ24_Q_NONE) | (1u << SPARQ24_Q_INT) |
+                           (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
+                           (1u << SPARQ24_Q_NVFP4);
+  const unsigned dense_ok = kept_ok & ~(1u << SPARQ24_Q_NONE);
   auto same = [](const sparq24_qspec* a, const sparq24_qspec* b) {
     return a->fmt == b->fmt && (a->fmt != SPARQ24_Q_INT || a->bits == b->bits) &&
            (a->fmt != SPARQ24_Q_NVFP4 || a->tensor_amax_in == b->tensor_amax_in);
@@ -182,6 +185,9 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
     CHECK(check_q(&dense_q[i], dense_ok, cf, qm));
     if (dense_q[i].fmt == SPARQ24_Q_MXFP4 && d.K % 32) return SPARQ24_ERR_SHAPE;
     if (dense_q[i].fmt == SPARQ24_Q_NVFP4 && d.K % 16) return SPARQ24_ERR_SHAPE;
+    // block formats on kept values block the compressed row (K/2 values)
+    if (kept_q[i].fmt == SPARQ24_Q_MXFP4 && d.K % 64) return SPARQ24_ERR_SHAPE;
+    if (kept_q[i].fmt == SPARQ24_Q_NVFP4 && d.K % 32) return SPARQ24_ERR_SHAPE;
   }
   for (int i = 0; i < npairs; ++i) {
     int ki = -1, di = -1;
@@ -194,13 +200,17 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
     pl.f.kcol[i] = 2 + ki;
     pl.f.dcol[i] = di;  // fixed up below once nk is known
   }
-  int n_nv = 0;
+  int n_nv = 0, n_knv = 0;
   for (int j = 0; j < nk; ++j) {
     float qm;
     int cf;
     check_q(kept_u[j], kept_ok, cf, qm);
     pl.p.kept.fmt[j] = cf;
     pl.p.kept.qmax[j] = qm;
+    if (cf == CF_NV) {
+      ++n_knv;
+      pl.knv_in = kept_u[j]->tensor_amax_in;
+    }
   }
   for (int j = 0; j < nd; ++j) {
     float qm;
@@ -213,7 +223,7 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
       pl.nv_in = dense_u[j]->tensor_amax_in;
     }
   }
-  if (n_nv > 1) return SPARQ24_ERR_UNSUPPORTED;
+  if (n_nv > 1 || n_knv > 1) return SPARQ24_ERR_UNSUPPORTED;
   pl.p.kept.n = nk;
   pl.p.dense.n = nd;
   for (int i = 0; i < npairs; ++i) pl.f.dcol[i] += 2 + nk;
@@ -224,13 +234,16 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   pl.nblk = (pl.nrows + pl.rpb - 1) / pl.rpb;
   pl.need_nv_partials = n_nv == 1 && pl.nv_in == nullptr;
   pl.nparts = pl.need_nv_partials ? absmax_partial_count(d) : 0;
+  pl.need_knv_partials = n_knv == 1 && pl.knv_in == nullptr;
+  pl.nkparts = pl.need_knv_partials ? absmax_partial_count(d) : 0;
   const size_t rowpart = (size_t)pl.f.ncols * (size_t)energy_partial_rows(pl.nrows) * sizeof(double);
   const size_t sums = (size_t)pl.f.ncols * (size_t)pl.nblk *
                       (size_t)energy_chunks_per_block(pl.rpb) * sizeof(double);
   pl.off_rowpart = staging_bytes(d);
   pl.off_csum = pl.off_rowpart + round_up(rowpart, kAlign);
   pl.off_parts = pl.off_csum + round_up(sums, kAlign);
-  pl.need = pl.off_parts + round_up((size_t)pl.nparts * sizeof(uint32_t), kAlign);
+  pl.off_kparts = pl.off_parts + round_up((size_t)pl.nparts * sizeof(uint32_t), kAlign);
+  pl.need = pl.off_kparts + round_up((size_t)pl.nkparts * sizeof(uint32_t), kAlign);
   return SPARQ24_OK;
 }
 
@@ -249,6 +262,15 @@ sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, Energ
     pl.p.n_partials = pl.nparts;
   }
   pl.p.nv_tamax = pl.nv_in;
+  if (pl.need_knv_partials) {
+    uint32_t* kparts = (uint32_t*)(w + pl.off_kparts);
+    CHECK(launched(launch_kept_absmax_partials(d, pl.p.pairs48 ? PAT_48 : PAT_24,
+                                               score == SPARQ24_SCORE_WANDA, col_norm, kparts,
+                                               stream)));
+    pl.p.kept_nv_partials = kparts;
+    pl.p.n_kept_partials = pl.nkparts;
+  }
+  pl.p.kept_nv_tamax = pl.knv_in;
   int64_t nparts = 0;
   CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart,
                                     pl.rpb, &nparts, stream)));
@@ -335,31 +357,74 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
   return launched(launch_quant_rows(d, cfmt, qmax, codes, (float*)scales, stream));
 }
 
-sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, const float* col_norm,
-                                      const sparq24_qspec* q, void* codes, uint8_t* meta,
-                                      float* scales, void* ws, size_t* ws_bytes,
-                                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+sparq24_status prune_quantize_any(const sparq24_tensor* x, int pat, int32_t score,
+                                  const float* col_norm, const sparq24_qspec* q, void* codes,
+                                  uint8_t* meta, void* scales, float* tensor_scale_out, void* ws,
+                                  size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;
   CHECK(check_tensor(x, true, d));
   CHECK(check_score(score, col_norm));
   int cfmt;
   float qmax;
-  CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3), cfmt, qmax));
-  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
+                       (1u << SPARQ24_Q_NVFP4),
+                cfmt, qmax));
+  const bool block = cfmt == CF_MX || cfmt == CF_NV;
+  if (pat == PAT_48 && d.K % 16) return SPARQ24_ERR_SHAPE;
+  if (cfmt == CF_MX && d.K % 64) return SPARQ24_ERR_SHAPE;  // 32 kept values per block
+  if (cfmt == CF_NV && d.K % 32) return SPARQ24_ERR_SHAPE;  // 16 kept values per block
+  if (!block && d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  const bool nv_parts = cfmt == CF_NV && q->tensor_amax_in == nullptr;
+  const int nparts = nv_parts ? absmax_partial_count(d) : 0;
   const size_t stage = staging_bytes(d);
+  const size_t need = stage + round_up((size_t)nparts * sizeof(uint32_t), kAlign);
   bool query;
-  CHECK(workspace(ws, ws_bytes, stage, query));
+  CHECK(workspace(ws, ws_bytes, need, query));
   if (query) return SPARQ24_OK;
   if (d.B * d.R * d.K == 0) return SPARQ24_OK;
   if (!codes || !meta || !scales) return SPARQ24_ERR_INVALID;
+  if (cfmt == CF_NV && !tensor_scale_out) return SPARQ24_ERR_INVALID;
   if (!aligned16(codes) || !aligned16(meta) || !aligned16(scales)) return SPARQ24_ERR_ALIGN;
+  if (cfmt == CF_NV && ((uintptr_t)tensor_scale_out & 3u)) return SPARQ24_ERR_ALIGN;
   CHECK(device_ok());
   if (stage) {
     CHECK(launched(launch_transpose_rows(d, ws, stream)));
     d = staged_view(d, ws);
   }
-  return launched(launch_prune_quantize(d, score == SPARQ24_SCORE_WANDA, col_norm, cfmt, qmax,
-                                        codes, meta, scales, stream));
+  const bool wanda = score == SPARQ24_SCORE_WANDA;
+  if (block) {
+    uint32_t* parts = (uint32_t*)((char*)ws + stage);
+    if (nv_parts) CHECK(launched(launch_kept_absmax_partials(d, pat, wanda, col_norm, parts, stream)));
+    return launched(launch_prune_quant_fp4(d, pat, wanda, col_norm, cfmt, q->tensor_amax_in, parts,
+                                           nparts, codes, meta, (uint8_t*)scales,
+                                           tensor_scale_out, stream));
+  }
+  return launched(launch_prune_quantize(d, pat, wanda, col_norm, cfmt, qmax, codes, meta,
+                                        (float*)scales, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, const float* col_norm,
+                                      const sparq24_qspec* q, void* codes, uint8_t* meta,
+                                      void* scales, float* tensor_scale_out, void* ws,
+                                      size_t* ws_bytes, hipStream_t stream) {
+  return prune_quantize_any(x, PAT_24, score, col_norm, q, codes, meta, scales, tensor_scale_out,
+                            ws, ws_bytes, stream);
+}
+
+sparq24_status sparq24_prune_quantize_pairs48(const sparq24_tensor* x, const sparq24_qspec* q,
+                                              void* codes, uint8_t* meta, void* scales,
+                                              float* tensor_scale_out, void* ws,
+                                              size_t* ws_bytes, hipStream_t stream) {
+  return prune_quantize_any(x, PAT_48, SPARQ24_SCORE_MAGNITUDE, nullptr, q, codes, meta, scales,
+                            tensor_scale_out, ws, ws_bytes, stream);
 }
 
 sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score, const float* col_norm,
@@ -471,36 +536,39 @@ sparq24_status sparq24_copy(const void* src, void* dst, size_t bytes, hipStream_
 
 double sparq24_bits_per_element(const sparq24_qspec* q, int32_t sparse24, int64_t row_len,
                                 int32_t value_bits, int64_t tensor_elems) {
-  if (!q || row_len < 0 || tensor_elems < 0) return -1.0;
-  double v, scale;
+  if (!q || row_len < 0 || tensor_elems < 0 || sparse24 < 0 || sparse24 > 2) return -1.0;
+  double v, row = 0.0, block = 0.0, tensor = 0.0;
   switch (q->fmt) {
     case SPARQ24_Q_INT:
       if (q->bits < 2 || q->bits > 16) return -1.0;
       v = q->bits;
-      scale = row_len ? 32.0 / (double)row_len : 0.0;
+      row = row_len ? 32.0 / (double)row_len : 0.0;
       break;
     case SPARQ24_Q_FP8_E4M3:
       v = 8;
-      scale = row_len ? 32.0 / (double)row_len : 0.0;
+      row = row_len ? 32.0 / (double)row_len : 0.0;
       break;
     case SPARQ24_Q_NONE:
       if (value_bits <= 0) return -1.0;
       v = value_bits;
-      scale = 0.0;
       break;
     case SPARQ24_Q_MXFP4:
       v = 4;
-      scale = 8.0 / 32.0;
+      block = 8.0 / 32.0;
       break;
     case SPARQ24_Q_NVFP4:
       v = 4;
-      scale = 8.0 / 16.0 + (tensor_elems ? 32.0 / (double)tensor_elems : 0.0);
+      block = 8.0 / 16.0;
+      tensor = tensor_elems ? 32.0 / (double)tensor_elems : 0.0;
       break;
     default:
       return -1.0;
   }
-  // 2:4 keeps half the values and spends 2 position bits per kept value
-  return sparse24 ? v / 2.0 + 1.0 + scale : v + scale;
+  if (sparse24 == 0) return v + row + block + tensor;
+  // half the values are kept; block scales cover kept values; position bits:
+  // 2 per kept value (2:4) or 2 per kept pair (pairwise 4:8)
+  const double index = sparse24 == 1 ? 1.0 : 0.5;
+  return v / 2.0 + index + row + block / 2.0 + tensor;
 }
 
 const char* sparq24_status_string(sparq24_status s) {

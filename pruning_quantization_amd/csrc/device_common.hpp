@@ -430,6 +430,12 @@ __device__ inline uint32_t enc_e2m1_x8(const float* y) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
 }
 
+// Four E2M1 codes in bits 0..15 (element j in nibble j), same conversion.
+__device__ inline uint32_t enc_e2m1_x4(float a, float b, float c, float d) {
+  const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, 1.0f, 1);
+}
+
 // Symmetric INT rounding through the fp32 adder: for |y| <= qmax < 2^22,
 // fp32(clamp(y) + 1.5 * 2^23) holds round-half-even(clamp(y)) in its low
 // mantissa bits (the add rounds to nearest even at unit spacing).  Clamping

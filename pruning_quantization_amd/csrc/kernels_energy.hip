@@ -161,6 +161,46 @@ __device__ inline float sq_err_row(int fmt, float s, float inv, float qmax, cons
   return e[0];
 }
 
+// Error energy of 4 kept values (one unit) under a block format whose block
+// spans NB adjacent lanes' units (NV: 4 units = 16 kept, MX: 8 = 32);
+// every lane of the wave must call this.  Returns the fp32 sum of the four
+// squared fp32-rounded residuals.
+template <bool NV>
+__device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t a = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+    am = am > a ? am : a;
+  }
+  uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
+  am = am > w ? am : w;
+  w = (uint32_t)__shfl_xor((int)am, 2, 64);
+  am = am > w ? am : w;
+  float r[4];
+  if constexpr (NV) {
+    const uint32_t bc = enc_e4m3(__uint_as_float(am) * gnv);
+    const float bval = dec_e4m3(bc);
+    const float d = bval * s_t;
+    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    const uint32_t pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(dec_e2m1((pk >> (4 * e)) & 0xFu) * bval, s_t, -v[e]);
+  } else {
+    w = (uint32_t)__shfl_xor((int)am, 4, 64);
+    am = am > w ? am : w;
+    const int ex = mx_exp_e(am);
+    const float X = __builtin_ldexpf(1.0f, ex);
+    const uint32_t pk = enc_e2m1_x4(__builtin_ldexpf(v[0], -ex), __builtin_ldexpf(v[1], -ex),
+                                    __builtin_ldexpf(v[2], -ex), __builtin_ldexpf(v[3], -ex));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(dec_e2m1((pk >> (4 * e)) & 0xFu), X, -v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = r[e] * r[e];
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
 // Row partial sums go either to rowpart[col][row] (blocked reductions) or,
 // when the whole operand is one block (ACC), into a per-team LDS accumulator
 // that each team writes once, to rowpart[col][team] (nparts = all teams).
@@ -211,6 +251,13 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
     const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
   }
+  bool any_knv = false;
+  for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
+  float ks_t = 0.f, kgnv = 0.f;
+  if (any_knv) {
+    const float T = block_tensor_amax_e(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
+    if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
+  }
   const int64_t nrows = g.nrows;
   for_each_row_pipelined<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
@@ -247,7 +294,14 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
       const int fmt = p.kept.fmt[q];
       const float qmax = p.kept.qmax[q];
       double acc = 0.0;
-      if (fmt != CF_NONE) {
+      if (fmt == CF_MX || fmt == CF_NV) {
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+          acc += (double)(fmt == CF_NV ? kept_block_err4<true>(v, ks_t, kgnv)
+                                       : kept_block_err4<false>(v, 0.f, 0.f));
+        }
+      } else if (fmt != CF_NONE) {
         float s, inv;
         row_scale(amax, qmax, s, inv);
 #pragma unroll
@@ -335,6 +389,13 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
   }
+  bool any_knv = false;
+  for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
+  float ks_t = 0.f, kgnv = 0.f;
+  if (any_knv) {
+    const float T = block_tensor_amax_e(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
+    if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
+  }
   const int64_t nrows = g.nrows;
 
   for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
@@ -386,7 +447,17 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
       const int fmt = p.kept.fmt[q];
       const float qmax = p.kept.qmax[q];
       double acc = 0.0;
-      if (fmt != CF_NONE) {
+      if (fmt == CF_MX || fmt == CF_NV) {
+        // kept values of a unit in position order; dropped ones are not
+        // part of the compressed row
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const Kept<DT> kp = p.pairs48 ? gather_pairs48(u[j], mbs[j]) : gather_kept(u[j], mbs[j]);
+          const float v[4] = {kp.f(0), kp.f(1), kp.f(2), kp.f(3)};
+          acc += (double)(fmt == CF_NV ? kept_block_err4<true>(v, ks_t, kgnv)
+                                       : kept_block_err4<false>(v, 0.f, 0.f));
+        }
+      } else if (fmt != CF_NONE) {
         float s, inv;
         row_scale(famk, qmax, s, inv);
 #pragma unroll

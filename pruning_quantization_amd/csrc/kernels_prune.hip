@@ -205,21 +205,23 @@ __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
   }
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA, int CF>
+template <class DT, int TEAM, int UPL, bool WANDA, int CF, int PAT>
 SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ norm, float qmax,
                                          char* __restrict__ codes, uint8_t* __restrict__ meta,
                                          float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
   constexpr int CB = CF == CF_INT16 ? 8 : 4;  // code bytes per unit
-  // 16-bit magnitude: the kept maximum of a row equals its plain maximum
+  // 16-bit magnitude 2:4: the kept maximum of a row equals its plain maximum
   // (every group keeps its largest element), so the scale comes from one
   // packed-max pass over the raw row and selection + encode stream unit by
-  // unit afterwards.
-  constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA;
+  // unit afterwards.  Pairwise 4:8 can drop a row's largest element, so it
+  // takes the kept maximum like Wanda.
+  constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA && PAT == PAT_24;
   for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
     uint32_t am = 0;
     uint32_t mb[FAST16 ? 1 : UPL];
+    uint32_t mo[PAT == PAT_48 ? UPL : 1];  // neighbouring unit's nibble (4:8 meta bytes)
     if constexpr (FAST16) {
 #pragma unroll
       for (int j = 0; j < UPL; ++j) am = unit_absmax16_packed(u[j].w, am);
@@ -228,9 +230,16 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
         const int64_t i = (int64_t)j * TEAM + t;
-        mb[j] = 0;
-        if (i < g.nunits) mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
-        const uint32_t a = kept_absmax(gather_kept(u[j], mb[j]));  // zero units gather zeros
+        uint32_t a;
+        if constexpr (PAT == PAT_48) {
+          mb[j] = select_pairs48(u[j]);  // zero units select zeros
+          mo[j] = (uint32_t)__shfl_xor((int)mb[j], 1, 64);
+          a = kept_absmax(gather_pairs48(u[j], mb[j]));
+        } else {
+          mb[j] = 0;
+          if (i < g.nunits) mb[j] = select_unit<DT, WANDA>(u[j], norm, i * 8);
+          a = kept_absmax(gather_kept(u[j], mb[j]));  // zero units gather zeros
+        }
         am = am > a ? am : a;
       }
     }
@@ -240,7 +249,7 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
     row_scale(DT::to_f32(am), qmax, s, inv);
     // per-row output bases; unit j of this lane sits at a constant offset
     char* crow = codes + (row * g.nunits + t) * CB;
-    uint8_t* mrow = meta + row * g.nunits + t;
+    uint8_t* mrow = PAT == PAT_48 ? meta + row * (g.nunits / 2) + (t >> 1) : meta + row * g.nunits + t;
     auto emit = [&](int j) {
       Kept<DT> kp;
       uint32_t m;
@@ -249,6 +258,9 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
         kp.k[0] = r.k0;
         kp.k[1] = r.k1;
         m = r.mb;
+      } else if constexpr (PAT == PAT_48) {
+        kp = gather_pairs48(u[j], mb[j]);
+        m = mb[j];
       } else {
         kp = gather_kept(u[j], mb[j]);
         m = mb[j];
@@ -257,7 +269,11 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = kp.f(e) * inv;
       store_kept_codes<CF>(crow + j * TEAM * CB, y, qmax);
-      st(mrow + j * TEAM, (uint8_t)m);
+      if constexpr (PAT == PAT_48) {
+        if ((t & 1) == 0) st(mrow + j * (TEAM / 2), (uint8_t)(m | (mo[j] << 4)));
+      } else {
+        st(mrow + j * TEAM, (uint8_t)m);
+      }
     };
     if ((UPL - 1) * TEAM + t < g.nunits) {  // every unit of this lane exists
 #pragma unroll
@@ -367,27 +383,27 @@ hipError_t launch_prune_compress_pairs48(const RowDesc& d, void* vals, uint8_t* 
   });
 }
 
-hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm, int cfmt,
-                                 float qmax, void* codes, uint8_t* meta, float* scales,
+hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                 int cfmt, float qmax, void* codes, uint8_t* meta, float* scales,
                                  hipStream_t s) {
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
-      auto go = [&]<bool W, int CF>() {
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF>), grid, dim3(kBlock), 0, s, g,
-                           norm, qmax, (char*)codes, meta, scales);
+      auto go = [&]<bool W, int P, int CF>() {
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P>), grid, dim3(kBlock), 0, s,
+                           g, norm, qmax, (char*)codes, meta, scales);
         return hipGetLastError();
       };
-      if (wanda) {
-        if (cfmt == CF_FP8) return go.template operator()<true, CF_FP8>();
-        if (cfmt == CF_INT8) return go.template operator()<true, CF_INT8>();
-        return go.template operator()<true, CF_INT16>();
-      }
-      if (cfmt == CF_FP8) return go.template operator()<false, CF_FP8>();
-      if (cfmt == CF_INT8) return go.template operator()<false, CF_INT8>();
-      return go.template operator()<false, CF_INT16>();
+      auto fmt = [&]<bool W, int P>() {
+        if (cfmt == CF_FP8) return go.template operator()<W, P, CF_FP8>();
+        if (cfmt == CF_INT8) return go.template operator()<W, P, CF_INT8>();
+        return go.template operator()<W, P, CF_INT16>();
+      };
+      if (pat == PAT_48) return fmt.template operator()<false, PAT_48>();
+      if (wanda) return fmt.template operator()<true, PAT_24>();
+      return fmt.template operator()<false, PAT_24>();
     });
   });
 }

@@ -259,6 +259,144 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prune (2:4 or pairwise 4:8 [PD §6]) and quantize the kept values to MXFP4 /
+// NVFP4.  A unit (8 inputs) yields 4 kept values = 4 E2M1 codes (16 bits);
+// the compressed row is blocked like a dense one, so an NV block (16 kept)
+// is 4 adjacent lanes and an MX block (32 kept) 8.  With NVFP4 the sparse
+// operand is Blackwell's sparse FP4 layout of [PD §6].
+// ---------------------------------------------------------------------------
+template <class DT, int PAT, bool WANDA>
+__device__ inline uint32_t select_any(const Unit<DT>& u, const float* norm, int64_t i,
+                                      int64_t nunits, Kept<DT>& kp) {
+  uint32_t m;
+  if constexpr (PAT == PAT_48) {
+    m = select_pairs48(u);
+    kp = gather_pairs48(u, m);
+  } else {
+    m = 0;
+    if (!WANDA || i < nunits) m = select_unit<DT, WANDA>(u, norm, i * 8);
+    kp = gather_kept(u, m);
+  }
+  return m;
+}
+
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool NV>
+__global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
+    const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    const float* __restrict__ norm, const float* __restrict__ tamax_in,
+    const uint32_t* __restrict__ partials, int nparts, uint16_t* __restrict__ codes,
+    uint8_t* __restrict__ meta, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+  __shared__ uint32_t red[kBlock / 64];
+  float s_t = 0.f, g = 0.f;
+  if constexpr (NV) {
+    const float T = block_tensor_amax(tamax_in, partials, nparts, red);
+    nv_tensor_scales(T, s_t, g);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+  }
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;
+  const char* xr = x + b * bs + (active ? r : 0) * rs;
+  const int64_t orow = b * R + r;
+  // shuffles below need every lane of the wave, so masked lanes run along
+  for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+    Unit<DT> u[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+      else zero_unit(u[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      Kept<DT> kp;
+      const uint32_t m = select_any<DT, PAT, WANDA>(u[j], norm, i, nunits, kp);
+      float v[4];
+      uint32_t am = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = kp.f(e);
+        const uint32_t a = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+        am = am > a ? am : a;
+      }
+      uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
+      am = am > w ? am : w;
+      w = (uint32_t)__shfl_xor((int)am, 2, 64);
+      am = am > w ? am : w;
+      uint32_t sc, pk;
+      if constexpr (NV) {
+        sc = enc_e4m3(__uint_as_float(am) * g);
+        const float d = dec_e4m3(sc) * s_t;
+        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      } else {
+        w = (uint32_t)__shfl_xor((int)am, 4, 64);
+        am = am > w ? am : w;
+        const int e = mx_exponent(am);
+        sc = (uint32_t)(e + 127);
+        pk = enc_e2m1_x4(__builtin_ldexpf(v[0], -e), __builtin_ldexpf(v[1], -e),
+                         __builtin_ldexpf(v[2], -e), __builtin_ldexpf(v[3], -e));
+      }
+      const uint32_t mo = PAT == PAT_48 ? (uint32_t)__shfl_xor((int)m, 1, 64) : 0u;
+      if (active && i < nunits) {
+        st(codes + orow * nunits + i, (uint16_t)pk);
+        if constexpr (NV) {
+          if ((i & 3) == 0) st(scales + orow * (nunits / 4) + (i >> 2), (uint8_t)sc);
+        } else {
+          if ((i & 7) == 0) st(scales + orow * (nunits / 8) + (i >> 3), (uint8_t)sc);
+        }
+        if constexpr (PAT == PAT_48) {
+          if ((i & 1) == 0) st(meta + orow * (nunits / 2) + (i >> 1), (uint8_t)(m | (mo << 4)));
+        } else {
+          st(meta + orow * nunits + i, (uint8_t)m);
+        }
+      }
+    }
+  }
+}
+
+// Partial maxima of the kept values' magnitudes (the NVFP4 tensor maximum of
+// a sparse operand whose kept maximum can differ from its plain maximum).
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA>
+__global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
+    const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
+    const float* __restrict__ norm, uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[kBlock / 64];
+  const int t = threadIdx.x % TEAM;
+  constexpr int RPB = kBlock / TEAM;
+  uint32_t am = 0;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TEAM; row < B * R;
+       row += (int64_t)gridDim.x * RPB) {
+    const int64_t b = row / R, r = row % R;
+    const char* xr = x + b * bs + r * rs;
+    for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const int64_t i = c0 + j * TEAM + t;
+        if (i < nunits) {
+          Unit<DT> u;
+          load_unit(u, xr + i * (8 * DT::ESIZE));
+          Kept<DT> kp;
+          select_any<DT, PAT, WANDA>(u, norm, i, nunits, kp);
+          const uint32_t a = __float_as_uint(DT::to_f32(kept_absmax(kp)));
+          am = am > a ? am : a;
+        }
+      }
+    }
+  }
+  am = team_max_u32<64>(am, red);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = red[0];
+    for (int i = 1; i < kBlock / 64; ++i) m = m > red[i] ? m : red[i];
+    partials[blockIdx.x] = m;
+  }
+}
+
 hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
                              hipStream_t s) {
   const int64_t nunits = d.K / 8;
@@ -293,6 +431,50 @@ hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32
       hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, true>), row_grid(d, TEAM), dim3(kBlock), 0,
                          s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials, nparts,
                          (uint32_t*)codes, scales, ts_out);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                  int cfmt, const float* tamax_in, const uint32_t* partials,
+                                  int nparts, void* codes, uint8_t* meta, uint8_t* scales,
+                                  float* ts_out, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      auto go = [&]<int P, bool W, bool NV>() {
+        hipLaunchKernelGGL((k_prune_quant_fp4<DT, TEAM, UPL, P, W, NV>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, tamax_in,
+                           partials, nparts, (uint16_t*)codes, meta, scales, ts_out);
+        return hipGetLastError();
+      };
+      const bool nv = cfmt == CF_NV;
+      if (pat == PAT_48)
+        return nv ? go.template operator()<PAT_48, false, true>()
+                  : go.template operator()<PAT_48, false, false>();
+      if (wanda)
+        return nv ? go.template operator()<PAT_24, true, true>()
+                  : go.template operator()<PAT_24, true, false>();
+      return nv ? go.template operator()<PAT_24, false, true>()
+                : go.template operator()<PAT_24, false, false>();
+    });
+  });
+}
+
+hipError_t launch_kept_absmax_partials(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                       uint32_t* partials, hipStream_t s) {
+  if (pat == PAT_24 && !wanda) return launch_absmax_partials(d, partials, s);  // kept max == max
+  const int64_t nunits = d.K / 8;
+  const int nb = absmax_partial_count(d);
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      if (pat == PAT_48)
+        hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, PAT_48, false>), dim3(nb),
+                           dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials);
+      else
+        hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, PAT_24, true>), dim3(nb),
+                           dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials);
       return hipGetLastError();
     });
   });

@@ -20,6 +20,9 @@ struct RowDesc {
   bool flat;            // fully contiguous: bs == R*rs, rs == K*esize
 };
 
+// Sparsity pattern: element-wise 2:4 or pairwise 4:8.
+enum Pattern : int { PAT_24 = 0, PAT_48 = 1 };
+
 constexpr int kMaxQ = 16;
 
 struct QList {
@@ -34,6 +37,10 @@ struct EnergyParams {
   const float* nv_tamax;       // device T for NVFP4 (or null -> reduce partials)
   const uint32_t* nv_partials; // fp32 bit patterns of partial maxima
   int n_partials;
+  // NVFP4 on kept values: T over the kept values, same protocol
+  const float* kept_nv_tamax;
+  const uint32_t* kept_nv_partials;
+  int n_kept_partials;
 };
 
 // Row kernels that hold a whole row in registers support up to this many units.
@@ -43,9 +50,17 @@ hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm
                                  uint8_t* meta, hipStream_t s);
 hipError_t launch_prune_compress_pairs48(const RowDesc& d, void* vals, uint8_t* meta,
                                         hipStream_t s);
-hipError_t launch_prune_quantize(const RowDesc& d, bool wanda, const float* norm, int cfmt,
-                                 float qmax, void* codes, uint8_t* meta, float* scales,
+hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                 int cfmt, float qmax, void* codes, uint8_t* meta, float* scales,
                                  hipStream_t s);
+// Kept values in MXFP4 / NVFP4 (cfmt CF_MX / CF_NV), either pattern.
+hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                  int cfmt, const float* tamax_in, const uint32_t* partials,
+                                  int nparts, void* codes, uint8_t* meta, uint8_t* scales,
+                                  float* ts_out, hipStream_t s);
+// Partial maxima of |kept| (absmax_partial_count(d) of them).
+hipError_t launch_kept_absmax_partials(const RowDesc& d, int pat, bool wanda, const float* norm,
+                                       uint32_t* partials, hipStream_t s);
 hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
                              hipStream_t s);
 int absmax_partial_count(const RowDesc& d);

@@ -125,8 +125,17 @@ def test_energy_validation(L):
     assert f(ctypes.byref(t), 0, None, arr, darr, 2, 0, FAKE, None, ctypes.byref(n), None) == OK
     # 4 rows x (2 + 2 kept + 2 dense) doubles + one block of sums, rounded to 256 B
     assert n.value >= 4 * 6 * 8 + 6 * 8
+    # block formats on kept values block the compressed row: K % 64 (MX), K % 32 (NV)
     kept_mx = (B.CQSpec * 1)(q(B.Q_MXFP4))
-    assert f(ctypes.byref(t), 0, None, kept_mx, darr, 1, 0, FAKE, None, ctypes.byref(n), None) == UNSUPPORTED
+    kept_nv = (B.CQSpec * 1)(q(B.Q_NVFP4))
+    assert f(ctypes.byref(t), 0, None, kept_mx, darr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
+    assert f(ctypes.byref(tensor(k=32)), 0, None, kept_mx, darr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
+    assert f(ctypes.byref(tensor(k=48)), 0, None, kept_nv, darr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
+    n0 = n.value
+    assert f(ctypes.byref(t), 0, None, kept_nv, darr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
+    assert n.value > n0 - 1                    # kept NVFP4 adds the kept-maximum partials
+    none = (B.CQSpec * 1)(q(B.Q_NONE))
+    assert f(ctypes.byref(t), 0, None, none, none, 1, 0, FAKE, None, ctypes.byref(n), None) == UNSUPPORTED
     t48 = tensor(k=48)
     mx = (B.CQSpec * 1)(q(B.Q_MXFP4))
     assert f(ctypes.byref(t48), 0, None, arr, mx, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
@@ -149,6 +158,34 @@ def test_pairs48_validation(L):
     assert n.value > 0
 
 
+def test_prune_quantize_validation(L):
+    n = ctypes.c_size_t(7)
+    f = L.sparq24_prune_quantize
+    g = L.sparq24_prune_quantize_pairs48
+
+    def pq(t, qq, ws=None, nb=None, ts=FAKE, score=0, norm=None):
+        return f(ctypes.byref(t), score, norm, ctypes.byref(qq), FAKE, FAKE, FAKE, ts, ws, nb, None)
+
+    def pq48(t, qq, ws=None, nb=None, ts=FAKE):
+        return g(ctypes.byref(t), ctypes.byref(qq), FAKE, FAKE, FAKE, ts, ws, nb, None)
+
+    assert pq(tensor(k=32), q(B.Q_MXFP4), nb=ctypes.byref(n)) == SHAPE      # 32 kept per block
+    assert pq(tensor(k=64), q(B.Q_MXFP4), nb=ctypes.byref(n)) == OK and n.value == 0
+    assert pq(tensor(k=48), q(B.Q_NVFP4), nb=ctypes.byref(n)) == SHAPE      # 16 kept per block
+    assert pq(tensor(k=64), q(B.Q_NVFP4), nb=ctypes.byref(n)) == OK and n.value > 0
+    assert pq(tensor(k=64), q(B.Q_NONE), nb=ctypes.byref(n)) == UNSUPPORTED
+    assert pq(tensor(k=64), q(B.Q_NVFP4), ws=FAKE, nb=ctypes.byref(n), ts=None) == INVALID
+    assert pq(tensor(k=64), q(B.Q_NVFP4), ws=FAKE, nb=ctypes.byref(n), ts=FAKE + 2) == ALIGN
+    assert pq(tensor(k=64), q(B.Q_FP8), nb=ctypes.byref(n), score=1) == INVALID  # Wanda without norms
+    assert pq48(tensor(k=24), q(B.Q_FP8), nb=ctypes.byref(n)) == SHAPE
+    assert pq48(tensor(k=16), q(B.Q_FP8), nb=ctypes.byref(n)) == OK and n.value == 0
+    assert pq48(tensor(k=32), q(B.Q_MXFP4), nb=ctypes.byref(n)) == SHAPE
+    assert pq48(tensor(k=32), q(B.Q_NVFP4), nb=ctypes.byref(n)) == OK and n.value > 0
+    # transposed operands are staged through the workspace
+    assert pq48(tensor(rows=8, k=128, rs=1, ks=8), q(B.Q_FP8), nb=ctypes.byref(n)) == OK
+    assert n.value >= 8 * 128 * 2
+
+
 def test_copy_validation(L):
     assert L.sparq24_copy(FAKE, FAKE, 0, None) == OK
     assert L.sparq24_copy(FAKE, FAKE, 24, None) == ALIGN
@@ -163,6 +200,12 @@ def test_bits_per_element_matches_oracle(L):
         want = O.bits_per_element(O.QSpec(fmt, bits), sparse24=sp, row_len=rl or None)
         assert got == want
     assert B.bits_per_element("none", sparse24=True, value_bits=16) == 9.0
+    for fmt in ("mxfp4", "nvfp4", ("int", 8), "fp8"):
+        for pat in ("dense", "2:4", "pairs4:8"):
+            qq = fmt if isinstance(fmt, tuple) else (fmt, 0)
+            got = B.bits_per_element(qq, row_len=4096, tensor_elems=1 << 20, pattern=pat)
+            want = O.bits_per_element(O.QSpec(*qq), row_len=4096, tensor_elems=1 << 20, pattern=pat)
+            assert got == want, (fmt, pat)
     assert B.bits_per_element(("int", 1)) < 0
 
 

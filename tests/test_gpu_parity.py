@@ -366,3 +366,138 @@ def test_predict_R_pairs48(dtype, k):
         got = S.predict_R_pairs48(x, ["none"], ["mxfp4"])
         want = O.predict_R(raw, dtype, [O.QSpec("none")], [O.QSpec("mxfp4")], pattern="pairs4:8")
         rel_close(raw_np(got), want)
+
+
+# ---------------------------------------------------------------------------
+# Block formats on kept values and the sparse FP4 operand ([PD §3], [PD §6])
+# ---------------------------------------------------------------------------
+
+
+def check_pq(got, want, what):
+    names = ("codes", "meta", "scales", "tensor scale")
+    assert len(got) == len(want), (what, len(got), len(want))
+    for g, w, n in zip(got, want, names):
+        g = raw_np(g)
+        w = np.asarray(w)
+        if n == "tensor scale":
+            g, w = g.reshape(-1)[:1], np.asarray([w], dtype=np.float32)
+        assert_same(g, w, f"{what} {n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [64, 128, 1088, 4096])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_prune_quantize_block_kept(dtype, k, fmt):
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 17, 23, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        check_pq(S.prune_quantize(x, fmt), O.prune_quantize(raw, dtype, O.QSpec(fmt)),
+                 f"2:4 {fmt} {kind}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_prune_quantize_block_kept_wanda(fmt):
+    rng = np.random.default_rng(61)
+    k = 1024
+    raw = inputs(62, 31, k, "bf16", "ties")
+    norm = (rng.integers(0, 4, size=k) * 0.5 + rng.random(k) * (rng.random(k) < 0.5)).astype(np.float32)
+    x = to_dev(raw, "bf16")
+    n = torch.from_numpy(norm).cuda()
+    got = S.prune_quantize(x, fmt, score="wanda", col_norm=n)
+    check_pq(got, O.prune_quantize(raw, "bf16", O.QSpec(fmt), "wanda", norm), f"wanda {fmt}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [16, 48, 1024, 4096, 4112, 8192])
+def test_prune_quantize_pairs48_rows(dtype, k):
+    rows = 19 if k <= 4112 else 5
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 29, rows, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        for fmt, bits in (("fp8", 0), ("int", 8), ("int", 4), ("int", 12)):
+            got = S.prune_quantize_pairs48(x, (fmt, bits))
+            check_pq(got, O.prune_quantize_pairs48(raw, dtype, O.QSpec(fmt, bits)),
+                     f"4:8 {fmt}{bits} {kind}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [32, 64, 1024, 4096, 4160])
+def test_prune_quantize_pairs48_fp4(dtype, k):
+    for kind in ("normal", "ties"):
+        raw = inputs(k + 31, 27, k, dtype, kind)
+        x = to_dev(raw, dtype)
+        fmts = ["nvfp4"] + (["mxfp4"] if k % 64 == 0 else [])
+        for fmt in fmts:
+            got = S.prune_quantize_pairs48(x, fmt)
+            check_pq(got, O.prune_quantize_pairs48(raw, dtype, O.QSpec(fmt)), f"4:8 {fmt} {kind}")
+
+
+def test_prune_quantize_pairs48_kept_max_below_row_max():
+    # rows where a dropped pair holds the row's largest element: the INT/FP8
+    # row scale and the NVFP4 tensor maximum come from the kept values
+    rng = np.random.default_rng(77)
+    k = 256
+    x = rng.standard_normal((16, k)).astype(np.float32)
+    g = x.reshape(16, k // 8, 4, 2)
+    g[:, :, 0, :] = [5.0, 0.0]
+    g[:, :, 1:3, :] = 4.0
+    g[:, :, 3, :] = 0.0
+    for fmt, bits in (("int", 4), ("fp8", 0), ("nvfp4", 0)):
+        got = S.prune_quantize_pairs48(to_dev(x, "f32"), (fmt, bits))
+        want = O.prune_quantize_pairs48(x, "f32", O.QSpec(fmt, bits))
+        check_pq(got, want, f"kept max {fmt}")
+
+
+def test_prune_quantize_nv_given_tensor_amax():
+    raw = inputs(90, 33, 512, "bf16", "normal")
+    x = to_dev(raw, "bf16")
+    T = np.float32(7.5)
+    t = torch.tensor([T], dtype=torch.float32, device="cuda")
+    for pq, opq in ((S.prune_quantize, O.prune_quantize),
+                    (S.prune_quantize_pairs48, O.prune_quantize_pairs48)):
+        got = pq(x, "nvfp4", tensor_amax=t)
+        check_pq(got, opq(raw, "bf16", O.QSpec("nvfp4", tensor_amax=float(T))), "given T")
+
+
+def test_prune_quantize_pairs48_transposed():
+    rng = np.random.default_rng(5)
+    shape = (2, 256, 40)
+    raw = random_raw(rng, shape, "bf16")
+    x = to_dev(raw, "bf16")
+    rows = np.ascontiguousarray(np.swapaxes(raw, 1, 2)).reshape(-1, shape[1])
+    for q in (("fp8", 0), ("nvfp4", 0)):
+        got = S.prune_quantize_pairs48(x, q, axis=1)
+        want = O.prune_quantize_pairs48(rows, "bf16", O.QSpec(*q))
+        flat = [g.reshape(rows.shape[0], -1) if g.numel() > 1 else g for g in got]
+        if q[0] == "fp8":
+            flat[2] = got[2].reshape(-1)
+        check_pq(flat, want, f"transposed {q[0]}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k", [64, 1024, 4096])
+def test_predict_R_block_kept(dtype, k):
+    raw = inputs(k + 41, 37, k, dtype, "normal")
+    x = to_dev(raw, dtype)
+    kept = ["nvfp4", "mxfp4", "nvfp4", "fp8"]
+    dense = ["nvfp4", "mxfp4", ("int", 4), "nvfp4"]
+    okept = [qs_oracle(q) for q in kept]
+    odense = [qs_oracle(q) for q in dense]
+    got = S.predict_R(x, kept, dense, rows_per_block=8)
+    rel_close(raw_np(got), O.predict_R(raw, dtype, okept, odense, rows_per_block=8))
+    got = S.predict_R_pairs48(x, kept, dense, rows_per_block=8)
+    rel_close(raw_np(got), O.predict_R(raw, dtype, okept, odense, rows_per_block=8,
+                                       pattern="pairs4:8"))
+
+
+def test_predict_R_block_kept_wanda():
+    rng = np.random.default_rng(12)
+    k = 512
+    raw = inputs(13, 40, k, "bf16", "normal")
+    norm = (rng.random(k) * 2).astype(np.float32)
+    x = to_dev(raw, "bf16")
+    n = torch.from_numpy(norm).cuda()
+    got = S.predict_R(x, ["nvfp4", "mxfp4"], ["nvfp4", "fp8"], score="wanda", col_norm=n)
+    want = O.predict_R(raw, "bf16", [O.QSpec("nvfp4"), O.QSpec("mxfp4")],
+                       [O.QSpec("nvfp4"), O.QSpec("fp8")], "wanda", norm)
+    rel_close(raw_np(got), want)
