@@ -237,6 +237,23 @@ __device__ inline void sink_init(double* lacc, int ncols) {
   __syncthreads();
 }
 
+// Empty asm that claims to modify the packed magnitudes: values derived from
+// them (unpacked floats) are then rebuilt inside each quantizer loop instead
+// of being hoisted out of it, which would hold 8 floats per unit in
+// registers for the whole row.
+#ifndef SPARQ24_E_PIN
+#define SPARQ24_E_PIN 1
+#endif
+template <int UPL>
+__device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
+#if SPARQ24_E_PIN
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) asm volatile("" : "+v"(pk[j][h]));
+#endif
+}
+
 template <int TEAM, int UPL>
 SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
@@ -262,7 +279,6 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
   for_each_row_pipelined<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
     uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept g0, kept g1, dropped g0, dropped g1
-    uint32_t umax[UPL];    // unit maximum as a key (|x| in the high half)
     uint32_t am = 0;
     double kept2 = 0.0, drop = 0.0;
 #pragma unroll
@@ -270,8 +286,8 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
       uint32_t t0, t1;
       sel16_mags_packed(u[j].w[0], u[j].w[1], pk[j][0], pk[j][2], t0);
       sel16_mags_packed(u[j].w[2], u[j].w[3], pk[j][1], pk[j][3], t1);
-      umax[j] = t0 > t1 ? t0 : t1;
-      am = am > umax[j] ? am : umax[j];
+      const uint32_t um = t0 > t1 ? t0 : t1;
+      am = am > um ? am : um;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const double k0 = (double)mag_lo(pk[j][h]), k1 = (double)mag_hi(pk[j][h]);
@@ -291,6 +307,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
     }
     const float amax = __uint_as_float(am & 0xFFFF0000u);  // kept max == row max
     for (int q = 0; q < p.kept.n; ++q) {
+      pin_packed<UPL>(pk);
       const int fmt = p.kept.fmt[q];
       const float qmax = p.kept.qmax[q];
       double acc = 0.0;
@@ -314,6 +331,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
       if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
     }
     for (int q = 0; q < p.dense.n; ++q) {
+      pin_packed<UPL>(pk);
       const int fmt = p.dense.fmt[q];
       const float qmax = p.dense.qmax[q];
       double acc = 0.0;
@@ -329,7 +347,10 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
       } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
-          uint32_t bm = umax[j] & 0xFFFF0000u;  // fp32 bits of the unit's |x| max
+          // the unit's |x| max is its kept max (each group keeps its largest)
+          const uint32_t km2 = pk_max_u16(pk[j][0], pk[j][1]);
+          const uint32_t kh = km2 >> 16, kl = km2 & 0xFFFFu;
+          uint32_t bm = (kh > kl ? kh : kl) << 16;  // fp32 bits of the unit's |x| max
           uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
           bm = bm > w ? bm : w;
           float e[8];
@@ -618,12 +639,26 @@ __global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restri
     const double* colp[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) colp[c] = rowpart + (int64_t)((cb + c) < f.ncols ? cb + c : f.ncols - 1) * nrows;
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += kBlock) {
-      double v[CB];
+    // RU rows per thread per round, all loads issued before the adds; rows
+    // past the end add +0.0 (partials are sums of squares, never -0.0), so
+    // the order of additions per thread is rows t, t + kBlock, ... as ever
+    constexpr int RU = 4;
+    for (int64_t rb = r0 + threadIdx.x; rb < r1; rb += RU * kBlock) {
+      double v[RU][CB];
 #pragma unroll
-      for (int c = 0; c < CB; ++c) v[c] = colp[c][r];
+      for (int u = 0; u < RU; ++u) {
+        const int64_t r = rb + u * kBlock;
+        const int64_t rc = r < r1 ? r : r0;
 #pragma unroll
-      for (int c = 0; c < CB; ++c) a[c] += v[c];
+        for (int c = 0; c < CB; ++c) v[u][c] = colp[c][rc];
+        if (r >= r1)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) v[u][c] = 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) a[c] += v[u][c];
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] = a[c];

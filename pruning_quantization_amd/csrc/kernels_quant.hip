@@ -373,17 +373,20 @@ __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
     const int64_t b = row / R, r = row % R;
     const char* xr = x + b * bs + r * rs;
     for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+      Unit<DT> u[UPL];  // all loads of the chunk in flight before any use
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
         const int64_t i = c0 + j * TEAM + t;
-        if (i < nunits) {
-          Unit<DT> u;
-          load_unit(u, xr + i * (8 * DT::ESIZE));
-          Kept<DT> kp;
-          select_any<DT, PAT, WANDA>(u, norm, i, nunits, kp);
-          const uint32_t a = __float_as_uint(DT::to_f32(kept_absmax(kp)));
-          am = am > a ? am : a;
-        }
+        if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+        else zero_unit(u[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const int64_t i = c0 + j * TEAM + t;
+        Kept<DT> kp;
+        select_any<DT, PAT, WANDA>(u[j], norm, i, nunits, kp);  // zero units keep zeros
+        const uint32_t a = __float_as_uint(DT::to_f32(kept_absmax(kp)));
+        am = am > a ? am : a;
       }
     }
   }
