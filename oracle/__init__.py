@@ -37,6 +37,10 @@ from .reference import (  # noqa: F401
     select_pairs48,
     prune_compress_pairs48,
     decompress_pairs48,
+    hadamard_matrix,
+    hadamard_scale,
+    rotate,
+    rotation_exact,
     E4M3_GRID, E2M1_GRID,
     e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
     int_rtn_codes,

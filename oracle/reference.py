@@ -235,6 +235,80 @@ def decompress_pairs48(values: np.ndarray, meta: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Hadamard rotation along K ([PD §4]: before low-bit quantization the tensor
+# is multiplied by a rescaled +-1 orthogonal Hadamard matrix, which spreads
+# outliers over many elements)
+# ---------------------------------------------------------------------------
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1:
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_scale(n: int) -> float:
+    """fp64 1/sqrt(n) for n = 2^k: 2^-(k/2) for even k, and for odd k
+    2^-((k-1)/2) times the correctly rounded sqrt(1/2)."""
+    k = n.bit_length() - 1
+    c = 1.0 if k % 2 == 0 else math.sqrt(0.5)
+    return math.ldexp(c, -(k // 2))
+
+
+def _f32_to_bf16_bits(y32: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even of finite fp32 values to bf16 bit patterns."""
+    u = np.asarray(y32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def rotate(raw: np.ndarray, dtype: str, n: int) -> np.ndarray:
+    """Block Hadamard rotation along K: every aligned block b of n elements
+    becomes y = H_n x_b / sqrt(n), returned in the input's storage type.
+
+    The sums S = H_n x_b are formed in fp64 (a matrix product; exact whenever
+    :func:`rotation_exact` holds, so the summation order does not matter), a
+    zero sum is taken as +0, then fp64(S * hadamard_scale(n)) is rounded to
+    fp32 and, for 16-bit storage, from fp32 to the storage type (each step
+    round-to-nearest-even).  Applying it twice gives back the input up to
+    those roundings (H_n H_n = n I)."""
+    rows, k = raw.shape
+    if k % n:
+        raise ValueError("K must be a multiple of the block size")
+    x = decode_input(raw, dtype).reshape(rows * (k // n), n)
+    S = x @ hadamard_matrix(n).T + 0.0
+    y32 = (S * hadamard_scale(n)).astype(np.float32).reshape(rows, k)
+    if dtype == BF16:
+        return _f32_to_bf16_bits(y32)
+    if dtype == F16:
+        return y32.astype(np.float16)
+    return y32
+
+
+def rotation_exact(raw: np.ndarray, dtype: str, n: int) -> np.ndarray:
+    """Per block: True when every partial sum of any +-1 combination of the
+    block's values is exact in fp64, so that every summation order gives the
+    exact S of :func:`rotate`.  All values are multiples of 2^L (L the lowest
+    set bit over the block) and every partial sum is below n * 2^E (|x| <
+    2^E), so E + log2(n) - L <= 53 bits suffice."""
+    rows, k = raw.shape
+    x = np.abs(decode_input(raw, dtype).reshape(rows * (k // n), n))
+    f, e = np.frexp(x)                                   # x = f * 2^e, 0.5 <= f < 1
+    m = (f * 2.0 ** 53).astype(np.int64)                 # exact: <= 53 significant bits
+    lsb = np.where(m > 0, m & -m, 1).astype(np.float64)  # lowest set bit (1 for zeros)
+    low = np.where(m > 0, e - 53 + np.log2(lsb).astype(np.int64), 10 ** 6)
+    hi = np.where(m > 0, e, -10 ** 6).max(axis=1)
+    lo = low.min(axis=1)
+    need = np.where((m > 0).any(axis=1), hi + int(math.log2(n)) - lo, 0)
+    return (need <= 53).reshape(rows, k // n)
+
+
+# ---------------------------------------------------------------------------
 # Element encoders ([PD §3]: FP8, MXFP4 and NVFP4 as the dense rivals; a
 # reading fixes OCP e4m3 and E2M1 with round-to-nearest-even, saturating)
 # ---------------------------------------------------------------------------

@@ -602,3 +602,90 @@ def test_sparse_bits_accounting():
         O.bits_per_element(O.QSpec("int", 8), sparse24=True) == 5.0
     n = 1 << 20
     assert O.bits_per_element(O.QSpec("nvfp4"), pattern="pairs4:8", tensor_elems=n) == 2.75 + 32 / n
+
+
+# ---------------------------------------------------------------------------
+# Hadamard rotation ([PD §4]: rescaled +-1 orthogonal matrix, spreads outliers;
+# rotation roughly doubles R for linear-layer inputs)
+# ---------------------------------------------------------------------------
+
+
+def test_hadamard_matrix_is_sylvester_and_orthogonal():
+    for n in (1, 2, 8, 64, 512):
+        h = O.hadamard_matrix(n)
+        i = np.arange(n)
+        pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+        assert np.array_equal(h, (-1.0) ** pc)
+        assert np.array_equal(h @ h.T, n * np.eye(n))
+    for k in range(0, 13):
+        n = 1 << k
+        c = O.hadamard_scale(n)
+        assert abs(c * c * n - 1.0) <= 4e-16
+        if k % 2 == 0:
+            assert c == 2.0 ** (-k // 2)
+
+
+def test_hadamard8_hand_example():
+    ex = HAND["hadamard8"]
+    raw = bf16(ex["rows"])
+    y = O.rotate(raw, O.BF16, ex["n"])
+    want = np.stack([hexs(r).astype(np.uint16) if False else
+                     np.array([int(h, 16) for h in r], dtype=np.uint16) for r in ex["rotated_bf16"]])
+    assert np.array_equal(y, want)
+
+
+def test_rotation_one_hot_columns():
+    # e_j rotates to column j of H scaled by 1/sqrt(n); n = 64 has an exact scale 1/8
+    n = 64
+    x = np.eye(n, dtype=np.float32)
+    y = O.rotate(x, O.F32, n).astype(np.float64)
+    assert np.array_equal(y, O.hadamard_matrix(n).T / 8.0)
+
+
+def test_rotation_involution_and_energy():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((16, 512)).astype(np.float32)
+    for n in (8, 128, 512):
+        y = O.rotate(x, O.F32, n)
+        z = O.rotate(y, O.F32, n)
+        assert np.allclose(z, x, rtol=0, atol=1e-5)
+        e0 = (x.astype(np.float64) ** 2).sum(axis=1)
+        e1 = (y.astype(np.float64) ** 2).sum(axis=1)
+        assert np.allclose(e1, e0, rtol=2e-6)
+    raw = W.to_bf16_bits(x)
+    yb = O.decode_input(O.rotate(raw, O.BF16, 128), O.BF16)
+    xb = O.decode_input(raw, O.BF16)
+    assert np.allclose((yb ** 2).sum(axis=1), (xb ** 2).sum(axis=1), rtol=1e-2)
+
+
+def test_rotation_exactness_predicate():
+    raw = W.activation_x(3, 64, 1024)
+    assert O.rotation_exact(raw, O.BF16, 128).all()
+    x = np.zeros((1, 8), dtype=np.float32)
+    x[0, 0], x[0, 1] = 2.0 ** 40, 1.0 + 2.0 ** -23
+    assert not O.rotation_exact(x, O.F32, 8).all()
+    x[0, 1] = 1.0
+    assert O.rotation_exact(x, O.F32, 8).all()
+
+
+def test_rotation_flattens_outliers_and_raises_R():
+    # [PD §4]: rotation spreads the outlier channels, so 2:4 drops more energy
+    # while the dense quantizer's range narrows; R roughly doubles for X
+    raw = W.activation_x(0, 256, 4096)
+    rot = O.rotate(raw, O.BF16, 128)
+    assert O.rotation_exact(raw, O.BF16, 128).all()
+    ks, ds = [O.QSpec("fp8"), O.QSpec("fp8")], [O.QSpec("fp8"), O.QSpec("int", 8)]
+    r0 = O.predict_R(raw, O.BF16, ks, ds)[0]
+    r1 = O.predict_R(rot, O.BF16, ks, ds)[0]
+    assert r1[0, 0] > 2 * r0[0, 0]               # energy loss grows (outliers were always kept)
+    assert r1[1, 3] < r0[1, 3]                   # dense INT8 error shrinks
+    for p in range(2):
+        assert r1[p, 4] > 1.3 * r0[p, 4]         # R grows
+
+
+def test_rotation_leaves_gaussian_loss_unchanged():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((256, 1024)).astype(np.float32)
+    y = O.rotate(x, O.F32, 128)
+    e = O.error_energy(y, O.F32, O.QSpec("none"), O.QSpec("int", 8))[0]
+    assert 0.1309 <= e[1] / e[0] <= 0.1339         # still the Gaussian 13.2% [PD §4]
