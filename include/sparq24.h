@@ -230,6 +230,51 @@ sparq24_status sparq24_predict_R_pairs48(const sparq24_tensor* x, const sparq24_
                                          int64_t rows_per_block, double* out, void* ws,
                                          size_t* ws_bytes, hipStream_t stream);
 
+/* Sparsity pattern selector of the rotated calls below. */
+typedef enum { SPARQ24_PATTERN_24 = 0, SPARQ24_PATTERN_PAIRS48 = 1 } sparq24_pattern;
+
+/* Block Hadamard rotation along K [PD §4: before low-bit quantization the
+ * operand is multiplied by a rescaled +-1 orthogonal Hadamard matrix, which
+ * spreads outliers over many elements].  Every aligned block of `block`
+ * elements (a power of two, 8..512, dividing K) becomes y = H x / sqrt(block)
+ * with H the Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)).
+ * Precision: the sums S = H x are fp64 butterflies, exact (so independent of
+ * their order) whenever a block's values span at most 53 - log2(block) bits
+ * from the largest magnitude's leading bit to the lowest set bit of any
+ * element; a zero sum is +0; fp64(S * c), c the fp64 1/sqrt(block), is
+ * rounded to fp32 and then to the storage type (round-to-nearest-even).
+ * out [B][R][K] in x's storage type, K-contiguous.  Workspace: a transposed
+ * operand's staging copy, else none.  Errors: block not a power of two in
+ * range -> INVALID; K % block -> SHAPE. */
+sparq24_status sparq24_hadamard(const sparq24_tensor* x, int32_t block, void* out, void* ws,
+                                size_t* ws_bytes, hipStream_t stream);
+
+/* sparq24_quantize of the rotated operand, the rotation fused into the load
+ * (one read of x): identical outputs to sparq24_hadamard followed by
+ * sparq24_quantize.  block as sparq24_hadamard (0 is INVALID). */
+sparq24_status sparq24_quantize_rot(const sparq24_tensor* x, int32_t block,
+                                    const sparq24_qspec* q, void* codes, void* scales,
+                                    float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                    hipStream_t stream);
+
+/* Magnitude prune (pattern 2:4 or pairwise 4:8) + quantization of the kept
+ * values of the rotated operand, fused: identical outputs to sparq24_hadamard
+ * followed by sparq24_prune_quantize (2:4, magnitude) or
+ * sparq24_prune_quantize_pairs48. */
+sparq24_status sparq24_prune_quantize_rot(const sparq24_tensor* x, int32_t block, int32_t pattern,
+                                          const sparq24_qspec* q, void* codes, uint8_t* meta,
+                                          void* scales, float* tensor_scale_out, void* ws,
+                                          size_t* ws_bytes, hipStream_t stream);
+
+/* Predicted R of the rotated operand [PD §4: rotation roughly doubles R for
+ * Q, K and linear-layer inputs], magnitude selection with the given pattern:
+ * identical outputs to sparq24_hadamard followed by sparq24_predict_R (2:4)
+ * or sparq24_predict_R_pairs48, up to the energy tolerance. */
+sparq24_status sparq24_predict_R_rot(const sparq24_tensor* x, int32_t block, int32_t pattern,
+                                     const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
+                                     int32_t npairs, int64_t rows_per_block, double* out,
+                                     void* ws, size_t* ws_bytes, hipStream_t stream);
+
 /* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
  * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in
  * fp64, then rounded once.  x is an activation [tokens, channels] given with

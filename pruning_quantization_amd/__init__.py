@@ -13,14 +13,18 @@ from .binding import (  # noqa: F401
     copy,
     describe,
     error_energy,
+    hadamard,
     lib,
     predict_R,
     prune_compress,
     prune_compress_pairs48,
     predict_R_pairs48,
+    predict_R_rot,
     prune_quantize,
     prune_quantize_pairs48,
+    prune_quantize_rot,
     qspec,
     quantize,
+    quantize_rot,
     version,
 )

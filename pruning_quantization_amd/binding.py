@@ -49,7 +49,8 @@ class CQSpec(ctypes.Structure):
 SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize",
            "sparq24_error_energy", "sparq24_predict_R", "sparq24_col_l2norm", "sparq24_copy",
            "sparq24_prune_compress_pairs48", "sparq24_prune_quantize_pairs48",
-           "sparq24_predict_R_pairs48",
+           "sparq24_predict_R_pairs48", "sparq24_hadamard", "sparq24_quantize_rot",
+           "sparq24_prune_quantize_rot", "sparq24_predict_R_rot",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -81,6 +82,13 @@ def lib(path: Optional[str] = None):
         "sparq24_prune_compress_pairs48": [T, c_void_p, c_void_p, c_void_p],
         "sparq24_predict_R_pairs48": [T, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
                                       POINTER(c_size_t), c_void_p],
+        "sparq24_hadamard": [T, c_int32, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
+        "sparq24_quantize_rot": [T, c_int32, Q, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 POINTER(c_size_t), c_void_p],
+        "sparq24_prune_quantize_rot": [T, c_int32, c_int32, Q, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
+        "sparq24_predict_R_rot": [T, c_int32, c_int32, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
+                                  POINTER(c_size_t), c_void_p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -293,15 +301,9 @@ def prune_quantize_pairs48(x: torch.Tensor, q: QLike, axis: int = -1,
                            workspace)
 
 
-def quantize(x: torch.Tensor, q: QLike, axis: int = -1,
-             tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
-    """Dense quantization.  INT/FP8 -> (codes [..., K], scales fp32 [...]);
-    MXFP4 -> (codes [..., K/2], e8m0 [..., K/32]); NVFP4 -> (codes [..., K/2],
-    e4m3 block scales [..., K/16], tensor scale fp32 [1])."""
-    c, lead = describe(x, axis)
-    qs = qspec(q, tensor_amax)
+def _quantize(name, head, x, lead, c, qs, out, workspace):
     k = int(c.k)
-    L = lib()
+    fn = getattr(lib(), name)
     s = _stream(x)
     if out is None:
         if qs.fmt in (Q_INT, Q_FP8):
@@ -317,16 +319,67 @@ def quantize(x: torch.Tensor, q: QLike, axis: int = -1,
     else:
         codes, scales, ts = out
     if workspace is None:
-        ws, n = _workspace(x, lambda w, nb: L.sparq24_quantize(
-            ctypes.byref(c), ctypes.byref(qs), None, None, None, w, nb, s))
+        ws, n = _workspace(x, lambda w, nb: fn(ctypes.byref(c), *head, ctypes.byref(qs), None, None,
+                                               None, w, nb, s))
     else:
         ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
-    st = L.sparq24_quantize(ctypes.byref(c), ctypes.byref(qs), codes.data_ptr(), scales.data_ptr(),
-                            ts.data_ptr(), _ptr(ws), _wsarg(n), s)
-    _check("sparq24_quantize", st)
+    st = fn(ctypes.byref(c), *head, ctypes.byref(qs), codes.data_ptr(), scales.data_ptr(),
+            ts.data_ptr(), _ptr(ws), _wsarg(n), s)
+    _check(name, st)
     if qs.fmt == Q_NVFP4:
         return codes, scales, ts
     return codes, scales
+
+
+_PATTERNS = {"2:4": 0, "pairs4:8": 1}
+
+
+def prune_quantize_rot(x: torch.Tensor, block: int, q: QLike, pattern: str = "2:4", axis: int = -1,
+                       tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
+    """Magnitude prune (2:4 or pairwise 4:8) + quantization of the kept values
+    of the block-Hadamard-rotated operand (rotation fused).  Outputs as
+    :func:`prune_quantize` / :func:`prune_quantize_pairs48`."""
+    c, lead = describe(x, axis)
+    qs = qspec(q, tensor_amax)
+    return _prune_quantize("sparq24_prune_quantize_rot", (int(block), _PATTERNS[pattern]), x, lead,
+                           c, qs, 8 if pattern == "2:4" else 16, out, workspace)
+
+
+def hadamard(x: torch.Tensor, block: int, axis: int = -1, out: Optional[torch.Tensor] = None,
+             workspace=None):
+    """Block Hadamard rotation along ``axis`` -> [..., K] in x.dtype (the
+    rotated axis last)."""
+    c, lead = describe(x, axis)
+    k = int(c.k)
+    L = lib()
+    s = _stream(x)
+    if out is None:
+        out = torch.empty(*lead, k, dtype=x.dtype, device=x.device)
+    if workspace is None:
+        ws, n = _workspace(x, lambda w, nb: L.sparq24_hadamard(ctypes.byref(c), int(block), None, w,
+                                                               nb, s))
+    else:
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_hadamard(ctypes.byref(c), int(block), out.data_ptr(), _ptr(ws), _wsarg(n), s)
+    _check("sparq24_hadamard", st)
+    return out
+
+
+def quantize(x: torch.Tensor, q: QLike, axis: int = -1,
+             tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
+    """Dense quantization.  INT/FP8 -> (codes [..., K], scales fp32 [...]);
+    MXFP4 -> (codes [..., K/2], e8m0 [..., K/32]); NVFP4 -> (codes [..., K/2],
+    e4m3 block scales [..., K/16], tensor scale fp32 [1])."""
+    c, lead = describe(x, axis)
+    return _quantize("sparq24_quantize", (), x, lead, c, qspec(q, tensor_amax), out, workspace)
+
+
+def quantize_rot(x: torch.Tensor, block: int, q: QLike, axis: int = -1,
+                 tensor_amax: Optional[torch.Tensor] = None, out=None, workspace=None):
+    """:func:`quantize` of the block-Hadamard-rotated operand (rotation fused)."""
+    c, lead = describe(x, axis)
+    return _quantize("sparq24_quantize_rot", (int(block),), x, lead, c, qspec(q, tensor_amax),
+                     out, workspace)
 
 
 def _qarray(qs: Sequence[QLike]):
@@ -433,6 +486,35 @@ def predict_R_pairs48(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QL
     st = L.sparq24_predict_R_pairs48(ctypes.byref(c), ka, da, npairs, rows_per_block,
                                      out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_predict_R_pairs48", st)
+    return out
+
+
+def predict_R_rot(x: torch.Tensor, block: int, kept: Sequence[QLike], dense: Sequence[QLike],
+                  pattern: str = "2:4", axis: int = -1, rows_per_block: int = 0,
+                  out: Optional[torch.Tensor] = None, workspace=None):
+    """Predicted R of the block-Hadamard-rotated operand (rotation fused) ->
+    fp64 [nblk, npairs, 5]."""
+    if len(kept) != len(dense):
+        raise ValueError("kept and dense must pair up")
+    c, _ = describe(x, axis)
+    ka, da = _qarray(kept), _qarray(dense)
+    L = lib()
+    s = _stream(x)
+    nrows = int(c.batch) * int(c.rows)
+    rpb = rows_per_block or nrows
+    nblk = (nrows + rpb - 1) // rpb
+    npairs = len(kept)
+    pat = _PATTERNS[pattern]
+    if out is None:
+        out = torch.empty(nblk, npairs, 5, dtype=torch.float64, device=x.device)
+    if workspace is None:
+        ws, n = _workspace(x, lambda w, nb: L.sparq24_predict_R_rot(
+            ctypes.byref(c), int(block), pat, ka, da, npairs, rows_per_block, None, w, nb, s))
+    else:
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_predict_R_rot(ctypes.byref(c), int(block), pat, ka, da, npairs, rows_per_block,
+                                 out.data_ptr(), _ptr(ws), _wsarg(n), s)
+    _check("sparq24_predict_R_rot", st)
     return out
 
 

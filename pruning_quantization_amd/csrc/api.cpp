@@ -32,6 +32,8 @@ sparq24_status check_tensor(const sparq24_tensor* x, bool allow_transposed, RowD
   const int es = esize(x->dtype);
   d.x = (const char*)x->data;
   d.dtype = x->dtype;
+  d.rot.n = 0;
+  d.rot.c = 0.0;
   d.B = x->batch;
   d.R = x->rows;
   d.K = x->k;
@@ -84,6 +86,19 @@ sparq24_status check_score(int32_t score, const float* col_norm) {
     if (!col_norm) return SPARQ24_ERR_INVALID;
     if (!aligned16(col_norm)) return SPARQ24_ERR_ALIGN;
   }
+  return SPARQ24_OK;
+}
+
+// Hadamard block size: a power of two in 8..512 dividing K; fills d.rot with
+// c = fp64 1/sqrt(n) (an exact power of two for even log2 n, else that power
+// times the correctly rounded sqrt(1/2)).
+sparq24_status check_rot(int32_t block, RowDesc& d) {
+  if (block < 8 || block > 512 || (block & (block - 1))) return SPARQ24_ERR_INVALID;
+  if (d.K % block) return SPARQ24_ERR_SHAPE;
+  int k = 0;
+  while ((1 << k) < block) ++k;
+  d.rot.n = block;
+  d.rot.c = ldexp((k & 1) ? sqrt(0.5) : 1.0, -(k / 2));
   return SPARQ24_OK;
 }
 
@@ -316,11 +331,17 @@ sparq24_status sparq24_prune_compress(const sparq24_tensor* x, int32_t score, co
   return launched(launch_prune_compress(d, score == SPARQ24_SCORE_WANDA, col_norm, values, meta, stream));
 }
 
-sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q, void* codes,
-                                void* scales, float* tensor_scale_out, void* ws, size_t* ws_bytes,
-                                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared bodies of the calls; rot_block != 0 rotates the operand on load.
+sparq24_status quantize_any(const sparq24_tensor* x, int32_t rot_block, const sparq24_qspec* q,
+                            void* codes, void* scales, float* tensor_scale_out, void* ws,
+                            size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;
   CHECK(check_tensor(x, true, d));
+  if (rot_block) CHECK(check_rot(rot_block, d));
   int cfmt;
   float qmax;
   CHECK(check_q(q, (1u << SPARQ24_Q_INT) | (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
@@ -357,16 +378,14 @@ sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q,
   return launched(launch_quant_rows(d, cfmt, qmax, codes, (float*)scales, stream));
 }
 
-}  // extern "C"
-
-namespace {
-
-sparq24_status prune_quantize_any(const sparq24_tensor* x, int pat, int32_t score,
-                                  const float* col_norm, const sparq24_qspec* q, void* codes,
-                                  uint8_t* meta, void* scales, float* tensor_scale_out, void* ws,
-                                  size_t* ws_bytes, hipStream_t stream) {
+sparq24_status prune_quantize_any(const sparq24_tensor* x, int32_t rot_block, int pat,
+                                  int32_t score, const float* col_norm, const sparq24_qspec* q,
+                                  void* codes, uint8_t* meta, void* scales,
+                                  float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                  hipStream_t stream) {
   RowDesc d;
   CHECK(check_tensor(x, true, d));
+  if (rot_block) CHECK(check_rot(rot_block, d));
   CHECK(check_score(score, col_norm));
   int cfmt;
   float qmax;
@@ -407,71 +426,79 @@ sparq24_status prune_quantize_any(const sparq24_tensor* x, int pat, int32_t scor
                                         (float*)scales, stream));
 }
 
+// mode 0: error_energy (one pair, raw sums); 1: predict_R
+sparq24_status energy_any(const sparq24_tensor* x, int32_t rot_block, int pat, int32_t score,
+                          const float* col_norm, const sparq24_qspec* kept_q,
+                          const sparq24_qspec* dense_q, int32_t npairs, int64_t rows_per_block,
+                          int mode, double* out, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  CHECK(check_tensor(x, true, d));
+  if (rot_block) CHECK(check_rot(rot_block, d));
+  CHECK(check_score(score, col_norm));
+  if (pat == PAT_48 && score != SPARQ24_SCORE_MAGNITUDE) return SPARQ24_ERR_UNSUPPORTED;
+  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
+  if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
+  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
+  if (pat == PAT_48 && d.K % 16) return SPARQ24_ERR_SHAPE;
+  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  EnergyPlan pl;
+  CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
+  pl.p.pairs48 = pat == PAT_48 ? 1 : 0;
+  pl.f.mode = mode;
+  bool query;
+  CHECK(workspace(ws, ws_bytes, pl.need, query));
+  if (query) return SPARQ24_OK;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return run_energy(d, score, col_norm, pl, out, ws, stream);
+}
+
+int32_t pattern_code(int32_t pattern) {
+  return pattern == SPARQ24_PATTERN_24 ? PAT_24 : (pattern == SPARQ24_PATTERN_PAIRS48 ? PAT_48 : -1);
+}
+
 }  // namespace
 
 extern "C" {
+
+sparq24_status sparq24_quantize(const sparq24_tensor* x, const sparq24_qspec* q, void* codes,
+                                void* scales, float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                hipStream_t stream) {
+  return quantize_any(x, 0, q, codes, scales, tensor_scale_out, ws, ws_bytes, stream);
+}
 
 sparq24_status sparq24_prune_quantize(const sparq24_tensor* x, int32_t score, const float* col_norm,
                                       const sparq24_qspec* q, void* codes, uint8_t* meta,
                                       void* scales, float* tensor_scale_out, void* ws,
                                       size_t* ws_bytes, hipStream_t stream) {
-  return prune_quantize_any(x, PAT_24, score, col_norm, q, codes, meta, scales, tensor_scale_out,
-                            ws, ws_bytes, stream);
+  return prune_quantize_any(x, 0, PAT_24, score, col_norm, q, codes, meta, scales,
+                            tensor_scale_out, ws, ws_bytes, stream);
 }
 
 sparq24_status sparq24_prune_quantize_pairs48(const sparq24_tensor* x, const sparq24_qspec* q,
                                               void* codes, uint8_t* meta, void* scales,
                                               float* tensor_scale_out, void* ws,
                                               size_t* ws_bytes, hipStream_t stream) {
-  return prune_quantize_any(x, PAT_48, SPARQ24_SCORE_MAGNITUDE, nullptr, q, codes, meta, scales,
-                            tensor_scale_out, ws, ws_bytes, stream);
+  return prune_quantize_any(x, 0, PAT_48, SPARQ24_SCORE_MAGNITUDE, nullptr, q, codes, meta,
+                            scales, tensor_scale_out, ws, ws_bytes, stream);
 }
 
 sparq24_status sparq24_error_energy(const sparq24_tensor* x, int32_t score, const float* col_norm,
                                     const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
                                     int64_t rows_per_block, double* out, void* ws,
                                     size_t* ws_bytes, hipStream_t stream) {
-  RowDesc d;
-  CHECK(check_tensor(x, true, d));
-  CHECK(check_score(score, col_norm));
-  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
-  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
-  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
-  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
-  EnergyPlan pl;
-  CHECK(plan_energy(d, kept_q, dense_q, 1, rows_per_block, pl));
-  pl.f.mode = 0;
-  bool query;
-  CHECK(workspace(ws, ws_bytes, pl.need, query));
-  if (query) return SPARQ24_OK;
-  if (!out) return SPARQ24_ERR_INVALID;
-  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
-  CHECK(device_ok());
-  return run_energy(d, score, col_norm, pl, out, ws, stream);
+  return energy_any(x, 0, PAT_24, score, col_norm, kept_q, dense_q, 1, rows_per_block, 0, out, ws,
+                    ws_bytes, stream);
 }
 
 sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score, const float* col_norm,
                                  const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
                                  int32_t npairs, int64_t rows_per_block, double* out, void* ws,
                                  size_t* ws_bytes, hipStream_t stream) {
-  RowDesc d;
-  CHECK(check_tensor(x, true, d));
-  CHECK(check_score(score, col_norm));
-  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
-  if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
-  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
-  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
-  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
-  EnergyPlan pl;
-  CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
-  pl.f.mode = 1;
-  bool query;
-  CHECK(workspace(ws, ws_bytes, pl.need, query));
-  if (query) return SPARQ24_OK;
-  if (!out) return SPARQ24_ERR_INVALID;
-  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
-  CHECK(device_ok());
-  return run_energy(d, score, col_norm, pl, out, ws, stream);
+  return energy_any(x, 0, PAT_24, score, col_norm, kept_q, dense_q, npairs, rows_per_block, 1, out,
+                    ws, ws_bytes, stream);
 }
 
 sparq24_status sparq24_prune_compress_pairs48(const sparq24_tensor* x, void* values,
@@ -490,25 +517,56 @@ sparq24_status sparq24_predict_R_pairs48(const sparq24_tensor* x, const sparq24_
                                          const sparq24_qspec* dense_q, int32_t npairs,
                                          int64_t rows_per_block, double* out, void* ws,
                                          size_t* ws_bytes, hipStream_t stream) {
+  return energy_any(x, 0, PAT_48, SPARQ24_SCORE_MAGNITUDE, nullptr, kept_q, dense_q, npairs,
+                    rows_per_block, 1, out, ws, ws_bytes, stream);
+}
+
+sparq24_status sparq24_hadamard(const sparq24_tensor* x, int32_t block, void* out, void* ws,
+                                size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;
   CHECK(check_tensor(x, true, d));
-  if (!kept_q || !dense_q) return SPARQ24_ERR_INVALID;
-  if (npairs < 1 || npairs > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
-  if (rows_per_block < 0) return SPARQ24_ERR_INVALID;
-  if (d.K % 16) return SPARQ24_ERR_SHAPE;
-  if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
-  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
-  EnergyPlan pl;
-  CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
-  pl.p.pairs48 = 1;
-  pl.f.mode = 1;
+  CHECK(check_rot(block, d));
+  const size_t stage = staging_bytes(d);
   bool query;
-  CHECK(workspace(ws, ws_bytes, pl.need, query));
+  CHECK(workspace(ws, ws_bytes, stage, query));
   if (query) return SPARQ24_OK;
+  if (d.B * d.R * d.K == 0) return SPARQ24_OK;
   if (!out) return SPARQ24_ERR_INVALID;
   if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
   CHECK(device_ok());
-  return run_energy(d, SPARQ24_SCORE_MAGNITUDE, nullptr, pl, out, ws, stream);
+  if (stage) {
+    CHECK(launched(launch_transpose_rows(d, ws, stream)));
+    d = staged_view(d, ws);
+  }
+  return launched(launch_hadamard(d, out, stream));
+}
+
+sparq24_status sparq24_quantize_rot(const sparq24_tensor* x, int32_t block,
+                                    const sparq24_qspec* q, void* codes, void* scales,
+                                    float* tensor_scale_out, void* ws, size_t* ws_bytes,
+                                    hipStream_t stream) {
+  if (block == 0) return SPARQ24_ERR_INVALID;
+  return quantize_any(x, block, q, codes, scales, tensor_scale_out, ws, ws_bytes, stream);
+}
+
+sparq24_status sparq24_prune_quantize_rot(const sparq24_tensor* x, int32_t block, int32_t pattern,
+                                          const sparq24_qspec* q, void* codes, uint8_t* meta,
+                                          void* scales, float* tensor_scale_out, void* ws,
+                                          size_t* ws_bytes, hipStream_t stream) {
+  const int32_t pat = pattern_code(pattern);
+  if (block == 0 || pat < 0) return SPARQ24_ERR_INVALID;
+  return prune_quantize_any(x, block, pat, SPARQ24_SCORE_MAGNITUDE, nullptr, q, codes, meta,
+                            scales, tensor_scale_out, ws, ws_bytes, stream);
+}
+
+sparq24_status sparq24_predict_R_rot(const sparq24_tensor* x, int32_t block, int32_t pattern,
+                                     const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
+                                     int32_t npairs, int64_t rows_per_block, double* out,
+                                     void* ws, size_t* ws_bytes, hipStream_t stream) {
+  const int32_t pat = pattern_code(pattern);
+  if (block == 0 || pat < 0) return SPARQ24_ERR_INVALID;
+  return energy_any(x, block, pat, SPARQ24_SCORE_MAGNITUDE, nullptr, kept_q, dense_q, npairs,
+                    rows_per_block, 1, out, ws, ws_bytes, stream);
 }
 
 sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,

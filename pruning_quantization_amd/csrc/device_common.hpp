@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace sparq24 {
 
 constexpr int kBlock = 256;  // threads per workgroup for every row kernel
@@ -31,12 +33,14 @@ constexpr int kBlock = 256;  // threads per workgroup for every row kernel
 // Storage types.  W = dwords per 8-element unit.
 // ---------------------------------------------------------------------------
 struct BF16T {
+  static constexpr bool IS_BF16 = true;
   static constexpr int W = 4;
   static constexpr int ESIZE = 2;
   static constexpr uint32_t ABS = 0x7FFFu;
   __device__ static inline float to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 };
 struct F16T {
+  static constexpr bool IS_BF16 = false;
   static constexpr int W = 4;
   static constexpr int ESIZE = 2;
   static constexpr uint32_t ABS = 0x7FFFu;
@@ -45,6 +49,7 @@ struct F16T {
   }
 };
 struct F32T {
+  static constexpr bool IS_BF16 = false;
   static constexpr int W = 8;
   static constexpr int ESIZE = 4;
   static constexpr uint32_t ABS = 0x7FFFFFFFu;
@@ -514,9 +519,87 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 // SIMD.  The trip count is the same for every team, so team reductions that
 // synchronise a workgroup are reached by all of its threads.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Block Hadamard rotation along K [PD §4: before low-bit quantization the
+// operand is multiplied by a rescaled +-1 orthogonal Hadamard matrix].  Each
+// aligned block of n elements becomes y = H_n x / sqrt(n) (Sylvester order),
+// in the storage type: the sums S are fp64 butterflies (exact whenever the
+// block's values span at most 53 - log2(n) bits from the largest magnitude to
+// the lowest set bit, so the butterfly order does not matter), a zero sum is
+// +0, then fp64(S * c) is rounded to fp32 and to the storage type (RNE).
+// A block of n elements is n/8 units on adjacent lanes of one register j
+// (lane t owns units t, t + TEAM, ...; n <= 8 * TEAM), so the butterflies
+// run three stages inside a unit and log2(n/8) stages across lanes.
+// ---------------------------------------------------------------------------
+template <class DT>
+__device__ inline void unit_store_f32(Unit<DT>& u, const float* f) {
+  if constexpr (DT::ESIZE == 4) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u.w[e] = __float_as_uint(f[e]);
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (DT::IS_BF16) {
+        const uint32_t b = __float_as_uint(f[e]);
+        h[e] = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;  // RNE, finite values
+      } else {
+        h[e] = __builtin_bit_cast(uint16_t, (_Float16)f[e]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u.w[i] = h[2 * i] | (h[2 * i + 1] << 16);
+  }
+}
+
+template <int D>
+__device__ inline void had_xlane(double (&v)[8], int t) {
+  const bool upper = (t & D) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double p = __shfl_xor(v[e], D, 64);
+    v[e] = upper ? p - v[e] : v[e] + p;
+  }
+}
+
+template <class DT>
+__device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
+  double v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (double)u.f(e);
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!(e & d)) {
+        const double a = v[e], b = v[e | d];
+        v[e] = a + b;
+        v[e | d] = a - b;
+      }
+  if (nb > 1) had_xlane<1>(v, t);
+  if (nb > 2) had_xlane<2>(v, t);
+  if (nb > 4) had_xlane<4>(v, t);
+  if (nb > 8) had_xlane<8>(v, t);
+  if (nb > 16) had_xlane<16>(v, t);
+  if (nb > 32) had_xlane<32>(v, t);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)((v[e] + 0.0) * c);
+  unit_store_f32(u, f);
+}
+
+// Every lane of the wave must call this (zero units rotate to zeros).
+template <class DT, int UPL>
+__device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
+  if (r.n == 0) return;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) hadamard_unit(u[j], r.n >> 3, r.c, t);
+}
+
 struct RowGeom {
   const char* x;
   int64_t R, nrows, nunits, bs, rs;  // strides in bytes
+  Rot rot;                           // rotation on load (n == 0: none)
 };
 
 __device__ inline const char* row_ptr(const RowGeom& g, int64_t row) {
@@ -541,7 +624,7 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
 #define SPARQ24_PIPELINE 0
 #endif
 
-template <class DT, int TEAM, int UPL, class Body>
+template <class DT, int TEAM, int UPL, bool ROT = false, class Body>
 __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
   constexpr int TPB = kBlock / TEAM;
   const int t = threadIdx.x % TEAM;
@@ -553,6 +636,7 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
       Unit<DT> A[UPL];
       const int64_t ra = first + it * stride;
       load_row<DT, TEAM, UPL>(A, g, ra, t);
+      if constexpr (ROT) hadamard_units<DT, UPL>(A, g.rot, t);
       body(A, ra, t);
     }
     return;
@@ -563,9 +647,11 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
     const int64_t ra = first + it * stride;
     const int64_t rb = ra + stride;
     load_row<DT, TEAM, UPL>(B, g, rb, t);
+    if constexpr (ROT) hadamard_units<DT, UPL>(A, g.rot, t);
     body(A, ra, t);
     if (it + 1 < iters) {
       load_row<DT, TEAM, UPL>(A, g, rb + stride, t);
+      if constexpr (ROT) hadamard_units<DT, UPL>(B, g.rot, t);
       body(B, rb, t);
     }
   }

@@ -254,7 +254,7 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #endif
 }
 
-template <int TEAM, int UPL>
+template <int TEAM, int UPL, bool ROT>
 SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
@@ -276,7 +276,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
   }
   const int64_t nrows = g.nrows;
-  for_each_row_pipelined<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+  for_each_row_pipelined<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
     uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept g0, kept g1, dropped g0, dropped g1
     uint32_t am = 0;
@@ -394,7 +394,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
   sink_flush<TEAM>(sink, lacc, ncols);
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA>
+template <class DT, int TEAM, int UPL, bool WANDA, bool ROT>
 SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
                                                         EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
@@ -419,7 +419,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   }
   const int64_t nrows = g.nrows;
 
-  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
     uint32_t km[UPL];  // 8-bit kept mask per unit
     uint32_t mbs[UPL];
@@ -700,8 +700,9 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               const EnergyParams& p, double* rowpart, int64_t rows_per_block,
                               int64_t* nparts, hipStream_t s) {
   const int64_t nunits = d.K / 8;
-  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   const bool acc = rows_per_block >= g.nrows;  // one block: per-team partials
+  if (wanda && d.rot.n) return hipErrorInvalidValue;
   auto geom = [&](int, dim3 grid, PartialSink& k) {
     k.rowpart = rowpart;
     k.acc = acc;
@@ -713,7 +714,12 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
       geom(TEAM, grid, k);
-      hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL>), grid, dim3(kBlock), 0, s, g, p, k);
+      if (d.rot.n)
+        hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g, p,
+                           k);
+      else
+        hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
+                           p, k);
       return hipGetLastError();
     });
   }
@@ -722,12 +728,15 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
       geom(TEAM, grid, k);
-      if (wanda)
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g, norm,
-                           p, k);
-      else
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
+      if (wanda)  // rotated calls take no norms
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true, false>), grid, dim3(kBlock), 0, s, g,
                            norm, p, k);
+      else if (d.rot.n)
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, true>), grid, dim3(kBlock), 0, s, g,
+                           norm, p, k);
+      else
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, false>), grid, dim3(kBlock), 0, s,
+                           g, norm, p, k);
       return hipGetLastError();
     });
   });

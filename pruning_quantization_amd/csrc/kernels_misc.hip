@@ -140,4 +140,50 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Block Hadamard rotation of a K-contiguous operand into a dense copy
+// [PD §4]: load, rotate in registers (hadamard_units), store.
+// ---------------------------------------------------------------------------
+template <class DT, int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_hadamard(const char* __restrict__ x, int64_t R,
+                                                     int64_t nunits, int64_t bs, int64_t rs,
+                                                     Rot rot, char* __restrict__ out) {
+  const int t = threadIdx.x % TEAM;
+  const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
+  const int64_t b = blockIdx.y;
+  const bool active = r < R;
+  const char* xr = x + b * bs + (active ? r : 0) * rs;
+  char* orow = out + (b * R + r) * nunits * (8 * DT::ESIZE);
+  for (int64_t c0 = 0; c0 < nunits; c0 += TEAM * UPL) {
+    Unit<DT> u[UPL];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
+      else zero_unit(u[j]);
+    }
+    hadamard_units<DT, UPL>(u, rot, t);
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int64_t i = c0 + j * TEAM + t;
+      if (active && i < nunits) {
+        char* dst = orow + i * (8 * DT::ESIZE);
+        st4(dst, u[j].w[0], u[j].w[1], u[j].w[2], u[j].w[3]);
+        if constexpr (DT::W == 8) st4(dst + 16, u[j].w[4], u[j].w[5], u[j].w[6], u[j].w[7]);
+      }
+    }
+  }
+}
+
+hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      hipLaunchKernelGGL((k_hadamard<DT, TEAM, UPL>), row_grid(d, TEAM), dim3(kBlock), 0, s, d.x,
+                         d.R, nunits, d.bs, d.rs, d.rot, (char*)out);
+      return hipGetLastError();
+    });
+  });
+}
+
 }  // namespace sparq24

@@ -205,7 +205,7 @@ __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
   }
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA, int CF, int PAT>
+template <class DT, int TEAM, int UPL, bool WANDA, int CF, int PAT, bool ROT>
 SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ norm, float qmax,
                                          char* __restrict__ codes, uint8_t* __restrict__ meta,
                                          float* __restrict__ scales) {
@@ -217,7 +217,7 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
   // unit afterwards.  Pairwise 4:8 can drop a row's largest element, so it
   // takes the kept maximum like Wanda.
   constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA && PAT == PAT_24;
-  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
     uint32_t am = 0;
     uint32_t mb[FAST16 ? 1 : UPL];
@@ -387,23 +387,27 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
                                  int cfmt, float qmax, void* codes, uint8_t* meta, float* scales,
                                  hipStream_t s) {
   const int64_t nunits = d.K / 8;
-  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
+  if (wanda && d.rot.n) return hipErrorInvalidValue;  // rotated calls take no norms
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
-      auto go = [&]<bool W, int P, int CF>() {
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P>), grid, dim3(kBlock), 0, s,
-                           g, norm, qmax, (char*)codes, meta, scales);
+      auto go = [&]<bool W, int P, int CF, bool R>() {
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>), grid, dim3(kBlock), 0,
+                           s, g, norm, qmax, (char*)codes, meta, scales);
         return hipGetLastError();
       };
-      auto fmt = [&]<bool W, int P>() {
-        if (cfmt == CF_FP8) return go.template operator()<W, P, CF_FP8>();
-        if (cfmt == CF_INT8) return go.template operator()<W, P, CF_INT8>();
-        return go.template operator()<W, P, CF_INT16>();
+      auto fmt = [&]<bool W, int P, bool R>() {
+        if (cfmt == CF_FP8) return go.template operator()<W, P, CF_FP8, R>();
+        if (cfmt == CF_INT8) return go.template operator()<W, P, CF_INT8, R>();
+        return go.template operator()<W, P, CF_INT16, R>();
       };
-      if (pat == PAT_48) return fmt.template operator()<false, PAT_48>();
-      if (wanda) return fmt.template operator()<true, PAT_24>();
-      return fmt.template operator()<false, PAT_24>();
+      if (wanda) return fmt.template operator()<true, PAT_24, false>();
+      if (pat == PAT_48)
+        return d.rot.n ? fmt.template operator()<false, PAT_48, true>()
+                       : fmt.template operator()<false, PAT_48, false>();
+      return d.rot.n ? fmt.template operator()<false, PAT_24, true>()
+                     : fmt.template operator()<false, PAT_24, false>();
     });
   });
 }

@@ -36,12 +36,12 @@ __device__ inline uint32_t unit_absmax(const Unit<DT>& u) {
   }
 }
 
-template <class DT, int TEAM, int UPL>
+template <class DT, int TEAM, int UPL, bool ROT>
 SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
                                                        char* __restrict__ codes,
                                                        float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
-  for_each_row_pipelined<DT, TEAM, UPL>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     uint32_t am = 0;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
@@ -89,10 +89,10 @@ SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
 // ---------------------------------------------------------------------------
 constexpr int kAbsmaxBlocks = 512;
 
-template <class DT, int TEAM, int UPL>
+template <class DT, int TEAM, int UPL, bool ROT>
 __global__ __launch_bounds__(kBlock) void k_absmax_partial(
     const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
-    uint32_t* __restrict__ partials) {
+    uint32_t* __restrict__ partials, Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
   const int t = threadIdx.x % TEAM;
   constexpr int RPB = kBlock / TEAM;
@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kBlock) void k_absmax_partial(
         if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
         else zero_unit(u[j]);
       }
+      if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
 #pragma unroll
       for (int j = 0; j < UPL; ++j)
 #pragma unroll
@@ -141,8 +142,12 @@ hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStrea
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL>), dim3(nb), dim3(kBlock), 0, s, d.x,
-                         d.B, d.R, nunits, d.bs, d.rs, partials);
+      if (d.rot.n)
+        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, true>), dim3(nb), dim3(kBlock), 0, s,
+                           d.x, d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
+      else
+        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, false>), dim3(nb), dim3(kBlock), 0, s,
+                           d.x, d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
       return hipGetLastError();
     });
   });
@@ -191,11 +196,12 @@ __device__ inline int mx_exponent(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-template <class DT, int TEAM, int UPL, bool NV>
+template <class DT, int TEAM, int UPL, bool NV, bool ROT>
 __global__ __launch_bounds__(kBlock) void k_quant_block(
     const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     const float* __restrict__ tamax_in, const uint32_t* __restrict__ partials, int nparts,
-    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
+    Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
   float s_t = 0.f, g = 0.f;
   if constexpr (NV) {
@@ -218,6 +224,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
       if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
       else zero_unit(u[j]);
     }
+    if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = c0 + j * TEAM + t;
@@ -281,12 +288,13 @@ __device__ inline uint32_t select_any(const Unit<DT>& u, const float* norm, int6
   return m;
 }
 
-template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool NV>
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool NV, bool ROT>
 __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
     const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     const float* __restrict__ norm, const float* __restrict__ tamax_in,
     const uint32_t* __restrict__ partials, int nparts, uint16_t* __restrict__ codes,
-    uint8_t* __restrict__ meta, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+    uint8_t* __restrict__ meta, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
+    Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
   float s_t = 0.f, g = 0.f;
   if constexpr (NV) {
@@ -309,6 +317,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
       if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
       else zero_unit(u[j]);
     }
+    if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = c0 + j * TEAM + t;
@@ -360,10 +369,10 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
 
 // Partial maxima of the kept values' magnitudes (the NVFP4 tensor maximum of
 // a sparse operand whose kept maximum can differ from its plain maximum).
-template <class DT, int TEAM, int UPL, int PAT, bool WANDA>
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool ROT>
 __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
     const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
-    const float* __restrict__ norm, uint32_t* __restrict__ partials) {
+    const float* __restrict__ norm, uint32_t* __restrict__ partials, Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
   const int t = threadIdx.x % TEAM;
   constexpr int RPB = kBlock / TEAM;
@@ -380,6 +389,7 @@ __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
         if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
         else zero_unit(u[j]);
       }
+      if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
         const int64_t i = c0 + j * TEAM + t;
@@ -403,64 +413,77 @@ __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
 hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes, float* scales,
                              hipStream_t s) {
   const int64_t nunits = d.K / 8;
-  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs};
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL>), persistent_grid(g.nrows, TEAM),
-                         dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
+      if (d.rot.n)
+        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, true>), persistent_grid(g.nrows, TEAM),
+                           dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
+      else
+        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, false>), persistent_grid(g.nrows, TEAM),
+                           dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
+      return hipGetLastError();
+    });
+  });
+}
+
+template <bool NV>
+static hipError_t launch_quant_block(const RowDesc& d, const float* tamax_in,
+                                     const uint32_t* partials, int nparts, void* codes,
+                                     uint8_t* scales, float* ts_out, hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  return with_dtype(d.dtype, [&]<class DT>() {
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      if (d.rot.n)
+        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, true>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials,
+                           nparts, (uint32_t*)codes, scales, ts_out, d.rot);
+      else
+        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, false>), row_grid(d, TEAM),
+                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials,
+                           nparts, (uint32_t*)codes, scales, ts_out, d.rot);
       return hipGetLastError();
     });
   });
 }
 
 hipError_t launch_quant_mx(const RowDesc& d, void* codes, uint8_t* scales, hipStream_t s) {
-  const int64_t nunits = d.K / 8;
-  return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, false>), row_grid(d, TEAM), dim3(kBlock), 0,
-                         s, d.x, d.R, nunits, d.bs, d.rs, nullptr, nullptr, 0, (uint32_t*)codes,
-                         scales, nullptr);
-      return hipGetLastError();
-    });
-  });
+  return launch_quant_block<false>(d, nullptr, nullptr, 0, codes, scales, nullptr, s);
 }
 
 hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32_t* partials,
                            int nparts, void* codes, uint8_t* scales, float* ts_out,
                            hipStream_t s) {
-  const int64_t nunits = d.K / 8;
-  return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, true>), row_grid(d, TEAM), dim3(kBlock), 0,
-                         s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials, nparts,
-                         (uint32_t*)codes, scales, ts_out);
-      return hipGetLastError();
-    });
-  });
+  return launch_quant_block<true>(d, tamax_in, partials, nparts, codes, scales, ts_out, s);
 }
 
+// Rotation variants exist for magnitude selection only (the rotated calls
+// take no Wanda norms).
 hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const float* norm,
                                   int cfmt, const float* tamax_in, const uint32_t* partials,
                                   int nparts, void* codes, uint8_t* meta, uint8_t* scales,
                                   float* ts_out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
+  if (wanda && d.rot.n) return hipErrorInvalidValue;
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      auto go = [&]<int P, bool W, bool NV>() {
-        hipLaunchKernelGGL((k_prune_quant_fp4<DT, TEAM, UPL, P, W, NV>), row_grid(d, TEAM),
+      auto go = [&]<int P, bool W, bool NV, bool R>() {
+        hipLaunchKernelGGL((k_prune_quant_fp4<DT, TEAM, UPL, P, W, NV, R>), row_grid(d, TEAM),
                            dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, tamax_in,
-                           partials, nparts, (uint16_t*)codes, meta, scales, ts_out);
+                           partials, nparts, (uint16_t*)codes, meta, scales, ts_out, d.rot);
         return hipGetLastError();
+      };
+      auto mag = [&]<int P, bool NV>() {
+        return d.rot.n ? go.template operator()<P, false, NV, true>()
+                       : go.template operator()<P, false, NV, false>();
       };
       const bool nv = cfmt == CF_NV;
       if (pat == PAT_48)
-        return nv ? go.template operator()<PAT_48, false, true>()
-                  : go.template operator()<PAT_48, false, false>();
+        return nv ? mag.template operator()<PAT_48, true>() : mag.template operator()<PAT_48, false>();
       if (wanda)
-        return nv ? go.template operator()<PAT_24, true, true>()
-                  : go.template operator()<PAT_24, true, false>();
-      return nv ? go.template operator()<PAT_24, false, true>()
-                : go.template operator()<PAT_24, false, false>();
+        return nv ? go.template operator()<PAT_24, true, true, false>()
+                  : go.template operator()<PAT_24, true, false, false>();
+      return nv ? mag.template operator()<PAT_24, true>() : mag.template operator()<PAT_24, false>();
     });
   });
 }
@@ -468,17 +491,21 @@ hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const f
 hipError_t launch_kept_absmax_partials(const RowDesc& d, int pat, bool wanda, const float* norm,
                                        uint32_t* partials, hipStream_t s) {
   if (pat == PAT_24 && !wanda) return launch_absmax_partials(d, partials, s);  // kept max == max
+  if (wanda && d.rot.n) return hipErrorInvalidValue;
   const int64_t nunits = d.K / 8;
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      auto go = [&]<int P, bool W, bool R>() {
+        hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, P, W, R>), dim3(nb),
+                           dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials,
+                           d.rot);
+        return hipGetLastError();
+      };
       if (pat == PAT_48)
-        hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, PAT_48, false>), dim3(nb),
-                           dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials);
-      else
-        hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, PAT_24, true>), dim3(nb),
-                           dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials);
-      return hipGetLastError();
+        return d.rot.n ? go.template operator()<PAT_48, false, true>()
+                       : go.template operator()<PAT_48, false, false>();
+      return go.template operator()<PAT_24, true, false>();
     });
   });
 }

@@ -11,6 +11,13 @@ namespace sparq24 {
 enum CodeFmt : int { CF_INT8 = 0, CF_INT16 = 1, CF_FP8 = 2, CF_NONE = 3, CF_MX = 4, CF_NV = 5 };
 
 // One operand as the kernels see it: B x R vectors of K elements.
+// Block Hadamard rotation along K applied to an operand as it is loaded:
+// n = block size (0 = none, else a power of two in 8..512), c = fp64 1/sqrt(n).
+struct Rot {
+  int n;
+  double c;
+};
+
 struct RowDesc {
   const char* x;
   int dtype;            // sparq24_dtype
@@ -18,6 +25,7 @@ struct RowDesc {
   int64_t bs, rs, ks;   // strides in BYTES
   bool kcontig;         // ks == element size
   bool flat;            // fully contiguous: bs == R*rs, rs == K*esize
+  Rot rot;              // rotation applied on load (n == 0: none)
 };
 
 // Sparsity pattern: element-wise 2:4 or pairwise 4:8.
@@ -90,6 +98,8 @@ hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t 
 int col_strips(const RowDesc& d);
 hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Rotated copy of a K-contiguous operand (d.rot) into dense [B][R][K] `out`.
+hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s);
 // Transposed operand -> dense [B][R][K] copy in `out` (B*R*K elements).
 hipError_t launch_transpose_rows(const RowDesc& d, void* out, hipStream_t s);
 

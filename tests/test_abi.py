@@ -186,6 +186,31 @@ def test_prune_quantize_validation(L):
     assert n.value >= 8 * 128 * 2
 
 
+def test_rotation_validation(L):
+    n = ctypes.c_size_t(5)
+    h = L.sparq24_hadamard
+    for blk in (0, 4, 12, 1024):
+        assert h(ctypes.byref(tensor(k=1024)), blk, FAKE, None, ctypes.byref(n), None) == INVALID
+    assert h(ctypes.byref(tensor(k=192)), 128, FAKE, None, ctypes.byref(n), None) == SHAPE
+    assert h(ctypes.byref(tensor(k=256)), 128, FAKE, None, ctypes.byref(n), None) == OK and n.value == 0
+    assert h(ctypes.byref(tensor(rows=8, k=128, rs=1, ks=8)), 64, FAKE, None, ctypes.byref(n), None) == OK
+    assert n.value >= 8 * 128 * 2
+    fq = L.sparq24_quantize_rot
+    assert fq(ctypes.byref(tensor(k=256)), 0, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == INVALID
+    assert fq(ctypes.byref(tensor(k=256)), 64, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == OK
+    fp = L.sparq24_prune_quantize_rot
+    for pat, want in ((0, OK), (1, OK), (2, INVALID)):
+        assert fp(ctypes.byref(tensor(k=256)), 64, pat, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE,
+                  FAKE, None, ctypes.byref(n), None) == want
+    fr = L.sparq24_predict_R_rot
+    arr = (B.CQSpec * 1)(q(B.Q_FP8))
+    assert fr(ctypes.byref(tensor(k=256)), 128, 1, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
+    assert n.value > 0
+    assert fr(ctypes.byref(tensor(k=256)), 512, 0, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
+
+
 def test_copy_validation(L):
     assert L.sparq24_copy(FAKE, FAKE, 0, None) == OK
     assert L.sparq24_copy(FAKE, FAKE, 24, None) == ALIGN
