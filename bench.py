@@ -126,6 +126,11 @@ def main():
             "p48": (torch.empty(T, H // 2, dtype=torch.bfloat16, device=dev),
                     torch.empty(T, H // 16, dtype=torch.uint8, device=dev)),
             "R48": torch.empty(1, 2, 5, dtype=torch.float64, device=dev),
+            "pqr": (torch.empty(T, H // 2, dtype=torch.uint8, device=dev),
+                    torch.empty(T, H // 8, dtype=torch.uint8, device=dev),
+                    torch.empty(T, dtype=torch.float32, device=dev)),
+            "Rr": torch.empty(1, 2, 5, dtype=torch.float64, device=dev),
+            "had": torch.empty(T, H, dtype=torch.bfloat16, device=dev),
             "sfp4": (torch.empty(T, H // 4, dtype=torch.uint8, device=dev),
                      torch.empty(T, H // 16, dtype=torch.uint8, device=dev),
                      torch.empty(T, H // 32, dtype=torch.uint8, device=dev),
@@ -164,8 +169,20 @@ def main():
     def call_sfp4(i):  # sparse FP4: pairwise 4:8 with NVFP4 kept values
         S.prune_quantize_pairs48(pool[i], "nvfp4", out=outs[i]["sfp4"], workspace=ws)
 
+    # Hadamard rotation in blocks of 128 along K, fused into the load
+    def call_pqr(i):
+        S.prune_quantize_rot(pool[i], 128, "fp8", out=outs[i]["pqr"])
+
+    def call_Rr(i):
+        S.predict_R_rot(pool[i], 128, kept, dense, out=outs[i]["Rr"], workspace=ws)
+
+    def call_had(i):
+        S.hadamard(pool[i], 128, out=outs[i]["had"])
+
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
-                  "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4}
+                  "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
+                  "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
+                  "predict_R_rot128": call_Rr}
 
     def step(i):
         for f in calls.values():
@@ -186,6 +203,9 @@ def main():
         "predict_R_pairs48": xb + 2 * 5 * 8,
         # one read of X (the kept-maximum pre-pass reads it a second time)
         "prune_quantize_pairs48_nvfp4": xb + T * H // 4 + T * H // 16 + T * H // 32 + 4,
+        "hadamard128": 2 * xb,
+        "prune_quantize_fp8_rot128": xb + T * H // 2 + T * H // 8 + T * 4,
+        "predict_R_rot128": xb + 2 * 5 * 8,
     })
 
     # ---- spot parity against the oracle (not timed) ---------------------------------

@@ -552,13 +552,41 @@ __device__ inline void unit_store_f32(Unit<DT>& u, const float* f) {
   }
 }
 
+// Value of lane (lane ^ D) of the wave.  DPP row operations for D <= 8
+// (quad_perm [1,0,3,2] and [2,3,0,1]; D = 4 as a quad reverse followed by a
+// half-row mirror, i ^ 3 ^ 7 = i ^ 4; row_ror:8 on 16-lane rows), ds_swizzle
+// (xor mask 16 within 32 lanes) and ds_bpermute for 32.  Every lane of the
+// wave must be active.
+template <int CTRL>
+__device__ inline uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int D>
+__device__ inline uint32_t xor_lane32(uint32_t v) {
+  if constexpr (D == 1) return dpp32<0xB1>(v);
+  else if constexpr (D == 2) return dpp32<0x4E>(v);
+  else if constexpr (D == 4) return dpp32<0x141>(dpp32<0x1B>(v));
+  else if constexpr (D == 8) return dpp32<0x128>(v);
+  else if constexpr (D == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else return (uint32_t)__shfl_xor((int)v, D, 64);
+}
+template <int D>
+__device__ inline double xor_lane(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = xor_lane32<D>((uint32_t)b), hi = xor_lane32<D>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// One butterfly stage across lanes at unit distance D: the lower lane of a
+// pair keeps a + b, the upper one a - b (as fma(-1, b, a), exact like the
+// subtraction).
 template <int D>
 __device__ inline void had_xlane(double (&v)[8], int t) {
-  const bool upper = (t & D) != 0;
+  const double sgn = (t & D) ? -1.0 : 1.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double p = __shfl_xor(v[e], D, 64);
-    v[e] = upper ? p - v[e] : v[e] + p;
+    const double p = xor_lane<D>(v[e]);
+    v[e] = __builtin_fma(sgn, v[e], p);
   }
 }
 
