@@ -60,5 +60,8 @@ from .reference import (  # noqa: F401
     tensor_absmax,
     bits_per_element,
     QSpec,
+    Side,
+    reconstruct,
+    operator_error,
     TINY_AMAX,
 )

@@ -727,6 +727,60 @@ def predict_R(raw: np.ndarray, dtype: str, kept_qs: Sequence[QSpec],
 
 
 # ---------------------------------------------------------------------------
+# Operator-level error ([PD §2]: accuracy is the relative error of the
+# operator's output against a full-precision reference output)
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Side:
+    """One side of a comparison: ``pattern`` "dense", "2:4" or "pairs4:8"
+    (magnitude selection) and the quantizer of the values it keeps (fmt
+    "none" keeps the sparse side's values in the input's storage type)."""
+    pattern: str
+    q: QSpec
+
+
+def reconstruct(raw: np.ndarray, dtype: str, side: Side) -> np.ndarray:
+    """The operand the GEMM consumes on that side, fp64 [rows, K]: pruned
+    elements are zero, kept or dense values are dequantized (NVFP4's tensor
+    maximum over what is quantized: all values, or the kept ones)."""
+    if side.pattern == "dense":
+        if side.q.fmt == "none":
+            raise ValueError("a dense side needs a quantizer")
+        return _reconstruct_dense(raw, dtype, side.q, float(tensor_absmax(raw, dtype)))
+    if side.pattern == "2:4":
+        vals, meta = prune_compress(raw, dtype)
+        return decompress(_reconstruct_kept(vals, dtype, side.q), meta)
+    if side.pattern == "pairs4:8":
+        vals, meta = prune_compress_pairs48(raw, dtype)
+        return decompress_pairs48(_reconstruct_kept(vals, dtype, side.q), meta)
+    raise ValueError(side.pattern)
+
+
+def operator_error(a_raw: np.ndarray, a_dtype: str, b_raw: np.ndarray, b_dtype: str,
+                   sides: Sequence[Side]) -> np.ndarray:
+    """Squared output errors of Y = A B^T per row of A ([PD §2]).
+
+    A [M, K] is the operand under test, B [N, K] the unmodified second
+    operand (both with the reduction axis last).  Returns fp64 [M, 1 + S]:
+    column 0 is sum_n Y[m, n]^2 of the reference output (the exact product of
+    the stored values, formed in fp64), column 1 + s is sum_n (Yhat - Y)^2
+    where Yhat uses side s's reconstruction of A.  Since Yhat - Y =
+    (Ahat - A) B^T, the relative error energy of side s is column 1 + s
+    summed over rows divided by column 0 summed over rows; the measured R of
+    two sides is the square root of the ratio of their error energies."""
+    A = decode_input(a_raw, a_dtype)
+    B = decode_input(b_raw, b_dtype)
+    out = np.empty((A.shape[0], 1 + len(sides)))
+    out[:, 0] = ((A @ B.T) ** 2).sum(axis=1)
+    for i, side in enumerate(sides):
+        D = reconstruct(a_raw, a_dtype, side) - A
+        out[:, 1 + i] = ((D @ B.T) ** 2).sum(axis=1)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Wanda input-channel norms and the equal-bits accounting
 # ---------------------------------------------------------------------------
 

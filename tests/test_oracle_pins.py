@@ -689,3 +689,58 @@ def test_rotation_leaves_gaussian_loss_unchanged():
     y = O.rotate(x, O.F32, 128)
     e = O.error_energy(y, O.F32, O.QSpec("none"), O.QSpec("int", 8))[0]
     assert 0.1309 <= e[1] / e[0] <= 0.1339         # still the Gaussian 13.2% [PD §4]
+
+
+# ---------------------------------------------------------------------------
+# Operator-level error ([PD §2]: relative error of the operator output; [PD §4]:
+# the energy criterion predicts it)
+# ---------------------------------------------------------------------------
+
+
+def test_operator_error_with_orthogonal_b_equals_energy():
+    # B = H / sqrt(K) is orthogonal, so ||(Ahat - A) B^T||^2 = ||Ahat - A||^2:
+    # the operator-level error energy is exactly the tensor's error energy
+    rng = np.random.default_rng(21)
+    k = 256
+    raw = W.to_bf16_bits(rng.standard_normal((12, k)))
+    b = (O.hadamard_matrix(k) / 16.0).astype(np.float32)       # exact in fp32
+    sides = [O.Side("2:4", O.QSpec("fp8")), O.Side("dense", O.QSpec("int", 4)),
+             O.Side("pairs4:8", O.QSpec("nvfp4")), O.Side("dense", O.QSpec("mxfp4"))]
+    op = O.operator_error(raw, O.BF16, b, O.F32, sides)
+    e24 = O.error_energy(raw, O.BF16, O.QSpec("fp8"), O.QSpec("int", 4))[0]
+    e48 = O.error_energy(raw, O.BF16, O.QSpec("nvfp4"), O.QSpec("mxfp4"), pattern="pairs4:8")[0]
+    tot = op[:, 0].sum()
+    assert tot == pytest.approx(e24[0], rel=1e-12)
+    assert op[:, 1].sum() == pytest.approx(e24[1] + e24[2], rel=1e-9)
+    assert op[:, 2].sum() == pytest.approx(e24[3], rel=1e-9)
+    assert op[:, 3].sum() == pytest.approx(e48[1] + e48[2], rel=1e-9)
+    assert op[:, 4].sum() == pytest.approx(e48[3], rel=1e-9)
+
+
+def test_operator_error_exact_quantizer_is_zero():
+    # integer rows with amax 127: INT8 reproduces them, so the output is exact
+    rng = np.random.default_rng(5)
+    a = rng.integers(-127, 128, size=(6, 64)).astype(np.float32)
+    a[:, 0] = 127
+    b = rng.standard_normal((10, 64)).astype(np.float32)
+    op = O.operator_error(a, O.F32, b, O.F32, [O.Side("dense", O.QSpec("int", 8)),
+                                               O.Side("2:4", O.QSpec("none"))])
+    assert np.all(op[:, 1] == 0.0)
+    assert np.all(op[:, 2] > 0.0)
+
+
+def test_operator_error_random_b_tracks_energy():
+    # with an iid Gaussian B, E ||D B^T||^2 = N ||D||^2: the measured and the
+    # predicted error energies agree to a few percent, so measured and
+    # predicted R agree
+    rng = np.random.default_rng(9)
+    raw = W.activation_x(2, 64, 1024)
+    b = rng.standard_normal((2048, 1024)).astype(np.float32)
+    sides = [O.Side("2:4", O.QSpec("fp8")), O.Side("dense", O.QSpec("fp8")),
+             O.Side("dense", O.QSpec("int", 8))]
+    op = O.operator_error(raw, O.BF16, b, O.F32, sides).sum(axis=0)
+    r = O.predict_R(raw, O.BF16, [O.QSpec("fp8"), O.QSpec("fp8")],
+                    [O.QSpec("fp8"), O.QSpec("int", 8)])[0]
+    meas = [np.sqrt(op[1] / op[2]), np.sqrt(op[1] / op[3])]
+    assert meas[0] == pytest.approx(r[0, 4], rel=0.1)
+    assert meas[1] == pytest.approx(r[1, 4], rel=0.1)
