@@ -179,10 +179,22 @@ def main():
     def call_had(i):
         S.hadamard(pool[i], 128, out=outs[i]["had"])
 
+    # operator-level output error of Y = X W^T against a synthetic MLP weight
+    # W [14336, H] (bf16 N(0, 0.02^2)): reference + 2:4+FP8 and dense FP8 sides
+    n_w = 14336
+    w_op = torch.from_numpy(W.weight_w(a.seed + 1, n_w, H).view(np.int16)).view(torch.bfloat16).to(dev)
+    op_sides = [("2:4", ("fp8", 0)), ("dense", ("fp8", 0))]
+    op_out = torch.empty(T, 1 + len(op_sides), dtype=torch.float64, device=dev)
+    op_ws = torch.empty(T * 2 * H * 2 + (1 + len(op_sides)) * T * ((n_w + 127) // 128) * 4 + (1 << 20),
+                        dtype=torch.uint8, device=dev)
+
+    def call_op(i):
+        S.operator_error(pool[i], w_op, op_sides, out=op_out, workspace=op_ws)
+
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
                   "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
                   "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
-                  "predict_R_rot128": call_Rr}
+                  "predict_R_rot128": call_Rr, "operator_error_2sides": call_op}
 
     def step(i):
         for f in calls.values():
@@ -206,7 +218,11 @@ def main():
         "hadamard128": 2 * xb,
         "prune_quantize_fp8_rot128": xb + T * H // 2 + T * H // 8 + T * 4,
         "predict_R_rot128": xb + 2 * 5 * 8,
+        "operator_error_2sides": xb + n_w * H * 2,
     })
+    # MFMA work of the compute-bound call: the reference product plus, per side,
+    # the product of the [hi | lo] residual (2K deep)
+    flops = {"operator_error_2sides": 2.0 * T * n_w * H * (1 + 2 * len(op_sides))}
 
     # ---- spot parity against the oracle (not timed) ---------------------------------
     step(0)
@@ -293,6 +309,9 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * a.pool)
         per_call[name] = {"us": round(us, 3), "GBps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+        if name in flops:
+            tf = flops[name] / (us * 1e-6) / 1e12
+            per_call[name].update({"TFLOPs": round(tf, 1), "mfma_frac_bf16": round(tf / 2500.0, 4)})
 
     # ---- copy baseline: library copy kernel over the same rotation -------------------
     src = [p.view(torch.uint8).view(-1) for p in pool]

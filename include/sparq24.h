@@ -231,7 +231,11 @@ sparq24_status sparq24_predict_R_pairs48(const sparq24_tensor* x, const sparq24_
                                          size_t* ws_bytes, hipStream_t stream);
 
 /* Sparsity pattern selector of the rotated calls below. */
-typedef enum { SPARQ24_PATTERN_24 = 0, SPARQ24_PATTERN_PAIRS48 = 1 } sparq24_pattern;
+typedef enum {
+  SPARQ24_PATTERN_24 = 0,      /* element-wise 2:4 */
+  SPARQ24_PATTERN_PAIRS48 = 1, /* pairwise 4:8 */
+  SPARQ24_PATTERN_DENSE = 2    /* no pruning (operator error only) */
+} sparq24_pattern;
 
 /* Block Hadamard rotation along K [PD §4: before low-bit quantization the
  * operand is multiplied by a rescaled +-1 orthogonal Hadamard matrix, which
@@ -274,6 +278,35 @@ sparq24_status sparq24_predict_R_rot(const sparq24_tensor* x, int32_t block, int
                                      const sparq24_qspec* kept_q, const sparq24_qspec* dense_q,
                                      int32_t npairs, int64_t rows_per_block, double* out,
                                      void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* One side of an operator-level comparison: the operand A as a GEMM would
+ * consume it.  pattern: SPARQ24_PATTERN_DENSE (q: INT, FP8, MXFP4 or NVFP4
+ * over all values, as sparq24_quantize), SPARQ24_PATTERN_24 or
+ * SPARQ24_PATTERN_PAIRS48 (magnitude selection; q over the kept values as
+ * sparq24_prune_quantize, or NONE to keep them in bf16). */
+typedef struct {
+  int32_t pattern;
+  sparq24_qspec q;
+} sparq24_side;
+
+/* Operator-level output error [PD §2: accuracy is the relative error of the
+ * operator output against a full-precision reference; PD §4: the energy
+ * criterion predicts it].  For Y = A B^T with A [M][K] (the operand under
+ * test) and B [N][K] (the unmodified second operand), both bf16 and
+ * K-contiguous (batches folded into rows), out[m][0] = sum_n Y[m][n]^2 and
+ * out[m][1 + s] = sum_n ((Ahat_s - A) B^T)[m][n]^2 for every side s, fp64
+ * [M][1 + nsides].  The relative error energy of side s is the column sum
+ * of 1 + s over the column sum of 0; the measured R of two sides is the
+ * square root of the ratio of their error energies.
+ * Arithmetic: Ahat - A per element is one fp32 FMA (code * scale - x), split
+ * into bf16 hi + lo (within 2^-17 relative); products are bf16 MFMAs with
+ * fp32 accumulation; per-row energies are fp32 over 128 output columns, then
+ * summed in fp64.  K % 64 == 0; 1 <= nsides <= SPARQ24_MAX_PAIRS.
+ * Workspace: M * 2K bf16 for one side's residual, (1 + nsides) * M * N/128
+ * fp32 partials, NVFP4 partial maxima. */
+sparq24_status sparq24_operator_error(const sparq24_tensor* a, const sparq24_tensor* b,
+                                      const sparq24_side* sides, int32_t nsides, double* out,
+                                      void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
  * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in

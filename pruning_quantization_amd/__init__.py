@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     error_energy,
     hadamard,
     lib,
+    operator_error,
     predict_R,
     prune_compress,
     prune_compress_pairs48,

@@ -45,12 +45,16 @@ class CQSpec(ctypes.Structure):
     _fields_ = [("fmt", c_int32), ("bits", c_int32), ("tensor_amax_in", c_void_p)]
 
 
+class CSide(ctypes.Structure):
+    _fields_ = [("pattern", c_int32), ("q", CQSpec)]
+
+
 #: Every symbol the C header declares.
 SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize",
            "sparq24_error_energy", "sparq24_predict_R", "sparq24_col_l2norm", "sparq24_copy",
            "sparq24_prune_compress_pairs48", "sparq24_prune_quantize_pairs48",
            "sparq24_predict_R_pairs48", "sparq24_hadamard", "sparq24_quantize_rot",
-           "sparq24_prune_quantize_rot", "sparq24_predict_R_rot",
+           "sparq24_prune_quantize_rot", "sparq24_predict_R_rot", "sparq24_operator_error",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -83,6 +87,8 @@ def lib(path: Optional[str] = None):
         "sparq24_predict_R_pairs48": [T, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
                                       POINTER(c_size_t), c_void_p],
         "sparq24_hadamard": [T, c_int32, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
+        "sparq24_operator_error": [T, T, POINTER(CSide), c_int32, c_void_p, c_void_p,
+                                   POINTER(c_size_t), c_void_p],
         "sparq24_quantize_rot": [T, c_int32, Q, c_void_p, c_void_p, c_void_p, c_void_p,
                                  POINTER(c_size_t), c_void_p],
         "sparq24_prune_quantize_rot": [T, c_int32, c_int32, Q, c_void_p, c_void_p, c_void_p,
@@ -515,6 +521,35 @@ def predict_R_rot(x: torch.Tensor, block: int, kept: Sequence[QLike], dense: Seq
     st = L.sparq24_predict_R_rot(ctypes.byref(c), int(block), pat, ka, da, npairs, rows_per_block,
                                  out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_predict_R_rot", st)
+    return out
+
+
+def operator_error(a: torch.Tensor, b: torch.Tensor, sides: Sequence[Tuple[str, QLike]],
+                   out: Optional[torch.Tensor] = None, workspace=None):
+    """Operator-level output error of Y = A B^T (A [M, K], B [N, K], bf16) ->
+    fp64 [M, 1 + S]: column 0 the reference output energy per row, column
+    1 + s side s's output error energy per row.  A side is (pattern, q) with
+    pattern "dense", "2:4" or "pairs4:8"."""
+    ca, _ = describe(a, -1)
+    cb, _ = describe(b, -1)
+    pats = {"2:4": 0, "pairs4:8": 1, "dense": 2}
+    arr = (CSide * len(sides))()
+    for i, (pat, q) in enumerate(sides):
+        arr[i].pattern = pats[pat]
+        arr[i].q = qspec(q)
+    M = int(ca.batch) * int(ca.rows)
+    L = lib()
+    s = _stream(a)
+    if out is None:
+        out = torch.empty(M, 1 + len(sides), dtype=torch.float64, device=a.device)
+    if workspace is None:
+        ws, n = _workspace(a, lambda w, nb: L.sparq24_operator_error(
+            ctypes.byref(ca), ctypes.byref(cb), arr, len(sides), None, w, nb, s))
+    else:
+        ws, n = workspace, (c_size_t(workspace.numel()) if workspace is not None else None)
+    st = L.sparq24_operator_error(ctypes.byref(ca), ctypes.byref(cb), arr, len(sides),
+                                  out.data_ptr(), _ptr(ws), _wsarg(n), s)
+    _check("sparq24_operator_error", st)
     return out
 
 

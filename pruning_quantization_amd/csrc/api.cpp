@@ -569,6 +569,68 @@ sparq24_status sparq24_predict_R_rot(const sparq24_tensor* x, int32_t block, int
                     rows_per_block, 1, out, ws, ws_bytes, stream);
 }
 
+sparq24_status sparq24_operator_error(const sparq24_tensor* a, const sparq24_tensor* b,
+                                     const sparq24_side* sides, int32_t nsides, double* out,
+                                     void* ws, size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d, e;
+  CHECK(check_tensor(a, false, d));
+  CHECK(check_tensor(b, false, e));
+  if (d.dtype != SPARQ24_BF16 || e.dtype != SPARQ24_BF16) return SPARQ24_ERR_UNSUPPORTED;
+  if (!sides || nsides < 1 || nsides > SPARQ24_MAX_PAIRS) return SPARQ24_ERR_INVALID;
+  if (d.K != e.K) return SPARQ24_ERR_SHAPE;
+  if (d.K % 64) return SPARQ24_ERR_SHAPE;  // GEMM K slabs (and every block format)
+  if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
+  if (d.B * d.R == 0 || e.B * e.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
+  if (d.B > 1 || e.B > 1) return SPARQ24_ERR_UNSUPPORTED;  // rows must share one stride
+  SideParams sp[SPARQ24_MAX_PAIRS];
+  int nv_sides = 0;
+  for (int i = 0; i < nsides; ++i) {
+    const int pat = sides[i].pattern == SPARQ24_PATTERN_24        ? PAT_24
+                    : sides[i].pattern == SPARQ24_PATTERN_PAIRS48 ? PAT_48
+                    : sides[i].pattern == SPARQ24_PATTERN_DENSE   ? PAT_DENSE
+                                                                  : -1;
+    if (pat < 0) return SPARQ24_ERR_INVALID;
+    int cf;
+    float qm;
+    const unsigned ok = (pat == PAT_DENSE ? 0u : (1u << SPARQ24_Q_NONE)) | (1u << SPARQ24_Q_INT) |
+                        (1u << SPARQ24_Q_FP8_E4M3) | (1u << SPARQ24_Q_MXFP4) |
+                        (1u << SPARQ24_Q_NVFP4);
+    CHECK(check_q(&sides[i].q, ok, cf, qm));
+    sp[i] = SideParams{pat, cf, qm, sides[i].q.tensor_amax_in, nullptr, 0};
+    if (cf == CF_NV && !sides[i].q.tensor_amax_in) ++nv_sides;
+  }
+  const int64_t M = d.R, N = e.R, K = d.K;
+  const int64_t nt = gemm_col_tiles(N);
+  const int nparts = nv_sides ? absmax_partial_count(d) : 0;
+  const size_t delta_bytes = round_up((size_t)M * (size_t)(2 * K) * 2, kAlign);
+  const size_t part_bytes = round_up((size_t)(1 + nsides) * (size_t)M * (size_t)nt * sizeof(float), kAlign);
+  const size_t need = delta_bytes + part_bytes + round_up((size_t)nparts * sizeof(uint32_t), kAlign);
+  bool query;
+  CHECK(workspace(ws, ws_bytes, need, query));
+  if (query) return SPARQ24_OK;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  char* w = (char*)ws;
+  void* delta = w;
+  float* part = (float*)(w + delta_bytes);
+  uint32_t* parts = (uint32_t*)(w + delta_bytes + part_bytes);
+  const int64_t lda = d.rs / 2, ldb = e.rs / 2;
+  CHECK(launched(launch_gemm_rowsq(d.x, lda, e.x, ldb, M, N, K, K, part, stream)));
+  for (int i = 0; i < nsides; ++i) {
+    if (sp[i].fmt == CF_NV && !sp[i].tamax_in) {
+      if (sp[i].pattern == PAT_DENSE) CHECK(launched(launch_absmax_partials(d, parts, stream)));
+      else CHECK(launched(launch_kept_absmax_partials(d, sp[i].pattern, false, nullptr, parts, stream)));
+      sp[i].partials = parts;
+      sp[i].nparts = nparts;
+    }
+    CHECK(launched(launch_side_delta(d, sp[i], delta, stream)));
+    CHECK(launched(launch_gemm_rowsq(delta, 2 * K, e.x, ldb, M, N, 2 * K, K,
+                                     part + (size_t)(1 + i) * (size_t)M * (size_t)nt, stream)));
+  }
+  return launched(launch_rowsq_final(part, M, nt, 1 + nsides, out, stream));
+}
+
 sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
                                   size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;

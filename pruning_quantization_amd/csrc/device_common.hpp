@@ -685,6 +685,63 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block-format and tensor-scale helpers shared by the quantizer, energy and
+// operator-error kernels.
+// ---------------------------------------------------------------------------
+// Reduce the partial maxima in a workgroup (every thread gets T).
+__device__ inline float block_tensor_amax(const float* tamax_in, const uint32_t* partials,
+                                          int nparts, uint32_t* lds) {
+  if (tamax_in) return *tamax_in;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kBlock) m = m > partials[i] ? m : partials[i];
+  m = team_max_u32<64>(m, lds);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kBlock / 64; ++i) r = r > lds[i] ? r : lds[i];
+  return __uint_as_float(r);
+}
+
+// NVFP4 tensor scale and block-scale multiplier from T.
+__device__ inline void nv_tensor_scales(float T, float& s_t, float& g) {
+  if (T >= 0x1p-64f) {
+    s_t = T / 2688.0f;
+    g = 448.0f / T;
+  } else {
+    s_t = 0.0f;
+    g = 0.0f;
+  }
+}
+
+__device__ inline int mx_exponent(uint32_t amax_bits) {
+  // floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 -> -127
+  if (amax_bits == 0) return -127;
+  int fl;
+  const uint32_t ex = amax_bits >> 23;
+  if (ex) fl = (int)ex - 127;
+  else fl = (31 - __builtin_clz(amax_bits)) - 149;  // fp32 subnormal
+  int e = fl - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Quantize-dequantize of 4 values with a per-row scale: returns the 4 code
+// values (exact floats) in c[].  fmt: CF_FP8 or CF_INT8/CF_INT16.
+__device__ inline void qdq_row4(int fmt, float inv, float qmax, const float* v, float* c) {
+  if (fmt == CF_FP8) {
+    const uint32_t w = enc_e4m3_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    c[0] = dec_e4m3_hw<0>(w);
+    c[1] = dec_e4m3_hw<1>(w);
+    c[2] = dec_e4m3_hw<2>(w);
+    c[3] = dec_e4m3_hw<3>(w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = int_code_value(int_round_magic(v[e] * inv, qmax));
+  }
+}
+
 // Per-row symmetric scale: s = fp32(amax / qmax), inv = fp32(qmax / amax);
 // rows with amax < 2^-64 get s = inv = 0.
 __device__ inline void row_scale(float amax, float qmax, float& s, float& inv) {

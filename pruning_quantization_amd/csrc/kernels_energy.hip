@@ -18,31 +18,6 @@
 
 namespace sparq24 {
 
-__device__ inline float block_tensor_amax_e(const float* tamax_in, const uint32_t* partials,
-                                            int nparts, uint32_t* lds) {
-  if (tamax_in) return *tamax_in;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += kBlock) m = m > partials[i] ? m : partials[i];
-  m = team_max_u32<64>(m, lds);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = m;
-  __syncthreads();
-  uint32_t r = lds[0];
-#pragma unroll
-  for (int i = 1; i < kBlock / 64; ++i) r = r > lds[i] ? r : lds[i];
-  return __uint_as_float(r);
-}
-
-__device__ inline int mx_exp_e(uint32_t amax_bits) {
-  if (amax_bits == 0) return -127;
-  int fl;
-  const uint32_t ex = amax_bits >> 23;
-  if (ex) fl = (int)ex - 127;
-  else fl = (31 - __builtin_clz(amax_bits)) - 149;
-  int e = fl - 2;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
 template <class DT>
 __device__ inline uint32_t unit_absmax_e(const Unit<DT>& u) {
   uint32_t m = 0;
@@ -65,21 +40,6 @@ __device__ inline uint32_t unit_absmax_e(const Unit<DT>& u) {
 __device__ inline void acc_err(double& acc, float xhat_unit, float scale, float v) {
   const float e = __builtin_fmaf(xhat_unit, scale, -v);  // one rounding of code*s - x
   acc = __builtin_fma((double)e, (double)e, acc);
-}
-
-// Quantize-dequantize of 4 values with a per-row scale: returns the 4 code
-// values (exact floats) in c[].  fmt: CF_FP8 or CF_INT8/CF_INT16.
-__device__ inline void qdq_row4(int fmt, float inv, float qmax, const float* v, float* c) {
-  if (fmt == CF_FP8) {
-    const uint32_t w = enc_e4m3_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    c[0] = dec_e4m3_hw<0>(w);
-    c[1] = dec_e4m3_hw<1>(w);
-    c[2] = dec_e4m3_hw<2>(w);
-    c[3] = dec_e4m3_hw<3>(w);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c[e] = int_code_value(int_round_magic(v[e] * inv, qmax));
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -189,7 +149,7 @@ __device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
   } else {
     w = (uint32_t)__shfl_xor((int)am, 4, 64);
     am = am > w ? am : w;
-    const int ex = mx_exp_e(am);
+    const int ex = mx_exponent(am);
     const float X = __builtin_ldexpf(1.0f, ex);
     const uint32_t pk = enc_e2m1_x4(__builtin_ldexpf(v[0], -ex), __builtin_ldexpf(v[1], -ex),
                                     __builtin_ldexpf(v[2], -ex), __builtin_ldexpf(v[3], -ex));
@@ -265,14 +225,14 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
   if (any_nv) {
-    const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
+    const float T = block_tensor_amax(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
   }
   bool any_knv = false;
   for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
   float ks_t = 0.f, kgnv = 0.f;
   if (any_knv) {
-    const float T = block_tensor_amax_e(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
+    const float T = block_tensor_amax(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
   }
   const int64_t nrows = g.nrows;
@@ -359,7 +319,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
           if (fmt == CF_MX) {
             w = (uint32_t)__shfl_xor((int)bm, 2, 64);
             bm = bm > w ? bm : w;
-            const int ex = mx_exp_e(bm);
+            const int ex = mx_exponent(bm);
             const float X = __builtin_ldexpf(1.0f, ex);
             float y[8];
 #pragma unroll
@@ -407,14 +367,14 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
   if (any_nv) {
-    const float T = block_tensor_amax_e(p.nv_tamax, p.nv_partials, p.n_partials, redu);
+    const float T = block_tensor_amax(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
   }
   bool any_knv = false;
   for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
   float ks_t = 0.f, kgnv = 0.f;
   if (any_knv) {
-    const float T = block_tensor_amax_e(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
+    const float T = block_tensor_amax(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
   }
   const int64_t nrows = g.nrows;
@@ -529,7 +489,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
           if (fmt == CF_MX) {
             w = (uint32_t)__shfl_xor((int)am, 2, 64);
             am = am > w ? am : w;
-            const int ex = mx_exp_e(am);
+            const int ex = mx_exponent(am);
             const float X = __builtin_ldexpf(1.0f, ex);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(v[e], -ex);

@@ -153,49 +153,11 @@ hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStrea
   });
 }
 
-// Reduce the partial maxima in a workgroup (every thread gets T).
-__device__ inline float block_tensor_amax(const float* tamax_in, const uint32_t* partials,
-                                          int nparts, uint32_t* lds) {
-  if (tamax_in) return *tamax_in;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += kBlock) m = m > partials[i] ? m : partials[i];
-  m = team_max_u32<64>(m, lds);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = m;
-  __syncthreads();
-  uint32_t r = lds[0];
-#pragma unroll
-  for (int i = 1; i < kBlock / 64; ++i) r = r > lds[i] ? r : lds[i];
-  return __uint_as_float(r);
-}
-
-// NVFP4 tensor scale and block-scale multiplier from T.
-__device__ inline void nv_tensor_scales(float T, float& s_t, float& g) {
-  if (T >= 0x1p-64f) {
-    s_t = T / 2688.0f;
-    g = 448.0f / T;
-  } else {
-    s_t = 0.0f;
-    g = 0.0f;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // MXFP4 / NVFP4.  Lane t owns units t, t+TEAM, ...; an MX block (32
 // elements) is 4 adjacent lanes, an NV block (16 elements) 2 adjacent lanes,
 // combined with cross-lane xor shuffles.
 // ---------------------------------------------------------------------------
-__device__ inline int mx_exponent(uint32_t amax_bits) {
-  // floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 -> -127
-  if (amax_bits == 0) return -127;
-  int fl;
-  const uint32_t ex = amax_bits >> 23;
-  if (ex) fl = (int)ex - 127;
-  else fl = (31 - __builtin_clz(amax_bits)) - 149;  // fp32 subnormal
-  int e = fl - 2;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
 template <class DT, int TEAM, int UPL, bool NV, bool ROT>
 __global__ __launch_bounds__(kBlock) void k_quant_block(
     const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,

@@ -29,7 +29,19 @@ struct RowDesc {
 };
 
 // Sparsity pattern: element-wise 2:4 or pairwise 4:8.
-enum Pattern : int { PAT_24 = 0, PAT_48 = 1 };
+enum Pattern : int { PAT_24 = 0, PAT_48 = 1, PAT_DENSE = 2 };
+
+// One side of an operator-error comparison (the operand as a GEMM would
+// consume it): selection pattern, quantizer of what it keeps, NVFP4 tensor
+// maximum (given, or reduced from partial maxima).
+struct SideParams {
+  int pattern;
+  int fmt;
+  float qmax;
+  const float* tamax_in;
+  const uint32_t* partials;
+  int nparts;
+};
 
 constexpr int kMaxQ = 16;
 
@@ -98,6 +110,14 @@ hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t 
 int col_strips(const RowDesc& d);
 hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Operator-level error: D = Ahat - A as bf16 hi | lo rows [M][2K]; GEMM with a
+// per-row energy epilogue over 128-column tiles; fp64 row sums.
+hipError_t launch_side_delta(const RowDesc& d, const SideParams& sp, void* out, hipStream_t s);
+int64_t gemm_col_tiles(int64_t N);
+hipError_t launch_gemm_rowsq(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                             int64_t N, int64_t Kp, int64_t K, float* part, hipStream_t s);
+hipError_t launch_rowsq_final(const float* part, int64_t M, int64_t ntiles, int ncols, double* out,
+                              hipStream_t s);
 // Rotated copy of a K-contiguous operand (d.rot) into dense [B][R][K] `out`.
 hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s);
 // Transposed operand -> dense [B][R][K] copy in `out` (B*R*K elements).
