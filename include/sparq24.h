@@ -308,6 +308,21 @@ sparq24_status sparq24_operator_error(const sparq24_tensor* a, const sparq24_ten
                                       const sparq24_side* sides, int32_t nsides, double* out,
                                       void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/* GEMM on the compressed 2:4 operand [PD §3: the 2:4 side multiplies the
+ * pruned, compressed operand with a sparse GEMM]: c [M][N] fp32 (row-major)
+ * = A B^T, A given as the output of sparq24_prune_compress (bf16 kept values
+ * [M][K/2], metadata [M][K/8]), B a dense bf16 [N][K] K-contiguous operand.
+ * gfx950's v_smfmac_f32_16x16x64_bf16 reads the layout as is: per lane 8
+ * kept values of 16 logical k and their 16 metadata bits.  Products are
+ * exact, sums fp32.  K % 64 == 0; pointers 16-byte aligned. */
+sparq24_status sparq24_sparse_gemm(const void* values, const uint8_t* meta, int64_t m, int64_t k,
+                                   const sparq24_tensor* b, float* c, hipStream_t stream);
+
+/* The same GEMM tile on a dense bf16 A [M][K] (the comparison the pages
+ * draw between a sparse GEMM and its dense rival): c [M][N] fp32 = A B^T. */
+sparq24_status sparq24_dense_gemm(const sparq24_tensor* a, const sparq24_tensor* b, float* c,
+                                  hipStream_t stream);
+
 /* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
  * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in
  * fp64, then rounded once.  x is an activation [tokens, channels] given with

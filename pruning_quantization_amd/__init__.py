@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     bits_per_element,
     col_l2norm,
     copy,
+    dense_gemm,
     describe,
     error_energy,
     hadamard,
@@ -27,5 +28,6 @@ from .binding import (  # noqa: F401
     qspec,
     quantize,
     quantize_rot,
+    sparse_gemm,
     version,
 )

@@ -55,6 +55,7 @@ SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize
            "sparq24_prune_compress_pairs48", "sparq24_prune_quantize_pairs48",
            "sparq24_predict_R_pairs48", "sparq24_hadamard", "sparq24_quantize_rot",
            "sparq24_prune_quantize_rot", "sparq24_predict_R_rot", "sparq24_operator_error",
+           "sparq24_sparse_gemm", "sparq24_dense_gemm",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -89,6 +90,8 @@ def lib(path: Optional[str] = None):
         "sparq24_hadamard": [T, c_int32, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
         "sparq24_operator_error": [T, T, POINTER(CSide), c_int32, c_void_p, c_void_p,
                                    POINTER(c_size_t), c_void_p],
+        "sparq24_sparse_gemm": [c_void_p, c_void_p, c_int64, c_int64, T, c_void_p, c_void_p],
+        "sparq24_dense_gemm": [T, T, c_void_p, c_void_p],
         "sparq24_quantize_rot": [T, c_int32, Q, c_void_p, c_void_p, c_void_p, c_void_p,
                                  POINTER(c_size_t), c_void_p],
         "sparq24_prune_quantize_rot": [T, c_int32, c_int32, Q, c_void_p, c_void_p, c_void_p,
@@ -550,6 +553,34 @@ def operator_error(a: torch.Tensor, b: torch.Tensor, sides: Sequence[Tuple[str, 
     st = L.sparq24_operator_error(ctypes.byref(ca), ctypes.byref(cb), arr, len(sides),
                                   out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_operator_error", st)
+    return out
+
+
+def sparse_gemm(values: torch.Tensor, meta: torch.Tensor, b: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A B^T (fp32 [M, N]) with A the 2:4-compressed output of
+    :func:`prune_compress` (bf16 values [M, K/2], meta [M, K/8]) and B bf16
+    [N, K], on the sparse MFMA."""
+    m, k = int(values.shape[0]), int(values.shape[1]) * 2
+    cb, _ = describe(b, -1)
+    n = int(cb.batch) * int(cb.rows)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.float32, device=b.device)
+    st = lib().sparq24_sparse_gemm(values.data_ptr(), meta.data_ptr(), m, k, ctypes.byref(cb),
+                                   out.data_ptr(), _stream(b))
+    _check("sparq24_sparse_gemm", st)
+    return out
+
+
+def dense_gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A B^T (fp32 [M, N]) for bf16 A [M, K] and B [N, K], same tile."""
+    ca, _ = describe(a, -1)
+    cb, _ = describe(b, -1)
+    m, n = int(ca.batch) * int(ca.rows), int(cb.batch) * int(cb.rows)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.float32, device=a.device)
+    st = lib().sparq24_dense_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), _stream(a))
+    _check("sparq24_dense_gemm", st)
     return out
 
 

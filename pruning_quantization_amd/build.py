@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparq24.so")
 
 SOURCES = ["api.cpp", "kernels_prune.hip", "kernels_quant.hip", "kernels_energy.hip",
-           "kernels_misc.hip", "kernels_operr.hip"]
+           "kernels_misc.hip", "kernels_operr.hip", "kernels_spgemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

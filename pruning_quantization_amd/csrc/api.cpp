@@ -631,6 +631,36 @@ sparq24_status sparq24_operator_error(const sparq24_tensor* a, const sparq24_ten
   return launched(launch_rowsq_final(part, M, nt, 1 + nsides, out, stream));
 }
 
+sparq24_status sparq24_sparse_gemm(const void* values, const uint8_t* meta, int64_t m, int64_t k,
+                                   const sparq24_tensor* b, float* c, hipStream_t stream) {
+  RowDesc e;
+  CHECK(check_tensor(b, false, e));
+  if (m < 0 || k < 0) return SPARQ24_ERR_INVALID;
+  if (e.dtype != SPARQ24_BF16) return SPARQ24_ERR_UNSUPPORTED;
+  if (e.B > 1) return SPARQ24_ERR_UNSUPPORTED;
+  if (k != e.K || k % 64) return SPARQ24_ERR_SHAPE;
+  if (m == 0 || e.R == 0) return SPARQ24_OK;
+  if (!values || !meta || !c) return SPARQ24_ERR_INVALID;
+  if (!aligned16(values) || !aligned16(meta) || !aligned16(c)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_sparse_gemm(values, meta, m, k, e.x, e.rs / 2, e.R, c, e.R, stream));
+}
+
+sparq24_status sparq24_dense_gemm(const sparq24_tensor* a, const sparq24_tensor* b, float* c,
+                                  hipStream_t stream) {
+  RowDesc d, e;
+  CHECK(check_tensor(a, false, d));
+  CHECK(check_tensor(b, false, e));
+  if (d.dtype != SPARQ24_BF16 || e.dtype != SPARQ24_BF16) return SPARQ24_ERR_UNSUPPORTED;
+  if (d.B > 1 || e.B > 1) return SPARQ24_ERR_UNSUPPORTED;
+  if (d.K != e.K || d.K % 64) return SPARQ24_ERR_SHAPE;
+  if (d.R == 0 || e.R == 0) return SPARQ24_OK;
+  if (!c) return SPARQ24_ERR_INVALID;
+  if (!aligned16(c)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_dense_gemm(d.x, d.rs / 2, d.R, d.K, e.x, e.rs / 2, e.R, c, e.R, stream));
+}
+
 sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
                                   size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;

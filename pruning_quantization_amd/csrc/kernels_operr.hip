@@ -9,6 +9,7 @@
 // per row and 128-column tile.  The reference energy sum_n Y[m][n]^2 is the
 // same GEMM on A itself.  A and B are bf16 (the GEMM operand type).
 #include "dispatch.hpp"
+#include "gemm_tile.hpp"
 
 namespace sparq24 {
 
@@ -179,143 +180,6 @@ SPARQ24_ROW_KERNEL void k_side_delta(RowGeom g, SideParams sp, uint16_t* __restr
   });
 }
 
-// ---------------------------------------------------------------------------
-// GEMM with a row-energy epilogue: part[m][tile] = sum over the tile's
-// columns n of C[m][n]^2, C = A' B'^T with A' [M][Kp] and B'[n][k] =
-// B[n][k % K] (so [B | B] against [hi | lo]).  bf16 MFMA 16x16x32 (fp32
-// accumulation), 64-deep K slabs double-buffered in LDS (rows padded to
-// 144 B so the 16 rows a ds_read_b128 group touches fall in distinct banks).
-// A lane's 8 k values of a fragment are the same positions for A and B,
-// which is all the product needs.  Partial energies are fp32 over a tile's
-// columns.
-// ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kGK = 64, kGPad = 8;
-
-// Workgroup tile BM x BN with (BM / WTM) x (BN / WTN) waves, each owning a
-// WTM x WTN output block of 16 x 16 MFMA tiles.
-template <int BM, int BN, int WTM, int WTN>
-__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_rowsq(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int64_t M, int64_t N, int64_t Kp, int64_t K, float* __restrict__ part, int64_t ntiles) {
-  constexpr int WN = BN / WTN, NT = (BM / WTM) * WN * 64;
-  constexpr int TI = WTM / 16, TJ = WTN / 16;
-  constexpr int QA = BM * 8 / NT, QB = BN * 8 / NT;  // 16-byte chunks per thread per slab
-  static_assert(QA * NT == BM * 8 && QB * NT == BN * 8, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][kGK + kGPad];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][kGK + kGPad];
-  __shared__ float red[WN][BM];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
-  // XCD-aware tile order: workgroups are dealt to the 8 XCDs round robin, so
-  // workgroup p runs on XCD p % 8.  Renumber so that each XCD owns a
-  // contiguous range of logical tiles, and walk that range in groups of
-  // kGroupM row tiles (row tile fastest): the ~32 tiles an XCD runs at once
-  // then share a few A row slabs and B column slabs in its L2.
-  const int64_t ntm = (M + BM - 1) / BM, total = ntm * ntiles;
-  const int64_t pid = blockIdx.x, per = total / 8;
-  const int64_t lid = pid < per * 8 ? (pid % 8) * per + pid / 8 : pid;
-  constexpr int64_t kGroupM = 8;
-  const int64_t ingroup = kGroupM * ntiles, first = (lid / ingroup) * kGroupM;
-  const int64_t gsz = ntm - first < kGroupM ? ntm - first : kGroupM;
-  const int64_t tm = first + (lid % ingroup) % gsz, tn = (lid % ingroup) / gsz;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  uint4 ra[QA], rb[QB];
-  // Branch-free slab loads (the loop body stays one scheduling region): rows
-  // past the edge read the last row and are zeroed by a select.
-  auto gload = [&](int64_t k0) {
-    const int64_t kb0 = k0 % K;
-#pragma unroll
-    for (int q = 0; q < QA; ++q) {
-      const int c = tid + NT * q, r = c >> 3, cc = c & 7;
-      const int64_t m = m0 + r;
-      const uint4 v = *reinterpret_cast<const uint4*>(A + (m < M ? m : M - 1) * lda + k0 + cc * 8);
-      ra[q] = m < M ? v : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const int c = tid + NT * q, r = c >> 3, cc = c & 7;
-      const int64_t n = n0 + r;
-      const uint4 v = *reinterpret_cast<const uint4*>(B + (n < N ? n : N - 1) * ldb + kb0 + cc * 8);
-      rb[q] = n < N ? v : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < QA; ++q) {
-      const int c = tid + NT * q, r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][r][cc * 8]) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const int c = tid + NT * q, r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sB[buf][r][cc * 8]) = rb[q];
-    }
-  };
-  f32x4_t acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bf16x8_t af[TI], bfr[TJ];
-  const int64_t nk = Kp / kGK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    // the next slab (the last one again on the final step: harmless, never read)
-    gload((kt + 1 < nk ? kt + 1 : kt) * kGK);
-#pragma unroll
-    for (int st = 0; st < kGK / 32; ++st) {
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][wm * WTM + i * 16 + (lane & 15)][st * 32 + (lane >> 4) * 8]);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[cur][wn * WTN + j * 16 + (lane & 15)][st * 32 + (lane >> 4) * 8]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      // all fragment reads of the step issue before its MFMAs (one wait)
-      __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
-    }
-    sstore(cur ^ 1);
-    __syncthreads();
-  }
-  // lane holds C[4 * (lane >> 4) + v][lane & 15] of each 16x16 tile
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) sq = __builtin_fmaf(acc[i][j][v], acc[i][j][v], sq);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-      if ((lane & 15) == 0) red[wn][wm * WTM + i * 16 + 4 * (lane >> 4) + v] = sq;
-    }
-  __syncthreads();
-  for (int r = tid; r < BM; r += NT) {
-    const int64_t m = m0 + r;
-    float a = 0.f;
-#pragma unroll
-    for (int q = 0; q < WN; ++q) a += red[q][r];
-    if (m < M) part[m * ntiles + tn] = a;
-  }
-}
-
-#ifndef SPARQ24_GEMM_BIG
-#define SPARQ24_GEMM_BIG 1
-#endif
-// 256 x 256 tiles of 128 x 64 per wave (fewer LDS reads per MFMA), or
-// 128 x 128 tiles of 64 x 64 per wave.
-constexpr int kGN = SPARQ24_GEMM_BIG ? 256 : 128;
-constexpr int kGM = SPARQ24_GEMM_BIG ? 256 : 128;
-
 // out[m][col] = sum over tiles of part[col][m][tile] in fp64, fixed order.
 __global__ __launch_bounds__(kBlock) void k_rowsq_final(const float* __restrict__ part, int64_t M,
                                                         int64_t ntiles, int ncols,
@@ -347,15 +211,8 @@ hipError_t launch_side_delta(const RowDesc& d, const SideParams& sp, void* out, 
 
 hipError_t launch_gemm_rowsq(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                              int64_t N, int64_t Kp, int64_t K, float* part, hipStream_t s) {
-  const int64_t nt = gemm_col_tiles(N);
-  const dim3 grid((unsigned)(nt * ((M + kGM - 1) / kGM)));
-  if constexpr (SPARQ24_GEMM_BIG)
-    hipLaunchKernelGGL((k_gemm_rowsq<256, 256, 128, 64>), grid, dim3(512), 0, s,
-                       (const uint16_t*)A, lda, (const uint16_t*)B, ldb, M, N, Kp, K, part, nt);
-  else
-    hipLaunchKernelGGL((k_gemm_rowsq<128, 128, 64, 64>), grid, dim3(256), 0, s,
-                       (const uint16_t*)A, lda, (const uint16_t*)B, ldb, M, N, Kp, K, part, nt);
-  return hipGetLastError();
+  const GemmArgs g{A, lda, nullptr, 0, B, ldb, M, N, Kp, K, part, gemm_col_tiles(N)};
+  return launch_gemm<false, EPI_ROWSQ>(g, s);
 }
 
 hipError_t launch_rowsq_final(const float* part, int64_t M, int64_t ntiles, int ncols, double* out,

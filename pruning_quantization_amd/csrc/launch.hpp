@@ -118,6 +118,13 @@ hipError_t launch_gemm_rowsq(const void* A, int64_t lda, const void* B, int64_t 
                              int64_t N, int64_t Kp, int64_t K, float* part, hipStream_t s);
 hipError_t launch_rowsq_final(const float* part, int64_t M, int64_t ntiles, int ncols, double* out,
                               hipStream_t s);
+// C [M][N] fp32 (row stride ldc) = A B^T: A 2:4-compressed (values [M][K/2],
+// meta [M][K/8]) on the sparse MFMA, or dense bf16 rows (row stride lda).
+hipError_t launch_sparse_gemm(const void* values, const uint8_t* meta, int64_t M, int64_t K,
+                              const void* B, int64_t ldb, int64_t N, float* C, int64_t ldc,
+                              hipStream_t s);
+hipError_t launch_dense_gemm(const void* A, int64_t lda, int64_t M, int64_t K, const void* B,
+                             int64_t ldb, int64_t N, float* C, int64_t ldc, hipStream_t s);
 // Rotated copy of a K-contiguous operand (d.rot) into dense [B][R][K] `out`.
 hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s);
 // Transposed operand -> dense [B][R][K] copy in `out` (B*R*K elements).
