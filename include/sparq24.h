@@ -323,6 +323,16 @@ sparq24_status sparq24_sparse_gemm(const void* values, const uint8_t* meta, int6
 sparq24_status sparq24_dense_gemm(const sparq24_tensor* a, const sparq24_tensor* b, float* c,
                                   hipStream_t stream);
 
+/* The dense FP8 rival's GEMM [PD §2: 2:4 with 16-bit values against dense
+ * FP8 at equal nominal throughput]: c [M][N] fp32 = (scale_a[m] * scale_b[n])
+ * * sum_k a[m][k] b[n][k] with a [M][K] and b [N][K] the e4m3 codes and
+ * per-row scales of sparq24_quantize (FP8).  gfx950's
+ * v_mfma_f32_16x16x128_f8f6f4; e4m3 products are exact in fp32, sums fp32,
+ * then two fp32 scale multiplies.  K % 128 == 0. */
+sparq24_status sparq24_fp8_gemm(const uint8_t* a, const float* scale_a, int64_t m,
+                                const uint8_t* b, const float* scale_b, int64_t n, int64_t k,
+                                float* c, hipStream_t stream);
+
 /* Wanda's input-channel norms [PD §2]: norms[k] = fp32(sqrt(sum over all
  * (b, r) of x[b][r][k]^2)), the sum in fp64 (fixed order), the square root in
  * fp64, then rounded once.  x is an activation [tokens, channels] given with

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     dense_gemm,
     describe,
     error_energy,
+    fp8_gemm,
     hadamard,
     lib,
     operator_error,

@@ -55,7 +55,7 @@ SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize
            "sparq24_prune_compress_pairs48", "sparq24_prune_quantize_pairs48",
            "sparq24_predict_R_pairs48", "sparq24_hadamard", "sparq24_quantize_rot",
            "sparq24_prune_quantize_rot", "sparq24_predict_R_rot", "sparq24_operator_error",
-           "sparq24_sparse_gemm", "sparq24_dense_gemm",
+           "sparq24_sparse_gemm", "sparq24_dense_gemm", "sparq24_fp8_gemm",
            "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
 
 _lib = None
@@ -92,6 +92,8 @@ def lib(path: Optional[str] = None):
                                    POINTER(c_size_t), c_void_p],
         "sparq24_sparse_gemm": [c_void_p, c_void_p, c_int64, c_int64, T, c_void_p, c_void_p],
         "sparq24_dense_gemm": [T, T, c_void_p, c_void_p],
+        "sparq24_fp8_gemm": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64,
+                             c_void_p, c_void_p],
         "sparq24_quantize_rot": [T, c_int32, Q, c_void_p, c_void_p, c_void_p, c_void_p,
                                  POINTER(c_size_t), c_void_p],
         "sparq24_prune_quantize_rot": [T, c_int32, c_int32, Q, c_void_p, c_void_p, c_void_p,
@@ -581,6 +583,20 @@ def dense_gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = N
         out = torch.empty(m, n, dtype=torch.float32, device=a.device)
     st = lib().sparq24_dense_gemm(ctypes.byref(ca), ctypes.byref(cb), out.data_ptr(), _stream(a))
     _check("sparq24_dense_gemm", st)
+    return out
+
+
+def fp8_gemm(codes_a: torch.Tensor, scale_a: torch.Tensor, codes_b: torch.Tensor,
+             scale_b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = diag(scale_a) (A B^T) diag(scale_b) (fp32 [M, N]) from the e4m3
+    codes [M, K], [N, K] and per-row scales of :func:`quantize` (FP8)."""
+    m, k = int(codes_a.shape[0]), int(codes_a.shape[1])
+    n = int(codes_b.shape[0])
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.float32, device=codes_a.device)
+    st = lib().sparq24_fp8_gemm(codes_a.data_ptr(), scale_a.data_ptr(), m, codes_b.data_ptr(),
+                                scale_b.data_ptr(), n, k, out.data_ptr(), _stream(codes_a))
+    _check("sparq24_fp8_gemm", st)
     return out
 
 

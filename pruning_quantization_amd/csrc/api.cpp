@@ -661,6 +661,20 @@ sparq24_status sparq24_dense_gemm(const sparq24_tensor* a, const sparq24_tensor*
   return launched(launch_dense_gemm(d.x, d.rs / 2, d.R, d.K, e.x, e.rs / 2, e.R, c, e.R, stream));
 }
 
+sparq24_status sparq24_fp8_gemm(const uint8_t* a, const float* scale_a, int64_t m,
+                                const uint8_t* b, const float* scale_b, int64_t n, int64_t k,
+                                float* c, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0) return SPARQ24_ERR_INVALID;
+  if (k % 128) return SPARQ24_ERR_SHAPE;
+  if (m == 0 || n == 0) return SPARQ24_OK;
+  if (!a || !b || !scale_a || !scale_b || !c) return SPARQ24_ERR_INVALID;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || ((uintptr_t)scale_a & 3u) ||
+      ((uintptr_t)scale_b & 3u))
+    return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  return launched(launch_fp8_gemm(a, k, scale_a, m, k, b, k, scale_b, n, c, n, stream));
+}
+
 sparq24_status sparq24_col_l2norm(const sparq24_tensor* x, float* norms, void* ws,
                                   size_t* ws_bytes, hipStream_t stream) {
   RowDesc d;

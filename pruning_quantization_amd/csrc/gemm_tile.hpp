@@ -16,7 +16,9 @@
 // fragment read touches fall in distinct banks), fp32 accumulation.  A
 // lane's k values of a fragment are the same positions for A and B, which is
 // all the dense product needs.  Epilogue: per-row sums of C^2 over the tile's
-// columns (EPI_ROWSQ) or C stored as fp32 (EPI_STORE).
+// columns (EPI_ROWSQ) or C stored as fp32 (EPI_STORE).  GM_FP8 runs the same
+// tile on e4m3 codes with v_mfma_f32_16x16x128_f8f6f4 and applies the per-row
+// scales of both operands when storing C.
 #pragma once
 
 #include "device_common.hpp"
@@ -29,6 +31,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kGK = 64, kGPad = 8;
 constexpr int kGM = 256, kGN = 256;
 enum GemmEpi : int { EPI_ROWSQ = 0, EPI_STORE = 1 };
+// Operand kinds: dense bf16, 2:4-compressed bf16 A (sparse MFMA), dense e4m3
+// codes with per-row fp32 scales (C = scale_a[m] * scale_b[n] * sum a b).
+enum GemmMode : int { GM_BF16 = 0, GM_SPARSE = 1, GM_FP8 = 2 };
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 struct GemmArgs {
   const void* A;     // dense bf16 rows, or the kept values of a compressed operand
@@ -38,12 +44,17 @@ struct GemmArgs {
   const void* B;
   int64_t ldb;
   int64_t M, N, Kp, K;
-  float* out;        // EPI_ROWSQ: part [M][ntiles]; EPI_STORE: C [M][ntiles... ldc]
+  float* out;        // EPI_ROWSQ: part [M][ntiles]; EPI_STORE: C [M][ldc]
   int64_t ld_out;    // EPI_ROWSQ: ntiles; EPI_STORE: elements between rows of C
+  const float* scale_a;  // GM_FP8: per-row scales of A [M] and B [N]
+  const float* scale_b;
 };
 
-template <int BM, int BN, int WTM, int WTN, bool SPARSE, int EPI>
+// Strides and depths of GM_FP8 are counted in pairs of codes (16-bit units),
+// so a 64-unit slab is 128 codes and every load path is shared.
+template <int BM, int BN, int WTM, int WTN, int MODE, int EPI>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm(GemmArgs g) {
+  constexpr bool SPARSE = MODE == GM_SPARSE;
   constexpr int WN = BN / WTN, NT = (BM / WTM) * WN * 64;
   constexpr int TI = WTM / 16, TJ = WTN / 16;
   constexpr int AW = SPARSE ? kGK / 2 : kGK;           // A elements per row per slab
@@ -133,18 +144,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm(GemmArgs 
     gload((kt + 1 < nk ? kt + 1 : kt) * kGK);
     if constexpr (SPARSE) {
       // one 64-deep sparse MFMA per tile: A lane group h = lane / 16 covers
-      // logical k 16h .. 16h + 15 (8 kept values, metadata bytes 2h, 2h + 1)
-      bf16x8_t af[TI];
-      int ix[TI];
-      bf16x16_t bfr[TJ];
+      // logical k 16h .. 16h + 15 (8 kept values, metadata bytes 2h, 2h + 1).
+      // Row tiles in two halves keep the live fragments within budget.
       const int h = lane >> 4;
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int r = wm * WTM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][r][h * 8]);
-        const uint2 mm = sM[cur][r];
-        ix[i] = (int)(((h < 2 ? mm.x : mm.y) >> (16 * (h & 1))) & 0xFFFFu);
-      }
+      bf16x16_t bfr[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         // B: lane group h holds logical k 8h .. 8h + 7 and 32 + 8h .. 32 + 8h + 7
@@ -153,13 +156,56 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm(GemmArgs 
         const bf16x8_t hi = *reinterpret_cast<const bf16x8_t*>(br + 32 + h * 8);
         bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       }
+auto do_half = [&]<int half>() {
+        constexpr int TH = TI / 2;
+        bf16x8_t af[TH];
+        int ix[TH];
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+        for (int ii = 0; ii < TH; ++ii) {
+          const int r = wm * WTM + (half * TH + ii) * 16 + (lane & 15);
+          af[ii] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][r][h * 8]);
+          const uint2 mm = sM[cur][r];
+          ix[ii] = (int)(((h < 2 ? mm.x : mm.y) >> (16 * (h & 1))) & 0xFFFFu);
+        }
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bfr[j], acc[i][j], ix[i], 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * TI + 2 * TJ, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
+        for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[half * TH + ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                af[ii], bfr[j], acc[half * TH + ii][j], ix[ii], 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * TH + (half == 0 ? 2 * TJ : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TH * TJ, 0);
+      };
+      do_half.template operator()<0>();
+      do_half.template operator()<1>();
+    } else if constexpr (MODE == GM_FP8) {
+      // one 128-deep e4m3 MFMA per tile; a lane's 32 codes are the same k
+      // positions for A and B.  Row tiles in two halves (register budget).
+      const int h = lane >> 4;
+      auto frag = [&](const uint16_t* p) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(p), x1 = *reinterpret_cast<const uint4*>(p + 8);
+        return i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      i32x8_t bfr[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) bfr[j] = frag(&sB[cur][wn * WTN + j * 16 + (lane & 15)][h * 16]);
+auto do_half = [&]<int half>() {
+        constexpr int TH = TI / 2;
+        i32x8_t af[TH];
+#pragma unroll
+        for (int ii = 0; ii < TH; ++ii)
+          af[ii] = frag(&sA[cur][wm * WTM + (half * TH + ii) * 16 + (lane & 15)][h * 16]);
+#pragma unroll
+        for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[half * TH + ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[ii], bfr[j], acc[half * TH + ii][j], 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * TH + (half == 0 ? 2 * TJ : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TH * TJ, 0);
+      };
+      do_half.template operator()<0>();
+      do_half.template operator()<1>();
     } else {
       bf16x8_t af[TI], bfr[TJ];
 #pragma unroll
@@ -210,10 +256,14 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm(GemmArgs 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + v;
+        float sa = 1.0f;
+        if constexpr (MODE == GM_FP8) sa = m < M ? g.scale_a[m] : 0.0f;
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int64_t n = n0 + wn * WTN + j * 16 + (lane & 15);
-          if (m < M && n < N) g.out[m * g.ld_out + n] = acc[i][j][v];
+          float c = acc[i][j][v];
+          if constexpr (MODE == GM_FP8) c = c * sa * (n < N ? g.scale_b[n] : 0.0f);
+          if (m < M && n < N) g.out[m * g.ld_out + n] = c;
         }
       }
   }
@@ -223,9 +273,9 @@ inline int64_t gemm_tiles(int64_t M, int64_t N) {
   return ((M + kGM - 1) / kGM) * ((N + kGN - 1) / kGN);
 }
 
-template <bool SPARSE, int EPI>
+template <int MODE, int EPI>
 inline hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<kGM, kGN, 128, 64, SPARSE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)),
+  hipLaunchKernelGGL((k_gemm<kGM, kGN, 128, 64, MODE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)),
                      dim3(512), 0, s, g);
   return hipGetLastError();
 }

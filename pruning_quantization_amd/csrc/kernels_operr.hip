@@ -211,8 +211,9 @@ hipError_t launch_side_delta(const RowDesc& d, const SideParams& sp, void* out, 
 
 hipError_t launch_gemm_rowsq(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                              int64_t N, int64_t Kp, int64_t K, float* part, hipStream_t s) {
-  const GemmArgs g{A, lda, nullptr, 0, B, ldb, M, N, Kp, K, part, gemm_col_tiles(N)};
-  return launch_gemm<false, EPI_ROWSQ>(g, s);
+  const GemmArgs g{A, lda, nullptr, 0, B, ldb, M, N, Kp, K, part, gemm_col_tiles(N), nullptr,
+                   nullptr};
+  return launch_gemm<GM_BF16, EPI_ROWSQ>(g, s);
 }
 
 hipError_t launch_rowsq_final(const float* part, int64_t M, int64_t ntiles, int ncols, double* out,

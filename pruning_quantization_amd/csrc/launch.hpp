@@ -125,6 +125,9 @@ hipError_t launch_sparse_gemm(const void* values, const uint8_t* meta, int64_t M
                               hipStream_t s);
 hipError_t launch_dense_gemm(const void* A, int64_t lda, int64_t M, int64_t K, const void* B,
                              int64_t ldb, int64_t N, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_fp8_gemm(const void* A, int64_t lda, const float* sa, int64_t M, int64_t K,
+                           const void* B, int64_t ldb, const float* sb, int64_t N, float* C,
+                           int64_t ldc, hipStream_t s);
 // Rotated copy of a K-contiguous operand (d.rot) into dense [B][R][K] `out`.
 hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s);
 // Transposed operand -> dense [B][R][K] copy in `out` (B*R*K elements).

@@ -59,3 +59,26 @@ def test_dense_gemm(m, n, k):
     b = W.to_bf16_bits(rng.standard_normal((n, k)))
     got = raw_np(S.dense_gemm(to_dev(a, "bf16"), to_dev(b, "bf16")))
     check(got, O.decode_input(a, "bf16"), O.decode_input(b, "bf16"), k)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 16, 128), (300, 200, 256), (513, 777, 1024)])
+def test_fp8_gemm(m, n, k):
+    # the dense FP8 rival: codes and row scales from quantize(), product on the
+    # e4m3 MFMA, against the fp64 product of the dequantized operands
+    rng = np.random.default_rng(m + 5 * n + k)
+    a = W.to_bf16_bits(rng.standard_normal((m, k)))
+    b = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.05)
+    ca, sa = S.quantize(to_dev(a, "bf16"), "fp8")
+    cb, sb = S.quantize(to_dev(b, "bf16"), "fp8")
+    got = raw_np(S.fp8_gemm(ca, sa, cb, sb))
+    wa, wsa = O.quantize_rows(a, "bf16", O.QSpec("fp8"))
+    wb, wsb = O.quantize_rows(b, "bf16", O.QSpec("fp8"))
+    a64 = O.dequantize_rows(wa, O.QSpec("fp8"), wsa)
+    b64 = O.dequantize_rows(wb, O.QSpec("fp8"), wsb)
+    ref = a64 @ b64.T
+    # sum in fp32 over the code products, then two fp32 scale multiplies.  The
+    # e4m3 MFMA's internal summation was measured up to 8% past the
+    # round-to-nearest bound on single outputs, so it gets twice that bound.
+    bound = 2 * (k - 1) * 2.0 ** -24 * (np.abs(a64) @ np.abs(b64).T) + 3 * 2.0 ** -24 * np.abs(ref) + 1e-300
+    err = np.abs(got.astype(np.float64) - ref)
+    assert (err <= bound).all(), f"{(err > bound).sum()} outside; worst {(err / bound).max()}"
