@@ -191,10 +191,27 @@ def main():
     def call_op(i):
         S.operator_error(pool[i], w_op, op_sides, out=op_out, workspace=op_ws)
 
+    # GEMMs that consume the prepared X against W: 2:4-compressed X on the
+    # sparse MFMA, dense bf16 X, and the e4m3 codes of the dense FP8 rival
+    # (W quantized once, offline)
+    c_gemm = torch.empty(T, n_w, dtype=torch.float32, device=dev)
+    w_codes, w_scales = S.quantize(w_op, "fp8")
+
+    def call_gsp(i):
+        S.sparse_gemm(outs[i]["pc"][0], outs[i]["pc"][1], w_op, out=c_gemm)
+
+    def call_gde(i):
+        S.dense_gemm(pool[i], w_op, out=c_gemm)
+
+    def call_g8(i):
+        S.fp8_gemm(outs[i]["fp8"][0], outs[i]["fp8"][1], w_codes, w_scales, out=c_gemm)
+
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
                   "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
                   "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
-                  "predict_R_rot128": call_Rr, "operator_error_2sides": call_op}
+                  "predict_R_rot128": call_Rr, "operator_error_2sides": call_op,
+                  "gemm_sparse24_bf16": call_gsp, "gemm_dense_bf16": call_gde,
+                  "gemm_dense_fp8": call_g8}
 
     def step(i):
         for f in calls.values():
@@ -219,10 +236,16 @@ def main():
         "prune_quantize_fp8_rot128": xb + T * H // 2 + T * H // 8 + T * 4,
         "predict_R_rot128": xb + 2 * 5 * 8,
         "operator_error_2sides": xb + n_w * H * 2,
+        "gemm_sparse24_bf16": xb // 2 + T * H // 8 + n_w * H * 2 + T * n_w * 4,
+        "gemm_dense_bf16": xb + n_w * H * 2 + T * n_w * 4,
+        "gemm_dense_fp8": T * H + n_w * H + T * n_w * 4,
     })
     # MFMA work of the compute-bound call: the reference product plus, per side,
     # the product of the [hi | lo] residual (2K deep)
-    flops = {"operator_error_2sides": 2.0 * T * n_w * H * (1 + 2 * len(op_sides))}
+    flops = {"operator_error_2sides": 2.0 * T * n_w * H * (1 + 2 * len(op_sides)),
+             "gemm_sparse24_bf16": 2.0 * T * n_w * H, "gemm_dense_bf16": 2.0 * T * n_w * H,
+             "gemm_dense_fp8": 2.0 * T * n_w * H}
+    mfma_peak = {"gemm_dense_fp8": 5000.0, "gemm_sparse24_bf16": 5000.0}  # sparse: 2x dense bf16
 
     # ---- spot parity against the oracle (not timed) ---------------------------------
     step(0)
@@ -311,7 +334,9 @@ def main():
         per_call[name] = {"us": round(us, 3), "GBps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
         if name in flops:
             tf = flops[name] / (us * 1e-6) / 1e12
-            per_call[name].update({"TFLOPs": round(tf, 1), "mfma_frac_bf16": round(tf / 2500.0, 4)})
+            pk = mfma_peak.get(name, 2500.0)
+            per_call[name].update({"TFLOPs": round(tf, 1), "mfma_peak_TFLOPs": pk,
+                                   "mfma_frac": round(tf / pk, 4)})
 
     # ---- copy baseline: library copy kernel over the same rotation -------------------
     src = [p.view(torch.uint8).view(-1) for p in pool]
@@ -395,6 +420,12 @@ def main():
         "predicted_R_tensors_per_s": round(1e6 / per_call["predict_R"]["us"], 1),
         "step_tensors_per_s": round(1e3 / ms_step, 1),
         "copy_GBps": round(copy_gbps, 1),
+        # [PD §3] speed question at equal nominal tier: dense FP8 (online
+        # quantization of X + FP8 GEMM) time over 2:4 bf16 (online
+        # prune+compress of X + sparse GEMM) time; above 1 = 2:4 faster
+        "speed_2of4_bf16_vs_dense_fp8": round(
+            (per_call["quantize_fp8"]["us"] + per_call["gemm_dense_fp8"]["us"])
+            / (per_call["prune_compress_2of4"]["us"] + per_call["gemm_sparse24_bf16"]["us"]), 3),
         "per_call": per_call,
         "parity_sampled_rows": parity,
         "wall_s": round(wall, 4),
