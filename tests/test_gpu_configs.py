@@ -183,3 +183,88 @@ def test_heavy_tailed_4x_tier():
         want = O.predict_R(sub, "bf16", [O.QSpec("fp8")] * 2,
                            [O.QSpec("mxfp4"), O.QSpec("nvfp4", tensor_amax=T)])
         rel_close(got[blk:blk + 1], want)
+
+
+# ---------------------------------------------------------------------------
+# Full-size checks of the rows beyond the fused path: the sparse FP4 operand
+# (pairwise 4:8 + NVFP4) on the heavy-tailed tier, the rotated activation,
+# the operator-level error and the GEMMs on the prepared operands
+# ---------------------------------------------------------------------------
+
+
+def test_heavy_sparse_fp4():
+    bits = W.student_t_x(7, 16384, 4096)
+    x = to_dev(bits, "bf16")
+    kv, _ = O.prune_compress_pairs48(bits, "bf16")              # whole-tensor kept maximum
+    Tk = float(np.max(np.abs(O.decode_input(kv, "bf16"))))
+    del kv
+    rows = sample_rows(16384, seed=17)
+    c, m, sc, ts = S.prune_quantize_pairs48(x, "nvfp4")
+    wc, wm, wsc, wts = O.prune_quantize_pairs48(bits[rows], "bf16", O.QSpec("nvfp4", tensor_amax=Tk))
+    assert raw_np(ts)[0] == wts
+    assert_same(raw_np(c)[rows], wc, "sparse fp4 codes")
+    assert_same(raw_np(m)[rows], wm, "sparse fp4 meta")
+    assert_same(raw_np(sc)[rows], wsc, "sparse fp4 scales")
+    got = raw_np(S.predict_R_pairs48(x, ["nvfp4"], ["nvfp4"], rows_per_block=128))
+    T = float(O.tensor_absmax(bits, "bf16"))
+    for blk in (0, 99):
+        sub = bits[blk * 128:(blk + 1) * 128]
+        want = O.predict_R(sub, "bf16", [O.QSpec("nvfp4", tensor_amax=Tk)],
+                           [O.QSpec("nvfp4", tensor_amax=T)], pattern="pairs4:8")
+        rel_close(got[blk:blk + 1], want)
+
+
+def test_act_rotated(act):
+    bits, x = act
+    assert O.rotation_exact(bits, "bf16", 128).all()
+    rot = O.rotate(bits, "bf16", 128)
+    c, m, s = S.prune_quantize_rot(x, 128, "fp8")
+    wc, wm, ws = O.prune_quantize(rot, "bf16", O.QSpec("fp8"))
+    assert_same(raw_np(c), wc, "rotated codes")
+    assert_same(raw_np(m), wm, "rotated meta")
+    assert_same(raw_np(s), ws, "rotated scales")
+    kept, dense = ["fp8", "fp8"], ["fp8", ("int", 8)]
+    got = raw_np(S.predict_R_rot(x, 128, kept, dense))
+    want = O.predict_R(rot, "bf16", [O.QSpec("fp8")] * 2, [O.QSpec("fp8"), O.QSpec("int", 8)])
+    rel_close(got, want)
+
+
+@pytest.fixture(scope="module")
+def weight():
+    bits = W.weight_w(2, 14336, 4096)
+    return bits, to_dev(bits, "bf16")
+
+
+def test_act_operator_error(act, weight):
+    bits, x = act
+    wbits, w = weight
+    sides = [("2:4", ("fp8", 0)), ("dense", ("fp8", 0)), ("dense", ("int", 8))]
+    got = raw_np(S.operator_error(x, w, sides))
+    rows = sample_rows(4096, k=12, seed=21)
+    want = O.operator_error(bits[rows], "bf16", wbits, "bf16",
+                            [O.Side(p, O.QSpec(*q)) for p, q in sides])
+    rel_close(got[rows], want, rtol=1e-3)
+
+
+def test_act_gemms(act, weight):
+    bits, x = act
+    wbits, w = weight
+    rows = sample_rows(4096, k=8, seed=22)
+    b64 = O.decode_input(wbits, "bf16")
+    k = 4096
+
+    def check(got, a64, bnd_scale=1.0, extra=0.0):
+        ref = a64 @ b64.T
+        bound = bnd_scale * (k - 1) * 2.0 ** -24 * (np.abs(a64) @ np.abs(b64).T) + extra * np.abs(ref) + 1e-300
+        assert (np.abs(got.astype(np.float64) - ref) <= bound).all()
+
+    vals, meta = S.prune_compress(x)
+    check(raw_np(S.sparse_gemm(vals, meta, w))[rows],
+          O.reconstruct(bits[rows], "bf16", O.Side("2:4", O.QSpec("none"))))
+    check(raw_np(S.dense_gemm(x, w))[rows], O.decode_input(bits[rows], "bf16"))
+    ca, sa = S.quantize(x, "fp8")
+    cb, sb = S.quantize(w, "fp8")
+    wcb, wsb = O.quantize_rows(wbits, "bf16", O.QSpec("fp8"))
+    b64 = O.dequantize_rows(wcb, O.QSpec("fp8"), wsb)
+    check(raw_np(S.fp8_gemm(ca, sa, cb, sb))[rows],
+          O.reconstruct(bits[rows], "bf16", O.Side("dense", O.QSpec("fp8"))), 2.0, 3 * 2.0 ** -24)
