@@ -239,6 +239,13 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
     }
   }
   if (n_nv > 1 || n_knv > 1) return SPARQ24_ERR_UNSUPPORTED;
+  for (int j = 0; j < nk; ++j) {
+    pl.p.kept_twin[j] = -1;
+    const int cf = pl.p.kept.fmt[j];
+    if (cf != CF_INT8 && cf != CF_INT16 && cf != CF_FP8) continue;
+    for (int i = 0; i < nd; ++i)
+      if (pl.p.dense.fmt[i] == cf && pl.p.dense.qmax[i] == pl.p.kept.qmax[j]) pl.p.kept_twin[j] = i;
+  }
   pl.p.kept.n = nk;
   pl.p.dense.n = nd;
   for (int i = 0; i < npairs; ++i) pl.f.dcol[i] += 2 + nk;
@@ -290,7 +297,7 @@ sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, Energ
   CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart,
                                     pl.rpb, &nparts, stream)));
   double* csum = (double*)(w + pl.off_csum);
-  if (pl.rpb >= pl.nrows)  // one block: reduce the per-team partials
+  if (pl.rpb >= pl.nrows)  // one block: reduce the per-workgroup partials
     return launched(launch_energy_finalize(rowpart, nparts, nparts, 1, pl.f, csum, out, stream));
   return launched(launch_energy_finalize(rowpart, pl.nrows, pl.rpb, pl.nblk, pl.f, csum, out, stream));
 }

@@ -1,8 +1,10 @@
 // Exhaustive check that gfx950's hardware conversions used by the kernels
-// (v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32 at scale 1, v_cvt_f32_fp8)
-// give exactly the codes of the exact integer encoders enc_e4m3 / enc_e2m1
-// (round to nearest even, saturating, sign copied) for every finite fp32
-// input, and that decoding every e4m3 code matches dec_e4m3.
+// (v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32 at scale 1, v_cvt_f32_fp8,
+// v_cvt_scalef32_pk_f32_fp4 at scale 1) give exactly the codes of the exact
+// integer encoders enc_e4m3 / enc_e2m1 (round to nearest even, saturating,
+// sign copied) for every finite fp32 input, that decoding every e4m3 code
+// matches dec_e4m3, and that decoding every byte of E2M1 pairs, from each
+// byte position of a dword, matches dec_e2m1.
 // Every store goes to cnt[0..4] or slots[0..63], guarded by the slot index;
 // the grid-stride loop is bounded by 2^32.  Exit status 0 = no mismatch.
 #include <hip/hip_runtime.h>
@@ -55,18 +57,27 @@ __global__ void probe(unsigned long long* cnt, unsigned* slots) {
     const float hw = __builtin_amdgcn_cvt_f32_fp8((int)g, 0);
     if (__float_as_uint(hw) != __float_as_uint(dec_e4m3((unsigned)g))) atomicAdd(&cnt[4], 1ull);
   }
+  if (g < 256) {
+    const unsigned lo = dec_e2m1_bits((unsigned)g & 15u), hi = dec_e2m1_bits((unsigned)g >> 4);
+    const unsigned w = (unsigned)g * 0x01010101u;  // the byte in all four positions
+    const f32x2 d0 = dec_e2m1_hw_x2<0>(w), d1 = dec_e2m1_hw_x2<1>(w);
+    const f32x2 d2 = dec_e2m1_hw_x2<2>(w), d3 = dec_e2m1_hw_x2<3>(w);
+    const f32x2 d[4] = {d0, d1, d2, d3};
+    for (int k = 0; k < 4; ++k)
+      if (__float_as_uint(d[k].x) != lo || __float_as_uint(d[k].y) != hi) atomicAdd(&cnt[5], 1ull);
+  }
 }
 
 int main() {
   unsigned long long* cnt;
   unsigned* slots;
-  if (hipMalloc(&cnt, 5 * sizeof(unsigned long long)) != hipSuccess) return 1;
+  if (hipMalloc(&cnt, 6 * sizeof(unsigned long long)) != hipSuccess) return 1;
   if (hipMalloc(&slots, 64 * sizeof(unsigned)) != hipSuccess) return 1;
-  (void)hipMemset(cnt, 0, 5 * sizeof(unsigned long long));
+  (void)hipMemset(cnt, 0, 6 * sizeof(unsigned long long));
   (void)hipMemset(slots, 0, 64 * sizeof(unsigned));
   hipLaunchKernelGGL(probe, dim3(65536), dim3(256), 0, 0, cnt, slots);
   if (hipDeviceSynchronize() != hipSuccess) { printf("kernel failed\n"); return 2; }
-  unsigned long long h[5];
+  unsigned long long h[6];
   unsigned s[64];
   (void)hipMemcpy(h, cnt, sizeof(h), hipMemcpyDeviceToHost);
   (void)hipMemcpy(s, slots, sizeof(s), hipMemcpyDeviceToHost);
@@ -80,5 +91,6 @@ int main() {
     }
   }
   printf("e4m3 decode: %llu mismatches\n", h[4]);
-  return (h[0] | h[1] | h[2] | h[3] | h[4]) ? 3 : 0;
+  printf("e2m1 pair decode, scale 1, byte positions 0..3: %llu mismatches\n", h[5]);
+  return (h[0] | h[1] | h[2] | h[3] | h[4] | h[5]) ? 3 : 0;
 }

@@ -425,6 +425,19 @@ __device__ inline float dec_e2m1(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
+// Bit pattern of dec_e2m1(c) (for the conversion check).
+__device__ inline uint32_t dec_e2m1_bits(uint32_t c) { return __float_as_uint(dec_e2m1(c)); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Values of the two E2M1 codes in byte SEL of w (low nibble -> .x), with
+// gfx950's v_cvt_scalef32_pk_f32_fp4 at scale 1; equal to dec_e2m1 on every
+// byte and byte position (checked exhaustively by check_converts).
+template <int SEL>
+__device__ inline f32x2 dec_e2m1_hw_x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
 // Eight E2M1 codes packed two per byte (element 2j in the low nibble of byte
 // j) with gfx950's v_cvt_scalef32_pk_fp4_f32 at scale 1; over every finite
 // fp32 it returns exactly enc_e2m1 (RNE, saturating at 6, sign copied).
@@ -636,6 +649,14 @@ __device__ inline const char* row_ptr(const RowGeom& g, int64_t row) {
   return g.x + b * g.bs + (row - b * g.R) * g.rs;
 }
 
+// Branch-free by default: every lane issues all UPL loads (a unit past the
+// row's end or a row past the last re-reads unit 0 of the operand, which
+// always exists when a kernel runs) and zeroes those units afterwards.  With
+// no load under a branch the compiler waits for each unit's load just before
+// its first use, so work on early units overlaps the arrival of later ones.
+#ifndef SPARQ24_LOAD_BRANCHFREE
+#define SPARQ24_LOAD_BRANCHFREE 1
+#endif
 template <class DT, int TEAM, int UPL>
 __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t row, int t) {
   const bool act = row < g.nrows;
@@ -643,8 +664,14 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
     const int64_t i = (int64_t)j * TEAM + t;
+#if SPARQ24_LOAD_BRANCHFREE
+    const bool ok = act && i < g.nunits;
+    load_unit(u[j], ok ? xr + i * (8 * DT::ESIZE) : g.x);
+    if (!ok) zero_unit(u[j]);
+#else
     if (act && i < g.nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
     else zero_unit(u[j]);
+#endif
   }
 }
 

@@ -36,12 +36,6 @@ __device__ inline uint32_t unit_absmax_e(const Unit<DT>& u) {
   return m;
 }
 
-// squared fp32 residual accumulated in fp64
-__device__ inline void acc_err(double& acc, float xhat_unit, float scale, float v) {
-  const float e = __builtin_fmaf(xhat_unit, scale, -v);  // one rounding of code*s - x
-  acc = __builtin_fma((double)e, (double)e, acc);
-}
-
 // ---------------------------------------------------------------------------
 // bf16 + magnitude fast path.  The top-2 network already orders each group's
 // keys; a key's high half is the element's bf16 magnitude, i.e. the fp32 bit
@@ -92,33 +86,88 @@ __device__ inline void sel16_mags(uint32_t w0, uint32_t w1, float* kept2, float*
   top = t1;
 }
 
-// Sum of squared residuals of N magnitudes under a per-row scale (pairwise fp32).
+// Squared residual energy of N magnitudes (N = 4 or 8) under a per-row scale
+// (s, inv) taken from a row maximum that no magnitude exceeds.  Each residual
+// is one fp32 rounding of code*s - v; the squares go into two fp32 chains of
+// fused multiply-adds that are added at the end (at most N/2 + 1 roundings
+// after the residual's, < 3.6e-7 relative for N = 8).
 template <int N>
-__device__ inline float sq_err_row(int fmt, float s, float inv, float qmax, const float* v) {
-  float e[N];
-  if (fmt == CF_FP8) {
+__device__ inline float mag_sq_err_fp8(float s, float inv, const float* v) {
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < N; q += 4) {
-      const uint32_t w = enc_e4m3_x4(v[q] * inv, v[q + 1] * inv, v[q + 2] * inv, v[q + 3] * inv);
-      e[q + 0] = __builtin_fmaf(dec_e4m3_hw<0>(w), s, -v[q + 0]);
-      e[q + 1] = __builtin_fmaf(dec_e4m3_hw<1>(w), s, -v[q + 1]);
-      e[q + 2] = __builtin_fmaf(dec_e4m3_hw<2>(w), s, -v[q + 2]);
-      e[q + 3] = __builtin_fmaf(dec_e4m3_hw<3>(w), s, -v[q + 3]);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const float c = __builtin_rintf(__builtin_fminf(v[q] * inv, qmax));
-      e[q] = __builtin_fmaf(c, s, -v[q]);
-    }
+  for (int q = 0; q < N; q += 4) {
+    const uint32_t w = enc_e4m3_x4(v[q] * inv, v[q + 1] * inv, v[q + 2] * inv, v[q + 3] * inv);
+    const float e0 = __builtin_fmaf(dec_e4m3_hw<0>(w), s, -v[q + 0]);
+    const float e1 = __builtin_fmaf(dec_e4m3_hw<1>(w), s, -v[q + 1]);
+    const float e2 = __builtin_fmaf(dec_e4m3_hw<2>(w), s, -v[q + 2]);
+    const float e3 = __builtin_fmaf(dec_e4m3_hw<3>(w), s, -v[q + 3]);
+    a0 = __builtin_fmaf(e0, e0, a0);
+    a1 = __builtin_fmaf(e1, e1, a1);
+    a0 = __builtin_fmaf(e2, e2, a0);
+    a1 = __builtin_fmaf(e3, e3, a1);
   }
+  return a0 + a1;
+}
+
+// Same for symmetric INT.  v <= amax and inv = fp32(qmax / amax) give
+// v * inv <= qmax * (1 + 2^-24)^2 < qmax + 1/2, so round-to-nearest-even
+// never leaves [0, qmax] and the clamp of the encoder is a no-op here.
+template <int N>
+__device__ inline float mag_sq_err_int(float s, float inv, const float* v) {
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-  for (int q = 0; q < N; ++q) e[q] = e[q] * e[q];
+  for (int q = 0; q < N; q += 2) {
+    const float e0 = __builtin_fmaf(__builtin_rintf(v[q] * inv), s, -v[q]);
+    const float e1 = __builtin_fmaf(__builtin_rintf(v[q + 1] * inv), s, -v[q + 1]);
+    a0 = __builtin_fmaf(e0, e0, a0);
+    a1 = __builtin_fmaf(e1, e1, a1);
+  }
+  return a0 + a1;
+}
+
+// fp32 sum of the squares of 8 residuals: four chains of two fused
+// multiply-adds, added pairwise (4 roundings after the residuals').
+__device__ inline float sq_sum8(const float* e) {
+  float a[4];
 #pragma unroll
-  for (int w = 1; w < N; w *= 2)
+  for (int k = 0; k < 4; ++k) a[k] = __builtin_fmaf(e[k + 4], e[k + 4], e[k] * e[k]);
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// Residuals of 8 values whose E2M1 codes are packed in pk (value 2j in the
+// low nibble of byte j), decoded in hardware and scaled by m then s
+// (x_hat = code * m * s; code * m is exact for the callers' m).
+__device__ inline void e2m1_residuals8(uint32_t pk, float m, float s, const float* v, float* e) {
+  const f32x2 c[4] = {dec_e2m1_hw_x2<0>(pk), dec_e2m1_hw_x2<1>(pk), dec_e2m1_hw_x2<2>(pk),
+                      dec_e2m1_hw_x2<3>(pk)};
 #pragma unroll
-    for (int q = 0; q + w < N; q += 2 * w) e[q] += e[q + w];
-  return e[0];
+  for (int k = 0; k < 4; ++k) {
+    e[2 * k] = __builtin_fmaf(c[k].x * m, s, -v[2 * k]);
+    e[2 * k + 1] = __builtin_fmaf(c[k].y * m, s, -v[2 * k + 1]);
+  }
+}
+
+// Squared residual energy of the 8 values of one unit under MXFP4 with block
+// exponent ex (x_hat = code * 2^ex).
+__device__ inline float unit_sq_err_mx8(const float* v, int ex) {
+  float y[8], e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = __builtin_ldexpf(v[k], -ex);
+  e2m1_residuals8(enc_e2m1_x8(y), 1.0f, __builtin_ldexpf(1.0f, ex), v, e);
+  return sq_sum8(e);
+}
+
+// Same under NVFP4: bm = fp32 bits of the 16-value block's absolute maximum,
+// s_t / gnv the tensor scale and block-scale multiplier.
+__device__ inline float unit_sq_err_nv8(const float* v, uint32_t bm, float s_t, float gnv) {
+  const float bval = dec_e4m3(enc_e4m3(__uint_as_float(bm) * gnv));
+  const float d = bval * s_t;
+  const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+  float y[8], e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = v[k] * inv;
+  e2m1_residuals8(enc_e2m1_x8(y), bval, s_t, v, e);
+  return sq_sum8(e);
 }
 
 // Error energy of 4 kept values (one unit) under a block format whose block
@@ -138,27 +187,116 @@ __device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
   w = (uint32_t)__shfl_xor((int)am, 2, 64);
   am = am > w ? am : w;
   float r[4];
+  uint32_t pk;
+  float m, sc;
   if constexpr (NV) {
-    const uint32_t bc = enc_e4m3(__uint_as_float(am) * gnv);
-    const float bval = dec_e4m3(bc);
+    const float bval = dec_e4m3(enc_e4m3(__uint_as_float(am) * gnv));
     const float d = bval * s_t;
     const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-    const uint32_t pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(dec_e2m1((pk >> (4 * e)) & 0xFu) * bval, s_t, -v[e]);
+    pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    m = bval;
+    sc = s_t;
   } else {
     w = (uint32_t)__shfl_xor((int)am, 4, 64);
     am = am > w ? am : w;
     const int ex = mx_exponent(am);
-    const float X = __builtin_ldexpf(1.0f, ex);
-    const uint32_t pk = enc_e2m1_x4(__builtin_ldexpf(v[0], -ex), __builtin_ldexpf(v[1], -ex),
-                                    __builtin_ldexpf(v[2], -ex), __builtin_ldexpf(v[3], -ex));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(dec_e2m1((pk >> (4 * e)) & 0xFu), X, -v[e]);
+    pk = enc_e2m1_x4(__builtin_ldexpf(v[0], -ex), __builtin_ldexpf(v[1], -ex),
+                     __builtin_ldexpf(v[2], -ex), __builtin_ldexpf(v[3], -ex));
+    m = 1.0f;
+    sc = __builtin_ldexpf(1.0f, ex);
   }
+  const f32x2 c0 = dec_e2m1_hw_x2<0>(pk), c1 = dec_e2m1_hw_x2<1>(pk);
+  r[0] = __builtin_fmaf(c0.x * m, sc, -v[0]);
+  r[1] = __builtin_fmaf(c0.y * m, sc, -v[1]);
+  r[2] = __builtin_fmaf(c1.x * m, sc, -v[2]);
+  r[3] = __builtin_fmaf(c1.y * m, sc, -v[3]);
+  return __builtin_fmaf(r[0], r[0], r[2] * r[2]) + __builtin_fmaf(r[1], r[1], r[3] * r[3]);
+}
+
+// Reduce rows r0..r1-1 of every partial column (rowpart[col][row], nrows per
+// column) in a fixed order and write block blk's outputs: mode 0 = Sx2,
+// Sdropped, kept error, dense error; mode 1 = E_prune, E_qkept, E_2:4,
+// E_dense, R per pair.  Every thread of the workgroup must call this.
+__device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t nrows,
+                                     int64_t r0, int64_t r1, const FinalizeParams& f,
+                                     double* __restrict__ out, int64_t blk) {
+  constexpr int CB = 8;  // columns reduced together: CB independent loads per row
+  __shared__ double sh[CB][kBlock];
+  __shared__ double sb[2 + 2 * kMaxQ];
+  for (int cb = 0; cb < f.ncols; cb += CB) {
+    double a[CB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = r[e] * r[e];
-  return (r[0] + r[1]) + (r[2] + r[3]);
+    for (int c = 0; c < CB; ++c) a[c] = 0.0;
+    // branch-free body: columns past the end re-read the last one (ignored),
+    // so all CB loads of a row can be in flight together
+    const double* colp[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) colp[c] = rowpart + (int64_t)((cb + c) < f.ncols ? cb + c : f.ncols - 1) * nrows;
+    // RU rows per thread per round, all loads issued before the adds; rows
+    // past the end add +0.0 (partials are sums of squares, never -0.0), so
+    // the order of additions per thread is rows t, t + kBlock, ... as ever
+    constexpr int RU = 4;
+    for (int64_t rb = r0 + threadIdx.x; rb < r1; rb += RU * kBlock) {
+      double v[RU][CB];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const int64_t r = rb + u * kBlock;
+        const int64_t rc = r < r1 ? r : r0;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) v[u][c] = colp[c][rc];
+        if (r >= r1)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) v[u][c] = 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) a[c] += v[u][c];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] = a[c];
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] += sh[c][threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x < CB && cb + (int)threadIdx.x < f.ncols) sb[cb + threadIdx.x] = sh[threadIdx.x][0];
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  if (f.mode == 0) {
+    double* o = out + blk * 4;
+    o[0] = sb[0];
+    o[1] = sb[1];
+    o[2] = sb[f.kcol[0]];
+    o[3] = sb[f.dcol[0]];
+  } else {
+    const double tot = sb[0];
+    for (int p = 0; p < f.npairs; ++p) {
+      double* o = out + (blk * f.npairs + p) * 5;
+      const double ep = sb[1] / tot;
+      const double eq = sb[f.kcol[p]] / tot;
+      const double e24 = ep + eq;
+      const double ed = sb[f.dcol[p]] / tot;
+      o[0] = ep;
+      o[1] = eq;
+      o[2] = e24;
+      o[3] = ed;
+      o[4] = __builtin_sqrt(e24 / ed);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restrict__ rowpart,
+                                                          int64_t nrows, int64_t rpb,
+                                                          FinalizeParams f,
+                                                          double* __restrict__ out) {
+  const int64_t blk = blockIdx.x;
+  const int64_t r0 = blk * rpb;
+  const int64_t r1 = (r0 + rpb) < nrows ? (r0 + rpb) : nrows;
+  finalize_rows(rowpart, nrows, r0, r1, f, out, blk);
 }
 
 // Row partial sums go either to rowpart[col][row] (blocked reductions) or,
@@ -214,8 +352,17 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #endif
 }
 
+// 4096-element rows without rotation fit 120 VGPRs without spilling: four
+// waves per SIMD keep a whole 4096-row operand resident in one pass.
+#ifndef SPARQ24_E_WAVES
+#define SPARQ24_E_WAVES 4
+#endif
 template <int TEAM, int UPL, bool ROT>
-SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
+constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT) ? SPARQ24_E_WAVES : 1;
+
+template <int TEAM, int UPL, bool ROT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT>)))
+void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
   __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
@@ -266,25 +413,41 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
       sink_put<TEAM>(sink, lacc, row, 1, drop);
     }
     const float amax = __uint_as_float(am & 0xFFFF0000u);  // kept max == row max
+    // kept-side quantizers; a row format with a dense twin (same format and
+    // qmax) is evaluated by the twin's pass below, since both take their
+    // scale from the same maximum and quantize each kept value identically
     for (int q = 0; q < p.kept.n; ++q) {
+      if (p.kept_twin[q] >= 0) continue;
       pin_packed<UPL>(pk);
       const int fmt = p.kept.fmt[q];
-      const float qmax = p.kept.qmax[q];
       double acc = 0.0;
-      if (fmt == CF_MX || fmt == CF_NV) {
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          acc += (double)(fmt == CF_NV ? kept_block_err4<true>(v, ks_t, kgnv)
-                                       : kept_block_err4<false>(v, 0.f, 0.f));
-        }
-      } else if (fmt != CF_NONE) {
+      if (fmt == CF_FP8 || fmt == CF_INT8 || fmt == CF_INT16) {
         float s, inv;
-        row_scale(amax, qmax, s, inv);
+        row_scale(amax, p.kept.qmax[q], s, inv);
+        if (fmt == CF_FP8) {
+#pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            acc += (double)mag_sq_err_fp8<4>(s, inv, v);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            acc += (double)mag_sq_err_int<4>(s, inv, v);
+          }
+        }
+      } else if (fmt == CF_NV) {
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
           const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          acc += (double)sq_err_row<4>(fmt, s, inv, qmax, v);
+          acc += (double)kept_block_err4<true>(v, ks_t, kgnv);
+        }
+      } else if (fmt == CF_MX) {
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+          acc += (double)kept_block_err4<false>(v, 0.f, 0.f);
         }
       }
       acc = team_sum_f64<TEAM>(acc, redd);
@@ -293,16 +456,37 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
     for (int q = 0; q < p.dense.n; ++q) {
       pin_packed<UPL>(pk);
       const int fmt = p.dense.fmt[q];
-      const float qmax = p.dense.qmax[q];
       double acc = 0.0;
       if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
+        int twin = -1;
+        for (int k = 0; k < p.kept.n; ++k)
+          if (p.kept_twin[k] == q) twin = k;
         float s, inv;
-        row_scale(amax, qmax, s, inv);
+        row_scale(amax, p.dense.qmax[q], s, inv);
+        double acck = 0.0;  // kept positions; acc holds the dropped ones
+        if (fmt == CF_FP8) {
 #pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
-                              mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-          acc += (double)sq_err_row<8>(fmt, s, inv, qmax, v);
+          for (int j = 0; j < UPL; ++j) {
+            const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+            acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
+            acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+            acck += (double)mag_sq_err_int<4>(s, inv, vk);
+            acc += (double)mag_sq_err_int<4>(s, inv, vd);
+          }
+        }
+        if (twin >= 0) {
+          acck = team_sum_f64<TEAM>(acck, redd);
+          acc = team_sum_f64<TEAM>(acc, redd) + acck;
+          if (writer) sink_put<TEAM>(sink, lacc, row, 2 + twin, acck);
+        } else {
+          acc = team_sum_f64<TEAM>(acc + acck, redd);
         }
       } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
@@ -313,41 +497,18 @@ SPARQ24_ROW_KERNEL void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, Partial
           uint32_t bm = (kh > kl ? kh : kl) << 16;  // fp32 bits of the unit's |x| max
           uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
           bm = bm > w ? bm : w;
-          float e[8];
           const float vj[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
                                mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
           if (fmt == CF_MX) {
             w = (uint32_t)__shfl_xor((int)bm, 2, 64);
             bm = bm > w ? bm : w;
-            const int ex = mx_exponent(bm);
-            const float X = __builtin_ldexpf(1.0f, ex);
-            float y[8];
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) y[q2] = __builtin_ldexpf(vj[q2], -ex);
-            const uint32_t pk = enc_e2m1_x8(y);
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2)
-              e[q2] = __builtin_fmaf(dec_e2m1((pk >> (4 * q2)) & 0xFu), X, -vj[q2]);
+            acc += (double)unit_sq_err_mx8(vj, mx_exponent(bm));
           } else {
-            const uint32_t bc = enc_e4m3(__uint_as_float(bm) * gnv);
-            const float bval = dec_e4m3(bc);
-            const float d = bval * s_t;
-            const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-            float y[8];
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) y[q2] = vj[q2] * inv;
-            const uint32_t pk = enc_e2m1_x8(y);
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2)
-              e[q2] = __builtin_fmaf(dec_e2m1((pk >> (4 * q2)) & 0xFu) * bval, s_t, -vj[q2]);
+            acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv);
           }
-#pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) e[q2] = e[q2] * e[q2];
-          const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-          acc += (double)s8;
         }
+        acc = team_sum_f64<TEAM>(acc, redd);
       }
-      acc = team_sum_f64<TEAM>(acc, redd);
       if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + q, acc);
     }
   });
@@ -423,10 +584,10 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     }
     const float famk = DT::to_f32(amk), famd = DT::to_f32(amd);
 
-    // kept-side quantizers: per-row scale from the kept maximum
+    // kept-side quantizers: per-row scale from the kept maximum.  Every
+    // quantizer here is symmetric in sign, so residuals are taken on |x|.
     for (int q = 0; q < p.kept.n; ++q) {
       const int fmt = p.kept.fmt[q];
-      const float qmax = p.kept.qmax[q];
       double acc = 0.0;
       if (fmt == CF_MX || fmt == CF_NV) {
         // kept values of a unit in position order; dropped ones are not
@@ -440,19 +601,24 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
         }
       } else if (fmt != CF_NONE) {
         float s, inv;
-        row_scale(famk, qmax, s, inv);
+        row_scale(famk, p.kept.qmax[q], s, inv);
+        if (fmt == CF_FP8) {
 #pragma unroll
-        for (int j = 0; j < UPL; ++j)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            // all 8 elements are evaluated; dropped ones contribute zero
-            float v[4], c[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = ((km[j] >> (4 * h + e)) & 1u) ? u[j].f(4 * h + e) : 0.0f;
-            qdq_row4(fmt, inv, qmax, v, c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
+          for (int j = 0; j < UPL; ++j) {
+            const Kept<DT> kp = p.pairs48 ? gather_pairs48(u[j], mbs[j]) : gather_kept(u[j], mbs[j]);
+            const float v[4] = {__builtin_fabsf(kp.f(0)), __builtin_fabsf(kp.f(1)),
+                                __builtin_fabsf(kp.f(2)), __builtin_fabsf(kp.f(3))};
+            acc += (double)mag_sq_err_fp8<4>(s, inv, v);
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const Kept<DT> kp = p.pairs48 ? gather_pairs48(u[j], mbs[j]) : gather_kept(u[j], mbs[j]);
+            const float v[4] = {__builtin_fabsf(kp.f(0)), __builtin_fabsf(kp.f(1)),
+                                __builtin_fabsf(kp.f(2)), __builtin_fabsf(kp.f(3))};
+            acc += (double)mag_sq_err_int<4>(s, inv, v);
+          }
+        }
       }
       acc = team_sum_f64<TEAM>(acc, redd);
       if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
@@ -461,51 +627,42 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     // dense quantizers
     for (int q = 0; q < p.dense.n; ++q) {
       const int fmt = p.dense.fmt[q];
-      const float qmax = p.dense.qmax[q];
       double acc = 0.0;
       if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
         float s, inv;
-        row_scale(famd, qmax, s, inv);
+        row_scale(famd, p.dense.qmax[q], s, inv);
+        if (fmt == CF_FP8) {
 #pragma unroll
-        for (int j = 0; j < UPL; ++j)
+          for (int j = 0; j < UPL; ++j) {
+            float v[8];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float v[4], c[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = u[j].f(4 * h + e);
-            qdq_row4(fmt, inv, qmax, v, c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc_err(acc, c[e], s, v[e]);
+            for (int e = 0; e < 8; ++e) v[e] = __builtin_fabsf(u[j].f(e));
+            acc += (double)mag_sq_err_fp8<8>(s, inv, v);
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = __builtin_fabsf(u[j].f(e));
+            acc += (double)mag_sq_err_int<8>(s, inv, v);
+          }
+        }
       } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
           uint32_t am = __float_as_uint(DT::to_f32(unit_absmax_e(u[j])));
           uint32_t w = (uint32_t)__shfl_xor((int)am, 1, 64);
           am = am > w ? am : w;
-          float y[8], v[8];
+          float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = u[j].f(e);
           if (fmt == CF_MX) {
             w = (uint32_t)__shfl_xor((int)am, 2, 64);
             am = am > w ? am : w;
-            const int ex = mx_exponent(am);
-            const float X = __builtin_ldexpf(1.0f, ex);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(v[e], -ex);
-            const uint32_t pk = enc_e2m1_x8(y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc_err(acc, dec_e2m1((pk >> (4 * e)) & 0xFu), X, v[e]);
+            acc += (double)unit_sq_err_mx8(v, mx_exponent(am));
           } else {
-            const uint32_t bc = enc_e4m3(__uint_as_float(am) * gnv);
-            const float bval = dec_e4m3(bc);
-            const float d = bval * s_t;
-            const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = v[e] * inv;
-            const uint32_t pk = enc_e2m1_x8(y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc_err(acc, dec_e2m1((pk >> (4 * e)) & 0xFu) * bval, s_t, v[e]);
+            acc += (double)unit_sq_err_nv8(v, am, s_t, gnv);
           }
         }
       }
@@ -580,82 +737,6 @@ __global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restr
 
 // One-kernel finalize when every block of rows is a single chunk: workgroup
 // b sums each column over its rows (fixed order) and forms the outputs.
-__global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restrict__ rowpart,
-                                                          int64_t nrows, int64_t rpb,
-                                                          FinalizeParams f,
-                                                          double* __restrict__ out) {
-  constexpr int CB = 8;  // columns reduced together: CB independent loads per row
-  __shared__ double sh[CB][kBlock];
-  __shared__ double sb[2 + 2 * kMaxQ];
-  const int64_t blk = blockIdx.x;
-  const int64_t r0 = blk * rpb;
-  const int64_t r1 = (r0 + rpb) < nrows ? (r0 + rpb) : nrows;
-  for (int cb = 0; cb < f.ncols; cb += CB) {
-    double a[CB];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) a[c] = 0.0;
-    // branch-free body: columns past the end re-read the last one (ignored),
-    // so all CB loads of a row can be in flight together
-    const double* colp[CB];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) colp[c] = rowpart + (int64_t)((cb + c) < f.ncols ? cb + c : f.ncols - 1) * nrows;
-    // RU rows per thread per round, all loads issued before the adds; rows
-    // past the end add +0.0 (partials are sums of squares, never -0.0), so
-    // the order of additions per thread is rows t, t + kBlock, ... as ever
-    constexpr int RU = 4;
-    for (int64_t rb = r0 + threadIdx.x; rb < r1; rb += RU * kBlock) {
-      double v[RU][CB];
-#pragma unroll
-      for (int u = 0; u < RU; ++u) {
-        const int64_t r = rb + u * kBlock;
-        const int64_t rc = r < r1 ? r : r0;
-#pragma unroll
-        for (int c = 0; c < CB; ++c) v[u][c] = colp[c][rc];
-        if (r >= r1)
-#pragma unroll
-          for (int c = 0; c < CB; ++c) v[u][c] = 0.0;
-      }
-#pragma unroll
-      for (int u = 0; u < RU; ++u)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) a[c] += v[u][c];
-    }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] = a[c];
-    __syncthreads();
-    for (int w = kBlock / 2; w > 0; w >>= 1) {
-      if ((int)threadIdx.x < w)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] += sh[c][threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x < CB && cb + (int)threadIdx.x < f.ncols) sb[cb + threadIdx.x] = sh[threadIdx.x][0];
-    __syncthreads();
-  }
-  if (threadIdx.x != 0) return;
-  if (f.mode == 0) {
-    double* o = out + blk * 4;
-    o[0] = sb[0];
-    o[1] = sb[1];
-    o[2] = sb[f.kcol[0]];
-    o[3] = sb[f.dcol[0]];
-  } else {
-    const double tot = sb[0];
-    for (int p = 0; p < f.npairs; ++p) {
-      double* o = out + (blk * f.npairs + p) * 5;
-      const double ep = sb[1] / tot;
-      const double eq = sb[f.kcol[p]] / tot;
-      const double e24 = ep + eq;
-      const double ed = sb[f.dcol[p]] / tot;
-      o[0] = ep;
-      o[1] = eq;
-      o[2] = e24;
-      o[3] = ed;
-      o[4] = __builtin_sqrt(e24 / ed);
-    }
-  }
-}
-
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               const EnergyParams& p, double* rowpart, int64_t rows_per_block,
                               int64_t* nparts, hipStream_t s) {

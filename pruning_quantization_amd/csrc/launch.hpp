@@ -54,6 +54,11 @@ struct QList {
 struct EnergyParams {
   QList kept, dense;
   int pairs48;                 // 1: pairwise 4:8 selection instead of 2:4
+  // For each kept quantizer, the dense quantizer with the same row format and
+  // qmax (INT/FP8), or -1.  Only the bf16 magnitude 2:4 kernel uses it: there
+  // the kept maximum is the row maximum, so the twin's codes on the kept
+  // positions are the kept-side codes.
+  int kept_twin[kMaxQ];
   const float* nv_tamax;       // device T for NVFP4 (or null -> reduce partials)
   const uint32_t* nv_partials; // fp32 bit patterns of partial maxima
   int n_partials;

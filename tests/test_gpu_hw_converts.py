@@ -22,4 +22,4 @@ def test_hw_conversions_match_exact_encoders():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=100)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count(": 0 mismatches") == 5
+    assert r.stdout.count(": 0 mismatches") == 6
