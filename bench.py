@@ -206,12 +206,35 @@ def main():
     def call_g8(i):
         S.fp8_gemm(outs[i]["fp8"][0], outs[i]["fp8"][1], w_codes, w_scales, out=c_gemm)
 
+    # predicted R of the other two scoring workloads (one tensor each, not
+    # rotated: both calls are VALU-bound): the MLP weight W with Wanda 2:4
+    # (norms of X's channels) over the equal-bits sweep 2:4+INT-2m vs dense
+    # INT-(m+1), m = 2..8; and the heavy-tailed 4x-tier activation, 2:4+FP8 vs
+    # MXFP4 and NVFP4 per block of 128 rows
+    norms = S.col_l2norm(x0)
+    sweep_kept = [("int", 2 * m) for m in range(2, 9)]
+    sweep_dense = [("int", m + 1) for m in range(2, 9)]
+    r_sweep = torch.empty(1, len(sweep_kept), 5, dtype=torch.float64, device=dev)
+    n_h = 16384
+    x_heavy = torch.from_numpy(W.student_t_x(a.seed + 2, n_h, H).view(np.int16)).view(torch.bfloat16).to(dev)
+    r_heavy = torch.empty(n_h // 128, 2, 5, dtype=torch.float64, device=dev)
+    ws_big = torch.empty(8 << 20, dtype=torch.uint8, device=dev)
+
+    def call_Rw(i):
+        S.predict_R(w_op, sweep_kept, sweep_dense, score="wanda", col_norm=norms, out=r_sweep,
+                    workspace=ws_big)
+
+    def call_Rh(i):
+        S.predict_R(x_heavy, ["fp8", "fp8"], ["mxfp4", "nvfp4"], rows_per_block=128, out=r_heavy,
+                    workspace=ws_big)
+
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
                   "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
                   "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
                   "predict_R_rot128": call_Rr, "operator_error_2sides": call_op,
                   "gemm_sparse24_bf16": call_gsp, "gemm_dense_bf16": call_gde,
-                  "gemm_dense_fp8": call_g8}
+                  "gemm_dense_fp8": call_g8, "predict_R_wanda_sweep_W": call_Rw,
+                  "predict_R_heavy_blocks128": call_Rh}
 
     def step(i):
         for f in calls.values():
@@ -239,6 +262,9 @@ def main():
         "gemm_sparse24_bf16": xb // 2 + T * H // 8 + n_w * H * 2 + T * n_w * 4,
         "gemm_dense_bf16": xb + n_w * H * 2 + T * n_w * 4,
         "gemm_dense_fp8": T * H + n_w * H + T * n_w * 4,
+        "predict_R_wanda_sweep_W": n_w * H * 2 + H * 4 + len(sweep_kept) * 5 * 8,
+        # one read of X (the NVFP4 tensor-maximum pass reads it a second time)
+        "predict_R_heavy_blocks128": n_h * H * 2 + (n_h // 128) * 2 * 5 * 8,
     })
     # MFMA work of the compute-bound call: the reference product plus, per side,
     # the product of the [hi | lo] residual (2K deep)
@@ -418,6 +444,12 @@ def main():
         "fused_prune_quant_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
         "fused_prune_quant_pct_copy": round(100 * achieved / copy_gbps, 2),
         "predicted_R_tensors_per_s": round(1e6 / per_call["predict_R"]["us"], 1),
+        # the weight W [14336, 4096] with all 7 equal-bits pairs; the heavy-tailed
+        # X [16384, 4096] with all 128 row blocks x 2 pairs
+        "predicted_R_wanda_sweep_W_tensors_per_s": round(
+            1e6 / per_call["predict_R_wanda_sweep_W"]["us"], 1),
+        "predicted_R_heavy_blocks128_tensors_per_s": round(
+            1e6 / per_call["predict_R_heavy_blocks128"]["us"], 1),
         "step_tensors_per_s": round(1e3 / ms_step, 1),
         "copy_GBps": round(copy_gbps, 1),
         # [PD §3] speed question at equal nominal tier: dense FP8 (online

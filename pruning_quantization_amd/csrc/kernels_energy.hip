@@ -86,6 +86,40 @@ __device__ inline void sel16_mags(uint32_t w0, uint32_t w1, float* kept2, float*
   top = t1;
 }
 
+// The two positions of 0..3 absent from a pair nibble (i0 | i1 << 2, i0 < i1),
+// in the same encoding.
+__device__ inline uint32_t other_pair(uint32_t n) {
+  const uint32_t dm = 0xFu ^ ((1u << (n & 3u)) | (1u << (n >> 2)));
+  return (uint32_t)__builtin_ctz(dm) | ((31u - (uint32_t)__builtin_clz(dm)) << 2);
+}
+
+// Selections of the packed-magnitude energy kernel.
+enum { SEL_MAG = 0, SEL_WANDA = 1, SEL_P48 = 2 };
+
+// Kept and dropped |x| of one bf16 unit as packed pairs: pk[0], pk[1] the
+// four kept magnitudes, pk[2], pk[3] the four dropped ones (Wanda 2:4 or
+// pairwise 4:8; magnitude 2:4 has its own faster path).  Units past the
+// row's end (valid = false) are zeros and select anything.
+template <int SEL>
+__device__ inline void unit_mags_packed(const Unit<BF16T>& u, const float* __restrict__ norm,
+                                        int64_t k0, bool valid, uint32_t (&pk)[4]) {
+  if constexpr (SEL == SEL_WANDA) {
+    const uint32_t mb = valid ? select_unit<BF16T, true>(u, norm, k0) : 0x44u;
+    const uint32_t n0 = mb & 0xFu, n1 = mb >> 4;
+    pk[0] = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(n0)) & 0x7FFF7FFFu;
+    pk[1] = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(n1)) & 0x7FFF7FFFu;
+    pk[2] = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(other_pair(n0))) & 0x7FFF7FFFu;
+    pk[3] = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(other_pair(n1))) & 0x7FFF7FFFu;
+  } else {
+    // a bf16 pair (2p, 2p+1) is dword p of the unit
+    const uint32_t nb = select_pairs48(u), dn = other_pair(nb);
+    pk[0] = pick4(nb & 3u, u.w[0], u.w[1], u.w[2], u.w[3]) & 0x7FFF7FFFu;
+    pk[1] = pick4(nb >> 2, u.w[0], u.w[1], u.w[2], u.w[3]) & 0x7FFF7FFFu;
+    pk[2] = pick4(dn & 3u, u.w[0], u.w[1], u.w[2], u.w[3]) & 0x7FFF7FFFu;
+    pk[3] = pick4(dn >> 2, u.w[0], u.w[1], u.w[2], u.w[3]) & 0x7FFF7FFFu;
+  }
+}
+
 // Squared residual energy of N magnitudes (N = 4 or 8) under a per-row scale
 // (s, inv) taken from a row maximum that no magnitude exceeds.  Each residual
 // is one fp32 rounding of code*s - v; the squares go into two fp32 chains of
@@ -352,17 +386,19 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #endif
 }
 
-// 4096-element rows without rotation fit 120 VGPRs without spilling: four
-// waves per SIMD keep a whole 4096-row operand resident in one pass.
+// 4096-element rows under magnitude 2:4 without rotation fit 120 VGPRs
+// without spilling: four waves per SIMD keep a whole 4096-row operand
+// resident in one pass.
 #ifndef SPARQ24_E_WAVES
 #define SPARQ24_E_WAVES 4
 #endif
-template <int TEAM, int UPL, bool ROT>
-constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT) ? SPARQ24_E_WAVES : 1;
+template <int TEAM, int UPL, bool ROT, int SEL>
+constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? SPARQ24_E_WAVES : 1;
 
-template <int TEAM, int UPL, bool ROT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT>)))
-void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
+template <int TEAM, int UPL, bool ROT, int SEL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL>)))
+void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams p,
+                        PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
   __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
@@ -385,16 +421,24 @@ void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
   const int64_t nrows = g.nrows;
   for_each_row_pipelined<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
-    uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept g0, kept g1, dropped g0, dropped g1
-    uint32_t am = 0;
+    uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept (0, 1), dropped (2, 3)
+    uint32_t am = 0;       // magnitude 2:4: max top key; otherwise packed kept max
+    uint32_t amd2 = 0;     // packed dropped max (Wanda, pairwise 4:8)
     double kept2 = 0.0, drop = 0.0;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
-      uint32_t t0, t1;
-      sel16_mags_packed(u[j].w[0], u[j].w[1], pk[j][0], pk[j][2], t0);
-      sel16_mags_packed(u[j].w[2], u[j].w[3], pk[j][1], pk[j][3], t1);
-      const uint32_t um = t0 > t1 ? t0 : t1;
-      am = am > um ? am : um;
+      if constexpr (SEL == SEL_MAG) {
+        uint32_t t0, t1;
+        sel16_mags_packed(u[j].w[0], u[j].w[1], pk[j][0], pk[j][2], t0);
+        sel16_mags_packed(u[j].w[2], u[j].w[3], pk[j][1], pk[j][3], t1);
+        const uint32_t um = t0 > t1 ? t0 : t1;
+        am = am > um ? am : um;
+      } else {
+        const int64_t i = (int64_t)j * TEAM + t;
+        unit_mags_packed<SEL>(u[j], norm, i * 8, i < g.nunits, pk[j]);
+        am = pk_max_u16(am, pk_max_u16(pk[j][0], pk[j][1]));
+        amd2 = pk_max_u16(amd2, pk_max_u16(pk[j][2], pk[j][3]));
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const double k0 = (double)mag_lo(pk[j][h]), k1 = (double)mag_hi(pk[j][h]);
@@ -405,25 +449,34 @@ void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
         drop = __builtin_fma(d1, d1, drop);
       }
     }
-    am = team_max_u32<TEAM>(am, redu);
+    // kept and row maxima as fp32 bit patterns (for magnitude 2:4 the group
+    // maximum is always kept, so the kept maximum is the row maximum)
+    uint32_t amk, amd;
+    if constexpr (SEL == SEL_MAG) {
+      amk = team_max_u32<TEAM>(am & 0xFFFF0000u, redu);
+      amd = amk;
+    } else {
+      amk = team_max_u32<TEAM>(unpack_max16(am) << 16, redu);
+      amd = team_max_u32<TEAM>(unpack_max16(pk_max_u16(am, amd2)) << 16, redu);
+    }
     double x2 = team_sum_f64<TEAM>(kept2 + drop, redd);
     drop = team_sum_f64<TEAM>(drop, redd);
     if (writer) {
       sink_put<TEAM>(sink, lacc, row, 0, x2);
       sink_put<TEAM>(sink, lacc, row, 1, drop);
     }
-    const float amax = __uint_as_float(am & 0xFFFF0000u);  // kept max == row max
+    const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
     // kept-side quantizers; a row format with a dense twin (same format and
     // qmax) is evaluated by the twin's pass below, since both take their
     // scale from the same maximum and quantize each kept value identically
     for (int q = 0; q < p.kept.n; ++q) {
-      if (p.kept_twin[q] >= 0) continue;
+      if (SEL == SEL_MAG && p.kept_twin[q] >= 0) continue;
       pin_packed<UPL>(pk);
       const int fmt = p.kept.fmt[q];
       double acc = 0.0;
       if (fmt == CF_FP8 || fmt == CF_INT8 || fmt == CF_INT16) {
         float s, inv;
-        row_scale(amax, p.kept.qmax[q], s, inv);
+        row_scale(famk, p.kept.qmax[q], s, inv);
         if (fmt == CF_FP8) {
 #pragma unroll
           for (int j = 0; j < UPL; ++j) {
@@ -459,10 +512,11 @@ void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
       double acc = 0.0;
       if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
         int twin = -1;
-        for (int k = 0; k < p.kept.n; ++k)
-          if (p.kept_twin[k] == q) twin = k;
+        if (SEL == SEL_MAG)
+          for (int k = 0; k < p.kept.n; ++k)
+            if (p.kept_twin[k] == q) twin = k;
         float s, inv;
-        row_scale(amax, p.dense.qmax[q], s, inv);
+        row_scale(famd, p.dense.qmax[q], s, inv);
         double acck = 0.0;  // kept positions; acc holds the dropped ones
         if (fmt == CF_FP8) {
 #pragma unroll
@@ -491,8 +545,11 @@ void k_energy_rows_bf16mag(RowGeom g, EnergyParams p, PartialSink sink) {
       } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
-          // the unit's |x| max is its kept max (each group keeps its largest)
-          const uint32_t km2 = pk_max_u16(pk[j][0], pk[j][1]);
+          // the unit's |x| max (magnitude 2:4: its kept max, as each group
+          // keeps its largest)
+          const uint32_t km2 = SEL == SEL_MAG ? pk_max_u16(pk[j][0], pk[j][1])
+                                              : pk_max_u16(pk_max_u16(pk[j][0], pk[j][1]),
+                                                           pk_max_u16(pk[j][2], pk[j][3]));
           const uint32_t kh = km2 >> 16, kl = km2 & 0xFFFFu;
           uint32_t bm = (kh > kl ? kh : kl) << 16;  // fp32 bits of the unit's |x| max
           uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
@@ -750,21 +807,32 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
     k.stride = acc ? (int64_t)grid.x : g.nrows;
     *nparts = acc ? (int64_t)grid.x : g.nrows;
   };
-  if (d.dtype == 1 && !wanda && !p.pairs48) {  // bf16, magnitude, 2:4
+  if (d.dtype == 1) {  // bf16: packed-magnitude kernel
+    const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
     return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
       geom(TEAM, grid, k);
-      if (d.rot.n)
-        hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL, true>), grid, dim3(kBlock), 0, s, g, p,
-                           k);
+      if (sel == SEL_WANDA)  // rotated calls take no norms
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_WANDA>), grid, dim3(kBlock), 0,
+                           s, g, norm, p, k);
+      else if (sel == SEL_P48 && d.rot.n)
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, true, SEL_P48>), grid, dim3(kBlock), 0,
+                           s, g, norm, p, k);
+      else if (sel == SEL_P48)
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_P48>), grid, dim3(kBlock), 0,
+                           s, g, norm, p, k);
+      else if (d.rot.n)
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, true, SEL_MAG>), grid, dim3(kBlock), 0,
+                           s, g, norm, p, k);
       else
-        hipLaunchKernelGGL((k_energy_rows_bf16mag<TEAM, UPL, false>), grid, dim3(kBlock), 0, s, g,
-                           p, k);
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_MAG>), grid, dim3(kBlock), 0,
+                           s, g, norm, p, k);
       return hipGetLastError();
     });
   }
-  return with_dtype(d.dtype, [&]<class DT>() {
+  // fp32 and fp16 operands
+  auto generic = [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
@@ -780,7 +848,10 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                            g, norm, p, k);
       return hipGetLastError();
     });
-  });
+  };
+  if (d.dtype == 0) return generic.template operator()<F32T>();
+  if (d.dtype == 2) return generic.template operator()<F16T>();
+  return hipErrorInvalidValue;
 }
 
 // Upper bound of the partial rows launch_energy_rows writes per column.
