@@ -49,18 +49,20 @@ def parse():
     return ap.parse_args()
 
 
+COUNTED_SOURCES = ["kernels_prune.hip", "kernels_quant.hip", "device_common.hpp", "dispatch.hpp",
+                   "launch.hpp"]
+
+
 def source_hash() -> str:
-    """sha256 over the library sources, to tell whether stored counters still
-    describe the kernels that run."""
-    import glob
+    """sha256 over the sources the measured row kernels are compiled from (the
+    prune and quantizer kernels and the headers they include), to tell whether
+    stored counters still describe the kernels that run."""
     import hashlib
 
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for f in sorted(glob.glob(os.path.join(root, "pruning_quantization_amd", "csrc", "*"))):
-        if os.path.basename(f) == "check_converts.hip":  # not part of the library
-            continue
-        with open(f, "rb") as fh:
+    for name in COUNTED_SOURCES:
+        with open(os.path.join(root, "pruning_quantization_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -393,7 +395,7 @@ def main():
 
     dom = "prune_quantize_fp8"
     achieved = per_call[dom]["GBps"]
-    kname = "k_prune_quantize<BF16T, 128, 4, false, 2, 0>"
+    kname = "k_prune_quantize<BF16T, 128, 4, false, 2, 0, false>"
     traffic, traffic_note = measured_traffic(kname, T, H)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
