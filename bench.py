@@ -181,6 +181,13 @@ def main():
     def call_had(i):
         S.hadamard(pool[i], 128, out=outs[i]["had"])
 
+    # whole-row rotation (one 4096-element block per row)
+    def call_pqK(i):
+        S.prune_quantize_rot(pool[i], H, "fp8", out=outs[i]["pqr"])
+
+    def call_RK(i):
+        S.predict_R_rot(pool[i], H, kept, dense, out=outs[i]["Rr"], workspace=ws)
+
     # operator-level output error of Y = X W^T against a synthetic MLP weight
     # W [14336, H] (bf16 N(0, 0.02^2)): reference + 2:4+FP8 and dense FP8 sides
     n_w = 14336
@@ -233,7 +240,8 @@ def main():
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
                   "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
                   "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
-                  "predict_R_rot128": call_Rr, "operator_error_2sides": call_op,
+                  "predict_R_rot128": call_Rr, "prune_quantize_fp8_rot_row": call_pqK,
+                  "predict_R_rot_row": call_RK, "operator_error_2sides": call_op,
                   "gemm_sparse24_bf16": call_gsp, "gemm_dense_bf16": call_gde,
                   "gemm_dense_fp8": call_g8, "predict_R_wanda_sweep_W": call_Rw,
                   "predict_R_heavy_blocks128": call_Rh}
@@ -260,6 +268,8 @@ def main():
         "hadamard128": 2 * xb,
         "prune_quantize_fp8_rot128": xb + T * H // 2 + T * H // 8 + T * 4,
         "predict_R_rot128": xb + 2 * 5 * 8,
+        "prune_quantize_fp8_rot_row": xb + T * H // 2 + T * H // 8 + T * 4,
+        "predict_R_rot_row": xb + 2 * 5 * 8,
         "operator_error_2sides": xb + n_w * H * 2,
         "gemm_sparse24_bf16": xb // 2 + T * H // 8 + n_w * H * 2 + T * n_w * 4,
         "gemm_dense_bf16": xb + n_w * H * 2 + T * n_w * 4,

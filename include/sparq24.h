@@ -240,7 +240,8 @@ typedef enum {
 /* Block Hadamard rotation along K [PD §4: before low-bit quantization the
  * operand is multiplied by a rescaled +-1 orthogonal Hadamard matrix, which
  * spreads outliers over many elements].  Every aligned block of `block`
- * elements (a power of two, 8..512, dividing K) becomes y = H x / sqrt(block)
+ * elements (a power of two, 8..4096, dividing K; so a whole row of up to
+ * 4096 elements) becomes y = H x / sqrt(block)
  * with H the Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)).
  * Precision: the sums S = H x are fp64 butterflies, exact (so independent of
  * their order) whenever a block's values span at most 53 - log2(block) bits
@@ -249,7 +250,8 @@ typedef enum {
  * rounded to fp32 and then to the storage type (round-to-nearest-even).
  * out [B][R][K] in x's storage type, K-contiguous.  Workspace: a transposed
  * operand's staging copy, else none.  Errors: block not a power of two in
- * range -> INVALID; K % block -> SHAPE. */
+ * range -> INVALID; K % block -> SHAPE; block > 512 with K > 8192 ->
+ * UNSUPPORTED (such blocks are rotated within one wave's registers). */
 sparq24_status sparq24_hadamard(const sparq24_tensor* x, int32_t block, void* out, void* ws,
                                 size_t* ws_bytes, hipStream_t stream);
 

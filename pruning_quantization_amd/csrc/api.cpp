@@ -89,12 +89,14 @@ sparq24_status check_score(int32_t score, const float* col_norm) {
   return SPARQ24_OK;
 }
 
-// Hadamard block size: a power of two in 8..512 dividing K; fills d.rot with
+// Hadamard block size: a power of two in 8..4096 dividing K (blocks over 512
+// elements need K <= 8192, where one wave holds a row); fills d.rot with
 // c = fp64 1/sqrt(n) (an exact power of two for even log2 n, else that power
 // times the correctly rounded sqrt(1/2)).
 sparq24_status check_rot(int32_t block, RowDesc& d) {
-  if (block < 8 || block > 512 || (block & (block - 1))) return SPARQ24_ERR_INVALID;
+  if (block < 8 || block > 4096 || (block & (block - 1))) return SPARQ24_ERR_INVALID;
   if (d.K % block) return SPARQ24_ERR_SHAPE;
+  if (block > 512 && d.K > 8192) return SPARQ24_ERR_UNSUPPORTED;
   int k = 0;
   while ((1 << k) < block) ++k;
   d.rot.n = block;

@@ -540,9 +540,10 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 // block's values span at most 53 - log2(n) bits from the largest magnitude to
 // the lowest set bit, so the butterfly order does not matter), a zero sum is
 // +0, then fp64(S * c) is rounded to fp32 and to the storage type (RNE).
-// A block of n elements is n/8 units on adjacent lanes of one register j
-// (lane t owns units t, t + TEAM, ...; n <= 8 * TEAM), so the butterflies
-// run three stages inside a unit and log2(n/8) stages across lanes.
+// A block of n <= 8 * TEAM elements is n/8 units on adjacent lanes of one
+// register j (lane t owns units t, t + TEAM, ...), so the butterflies run
+// three stages inside a unit and log2(n/8) stages across lanes; longer blocks
+// add stages across a lane's consecutive units (hadamard_long).
 // ---------------------------------------------------------------------------
 template <class DT>
 __device__ inline void unit_store_f32(Unit<DT>& u, const float* f) {
@@ -603,11 +604,9 @@ __device__ inline void had_xlane(double (&v)[8], int t) {
   }
 }
 
-template <class DT>
-__device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
-  double v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (double)u.f(e);
+// The three in-unit butterfly stages and the cross-lane stages of blocks of
+// nb units (nb <= 64) on fp64 values.
+__device__ inline void had_unit_lanes(double (&v)[8], int nb, int t) {
 #pragma unroll
   for (int d = 1; d < 8; d <<= 1)
 #pragma unroll
@@ -623,18 +622,82 @@ __device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
   if (nb > 8) had_xlane<8>(v, t);
   if (nb > 16) had_xlane<16>(v, t);
   if (nb > 32) had_xlane<32>(v, t);
+}
+
+template <class DT>
+__device__ inline void unit_store_rotated(Unit<DT>& u, const double (&v)[8], double c) {
   float f[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = (float)((v[e] + 0.0) * c);
   unit_store_f32(u, f);
 }
 
-// Every lane of the wave must call this (zero units rotate to zeros).
-template <class DT, int UPL>
-__device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
-  if (r.n == 0) return;
+template <class DT>
+__device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
+  double v[8];
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) hadamard_unit(u[j], r.n >> 3, r.c, t);
+  for (int e = 0; e < 8; ++e) v[e] = (double)u.f(e);
+  had_unit_lanes(v, nb, t);
+  unit_store_rotated(u, v, c);
+}
+
+// Blocks longer than a wave's 512 elements (one-wave teams): lane t's unit j
+// holds elements 8 (64 j + t) .. 8 (64 j + t) + 7 of its row or chunk, so a
+// block of n = 512 NJ elements is NJ consecutive units of every lane.  After
+// the unit and lane stages, the remaining log2(NJ) stages pair units j and
+// j ^ d of the same lane; one block's NJ units are held in fp64 at a time.
+template <class DT, int UPL, int NJ>
+__device__ inline void hadamard_long(Unit<DT> (&u)[UPL], double c, int t) {
+#pragma unroll
+  for (int j0 = 0; j0 < UPL; j0 += NJ) {
+    double v[NJ][8];
+#pragma unroll
+    for (int k = 0; k < NJ; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[k][e] = (double)u[j0 + k].f(e);
+      had_unit_lanes(v[k], 64, t);
+      // one unit's lane stages at a time: interleaving them would add a
+      // second set of fp64 temporaries per unit
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int d = 1; d < NJ; d <<= 1)
+#pragma unroll
+      for (int k = 0; k < NJ; ++k)
+        if (!(k & d))
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double a = v[k][e], b = v[k | d][e];
+            v[k][e] = a + b;
+            v[k | d][e] = a - b;
+          }
+#pragma unroll
+    for (int k = 0; k < NJ; ++k) unit_store_rotated(u[j0 + k], v[k], c);
+  }
+}
+
+// Every lane of the wave must call this (zero units rotate to zeros).
+// ROT = 1: blocks of up to 8 * TEAM elements, rotated unit by unit.  ROT = 2:
+// blocks of 1024 .. 4096 elements (one-wave teams, n / 512 <= UPL); a variant
+// of its own, since holding a block's units in fp64 needs far more registers.
+template <class DT, int TEAM, int UPL, int ROT>
+__device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
+  if constexpr (ROT == 1) {
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) hadamard_unit(u[j], r.n >> 3, r.c, t);
+  } else if constexpr (ROT == 2) {
+    static_assert(TEAM == 64, "long rotation blocks need one-wave teams");
+    const int nj = r.n >> 9;
+    if constexpr (UPL >= 2) {
+      if (nj == 2) hadamard_long<DT, UPL, 2>(u, r.c, t);
+    }
+    if constexpr (UPL >= 4) {
+      if (nj == 4) hadamard_long<DT, UPL, 4>(u, r.c, t);
+    }
+    if constexpr (UPL >= 8) {
+      if (nj == 8) hadamard_long<DT, UPL, 8>(u, r.c, t);
+    }
+  }
 }
 
 struct RowGeom {
@@ -679,7 +742,7 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
 #define SPARQ24_PIPELINE 0
 #endif
 
-template <class DT, int TEAM, int UPL, bool ROT = false, class Body>
+template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
 __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
   constexpr int TPB = kBlock / TEAM;
   const int t = threadIdx.x % TEAM;
@@ -691,7 +754,7 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
       Unit<DT> A[UPL];
       const int64_t ra = first + it * stride;
       load_row<DT, TEAM, UPL>(A, g, ra, t);
-      if constexpr (ROT) hadamard_units<DT, UPL>(A, g.rot, t);
+      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
       body(A, ra, t);
     }
     return;
@@ -702,11 +765,11 @@ __device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
     const int64_t ra = first + it * stride;
     const int64_t rb = ra + stride;
     load_row<DT, TEAM, UPL>(B, g, rb, t);
-    if constexpr (ROT) hadamard_units<DT, UPL>(A, g.rot, t);
+    if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
     body(A, ra, t);
     if (it + 1 < iters) {
       load_row<DT, TEAM, UPL>(A, g, rb + stride, t);
-      if constexpr (ROT) hadamard_units<DT, UPL>(B, g.rot, t);
+      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(B, g.rot, t);
       body(B, rb, t);
     }
   }

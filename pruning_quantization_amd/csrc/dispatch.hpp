@@ -55,6 +55,17 @@ inline hipError_t with_loop_variant(int64_t nunits, F&& f) {
   return f.template operator()<64, 8>();
 }
 
+// Rotation variant of a launch on teams of TEAM lanes: 0 none, 1 blocks of
+// up to 512 elements (unit by unit), 2 longer blocks (one-wave teams only;
+// callers pick one-wave teams for them).
+template <int TEAM, class F>
+inline hipError_t with_rot(const Rot& r, F&& f) {
+  if (r.n == 0) return f.template operator()<0>();
+  if (r.n <= 512) return f.template operator()<1>();
+  if constexpr (TEAM == 64) return f.template operator()<2>();
+  else return hipErrorInvalidValue;
+}
+
 inline dim3 row_grid(const RowDesc& d, int team) {
   const int64_t rpb = kBlock / team;
   return dim3((unsigned)((d.R + rpb - 1) / rpb), (unsigned)d.B, 1);

@@ -392,10 +392,10 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #ifndef SPARQ24_E_WAVES
 #define SPARQ24_E_WAVES 4
 #endif
-template <int TEAM, int UPL, bool ROT, int SEL>
+template <int TEAM, int UPL, int ROT, int SEL>
 constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? SPARQ24_E_WAVES : 1;
 
-template <int TEAM, int UPL, bool ROT, int SEL>
+template <int TEAM, int UPL, int ROT, int SEL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL>)))
 void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams p,
                         PartialSink sink) {
@@ -572,7 +572,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   sink_flush<TEAM>(sink, lacc, ncols);
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA, bool ROT>
+template <class DT, int TEAM, int UPL, bool WANDA, int ROT>
 SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
                                                         EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
@@ -813,22 +813,20 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
       geom(TEAM, grid, k);
-      if (sel == SEL_WANDA)  // rotated calls take no norms
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_WANDA>), grid, dim3(kBlock), 0,
-                           s, g, norm, p, k);
-      else if (sel == SEL_P48 && d.rot.n)
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, true, SEL_P48>), grid, dim3(kBlock), 0,
-                           s, g, norm, p, k);
-      else if (sel == SEL_P48)
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_P48>), grid, dim3(kBlock), 0,
-                           s, g, norm, p, k);
-      else if (d.rot.n)
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, true, SEL_MAG>), grid, dim3(kBlock), 0,
-                           s, g, norm, p, k);
-      else
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, false, SEL_MAG>), grid, dim3(kBlock), 0,
-                           s, g, norm, p, k);
-      return hipGetLastError();
+      if (sel == SEL_WANDA) {  // rotated calls take no norms
+        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, 0, SEL_WANDA>), grid, dim3(kBlock), 0, s,
+                           g, norm, p, k);
+        return hipGetLastError();
+      }
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        if (sel == SEL_P48)
+          hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, R, SEL_P48>), grid, dim3(kBlock), 0, s,
+                             g, norm, p, k);
+        else
+          hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, R, SEL_MAG>), grid, dim3(kBlock), 0, s,
+                             g, norm, p, k);
+        return hipGetLastError();
+      });
     });
   }
   // fp32 and fp16 operands
@@ -837,16 +835,16 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       const dim3 grid = persistent_grid(g.nrows, TEAM);
       PartialSink k;
       geom(TEAM, grid, k);
-      if (wanda)  // rotated calls take no norms
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true, false>), grid, dim3(kBlock), 0, s, g,
+      if (wanda) {  // rotated calls take no norms
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true, 0>), grid, dim3(kBlock), 0, s, g,
                            norm, p, k);
-      else if (d.rot.n)
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, true>), grid, dim3(kBlock), 0, s, g,
+        return hipGetLastError();
+      }
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, R>), grid, dim3(kBlock), 0, s, g,
                            norm, p, k);
-      else
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, false>), grid, dim3(kBlock), 0, s,
-                           g, norm, p, k);
-      return hipGetLastError();
+        return hipGetLastError();
+      });
     });
   };
   if (d.dtype == 0) return generic.template operator()<F32T>();

@@ -144,7 +144,7 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
 // Block Hadamard rotation of a K-contiguous operand into a dense copy
 // [PD §4]: load, rotate in registers (hadamard_units), store.
 // ---------------------------------------------------------------------------
-template <class DT, int TEAM, int UPL>
+template <class DT, int TEAM, int UPL, int ROT>
 __global__ __launch_bounds__(kBlock) void k_hadamard(const char* __restrict__ x, int64_t R,
                                                      int64_t nunits, int64_t bs, int64_t rs,
                                                      Rot rot, char* __restrict__ out) {
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void k_hadamard(const char* __restrict__ x,
       if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
       else zero_unit(u[j]);
     }
-    hadamard_units<DT, UPL>(u, rot, t);
+    hadamard_units<DT, TEAM, UPL, ROT>(u, rot, t);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = c0 + j * TEAM + t;
@@ -179,9 +179,12 @@ hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      hipLaunchKernelGGL((k_hadamard<DT, TEAM, UPL>), row_grid(d, TEAM), dim3(kBlock), 0, s, d.x,
-                         d.R, nunits, d.bs, d.rs, d.rot, (char*)out);
-      return hipGetLastError();
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        if constexpr (R == 0) return hipErrorInvalidValue;  // a rotation always has a block
+        hipLaunchKernelGGL((k_hadamard<DT, TEAM, UPL, R>), row_grid(d, TEAM), dim3(kBlock), 0, s,
+                           d.x, d.R, nunits, d.bs, d.rs, d.rot, (char*)out);
+        return hipGetLastError();
+      });
     });
   });
 }

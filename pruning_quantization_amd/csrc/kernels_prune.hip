@@ -205,7 +205,7 @@ __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
   }
 }
 
-template <class DT, int TEAM, int UPL, bool WANDA, int CF, int PAT, bool ROT>
+template <class DT, int TEAM, int UPL, bool WANDA, int CF, int PAT, int ROT>
 SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ norm, float qmax,
                                          char* __restrict__ codes, uint8_t* __restrict__ meta,
                                          float* __restrict__ scales) {
@@ -390,24 +390,40 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   if (wanda && d.rot.n) return hipErrorInvalidValue;  // rotated calls take no norms
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
+    // LONG: rotation blocks over 512 elements, which need one-wave teams
+    auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
       const dim3 grid = persistent_grid(g.nrows, TEAM);
-      auto go = [&]<bool W, int P, int CF, bool R>() {
+      auto go = [&]<bool W, int P, int CF, int R>() {
         hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>), grid, dim3(kBlock), 0,
                            s, g, norm, qmax, (char*)codes, meta, scales);
         return hipGetLastError();
       };
-      auto fmt = [&]<bool W, int P, bool R>() {
+      auto fmt = [&]<bool W, int P, int R>() {
         if (cfmt == CF_FP8) return go.template operator()<W, P, CF_FP8, R>();
         if (cfmt == CF_INT8) return go.template operator()<W, P, CF_INT8, R>();
         return go.template operator()<W, P, CF_INT16, R>();
       };
-      if (wanda) return fmt.template operator()<true, PAT_24, false>();
-      if (pat == PAT_48)
-        return d.rot.n ? fmt.template operator()<false, PAT_48, true>()
-                       : fmt.template operator()<false, PAT_48, false>();
-      return d.rot.n ? fmt.template operator()<false, PAT_24, true>()
-                     : fmt.template operator()<false, PAT_24, false>();
+      if constexpr (LONG) {
+        if constexpr (TEAM == 64)
+          return pat == PAT_48 ? fmt.template operator()<false, PAT_48, 2>()
+                               : fmt.template operator()<false, PAT_24, 2>();
+        else
+          return hipErrorInvalidValue;
+      } else {
+        if (wanda) return fmt.template operator()<true, PAT_24, 0>();
+        if (pat == PAT_48)
+          return d.rot.n ? fmt.template operator()<false, PAT_48, 1>()
+                         : fmt.template operator()<false, PAT_48, 0>();
+        return d.rot.n ? fmt.template operator()<false, PAT_24, 1>()
+                       : fmt.template operator()<false, PAT_24, 0>();
+      }
+    };
+    if (d.rot.n > 512)
+      return with_row_variant<0>(nunits, [&]<int TEAM, int UPL>() {
+        return body.template operator()<TEAM, UPL, true>();
+      });
+    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
+      return body.template operator()<TEAM, UPL, false>();
     });
   });
 }

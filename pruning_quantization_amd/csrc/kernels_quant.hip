@@ -36,7 +36,7 @@ __device__ inline uint32_t unit_absmax(const Unit<DT>& u) {
   }
 }
 
-template <class DT, int TEAM, int UPL, bool ROT>
+template <class DT, int TEAM, int UPL, int ROT>
 SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
                                                        char* __restrict__ codes,
                                                        float* __restrict__ scales) {
@@ -89,7 +89,7 @@ SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
 // ---------------------------------------------------------------------------
 constexpr int kAbsmaxBlocks = 512;
 
-template <class DT, int TEAM, int UPL, bool ROT>
+template <class DT, int TEAM, int UPL, int ROT>
 __global__ __launch_bounds__(kBlock) void k_absmax_partial(
     const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     uint32_t* __restrict__ partials, Rot rot) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void k_absmax_partial(
         if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
         else zero_unit(u[j]);
       }
-      if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
+      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(u, rot, t);
 #pragma unroll
       for (int j = 0; j < UPL; ++j)
 #pragma unroll
@@ -142,13 +142,11 @@ hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStrea
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      if (d.rot.n)
-        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, true>), dim3(nb), dim3(kBlock), 0, s,
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, R>), dim3(nb), dim3(kBlock), 0, s,
                            d.x, d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
-      else
-        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, false>), dim3(nb), dim3(kBlock), 0, s,
-                           d.x, d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
-      return hipGetLastError();
+        return hipGetLastError();
+      });
     });
   });
 }
@@ -158,7 +156,7 @@ hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStrea
 // elements) is 4 adjacent lanes, an NV block (16 elements) 2 adjacent lanes,
 // combined with cross-lane xor shuffles.
 // ---------------------------------------------------------------------------
-template <class DT, int TEAM, int UPL, bool NV, bool ROT>
+template <class DT, int TEAM, int UPL, bool NV, int ROT>
 __global__ __launch_bounds__(kBlock) void k_quant_block(
     const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     const float* __restrict__ tamax_in, const uint32_t* __restrict__ partials, int nparts,
@@ -186,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
       if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
       else zero_unit(u[j]);
     }
-    if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
+    if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(u, rot, t);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = c0 + j * TEAM + t;
@@ -250,7 +248,7 @@ __device__ inline uint32_t select_any(const Unit<DT>& u, const float* norm, int6
   return m;
 }
 
-template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool NV, bool ROT>
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool NV, int ROT>
 __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
     const char* __restrict__ x, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     const float* __restrict__ norm, const float* __restrict__ tamax_in,
@@ -279,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
       if (active && i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
       else zero_unit(u[j]);
     }
-    if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
+    if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(u, rot, t);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       const int64_t i = c0 + j * TEAM + t;
@@ -331,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
 
 // Partial maxima of the kept values' magnitudes (the NVFP4 tensor maximum of
 // a sparse operand whose kept maximum can differ from its plain maximum).
-template <class DT, int TEAM, int UPL, int PAT, bool WANDA, bool ROT>
+template <class DT, int TEAM, int UPL, int PAT, bool WANDA, int ROT>
 __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
     const char* __restrict__ x, int64_t B, int64_t R, int64_t nunits, int64_t bs, int64_t rs,
     const float* __restrict__ norm, uint32_t* __restrict__ partials, Rot rot) {
@@ -351,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void k_kept_absmax_partial(
         if (i < nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
         else zero_unit(u[j]);
       }
-      if constexpr (ROT) hadamard_units<DT, UPL>(u, rot, t);
+      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(u, rot, t);
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
         const int64_t i = c0 + j * TEAM + t;
@@ -377,15 +375,16 @@ hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
-      if (d.rot.n)
-        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, true>), persistent_grid(g.nrows, TEAM),
+    auto body = [&]<int TEAM, int UPL>() {
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, R>), persistent_grid(g.nrows, TEAM),
                            dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
-      else
-        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, false>), persistent_grid(g.nrows, TEAM),
-                           dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
-      return hipGetLastError();
-    });
+        return hipGetLastError();
+      });
+    };
+    if (d.rot.n > 512)  // rotation blocks over 512 elements need one-wave teams
+      return with_row_variant<0>(nunits, body);
+    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, body);
   });
 }
 
@@ -396,15 +395,12 @@ static hipError_t launch_quant_block(const RowDesc& d, const float* tamax_in,
   const int64_t nunits = d.K / 8;
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      if (d.rot.n)
-        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, true>), row_grid(d, TEAM),
+      return with_rot<TEAM>(d.rot, [&]<int R>() {
+        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, R>), row_grid(d, TEAM),
                            dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials,
                            nparts, (uint32_t*)codes, scales, ts_out, d.rot);
-      else
-        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, false>), row_grid(d, TEAM),
-                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials,
-                           nparts, (uint32_t*)codes, scales, ts_out, d.rot);
-      return hipGetLastError();
+        return hipGetLastError();
+      });
     });
   });
 }
@@ -429,22 +425,21 @@ hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const f
   if (wanda && d.rot.n) return hipErrorInvalidValue;
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      auto go = [&]<int P, bool W, bool NV, bool R>() {
+      auto go = [&]<int P, bool W, bool NV, int R>() {
         hipLaunchKernelGGL((k_prune_quant_fp4<DT, TEAM, UPL, P, W, NV, R>), row_grid(d, TEAM),
                            dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, tamax_in,
                            partials, nparts, (uint16_t*)codes, meta, scales, ts_out, d.rot);
         return hipGetLastError();
       };
       auto mag = [&]<int P, bool NV>() {
-        return d.rot.n ? go.template operator()<P, false, NV, true>()
-                       : go.template operator()<P, false, NV, false>();
+        return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<P, false, NV, R>(); });
       };
       const bool nv = cfmt == CF_NV;
       if (pat == PAT_48)
         return nv ? mag.template operator()<PAT_48, true>() : mag.template operator()<PAT_48, false>();
       if (wanda)
-        return nv ? go.template operator()<PAT_24, true, true, false>()
-                  : go.template operator()<PAT_24, true, false, false>();
+        return nv ? go.template operator()<PAT_24, true, true, 0>()
+                  : go.template operator()<PAT_24, true, false, 0>();
       return nv ? mag.template operator()<PAT_24, true>() : mag.template operator()<PAT_24, false>();
     });
   });
@@ -458,16 +453,15 @@ hipError_t launch_kept_absmax_partials(const RowDesc& d, int pat, bool wanda, co
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      auto go = [&]<int P, bool W, bool R>() {
+      auto go = [&]<int P, bool W, int R>() {
         hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, P, W, R>), dim3(nb),
                            dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials,
                            d.rot);
         return hipGetLastError();
       };
       if (pat == PAT_48)
-        return d.rot.n ? go.template operator()<PAT_48, false, true>()
-                       : go.template operator()<PAT_48, false, false>();
-      return go.template operator()<PAT_24, true, false>();
+        return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<PAT_48, false, R>(); });
+      return go.template operator()<PAT_24, true, 0>();
     });
   });
 }

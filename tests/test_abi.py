@@ -189,8 +189,8 @@ def test_prune_quantize_validation(L):
 def test_rotation_validation(L):
     n = ctypes.c_size_t(5)
     h = L.sparq24_hadamard
-    for blk in (0, 4, 12, 1024):
-        assert h(ctypes.byref(tensor(k=1024)), blk, FAKE, None, ctypes.byref(n), None) == INVALID
+    for blk in (0, 4, 12, 1536, 8192):
+        assert h(ctypes.byref(tensor(k=8192)), blk, FAKE, None, ctypes.byref(n), None) == INVALID
     assert h(ctypes.byref(tensor(k=192)), 128, FAKE, None, ctypes.byref(n), None) == SHAPE
     assert h(ctypes.byref(tensor(k=256)), 128, FAKE, None, ctypes.byref(n), None) == OK and n.value == 0
     assert h(ctypes.byref(tensor(rows=8, k=128, rs=1, ks=8)), 64, FAKE, None, ctypes.byref(n), None) == OK
@@ -209,6 +209,15 @@ def test_rotation_validation(L):
     assert fr(ctypes.byref(tensor(k=256)), 128, 1, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
     assert n.value > 0
     assert fr(ctypes.byref(tensor(k=256)), 512, 0, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
+    # whole-row blocks up to 4096 elements, rotated inside one wave's registers
+    assert fq(ctypes.byref(tensor(k=4096)), 4096, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == OK
+    assert fq(ctypes.byref(tensor(k=8192)), 8192, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == INVALID
+    assert fq(ctypes.byref(tensor(k=16384)), 1024, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == UNSUPPORTED
+    assert fq(ctypes.byref(tensor(k=16384)), 512, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
+              ctypes.byref(n), None) == OK
 
 
 def test_copy_validation(L):

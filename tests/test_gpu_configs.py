@@ -229,6 +229,22 @@ def test_act_rotated(act):
     rel_close(got, want)
 
 
+def test_act_rotated_whole_row(act):
+    # one 4096-element Hadamard block per token (the whole hidden dimension)
+    bits, x = act
+    assert O.rotation_exact(bits, "bf16", 4096).all()
+    rot = O.rotate(bits, "bf16", 4096)
+    c, m, s = S.prune_quantize_rot(x, 4096, "fp8")
+    wc, wm, ws = O.prune_quantize(rot, "bf16", O.QSpec("fp8"))
+    assert_same(raw_np(c), wc, "rotated codes")
+    assert_same(raw_np(m), wm, "rotated meta")
+    assert_same(raw_np(s), ws, "rotated scales")
+    kept, dense = ["fp8", "fp8"], ["fp8", ("int", 8)]
+    got = raw_np(S.predict_R_rot(x, 4096, kept, dense))
+    want = O.predict_R(rot, "bf16", [O.QSpec("fp8")] * 2, [O.QSpec("fp8"), O.QSpec("int", 8)])
+    rel_close(got, want)
+
+
 @pytest.fixture(scope="module")
 def weight():
     bits = W.weight_w(2, 14336, 4096)

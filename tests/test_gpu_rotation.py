@@ -61,6 +61,17 @@ def test_hadamard(dtype, n):
         assert_same(raw_np(got), O.rotate(raw, dtype, n), f"rotate n={n} k={k} {kind}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n", [1024, 2048, 4096])
+def test_hadamard_long_blocks(dtype, n):
+    # blocks over one wave's 512 elements: stages across a lane's units
+    for k, kind in ((n, "normal"), (8192, "ints"), (8192, "normal")):
+        raw = rot_inputs(n + k + 1, 13, k, dtype, kind)
+        exact(raw, dtype, n)
+        got = S.hadamard(to_dev(raw, dtype), n)
+        assert_same(raw_np(got), O.rotate(raw, dtype, n), f"rotate n={n} k={k} {kind}")
+
+
 def test_hadamard_transposed_and_strided():
     rng = np.random.default_rng(3)
     raw = W.to_bf16_bits(rng.standard_normal((2, 256, 40)))
@@ -73,7 +84,7 @@ def test_hadamard_transposed_and_strided():
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("n", [16, 128, 512])
+@pytest.mark.parametrize("n", [16, 128, 512, 1024, 2048])
 def test_quantize_rot(dtype, n):
     k = 2048
     raw = rot_inputs(7 * n, 37, k, dtype)
@@ -97,7 +108,7 @@ def test_quantize_rot(dtype, n):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("n", [8, 128, 256])
+@pytest.mark.parametrize("n", [8, 128, 256, 1024])
 def test_prune_quantize_rot(dtype, n):
     k = 1024
     for kind in ("normal", "ints"):
@@ -113,7 +124,7 @@ def test_prune_quantize_rot(dtype, n):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("n", [32, 128])
+@pytest.mark.parametrize("n", [32, 128, 4096])
 def test_predict_R_rot(dtype, n):
     k = 4096
     raw = rot_inputs(13 * n, 41, k, dtype)
@@ -126,6 +137,28 @@ def test_predict_R_rot(dtype, n):
     for pat in ("2:4", "pairs4:8"):
         got = S.predict_R_rot(x, n, kept, dense, pattern=pat, rows_per_block=16)
         rel_close(raw_np(got), O.predict_R(rot, dtype, ok, od, rows_per_block=16, pattern=pat))
+
+
+def test_whole_row_rotation_on_4096_rows():
+    # the whole-row rotation of a 4096-wide operand through every fused call
+    raw = rot_inputs(5, 300, 4096, "bf16")
+    exact(raw, "bf16", 4096)
+    x = to_dev(raw, "bf16")
+    rot = O.rotate(raw, "bf16", 4096)
+    for q in (("fp8", 0), ("int", 8)):
+        c, s = S.quantize_rot(x, 4096, q)
+        wc, ws = O.quantize_rows(rot, "bf16", O.QSpec(*q))
+        assert_same(raw_np(c), wc, f"codes {q}")
+        assert_same(raw_np(s), ws, f"scales {q}")
+    for q in (("fp8", 0), ("nvfp4", 0)):
+        check_pq(S.prune_quantize_rot(x, 4096, q), O.prune_quantize(rot, "bf16", O.QSpec(*q)),
+                 f"2:4 rot4096 {q}")
+        check_pq(S.prune_quantize_rot(x, 4096, q, pattern="pairs4:8"),
+                 O.prune_quantize_pairs48(rot, "bf16", O.QSpec(*q)), f"4:8 rot4096 {q}")
+    c, s = S.quantize_rot(x, 4096, "mxfp4")
+    wc, ws = O.quantize_mxfp4(rot, "bf16")
+    assert_same(raw_np(c), wc, "mx codes")
+    assert_same(raw_np(s), ws, "mx scales")
 
 
 def test_rotation_raises_R_on_outlier_activations():
