@@ -227,7 +227,7 @@ def main():
     n_h = 16384
     x_heavy = torch.from_numpy(W.student_t_x(a.seed + 2, n_h, H).view(np.int16)).view(torch.bfloat16).to(dev)
     r_heavy = torch.empty(n_h // 128, 2, 5, dtype=torch.float64, device=dev)
-    ws_big = torch.empty(8 << 20, dtype=torch.uint8, device=dev)
+    ws_big = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
     def call_Rw(i):
         S.predict_R(w_op, sweep_kept, sweep_dense, score="wanda", col_norm=norms, out=r_sweep,
@@ -237,6 +237,72 @@ def main():
         S.predict_R(x_heavy, ["fp8", "fp8"], ["mxfp4", "nvfp4"], rows_per_block=128, out=r_heavy,
                     workspace=ws_big)
 
+    # the remaining workloads' own calls, each on its operand at full size
+    # (operands below the 256 MB last-level cache rotate over copies):
+    # Wanda 2:4 of W; the attention operands Q, K (pruned along head_dim), V
+    # (pruned along the sequence: a strided operand) and P; the 4x tier's
+    # fused 2:4+FP8 and its MXFP4 / NVFP4 rivals
+    heavy2 = [x_heavy, x_heavy.clone()]
+    pc_w = (torch.empty(n_w, H // 2, dtype=torch.bfloat16, device=dev),
+            torch.empty(n_w, H // 8, dtype=torch.uint8, device=dev))
+
+    def bf(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_att = bf(W.attention_qkv(a.seed + 3, 32, 16384, 128)).view(-1, 128)
+    q_pool = [q_att, q_att.clone()]
+    k_att = bf(W.attention_qkv(a.seed + 4, 8, 16384, 128)).view(-1, 128)
+    k_pool = [k_att] + [k_att.clone() for _ in range(7)]
+    v_att = bf(W.attention_qkv(a.seed + 5, 8, 16384, 128))
+    v_pool = [v_att] + [v_att.clone() for _ in range(7)]
+    p_att = bf(W.attention_p(a.seed + 6, 32, 4096, 4096)).view(-1, 4096)
+    pc_q = (torch.empty(32 * 16384, 64, dtype=torch.bfloat16, device=dev),
+            torch.empty(32 * 16384, 16, dtype=torch.uint8, device=dev))
+    pc_k = (torch.empty(8 * 16384, 64, dtype=torch.bfloat16, device=dev),
+            torch.empty(8 * 16384, 16, dtype=torch.uint8, device=dev))
+    pc_v = (torch.empty(8, 128, 8192, dtype=torch.bfloat16, device=dev),
+            torch.empty(8, 128, 2048, dtype=torch.uint8, device=dev))
+    pc_p = (torch.empty(32 * 4096, 2048, dtype=torch.bfloat16, device=dev),
+            torch.empty(32 * 4096, 512, dtype=torch.uint8, device=dev))
+    r_p = torch.empty(32, 2, 5, dtype=torch.float64, device=dev)
+    pq_h = (torch.empty(n_h, H // 2, dtype=torch.uint8, device=dev),
+            torch.empty(n_h, H // 8, dtype=torch.uint8, device=dev),
+            torch.empty(n_h, dtype=torch.float32, device=dev))
+    mx_h = (torch.empty(n_h, H // 2, dtype=torch.uint8, device=dev),
+            torch.empty(n_h, H // 32, dtype=torch.uint8, device=dev),
+            torch.empty(1, dtype=torch.float32, device=dev))
+    nv_h = (torch.empty(n_h, H // 2, dtype=torch.uint8, device=dev),
+            torch.empty(n_h, H // 16, dtype=torch.uint8, device=dev),
+            torch.empty(1, dtype=torch.float32, device=dev))
+
+    def call_pcw(i):
+        S.prune_compress(w_op, score="wanda", col_norm=norms, out=pc_w)
+
+    def call_pcq(i):
+        S.prune_compress(q_pool[i % 2], out=pc_q)
+
+    def call_pck(i):
+        S.prune_compress(k_pool[i % 8], out=pc_k)
+
+    def call_pcv(i):
+        S.prune_compress(v_pool[i % 8], axis=1, out=pc_v)
+
+    def call_pcp(i):
+        S.prune_compress(p_att, out=pc_p)
+
+    def call_Rp(i):
+        S.predict_R(p_att, ["none", "none"], ["fp8", ("int", 8)], rows_per_block=4096, out=r_p,
+                    workspace=ws_big)
+
+    def call_pqh(i):
+        S.prune_quantize(heavy2[i % 2], "fp8", out=pq_h)
+
+    def call_mxh(i):
+        S.quantize(heavy2[i % 2], "mxfp4", out=mx_h)
+
+    def call_nvh(i):
+        S.quantize(heavy2[i % 2], "nvfp4", out=nv_h, workspace=ws_big)
+
     side_calls = {"prune_compress_2of4": call_pc, "prune_compress_pairs48": call_p48,
                   "predict_R_pairs48": call_R48, "prune_quantize_pairs48_nvfp4": call_sfp4,
                   "hadamard128": call_had, "prune_quantize_fp8_rot128": call_pqr,
@@ -244,7 +310,11 @@ def main():
                   "predict_R_rot_row": call_RK, "operator_error_2sides": call_op,
                   "gemm_sparse24_bf16": call_gsp, "gemm_dense_bf16": call_gde,
                   "gemm_dense_fp8": call_g8, "predict_R_wanda_sweep_W": call_Rw,
-                  "predict_R_heavy_blocks128": call_Rh}
+                  "predict_R_heavy_blocks128": call_Rh, "prune_compress_wanda_W": call_pcw,
+                  "prune_compress_attn_Q": call_pcq, "prune_compress_attn_K": call_pck,
+                  "prune_compress_attn_V_seq": call_pcv, "prune_compress_attn_P": call_pcp,
+                  "predict_R_attn_P_heads": call_Rp, "prune_quantize_fp8_heavy": call_pqh,
+                  "quantize_mxfp4_heavy": call_mxh, "quantize_nvfp4_heavy": call_nvh}
 
     def step(i):
         for f in calls.values():
@@ -277,6 +347,16 @@ def main():
         "predict_R_wanda_sweep_W": n_w * H * 2 + H * 4 + len(sweep_kept) * 5 * 8,
         # one read of X (the NVFP4 tensor-maximum pass reads it a second time)
         "predict_R_heavy_blocks128": n_h * H * 2 + (n_h // 128) * 2 * 5 * 8,
+        "prune_compress_wanda_W": n_w * H * 2 + n_w * H + n_w * H // 8 + H * 4,
+        "prune_compress_attn_Q": 32 * 16384 * 128 * 2 + 32 * 16384 * 64 * 2 + 32 * 16384 * 16,
+        "prune_compress_attn_K": 8 * 16384 * 128 * 2 + 8 * 16384 * 64 * 2 + 8 * 16384 * 16,
+        "prune_compress_attn_V_seq": 8 * 16384 * 128 * 2 + 8 * 16384 * 64 * 2 + 8 * 16384 * 16,
+        "prune_compress_attn_P": 32 * 4096 * 4096 * 2 + 32 * 4096 * 2048 * 2 + 32 * 4096 * 512,
+        "predict_R_attn_P_heads": 32 * 4096 * 4096 * 2 + 32 * 2 * 5 * 8,
+        "prune_quantize_fp8_heavy": n_h * H * 2 + n_h * H // 2 + n_h * H // 8 + n_h * 4,
+        "quantize_mxfp4_heavy": n_h * H * 2 + n_h * H // 2 + n_h * H // 32,
+        # one read of X (the tensor-maximum pass reads it a second time)
+        "quantize_nvfp4_heavy": n_h * H * 2 + n_h * H // 2 + n_h * H // 16 + 4,
     })
     # MFMA work of the compute-bound call: the reference product plus, per side,
     # the product of the [hi | lo] residual (2K deep)

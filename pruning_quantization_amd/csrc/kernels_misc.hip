@@ -86,23 +86,55 @@ hipError_t launch_col_l2norm(const RowDesc& d, double* partial, float* norms, hi
 // Transposed operand (row_stride == 1, reduction axis strided) -> dense
 // K-contiguous rows [B][R][K] through a 64x64 LDS tile, so both the reads
 // (along R) and the writes (along K) are contiguous.
-template <typename E>
+template <class E>
 __global__ __launch_bounds__(kBlock) void k_transpose_rows(const char* __restrict__ x, int64_t R,
                                                            int64_t K, int64_t bs, int64_t ks,
                                                            E* __restrict__ out) {
-  __shared__ E tile[64][65];
+  // 64 positions x 64 rows per tile.  In: 16-byte chunks along the rows of
+  // one position; out: 16-byte chunks along K of one row, each gathered from
+  // the tile two rows at a time.
+  constexpr int ES = sizeof(E), CE = 16 / ES, LINE = 64 * ES, LCH = LINE / 16;
+  __shared__ __align__(16) char tile[64 * LINE];  // [k][r]
   const int64_t k0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64, b = blockIdx.z;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int rcount = (int)((R - r0) < 64 ? (R - r0) : 64);
+  const int kcount = (int)((K - k0) < 64 ? (K - k0) : 64);  // multiple of 8
   const char* xb = x + b * bs;
-  for (int kk = ty; kk < 64; kk += kBlock / 64) {
-    const int64_t k = k0 + kk, r = r0 + tx;
-    tile[kk][tx] = (k < K && r < R) ? *reinterpret_cast<const E*>(xb + k * ks + r * (int64_t)sizeof(E))
-                                    : E(0);
+  for (int c = threadIdx.x; c < 64 * LCH; c += kBlock) {
+    const int kk = c / LCH, r = (c % LCH) * CE;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (kk < kcount && r < rcount) {
+      const char* p = xb + (k0 + kk) * ks + (r0 + r) * ES;
+      if (r + CE <= rcount) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        v = make_uint4(t.x, t.y, t.z, t.w);
+      } else {
+        E w[CE];
+        for (int i = 0; i < CE; ++i) w[i] = i < rcount - r ? reinterpret_cast<const E*>(p)[i] : E(0);
+        __builtin_memcpy(&v, w, 16);
+      }
+    }
+    *reinterpret_cast<uint4*>(tile + kk * LINE + r * ES) = v;
   }
   __syncthreads();
-  for (int rr = ty; rr < 64; rr += kBlock / 64) {
-    const int64_t r = r0 + rr, k = k0 + tx;
-    if (r < R && k < K) out[(b * R + r) * K + k] = tile[tx][rr];
+  constexpr int OCH = 64 / CE;  // output chunks per row per tile
+  for (int item = threadIdx.x; item < 32 * OCH; item += kBlock) {
+    const int rp = item % 32, c = item / 32;  // row pair, output chunk
+    const int rr = 2 * rp;
+    if (rr >= rcount || c * CE >= kcount) continue;
+    E a[CE], bb[CE];
+#pragma unroll
+    for (int i = 0; i < CE; ++i) {
+      const E* q = reinterpret_cast<const E*>(tile + (c * CE + i) * LINE + rr * ES);
+      a[i] = q[0];
+      bb[i] = q[1];
+    }
+    uint4 va, vb;
+    __builtin_memcpy(&va, a, 16);
+    __builtin_memcpy(&vb, bb, 16);
+    char* o = reinterpret_cast<char*>(out + (b * R + r0 + rr) * K + k0 + c * CE);
+    st4(o, va.x, va.y, va.z, va.w);
+    if (rr + 1 < rcount) st4(o + K * ES, vb.x, vb.y, vb.z, vb.w);
   }
 }
 

@@ -99,17 +99,24 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_rows(
 constexpr int kT_KT = 128;  // positions along K per tile (16 units)
 constexpr int kT_RT = 64;   // rows per tile
 
+// Loads move 16-byte chunks of a tile line (one k, kT_RT consecutive rows);
+// a chunk that crosses the last row is read element by element.  Selection
+// takes two adjacent rows per item (one 2E-byte LDS read per position), and
+// the compressed tile leaves in 16-byte chunks (8-byte ones when a row of
+// kept values is not a multiple of 16 bytes).
 template <class DT, bool WANDA>
 __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
     const char* __restrict__ x, int64_t R, int64_t K, int64_t bs, int64_t ks,
     const float* __restrict__ norm, char* __restrict__ vals, uint8_t* __restrict__ meta) {
   constexpr int E = DT::ESIZE;
+  constexpr int CE = 16 / E;                             // elements per 16-byte chunk
+  constexpr int LINE = kT_RT * E;                        // bytes of a tile line
+  constexpr int LCH = LINE / 16;                         // chunks per tile line
   constexpr int UT = kT_KT / 8;                          // units per tile row
   constexpr int OUT_ROW = kT_KT / 2 * E;                 // kept bytes per row per tile
-  constexpr int OUT_PAD = OUT_ROW + 16;
-  __shared__ __align__(16) char tile[kT_KT * kT_RT * E];  // [k][r]
-  __shared__ __align__(16) char otile[kT_RT * OUT_PAD];   // [r][kept bytes]
-  __shared__ __align__(16) uint8_t mtile[kT_RT * UT];     // [r][unit]
+  __shared__ __align__(16) char tile[kT_KT * LINE];      // [k][r]
+  __shared__ __align__(16) char otile[kT_RT * OUT_ROW];  // [r][kept bytes]
+  __shared__ __align__(16) uint8_t mtile[kT_RT * UT];    // [r][unit]
 
   const int64_t k0 = (int64_t)blockIdx.x * kT_KT;
   const int64_t r0 = (int64_t)blockIdx.y * kT_RT;
@@ -118,63 +125,110 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
   const int rcount = (int)((R - r0) < kT_RT ? (R - r0) : kT_RT);
   const int kcount = (int)((K - k0) < kT_KT ? (K - k0) : kT_KT);  // multiple of 8
 
-  // 1) load: each tile line (one k) is rcount contiguous elements
-  for (int e = threadIdx.x; e < kT_KT * kT_RT; e += kBlock) {
-    const int kk = e / kT_RT, rr = e % kT_RT;
-    uint32_t v = 0;
-    if (kk < kcount && rr < rcount) {
-      const char* p = xb + (k0 + kk) * ks + (r0 + rr) * E;
-      if constexpr (E == 2) v = *reinterpret_cast<const uint16_t*>(p);
-      else v = *reinterpret_cast<const uint32_t*>(p);
+  // 1) load
+  for (int c = threadIdx.x; c < kT_KT * LCH; c += kBlock) {
+    const int kk = c / LCH, r = (c % LCH) * CE;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (kk < kcount && r < rcount) {
+      const char* p = xb + (k0 + kk) * ks + (r0 + r) * E;
+      if (r + CE <= rcount) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        v = make_uint4(t.x, t.y, t.z, t.w);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (int i = 0; i < rcount - r; ++i) {
+          const uint32_t e = E == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(p)[i]
+                                    : reinterpret_cast<const uint32_t*>(p)[i];
+          if constexpr (E == 2) w[i >> 1] |= e << ((i & 1) * 16);
+          else w[i] = e;
+        }
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
-    if constexpr (E == 2) reinterpret_cast<uint16_t*>(tile)[e] = (uint16_t)v;
-    else reinterpret_cast<uint32_t*>(tile)[e] = v;
+    *reinterpret_cast<uint4*>(tile + kk * LINE + r * E) = v;
   }
   __syncthreads();
 
-  // 2) select per (row, unit)
-  for (int item = threadIdx.x; item < kT_RT * UT; item += kBlock) {
-    const int rr = item % kT_RT, uu = item / kT_RT;
+  // 2) select per (row pair, unit)
+  for (int item = threadIdx.x; item < (kT_RT / 2) * UT; item += kBlock) {
+    const int rp = item % (kT_RT / 2), uu = item / (kT_RT / 2);
+    const int rr = 2 * rp;
     if (rr < rcount && uu * 8 < kcount) {
-      Unit<DT> u;
+      Unit<DT> u0, u1;
 #pragma unroll
-      for (int i = 0; i < DT::W; ++i) u.w[i] = 0;
+      for (int i = 0; i < DT::W; ++i) u0.w[i] = u1.w[i] = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int e = (uu * 8 + i) * kT_RT + rr;
-        uint32_t v;
+        const char* q = tile + (uu * 8 + i) * LINE + rr * E;
         if constexpr (E == 2) {
-          v = reinterpret_cast<const uint16_t*>(tile)[e];
-          u.w[i >> 1] |= v << ((i & 1) * 16);
+          const uint32_t two = *reinterpret_cast<const uint32_t*>(q);  // rows rr, rr + 1
+          u0.w[i >> 1] |= (two & 0xFFFFu) << ((i & 1) * 16);
+          u1.w[i >> 1] |= (two >> 16) << ((i & 1) * 16);
         } else {
-          v = reinterpret_cast<const uint32_t*>(tile)[e];
-          u.w[i] = v;
+          const uint2 two = *reinterpret_cast<const uint2*>(q);
+          u0.w[i] = two.x;
+          u1.w[i] = two.y;
         }
       }
-      const uint32_t mb = select_unit<DT, WANDA>(u, norm, k0 + uu * 8);
-      store_kept(u, mb, otile + rr * OUT_PAD + uu * 4 * E);
-      mtile[rr * UT + uu] = (uint8_t)mb;
+      const uint32_t m0 = select_unit<DT, WANDA>(u0, norm, k0 + uu * 8);
+      const uint32_t m1 = select_unit<DT, WANDA>(u1, norm, k0 + uu * 8);
+      const Kept<DT> p0 = gather_kept(u0, m0), p1 = gather_kept(u1, m1);
+      char* o0 = otile + rr * OUT_ROW + uu * 4 * E;
+      if constexpr (E == 2) {
+        *reinterpret_cast<uint2*>(o0) = make_uint2(p0.k[0], p0.k[1]);
+        *reinterpret_cast<uint2*>(o0 + OUT_ROW) = make_uint2(p1.k[0], p1.k[1]);
+      } else {
+        *reinterpret_cast<uint4*>(o0) = make_uint4(p0.k[0], p0.k[1], p0.k[2], p0.k[3]);
+        *reinterpret_cast<uint4*>(o0 + OUT_ROW) = make_uint4(p1.k[0], p1.k[1], p1.k[2], p1.k[3]);
+      }
+      mtile[rr * UT + uu] = (uint8_t)m0;
+      mtile[(rr + 1) * UT + uu] = (uint8_t)m1;  // row rr + 1 past rcount is never written out
     }
   }
   __syncthreads();
 
   // 3) write: per row, kcount/2 kept elements and kcount/8 metadata bytes
   const int obytes = kcount / 2 * E;
-  constexpr int CH = 8;  // 8-byte chunks
-  const int nch = obytes / CH;
-  for (int item = threadIdx.x; item < kT_RT * (OUT_ROW / CH); item += kBlock) {
-    const int rr = item / (OUT_ROW / CH), c = item % (OUT_ROW / CH);
-    if (rr < rcount && c < nch) {
-      const int64_t orow = b * R + r0 + rr;
-      char* dst = vals + orow * (K / 2 * E) + k0 / 2 * E + c * CH;
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(otile + rr * OUT_PAD + c * CH);
+  const int64_t vrow = K / 2 * E;  // bytes per output row of kept values
+  if (vrow % 16 == 0) {
+    const int nch = obytes / 16;   // obytes is a multiple of 16 here unless K's tail is short
+    const int tail = obytes % 16;  // 0 or 8
+    for (int item = threadIdx.x; item < kT_RT * (OUT_ROW / 16); item += kBlock) {
+      const int rr = item / (OUT_ROW / 16), c = item % (OUT_ROW / 16);
+      if (rr < rcount) {
+        char* dst = vals + (b * R + r0 + rr) * vrow + k0 / 2 * E + c * 16;
+        const char* src = otile + rr * OUT_ROW + c * 16;
+        if (c < nch) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          st4(dst, v.x, v.y, v.z, v.w);
+        } else if (c == nch && tail) {
+          const uint2 v = *reinterpret_cast<const uint2*>(src);
+          st2(dst, v.x, v.y);
+        }
+      }
+    }
+  } else {
+    for (int item = threadIdx.x; item < kT_RT * (OUT_ROW / 8); item += kBlock) {
+      const int rr = item / (OUT_ROW / 8), c = item % (OUT_ROW / 8);
+      if (rr < rcount && c < obytes / 8) {
+        char* dst = vals + (b * R + r0 + rr) * vrow + k0 / 2 * E + c * 8;
+        const uint2 v = *reinterpret_cast<const uint2*>(otile + rr * OUT_ROW + c * 8);
+        st2(dst, v.x, v.y);
+      }
     }
   }
-  for (int item = threadIdx.x; item < kT_RT * UT; item += kBlock) {
-    const int rr = item / UT, uu = item % UT;
-    if (rr < rcount && uu * 8 < kcount) {
-      const int64_t orow = b * R + r0 + rr;
-      meta[orow * (K / 8) + k0 / 8 + uu] = mtile[rr * UT + uu];
+  const int mbytes = kcount / 8;
+  if ((K / 8) % 16 == 0 && mbytes == UT) {  // whole 16-byte metadata chunks
+    for (int rr = threadIdx.x; rr < rcount; rr += kBlock) {
+      const uint4 v = *reinterpret_cast<const uint4*>(mtile + rr * UT);
+      st4(meta + (b * R + r0 + rr) * (K / 8) + k0 / 8, v.x, v.y, v.z, v.w);
+    }
+  } else {
+    for (int item = threadIdx.x; item < kT_RT * UT; item += kBlock) {
+      const int rr = item / UT, uu = item % UT;
+      if (rr < rcount && uu < mbytes)
+        meta[(b * R + r0 + rr) * (K / 8) + k0 / 8 + uu] = mtile[rr * UT + uu];
     }
   }
 }

@@ -108,6 +108,25 @@ def test_prune_compress_transposed(dtype, shape):
     assert_same(raw_np(v).reshape(-1, shape[1] // 2), wv, "values")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_transposed_rows_not_filling_chunks(dtype):
+    # rows along the contiguous axis padded to 72 (16-byte aligned positions)
+    # but only 68 / 3 used: tiles end inside a 16-byte chunk
+    rng = np.random.default_rng(77)
+    for used in (68, 3):
+        raw = random_raw(rng, (2, 136, 72), dtype)
+        x = to_dev(raw, dtype)[:, :, :used]
+        rows = np.ascontiguousarray(np.swapaxes(raw[:, :, :used], 1, 2)).reshape(-1, 136)
+        v, m = S.prune_compress(x, axis=1)
+        wv, wm = O.prune_compress(rows, dtype)
+        assert_same(raw_np(m).reshape(-1, 17), wm, f"meta {used}")
+        assert_same(raw_np(v).reshape(-1, 68), wv, f"values {used}")
+        c, sc = S.quantize(x, "fp8", axis=1)                       # staged through the transpose
+        wc, ws = O.quantize_rows(rows, dtype, O.QSpec("fp8"))
+        assert_same(raw_np(sc).reshape(-1), ws, f"fp8 scales {used}")
+        assert_same(raw_np(c).reshape(-1, 136), wc, f"fp8 codes {used}")
+
+
 # ---------------------------------------------------------------------------
 # prune_quantize
 # ---------------------------------------------------------------------------
