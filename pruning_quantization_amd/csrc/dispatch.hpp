@@ -78,10 +78,32 @@ inline dim3 row_grid(const RowDesc& d, int team) {
 #endif
 constexpr int kBlocksPerCU = SPARQ24_BLOCKS_PER_CU;
 int device_cu_count();
-inline dim3 persistent_grid(int64_t nrows, int team) {
+
+// Workgroups of kernel K resident per CU (register and LDS limits), from the
+// runtime's occupancy calculator, queried once per kernel.
+template <auto K>
+inline int resident_blocks() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(K), kBlock,
+                                                     0) != hipSuccess ||
+        b < 1) {
+      (void)hipGetLastError();
+      b = kBlocksPerCU;
+    }
+    return b;
+  }();
+  return n;
+}
+
+// resident: workgroups of the kernel that fit on a CU at once.  A kernel
+// whose registers allow fewer than kBlocksPerCU gets only as many, so the
+// whole grid is resident and no second round of workgroups trails the first.
+inline dim3 persistent_grid(int64_t nrows, int team, int resident = kBlocksPerCU) {
   const int64_t rpb = kBlock / team;
   const int64_t need = (nrows + rpb - 1) / rpb;
-  const int64_t cap = (int64_t)device_cu_count() * kBlocksPerCU;
+  const int per_cu = resident < kBlocksPerCU ? resident : kBlocksPerCU;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
   const int64_t n = need < cap ? need : cap;
   return dim3((unsigned)(n > 0 ? n : 1));
 }

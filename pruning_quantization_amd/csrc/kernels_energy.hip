@@ -810,41 +810,35 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
     return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
-      const dim3 grid = persistent_grid(g.nrows, TEAM);
-      PartialSink k;
-      geom(TEAM, grid, k);
-      if (sel == SEL_WANDA) {  // rotated calls take no norms
-        hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, 0, SEL_WANDA>), grid, dim3(kBlock), 0, s,
-                           g, norm, p, k);
+      auto go = [&]<int R, int SEL>() {
+        constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL>;
+        const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
+        PartialSink k;
+        geom(TEAM, grid, k);
+        hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
         return hipGetLastError();
-      }
+      };
+      if (sel == SEL_WANDA)  // rotated calls take no norms
+        return go.template operator()<0, SEL_WANDA>();
       return with_rot<TEAM>(d.rot, [&]<int R>() {
-        if (sel == SEL_P48)
-          hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, R, SEL_P48>), grid, dim3(kBlock), 0, s,
-                             g, norm, p, k);
-        else
-          hipLaunchKernelGGL((k_energy_rows_bf16<TEAM, UPL, R, SEL_MAG>), grid, dim3(kBlock), 0, s,
-                             g, norm, p, k);
-        return hipGetLastError();
+        return sel == SEL_P48 ? go.template operator()<R, SEL_P48>()
+                              : go.template operator()<R, SEL_MAG>();
       });
     });
   }
   // fp32 and fp16 operands
   auto generic = [&]<class DT>() {
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
-      const dim3 grid = persistent_grid(g.nrows, TEAM);
-      PartialSink k;
-      geom(TEAM, grid, k);
-      if (wanda) {  // rotated calls take no norms
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, true, 0>), grid, dim3(kBlock), 0, s, g,
-                           norm, p, k);
+      auto go = [&]<bool WANDA, int R>() {
+        constexpr auto K = k_energy_rows<DT, TEAM, UPL, WANDA, R>;
+        const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
+        PartialSink k;
+        geom(TEAM, grid, k);
+        hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
         return hipGetLastError();
-      }
-      return with_rot<TEAM>(d.rot, [&]<int R>() {
-        hipLaunchKernelGGL((k_energy_rows<DT, TEAM, UPL, false, R>), grid, dim3(kBlock), 0, s, g,
-                           norm, p, k);
-        return hipGetLastError();
-      });
+      };
+      if (wanda) return go.template operator()<true, 0>();  // rotated calls take no norms
+      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<false, R>(); });
     });
   };
   if (d.dtype == 0) return generic.template operator()<F32T>();

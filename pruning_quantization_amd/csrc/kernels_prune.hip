@@ -446,9 +446,9 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
   return with_dtype(d.dtype, [&]<class DT>() {
     // LONG: rotation blocks over 512 elements, which need one-wave teams
     auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
-      const dim3 grid = persistent_grid(g.nrows, TEAM);
       auto go = [&]<bool W, int P, int CF, int R>() {
-        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>), grid, dim3(kBlock), 0,
+        constexpr auto K = k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>;
+        hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
                            s, g, norm, qmax, (char*)codes, meta, scales);
         return hipGetLastError();
       };

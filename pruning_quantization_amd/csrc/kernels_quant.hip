@@ -377,8 +377,9 @@ hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes
   return with_dtype(d.dtype, [&]<class DT>() {
     auto body = [&]<int TEAM, int UPL>() {
       return with_rot<TEAM>(d.rot, [&]<int R>() {
-        hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, R>), persistent_grid(g.nrows, TEAM),
-                           dim3(kBlock), 0, s, g, cfmt, qmax, (char*)codes, scales);
+        constexpr auto K = k_quant_rows<DT, TEAM, UPL, R>;
+        hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
+                           s, g, cfmt, qmax, (char*)codes, scales);
         return hipGetLastError();
       });
     };
