@@ -248,6 +248,15 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
     for (int i = 0; i < nd; ++i)
       if (pl.p.dense.fmt[i] == cf && pl.p.dense.qmax[i] == pl.p.kept.qmax[j]) pl.p.kept_twin[j] = i;
   }
+  auto is_int = [](int cf) { return cf == CF_INT8 || cf == CF_INT16; };
+  pl.p.n_kept_int = pl.p.n_kept_int_solo = pl.p.n_dense_int = 0;
+  for (int j = 0; j < nk; ++j) {
+    if (!is_int(pl.p.kept.fmt[j])) continue;
+    pl.p.kept_int[pl.p.n_kept_int++] = j;
+    if (pl.p.kept_twin[j] < 0) pl.p.kept_int_solo[pl.p.n_kept_int_solo++] = j;
+  }
+  for (int i = 0; i < nd; ++i)
+    if (is_int(pl.p.dense.fmt[i])) pl.p.dense_int[pl.p.n_dense_int++] = i;
   pl.p.kept.n = nk;
   pl.p.dense.n = nd;
   for (int i = 0; i < npairs; ++i) pl.f.dcol[i] += 2 + nk;

@@ -392,6 +392,12 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #ifndef SPARQ24_E_WAVES
 #define SPARQ24_E_WAVES 4
 #endif
+// INT quantizers evaluated per unpacked unit in one pass of the bf16 kernel.
+// 1: chunks of 2 or 4 share each unit's unpacking but raise register use
+// past four waves per SIMD (magnitude 2:4, spills) or three (Wanda), which
+// costs more than the shared unpacking saves.
+constexpr int kIntChunk = 1;
+
 template <int TEAM, int UPL, int ROT, int SEL>
 constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? SPARQ24_E_WAVES : 1;
 
@@ -466,29 +472,105 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
       sink_put<TEAM>(sink, lacc, row, 1, drop);
     }
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
-    // kept-side quantizers; a row format with a dense twin (same format and
-    // qmax) is evaluated by the twin's pass below, since both take their
-    // scale from the same maximum and quantize each kept value identically
+    // INT quantizers run in chunks of up to kIntChunk per pass over the row:
+    // each unit is unpacked once for the whole chunk.  A kept one with a
+    // dense twin (same format and qmax) under magnitude 2:4 is evaluated by
+    // the twin, since both take their scale from the same maximum and code
+    // each kept value identically: the dense pass accumulates kept and
+    // dropped positions apart and writes both columns.
+    // (quantizer indices are read from the kernel arguments by position:
+    // a pointer into them would force a private copy of the parameters)
+    auto kept_ints = [&]<int NQ>(int c0) {
+      pin_packed<UPL>(pk);
+      int idx[NQ];
+      float s[NQ], inv[NQ];
+      double acc[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        idx[i] = SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i];
+        row_scale(famk, p.kept.qmax[idx[i]], s[i], inv[i]);
+        acc[i] = 0.0;
+      }
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) acc[i] += (double)mag_sq_err_int<4>(s[i], inv[i], v);
+        __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+      }
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const double a = team_sum_f64<TEAM>(acc[i], redd);
+        if (writer) sink_put<TEAM>(sink, lacc, row, 2 + idx[i], a);
+      }
+    };
+    auto dense_ints = [&]<int NQ>(int c0) {
+      pin_packed<UPL>(pk);
+      int idx[NQ];
+      float s[NQ], inv[NQ];
+      double acck[NQ], accd[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        idx[i] = p.dense_int[c0 + i];
+        row_scale(famd, p.dense.qmax[idx[i]], s[i], inv[i]);
+        acck[i] = accd[i] = 0.0;
+      }
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+        const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          acck[i] += (double)mag_sq_err_int<4>(s[i], inv[i], vk);
+          accd[i] += (double)mag_sq_err_int<4>(s[i], inv[i], vd);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+      }
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        int twin = -1;
+        if (SEL == SEL_MAG)
+          for (int k = 0; k < p.kept.n; ++k)
+            if (p.kept_twin[k] == idx[i]) twin = k;
+        double a;
+        if (twin >= 0) {
+          const double ak = team_sum_f64<TEAM>(acck[i], redd);
+          a = team_sum_f64<TEAM>(accd[i], redd) + ak;
+          if (writer) sink_put<TEAM>(sink, lacc, row, 2 + twin, ak);
+        } else {
+          a = team_sum_f64<TEAM>(acck[i] + accd[i], redd);
+        }
+        if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + idx[i], a);
+      }
+    };
+    auto chunks = [&](int n, auto&& run) {
+      for (int c0 = 0; c0 < n; c0 += kIntChunk) {
+        const int nq = n - c0 < kIntChunk ? n - c0 : kIntChunk;
+        if constexpr (kIntChunk >= 4) {
+          if (nq == 4) { run.template operator()<4>(c0); continue; }
+          if (nq == 3) { run.template operator()<3>(c0); continue; }
+        }
+        if (nq == 2) run.template operator()<2>(c0);
+        else run.template operator()<1>(c0);
+      }
+    };
+    chunks(SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int, kept_ints);
+    chunks(p.n_dense_int, dense_ints);
+
+    // the other formats, one pass each
     for (int q = 0; q < p.kept.n; ++q) {
+      const int fmt = p.kept.fmt[q];
+      if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
       if (SEL == SEL_MAG && p.kept_twin[q] >= 0) continue;
       pin_packed<UPL>(pk);
-      const int fmt = p.kept.fmt[q];
       double acc = 0.0;
-      if (fmt == CF_FP8 || fmt == CF_INT8 || fmt == CF_INT16) {
+      if (fmt == CF_FP8) {
         float s, inv;
         row_scale(famk, p.kept.qmax[q], s, inv);
-        if (fmt == CF_FP8) {
 #pragma unroll
-          for (int j = 0; j < UPL; ++j) {
-            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            acc += (double)mag_sq_err_fp8<4>(s, inv, v);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < UPL; ++j) {
-            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            acc += (double)mag_sq_err_int<4>(s, inv, v);
-          }
+        for (int j = 0; j < UPL; ++j) {
+          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+          acc += (double)mag_sq_err_fp8<4>(s, inv, v);
         }
       } else if (fmt == CF_NV) {
 #pragma unroll
@@ -507,10 +589,11 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
       if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
     }
     for (int q = 0; q < p.dense.n; ++q) {
-      pin_packed<UPL>(pk);
       const int fmt = p.dense.fmt[q];
+      if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
+      pin_packed<UPL>(pk);
       double acc = 0.0;
-      if (fmt == CF_INT8 || fmt == CF_INT16 || fmt == CF_FP8) {
+      if (fmt == CF_FP8) {
         int twin = -1;
         if (SEL == SEL_MAG)
           for (int k = 0; k < p.kept.n; ++k)
@@ -518,22 +601,12 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         float s, inv;
         row_scale(famd, p.dense.qmax[q], s, inv);
         double acck = 0.0;  // kept positions; acc holds the dropped ones
-        if (fmt == CF_FP8) {
 #pragma unroll
-          for (int j = 0; j < UPL; ++j) {
-            const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-            acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
-            acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < UPL; ++j) {
-            const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-            acck += (double)mag_sq_err_int<4>(s, inv, vk);
-            acc += (double)mag_sq_err_int<4>(s, inv, vd);
-          }
+        for (int j = 0; j < UPL; ++j) {
+          const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+          const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+          acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
+          acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
         }
         if (twin >= 0) {
           acck = team_sum_f64<TEAM>(acck, redd);

@@ -59,6 +59,11 @@ struct EnergyParams {
   // the kept maximum is the row maximum, so the twin's codes on the kept
   // positions are the kept-side codes.
   int kept_twin[kMaxQ];
+  // INT quantizers (CF_INT8 / CF_INT16) by side, for the bf16 kernel's
+  // chunked passes: every kept one, the kept ones without a twin, every
+  // dense one (indices into kept / dense)
+  int kept_int[kMaxQ], kept_int_solo[kMaxQ], dense_int[kMaxQ];
+  int n_kept_int, n_kept_int_solo, n_dense_int;
   const float* nv_tamax;       // device T for NVFP4 (or null -> reduce partials)
   const uint32_t* nv_partials; // fp32 bit patterns of partial maxima
   int n_partials;
