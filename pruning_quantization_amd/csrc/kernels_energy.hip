@@ -882,7 +882,7 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   };
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
-    return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
+    auto body = [&]<int TEAM, int UPL>() {
       auto go = [&]<int R, int SEL>() {
         constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL>;
         const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
@@ -897,7 +897,10 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
         return sel == SEL_P48 ? go.template operator()<R, SEL_P48>()
                               : go.template operator()<R, SEL_MAG>();
       });
-    });
+    };
+    if (d.rot.n > 512)  // rotation blocks over 512 elements need one-wave teams
+      return with_row_variant<0>(nunits, body);
+    return with_row_variant<SPARQ24_WIDE_E>(nunits, body);
   }
   // fp32 and fp16 operands
   auto generic = [&]<class DT>() {
