@@ -485,7 +485,7 @@ def main():
 
     dom = "prune_quantize_fp8"
     achieved = per_call[dom]["GBps"]
-    kname = "k_prune_quantize<BF16T, 128, 4, false, 2, 0, false>"
+    kname = "k_prune_quantize<BF16T, 128, 4, false, 2, 0, 0>"
     traffic, traffic_note = measured_traffic(kname, T, H)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
