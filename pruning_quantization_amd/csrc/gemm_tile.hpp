@@ -269,14 +269,288 @@ auto do_half = [&]<int half>() {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-stage form of the same tile for bf16 and 2:4-compressed A (the e4m3
+// form stays on k_gemm): slabs go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging), S slabs deep, so each slab
+// is requested S - 1 slabs before it is consumed and L2 misses stay hidden.
+// LDS rows are unpadded; their 16-byte chunks are XOR-swizzled by row so the
+// 16 rows a fragment read touches fall in distinct bank groups.  Fragments
+// are read in inline-asm blocks that wait for their own results, so the only
+// waits on the slab loads are the explicit per-wave vmcnt waits before the
+// workgroup barrier that publishes a slab (the barrier is the raw s_barrier:
+// __syncthreads would drain every load in flight).  Rows past M or N are
+// loaded clamped (their products are never stored; the row-sum epilogue
+// masks the columns past N).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+struct GemmStages;
+template <>
+struct GemmStages<GM_BF16> {  // 32-deep slabs: A 16 KB + B 16 KB, 4 stages
+  static constexpr int SK = 32, S = 4, ACH = 4, BCH = 4, MB = 0;
+};
+template <>
+struct GemmStages<GM_SPARSE> {  // 64-deep slabs: A 16 KB + B 32 KB + meta 2 KB, 3 stages
+  static constexpr int SK = 64, S = 3, ACH = 4, BCH = 8, MB = 2048;
+};
+
+// chunk slot of chunk c in row r of an LDS slab with NCH 16-byte chunks per row
+template <int NCH>
+__device__ inline int gemm_swz(int r) {
+  return NCH == 8 ? (r & 7) : ((r >> 1) & 3);
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+template <int MODE, int EPI>
+__global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
+  using C = GemmStages<MODE>;
+  constexpr bool SPARSE = MODE == GM_SPARSE;
+  constexpr int BM = kGM, BN = kGN, WTM = 128, WTN = 64, WN = BN / WTN, NT = 512;
+  constexpr int TI = WTM / 16, TJ = WTN / 16, TH = TI / 2;
+  constexpr int SK = C::SK, S = C::S, ACH = C::ACH, BCH = C::BCH;
+  constexpr int A_BYTES = BM * ACH * 16, B_BYTES = BN * BCH * 16;
+  constexpr int STAGE = A_BYTES + B_BYTES + C::MB;
+  constexpr int QA = BM * ACH / NT, QB = BN * BCH / NT;
+  constexpr int QPS = QA + QB + (SPARSE ? 1 : 0);  // slab loads per thread per stage
+  static_assert(QA * NT == BM * ACH && QB * NT == BN * BCH, "tile / thread mismatch");
+  static_assert(A_BYTES + 3 * (BCH * 256) + 1024 < 65536, "ds_read offsets fit 16 bits");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
+  __shared__ float red[EPI == EPI_ROWSQ ? WN : 1][EPI == EPI_ROWSQ ? BM : 1];
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* B = (const uint16_t*)g.B;
+  const int64_t M = g.M, N = g.N, K = g.K;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
+  // XCD-aware tile order (as in k_gemm)
+  const int64_t ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM, total = ntm * ntn;
+  const int64_t pid = blockIdx.x, per = total / 8;
+  const int64_t lid = pid < per * 8 ? (pid % 8) * per + pid / 8 : pid;
+  constexpr int64_t kGroupM = 8;
+  const int64_t ingroup = kGroupM * ntn, first = (lid / ingroup) * kGroupM;
+  const int64_t gsz = ntm - first < kGroupM ? ntm - first : kGroupM;
+  const int64_t tm = first + (lid % ingroup) % gsz, tn = (lid % ingroup) / gsz;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  // Slab k0 into stage buffer buf: position p = q * NT + tid of a region is
+  // row p / NCH, slot p % NCH; a wave's load writes 64 consecutive positions.
+  auto issue = [&](int buf, int64_t k0) {
+    uint8_t* st = smem + buf * STAGE;
+    const int64_t ak = SPARSE ? k0 / 2 : k0, bk = k0 % K;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int p = q * NT + tid, r = p / ACH, c = (p % ACH) ^ gemm_swz<ACH>(r);
+      const int64_t m = m0 + r < M ? m0 + r : M - 1;
+      __builtin_amdgcn_global_load_lds(A + m * g.lda + ak + c * 8,
+                                       (lds_void_t*)(st + (q * NT + w * 64) * 16), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int p = q * NT + tid, r = p / BCH, c = (p % BCH) ^ gemm_swz<BCH>(r);
+      const int64_t n = n0 + r < N ? n0 + r : N - 1;
+      __builtin_amdgcn_global_load_lds(B + n * g.ldb + bk + c * 8,
+                                       (lds_void_t*)(st + A_BYTES + (q * NT + w * 64) * 16), 16, 0, 0);
+    }
+    if constexpr (SPARSE) {  // 8 metadata bytes per row: dword p is row p / 2, half p % 2
+      const int r = tid >> 1;
+      const int64_t m = m0 + r < M ? m0 + r : M - 1;
+      __builtin_amdgcn_global_load_lds(g.meta + m * g.ldm + k0 / 8 + (tid & 1) * 4,
+                                       (lds_void_t*)(st + A_BYTES + B_BYTES + w * 64 * 4), 4, 0, 0);
+    }
+  };
+
+  // per-lane LDS byte addresses of the fragment reads within stage 0
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_void_t*)smem;
+  const int fr = lane & 15, h = lane >> 4;
+  const unsigned a_ad = lds0 + (unsigned)(((wm * WTM + fr) * ACH + (h ^ gemm_swz<ACH>(fr))) * 16);
+  const unsigned b_ad = lds0 + A_BYTES + (unsigned)(((wn * WTN + fr) * BCH + (h ^ gemm_swz<BCH>(fr))) * 16);
+  // sparse: B's second chunk (k 32 + 8h) and the metadata halfword of lane group h
+  const unsigned b2_ad = lds0 + A_BYTES + (unsigned)(((wn * WTN + fr) * BCH + ((4 + h) ^ gemm_swz<BCH>(fr))) * 16);
+  const unsigned m_ad = lds0 + A_BYTES + B_BYTES + (unsigned)((wm * WTM + fr) * 8 + 2 * h);
+  constexpr int AR = 16 * ACH * 16, BR = 16 * BCH * 16;  // bytes between 16-row tiles
+
+  f32x4_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nk = g.Kp / SK;
+#pragma unroll
+  for (int s = 0; s + 1 < S; ++s) issue(s, (s < nk ? s : nk - 1) * SK);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt % S);
+    wait_vmcnt<(S - 2) * QPS>();  // this wave's loads of slab kt have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's have, and slab kt - 1 is consumed
+    asm volatile("" ::: "memory");
+    {
+      const int64_t nx = kt + S - 1;
+      issue((int)(nx % S), (nx < nk ? nx : nk - 1) * SK);
+    }
+    const unsigned so = (unsigned)(cur * STAGE);
+    const unsigned aa = a_ad + so, ba = b_ad + so;
+    if constexpr (SPARSE) {
+      const unsigned b2 = b2_ad + so, ma = m_ad + so;
+      u32x4_t bl[TJ], bh[TJ], af[TH];
+      unsigned ix[TH];
+      asm volatile(
+          "ds_read_b128 %0, %16 offset:%c20\n\t"
+          "ds_read_b128 %1, %16 offset:%c21\n\t"
+          "ds_read_b128 %2, %16 offset:%c22\n\t"
+          "ds_read_b128 %3, %16 offset:%c23\n\t"
+          "ds_read_b128 %4, %17 offset:%c20\n\t"
+          "ds_read_b128 %5, %17 offset:%c21\n\t"
+          "ds_read_b128 %6, %17 offset:%c22\n\t"
+          "ds_read_b128 %7, %17 offset:%c23\n\t"
+          "ds_read_b128 %8, %18\n\t"
+          "ds_read_b128 %9, %18 offset:%c24\n\t"
+          "ds_read_b128 %10, %18 offset:%c25\n\t"
+          "ds_read_b128 %11, %18 offset:%c26\n\t"
+          "ds_read_u16 %12, %19\n\t"
+          "ds_read_u16 %13, %19 offset:128\n\t"
+          "ds_read_u16 %14, %19 offset:256\n\t"
+          "ds_read_u16 %15, %19 offset:384\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(bl[0]), "=&v"(bl[1]), "=&v"(bl[2]), "=&v"(bl[3]), "=&v"(bh[0]), "=&v"(bh[1]),
+            "=&v"(bh[2]), "=&v"(bh[3]), "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]),
+            "=&v"(ix[0]), "=&v"(ix[1]), "=&v"(ix[2]), "=&v"(ix[3])
+          : "v"(ba), "v"(b2), "v"(aa), "v"(ma), "i"(0), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR),
+            "i"(2 * AR), "i"(3 * AR)
+          : "memory");
+      bf16x16_t bfr[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[j] = __builtin_shufflevector(__builtin_bit_cast(bf16x8_t, bl[j]), __builtin_bit_cast(bf16x8_t, bh[j]),
+                                         0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8_t, af[ii]), bfr[j],
+                                                                 acc[ii][j], (int)ix[ii], 0, 0);
+      asm volatile(
+          "ds_read_b128 %0, %8 offset:%c10\n\t"
+          "ds_read_b128 %1, %8 offset:%c11\n\t"
+          "ds_read_b128 %2, %8 offset:%c12\n\t"
+          "ds_read_b128 %3, %8 offset:%c13\n\t"
+          "ds_read_u16 %4, %9 offset:512\n\t"
+          "ds_read_u16 %5, %9 offset:640\n\t"
+          "ds_read_u16 %6, %9 offset:768\n\t"
+          "ds_read_u16 %7, %9 offset:896\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(ix[0]), "=&v"(ix[1]),
+            "=&v"(ix[2]), "=&v"(ix[3])
+          : "v"(aa), "v"(ma), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
+          : "memory");
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[TH + ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+              __builtin_bit_cast(bf16x8_t, af[ii]), bfr[j], acc[TH + ii][j], (int)ix[ii], 0, 0);
+    } else {
+      u32x4_t bf[TJ], af[TH];
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %8 offset:%c10\n\t"
+          "ds_read_b128 %2, %8 offset:%c11\n\t"
+          "ds_read_b128 %3, %8 offset:%c12\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "ds_read_b128 %5, %9 offset:%c13\n\t"
+          "ds_read_b128 %6, %9 offset:%c14\n\t"
+          "ds_read_b128 %7, %9 offset:%c15\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), "=&v"(af[0]), "=&v"(af[1]),
+            "=&v"(af[2]), "=&v"(af[3])
+          : "v"(ba), "v"(aa), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR), "i"(2 * AR), "i"(3 * AR)
+          : "memory");
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
+                                                               __builtin_bit_cast(bf16x8_t, bf[j]), acc[ii][j], 0, 0, 0);
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:%c5\n\t"
+          "ds_read_b128 %1, %4 offset:%c6\n\t"
+          "ds_read_b128 %2, %4 offset:%c7\n\t"
+          "ds_read_b128 %3, %4 offset:%c8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3])
+          : "v"(aa), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
+          : "memory");
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[TH + ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
+                                                                    __builtin_bit_cast(bf16x8_t, bf[j]),
+                                                                    acc[TH + ii][j], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing clamped slab loads land before LDS is reused or released
+  asm volatile("" ::: "memory");
+  // lane holds C[4 * (lane >> 4) + v][lane & 15] of each 16x16 tile
+  if constexpr (EPI == EPI_ROWSQ) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const bool nv = n0 + wn * WTN + j * 16 + (lane & 15) < N;  // clamped B rows past N
+          sq = __builtin_fmaf(acc[i][j][v], nv ? acc[i][j][v] : 0.0f, sq);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+        if ((lane & 15) == 0) red[wn][wm * WTM + i * 16 + 4 * (lane >> 4) + v] = sq;
+      }
+    __syncthreads();
+    for (int r = tid; r < BM; r += NT) {
+      const int64_t m = m0 + r;
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < WN; ++q) a += red[q][r];
+      if (m < M) g.out[m * g.ld_out + tn] = a;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + v;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int64_t n = n0 + wn * WTN + j * 16 + (lane & 15);
+          if (m < M && n < N) g.out[m * g.ld_out + n] = acc[i][j][v];
+        }
+      }
+  }
+}
+
+#ifndef SPARQ24_GEMM_DMA
+#define SPARQ24_GEMM_DMA 1
+#endif
+
 inline int64_t gemm_tiles(int64_t M, int64_t N) {
   return ((M + kGM - 1) / kGM) * ((N + kGN - 1) / kGN);
 }
 
 template <int MODE, int EPI>
 inline hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<kGM, kGN, 128, 64, MODE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)),
-                     dim3(512), 0, s, g);
+  if constexpr (SPARQ24_GEMM_DMA && MODE != GM_FP8)
+    hipLaunchKernelGGL((k_gemm_dma<MODE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)), dim3(512), 0,
+                       s, g);
+  else
+    hipLaunchKernelGGL((k_gemm<kGM, kGN, 128, 64, MODE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)),
+                       dim3(512), 0, s, g);
   return hipGetLastError();
 }
 
