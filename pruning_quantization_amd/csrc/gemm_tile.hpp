@@ -270,8 +270,8 @@ auto do_half = [&]<int half>() {
 }
 
 // ---------------------------------------------------------------------------
-// Multi-stage form of the same tile for bf16 and 2:4-compressed A (the e4m3
-// form stays on k_gemm): slabs go from global memory straight into LDS with
+// Multi-stage form of the same tile (every operand kind; k_gemm is the
+// register-staged form kept for comparison): slabs go from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging), S slabs deep, so each slab
 // is requested S - 1 slabs before it is consumed and L2 misses stay hidden.
 // LDS rows are unpadded; their 16-byte chunks are XOR-swizzled by row so the
@@ -294,6 +294,10 @@ struct GemmStages<GM_BF16> {  // 32-deep slabs: A 16 KB + B 16 KB, 4 stages
 template <>
 struct GemmStages<GM_SPARSE> {  // 64-deep slabs: A 16 KB + B 32 KB + meta 2 KB, 3 stages
   static constexpr int SK = 64, S = 3, ACH = 4, BCH = 8, MB = 2048;
+};
+template <>
+struct GemmStages<GM_FP8> {  // 128-code slabs (64 units): A 32 KB + B 32 KB, 2 stages
+  static constexpr int SK = 64, S = 2, ACH = 8, BCH = 8, MB = 0;
 };
 
 // chunk slot of chunk c in row r of an LDS slab with NCH 16-byte chunks per row
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
   constexpr int QPS = QA + QB + (SPARSE ? 1 : 0);  // slab loads per thread per stage
   static_assert(QA * NT == BM * ACH && QB * NT == BN * BCH, "tile / thread mismatch");
   static_assert(A_BYTES + 3 * (BCH * 256) + 1024 < 65536, "ds_read offsets fit 16 bits");
+  static_assert(MODE != GM_FP8 || 16 * ACH == 16 * BCH, "e4m3 A and B fragments share row offsets");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
   __shared__ float red[EPI == EPI_ROWSQ ? WN : 1][EPI == EPI_ROWSQ ? BM : 1];
   const uint16_t* A = (const uint16_t*)g.A;
@@ -454,6 +459,69 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
         for (int j = 0; j < TJ; ++j)
           acc[TH + ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
               __builtin_bit_cast(bf16x8_t, af[ii]), bfr[j], acc[TH + ii][j], (int)ix[ii], 0, 0);
+    } else if constexpr (MODE == GM_FP8) {
+      // a lane's 32 codes of a row are chunks 2h and 2h + 1 (k 32h .. 32h + 31),
+      // the same k positions for A and B; rows in two halves (register budget)
+      const unsigned al = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + ((2 * h) ^ gemm_swz<8>(fr))) * 16);
+      const unsigned ah = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + ((2 * h + 1) ^ gemm_swz<8>(fr))) * 16);
+      const unsigned bl = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + ((2 * h) ^ gemm_swz<8>(fr))) * 16);
+      const unsigned bh = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + ((2 * h + 1) ^ gemm_swz<8>(fr))) * 16);
+      u32x4_t b0[TJ], b1[TJ], x0[TH], x1[TH];
+      asm volatile(
+          "ds_read_b128 %0, %16\n\t"
+          "ds_read_b128 %1, %16 offset:%c20\n\t"
+          "ds_read_b128 %2, %16 offset:%c21\n\t"
+          "ds_read_b128 %3, %16 offset:%c22\n\t"
+          "ds_read_b128 %4, %17\n\t"
+          "ds_read_b128 %5, %17 offset:%c20\n\t"
+          "ds_read_b128 %6, %17 offset:%c21\n\t"
+          "ds_read_b128 %7, %17 offset:%c22\n\t"
+          "ds_read_b128 %8, %18\n\t"
+          "ds_read_b128 %9, %18 offset:%c20\n\t"
+          "ds_read_b128 %10, %18 offset:%c21\n\t"
+          "ds_read_b128 %11, %18 offset:%c22\n\t"
+          "ds_read_b128 %12, %19\n\t"
+          "ds_read_b128 %13, %19 offset:%c20\n\t"
+          "ds_read_b128 %14, %19 offset:%c21\n\t"
+          "ds_read_b128 %15, %19 offset:%c22\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(b0[0]), "=&v"(b0[1]), "=&v"(b0[2]), "=&v"(b0[3]), "=&v"(b1[0]), "=&v"(b1[1]),
+            "=&v"(b1[2]), "=&v"(b1[3]), "=&v"(x0[0]), "=&v"(x0[1]), "=&v"(x0[2]), "=&v"(x0[3]),
+            "=&v"(x1[0]), "=&v"(x1[1]), "=&v"(x1[2]), "=&v"(x1[3])
+          : "v"(bl), "v"(bh), "v"(al), "v"(ah), "i"(BR), "i"(2 * BR), "i"(3 * BR)
+          : "memory");
+      i32x8_t bfr[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[j] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b0[j], b1[j], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0[ii], x1[ii], 0, 1, 2, 3, 4, 5, 6, 7)), bfr[j],
+              acc[ii][j], 0, 0, 0, 0, 0, 0);
+      asm volatile(
+          "ds_read_b128 %0, %8 offset:%c10\n\t"
+          "ds_read_b128 %1, %8 offset:%c11\n\t"
+          "ds_read_b128 %2, %8 offset:%c12\n\t"
+          "ds_read_b128 %3, %8 offset:%c13\n\t"
+          "ds_read_b128 %4, %9 offset:%c10\n\t"
+          "ds_read_b128 %5, %9 offset:%c11\n\t"
+          "ds_read_b128 %6, %9 offset:%c12\n\t"
+          "ds_read_b128 %7, %9 offset:%c13\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x0[0]), "=&v"(x0[1]), "=&v"(x0[2]), "=&v"(x0[3]), "=&v"(x1[0]), "=&v"(x1[1]),
+            "=&v"(x1[2]), "=&v"(x1[3])
+          : "v"(al), "v"(ah), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
+          : "memory");
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[TH + ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0[ii], x1[ii], 0, 1, 2, 3, 4, 5, 6, 7)), bfr[j],
+              acc[TH + ii][j], 0, 0, 0, 0, 0, 0);
     } else {
       u32x4_t bf[TJ], af[TH];
       asm volatile(
@@ -526,10 +594,14 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + v;
+        float sa = 1.0f;
+        if constexpr (MODE == GM_FP8) sa = m < M ? g.scale_a[m] : 0.0f;
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int64_t n = n0 + wn * WTN + j * 16 + (lane & 15);
-          if (m < M && n < N) g.out[m * g.ld_out + n] = acc[i][j][v];
+          float c = acc[i][j][v];
+          if constexpr (MODE == GM_FP8) c = c * sa * (n < N ? g.scale_b[n] : 0.0f);
+          if (m < M && n < N) g.out[m * g.ld_out + n] = c;
         }
       }
   }
@@ -545,7 +617,7 @@ inline int64_t gemm_tiles(int64_t M, int64_t N) {
 
 template <int MODE, int EPI>
 inline hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if constexpr (SPARQ24_GEMM_DMA && MODE != GM_FP8)
+  if constexpr (SPARQ24_GEMM_DMA)
     hipLaunchKernelGGL((k_gemm_dma<MODE, EPI>), dim3((unsigned)gemm_tiles(g.M, g.N)), dim3(512), 0,
                        s, g);
   else
