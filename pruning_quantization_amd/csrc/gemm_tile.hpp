@@ -12,8 +12,10 @@
 // (established by an in-bounds lane-layout check of the instruction).
 //
 // Workgroup tile 256 x 256, eight waves of 128 x 64 (8 x 4 tiles of 16 x 16),
-// 64-deep K slabs double-buffered in LDS with padded rows (the 16 rows a
-// fragment read touches fall in distinct banks), fp32 accumulation.  A
+// fp32 accumulation.  k_gemm_dma (below, the form every launch uses) streams
+// slabs straight into LDS several slabs ahead; k_gemm, the register-staged
+// form with 64-deep K slabs double-buffered in padded LDS rows, is built only
+// with SPARQ24_GEMM_DMA=0, as the baseline it is measured against.  A
 // lane's k values of a fragment are the same positions for A and B, which is
 // all the dense product needs.  Epilogue: per-row sums of C^2 over the tile's
 // columns (EPI_ROWSQ) or C stored as fp32 (EPI_STORE).  GM_FP8 runs the same
@@ -270,10 +272,11 @@ auto do_half = [&]<int half>() {
 }
 
 // ---------------------------------------------------------------------------
-// Multi-stage form of the same tile (every operand kind; k_gemm is the
-// register-staged form kept for comparison): slabs go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no register staging), S slabs deep, so each slab
-// is requested S - 1 slabs before it is consumed and L2 misses stay hidden.
+// Multi-stage form of the same tile, used for every operand kind (k_gemm
+// above is the register-staged form, built only for comparison): slabs go
+// from global memory straight into LDS with global_load_lds (no register
+// staging), S slabs deep, so each slab is requested S - 1 slabs before it is
+// consumed and L2 misses stay hidden.
 // LDS rows are unpadded; their 16-byte chunks are XOR-swizzled by row so the
 // 16 rows a fragment read touches fall in distinct bank groups.  Fragments
 // are read in inline-asm blocks that wait for their own results, so the only
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
   constexpr int QPS = QA + QB + (SPARSE ? 1 : 0);  // slab loads per thread per stage
   static_assert(QA * NT == BM * ACH && QB * NT == BN * BCH, "tile / thread mismatch");
   static_assert(A_BYTES + 3 * (BCH * 256) + 1024 < 65536, "ds_read offsets fit 16 bits");
-  static_assert(MODE != GM_FP8 || 16 * ACH == 16 * BCH, "e4m3 A and B fragments share row offsets");
+  static_assert(MODE != GM_FP8 || ACH == BCH, "e4m3 A and B fragments share row offsets");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
   __shared__ float red[EPI == EPI_ROWSQ ? WN : 1][EPI == EPI_ROWSQ ? BM : 1];
   const uint16_t* A = (const uint16_t*)g.A;
