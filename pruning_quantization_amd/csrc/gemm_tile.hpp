@@ -291,8 +291,8 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 template <int MODE>
 struct GemmStages;
 template <>
-struct GemmStages<GM_BF16> {  // 32-deep slabs: A 16 KB + B 16 KB, 4 stages
-  static constexpr int SK = 32, S = 4, ACH = 4, BCH = 4, MB = 0;
+struct GemmStages<GM_BF16> {  // 64-deep slabs (full 128-byte rows): A 32 KB + B 32 KB, 2 stages
+  static constexpr int SK = 64, S = 2, ACH = 8, BCH = 8, MB = 0;
 };
 template <>
 struct GemmStages<GM_SPARSE> {  // 64-deep slabs: A 16 KB + B 32 KB + meta 2 KB, 3 stages
@@ -402,9 +402,8 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
       issue((int)(nx % S), (nx < nk ? nx : nk - 1) * SK);
     }
     const unsigned so = (unsigned)(cur * STAGE);
-    const unsigned aa = a_ad + so, ba = b_ad + so;
     if constexpr (SPARSE) {
-      const unsigned b2 = b2_ad + so, ma = m_ad + so;
+      const unsigned aa = a_ad + so, ba = b_ad + so, b2 = b2_ad + so, ma = m_ad + so;
       u32x4_t bl[TJ], bh[TJ], af[TH];
       unsigned ix[TH];
       asm volatile(
@@ -526,43 +525,50 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
               __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0[ii], x1[ii], 0, 1, 2, 3, 4, 5, 6, 7)), bfr[j],
               acc[TH + ii][j], 0, 0, 0, 0, 0, 0);
     } else {
-      u32x4_t bf[TJ], af[TH];
-      asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %8 offset:%c10\n\t"
-          "ds_read_b128 %2, %8 offset:%c11\n\t"
-          "ds_read_b128 %3, %8 offset:%c12\n\t"
-          "ds_read_b128 %4, %9\n\t"
-          "ds_read_b128 %5, %9 offset:%c13\n\t"
-          "ds_read_b128 %6, %9 offset:%c14\n\t"
-          "ds_read_b128 %7, %9 offset:%c15\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), "=&v"(af[0]), "=&v"(af[1]),
-            "=&v"(af[2]), "=&v"(af[3])
-          : "v"(ba), "v"(aa), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR), "i"(2 * AR), "i"(3 * AR)
-          : "memory");
+      // two 32-deep steps per slab; lane group h reads chunk 4 st + h of its rows
 #pragma unroll
-      for (int ii = 0; ii < TH; ++ii)
+      for (int st = 0; st < SK / 32; ++st) {
+        const unsigned aa = lds0 + so + (unsigned)(((wm * WTM + fr) * ACH + ((4 * st + h) ^ gemm_swz<ACH>(fr))) * 16);
+        const unsigned ba =
+            lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * BCH + ((4 * st + h) ^ gemm_swz<BCH>(fr))) * 16);
+        u32x4_t bf[TJ], af[TH];
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:%c10\n\t"
+            "ds_read_b128 %2, %8 offset:%c11\n\t"
+            "ds_read_b128 %3, %8 offset:%c12\n\t"
+            "ds_read_b128 %4, %9\n\t"
+            "ds_read_b128 %5, %9 offset:%c13\n\t"
+            "ds_read_b128 %6, %9 offset:%c14\n\t"
+            "ds_read_b128 %7, %9 offset:%c15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]), "=&v"(af[0]), "=&v"(af[1]),
+              "=&v"(af[2]), "=&v"(af[3])
+            : "v"(ba), "v"(aa), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR), "i"(2 * AR), "i"(3 * AR)
+            : "memory");
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
-                                                               __builtin_bit_cast(bf16x8_t, bf[j]), acc[ii][j], 0, 0, 0);
-      asm volatile(
-          "ds_read_b128 %0, %4 offset:%c5\n\t"
-          "ds_read_b128 %1, %4 offset:%c6\n\t"
-          "ds_read_b128 %2, %4 offset:%c7\n\t"
-          "ds_read_b128 %3, %4 offset:%c8\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3])
-          : "v"(aa), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
-          : "memory");
+        for (int ii = 0; ii < TH; ++ii)
 #pragma unroll
-      for (int ii = 0; ii < TH; ++ii)
+          for (int j = 0; j < TJ; ++j)
+            acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
+                                                                 __builtin_bit_cast(bf16x8_t, bf[j]), acc[ii][j], 0, 0, 0);
+        asm volatile(
+            "ds_read_b128 %0, %4 offset:%c5\n\t"
+            "ds_read_b128 %1, %4 offset:%c6\n\t"
+            "ds_read_b128 %2, %4 offset:%c7\n\t"
+            "ds_read_b128 %3, %4 offset:%c8\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3])
+            : "v"(aa), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
+            : "memory");
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[TH + ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
-                                                                    __builtin_bit_cast(bf16x8_t, bf[j]),
-                                                                    acc[TH + ii][j], 0, 0, 0);
+        for (int ii = 0; ii < TH; ++ii)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[TH + ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[ii]),
+                                                                      __builtin_bit_cast(bf16x8_t, bf[j]),
+                                                                      acc[TH + ii][j], 0, 0, 0);
+      }
     }
   }
   wait_vmcnt<0>();  // the trailing clamped slab loads land before LDS is reused or released
