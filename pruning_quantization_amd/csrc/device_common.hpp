@@ -677,9 +677,64 @@ __device__ inline void hadamard_long(Unit<DT> (&u)[UPL], double c, int t) {
 }
 
 // Every lane of the wave must call this (zero units rotate to zeros).
+// Blocks of 1024 .. 4096 elements on whole-workgroup teams (TEAM = kBlock =
+// 256 lanes; lane t's register j holds unit 256 j + t, so a 4096-element
+// block is 16 elements per lane).  After the unit and in-wave lane stages, a
+// 4096-element block adds the stage between a lane's registers j and j ^ 1,
+// and every block the stages between waves (lane bit 6, and bit 7 from 2048
+// elements on), done in one exchange through LDS.  Every thread of the
+// workgroup must call this (it holds two workgroup barriers).
+template <class DT, int UPL>
+__device__ inline void hadamard_team(Unit<DT> (&u)[UPL], const Rot& r, int t) {
+  static_assert(UPL <= 4, "rows of up to 8192 elements (32 KB of LDS per 2 registers)");
+  __shared__ double xw[UPL * 8][kBlock];
+  double v[UPL][8];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] = (double)u[j].f(e);
+    had_unit_lanes(v[j], 64, t);
+  }
+  if (r.n == 4096) {
+#pragma unroll
+    for (int j = 0; j + 1 < UPL; j += 2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double a = v[j][e], b = v[j + 1][e];
+        v[j][e] = a + b;
+        v[j + 1][e] = a - b;
+      }
+  }
+  __syncthreads();  // the previous row's reads of xw are done
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xw[j * 8 + e][t] = v[j][e];
+  __syncthreads();
+  const int q = t >> 6, l = t & 63;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double* col = xw[j * 8 + e];
+      if (r.n == 1024) {  // waves 2c, 2c + 1 hold one block: the lower keeps a + b, the upper a - b
+        const double p = col[t ^ 64];
+        v[j][e] = (q & 1) ? p - v[j][e] : v[j][e] + p;
+      } else {  // lane bits 6 and 7: the 4-point transform over the four waves
+        const double a0 = col[l], a1 = col[l + 64], a2 = col[l + 128], a3 = col[l + 192];
+        const double s01 = (q & 1) ? a0 - a1 : a0 + a1;
+        const double s23 = (q & 1) ? a2 - a3 : a2 + a3;
+        v[j][e] = (q & 2) ? s01 - s23 : s01 + s23;
+      }
+    }
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) unit_store_rotated(u[j], v[j], r.c);
+}
+
 // ROT = 1: blocks of up to 8 * TEAM elements, rotated unit by unit.  ROT = 2:
 // blocks of 1024 .. 4096 elements (one-wave teams, n / 512 <= UPL); a variant
 // of its own, since holding a block's units in fp64 needs far more registers.
+// ROT = 3: the same blocks on whole-workgroup teams (hadamard_team).
 template <class DT, int TEAM, int UPL, int ROT>
 __device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
   if constexpr (ROT == 1) {
@@ -697,6 +752,9 @@ __device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
     if constexpr (UPL >= 8) {
       if (nj == 8) hadamard_long<DT, UPL, 8>(u, r.c, t);
     }
+  } else if constexpr (ROT == 3) {
+    static_assert(TEAM == kBlock, "whole-workgroup teams only");
+    hadamard_team<DT, UPL>(u, r, t);
   }
 }
 

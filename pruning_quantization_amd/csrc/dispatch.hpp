@@ -56,14 +56,26 @@ inline hipError_t with_loop_variant(int64_t nunits, F&& f) {
 }
 
 // Rotation variant of a launch on teams of TEAM lanes: 0 none, 1 blocks of
-// up to 512 elements (unit by unit), 2 longer blocks (one-wave teams only;
-// callers pick one-wave teams for them).
+// up to 512 elements (unit by unit), 2 longer blocks on one-wave teams
+// (callers pick one-wave teams for them, or launch variant 3 on the teams of
+// with_long_rot_variant).
 template <int TEAM, class F>
 inline hipError_t with_rot(const Rot& r, F&& f) {
   if (r.n == 0) return f.template operator()<0>();
   if (r.n <= 512) return f.template operator()<1>();
   if constexpr (TEAM == 64) return f.template operator()<2>();
   else return hipErrorInvalidValue;
+}
+
+// Team shape for rotation blocks of 1024 .. 4096 elements on whole-workgroup
+// teams (rotation variant 3): UPL registers of kBlock units per lane (rows of
+// up to 8192 elements, the limit the ABI sets for such blocks).
+template <class F>
+inline hipError_t with_long_rot_variant(int64_t nunits, F&& f) {
+  if (nunits <= kBlock) return f.template operator()<kBlock, 1>();
+  if (nunits <= 2 * kBlock) return f.template operator()<kBlock, 2>();
+  if (nunits <= 4 * kBlock) return f.template operator()<kBlock, 4>();
+  return hipErrorInvalidValue;
 }
 
 inline dim3 row_grid(const RowDesc& d, int team) {

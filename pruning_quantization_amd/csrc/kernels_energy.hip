@@ -882,7 +882,8 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   };
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
-    auto body = [&]<int TEAM, int UPL>() {
+    // LONG: rotation blocks over 512 elements, on whole-workgroup teams
+    auto body = [&]<int TEAM, int UPL, bool LONG>() {
       auto go = [&]<int R, int SEL>() {
         constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL>;
         const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
@@ -891,16 +892,24 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
         hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
         return hipGetLastError();
       };
-      if (sel == SEL_WANDA)  // rotated calls take no norms
-        return go.template operator()<0, SEL_WANDA>();
-      return with_rot<TEAM>(d.rot, [&]<int R>() {
-        return sel == SEL_P48 ? go.template operator()<R, SEL_P48>()
-                              : go.template operator()<R, SEL_MAG>();
-      });
+      if constexpr (LONG) {
+        return sel == SEL_P48 ? go.template operator()<3, SEL_P48>() : go.template operator()<3, SEL_MAG>();
+      } else {
+        if (sel == SEL_WANDA)  // rotated calls take no norms
+          return go.template operator()<0, SEL_WANDA>();
+        return with_rot<TEAM>(d.rot, [&]<int R>() {
+          return sel == SEL_P48 ? go.template operator()<R, SEL_P48>()
+                                : go.template operator()<R, SEL_MAG>();
+        });
+      }
     };
-    if (d.rot.n > 512)  // rotation blocks over 512 elements need one-wave teams
-      return with_row_variant<0>(nunits, body);
-    return with_row_variant<SPARQ24_WIDE_E>(nunits, body);
+    if (d.rot.n > 512)
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return body.template operator()<TEAM, UPL, true>();
+      });
+    return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
+      return body.template operator()<TEAM, UPL, false>();
+    });
   }
   // fp32 and fp16 operands
   auto generic = [&]<class DT>() {

@@ -210,12 +210,19 @@ __global__ __launch_bounds__(kBlock) void k_hadamard(const char* __restrict__ x,
 hipError_t launch_hadamard(const RowDesc& d, void* out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   return with_dtype(d.dtype, [&]<class DT>() {
+    auto go = [&]<int TEAM, int UPL, int R>() {
+      hipLaunchKernelGGL((k_hadamard<DT, TEAM, UPL, R>), row_grid(d, TEAM), dim3(kBlock), 0, s, d.x,
+                         d.R, nunits, d.bs, d.rs, d.rot, (char*)out);
+      return hipGetLastError();
+    };
+    if (d.rot.n > 512)  // blocks over 512 elements, on whole-workgroup teams
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return go.template operator()<TEAM, UPL, 3>();
+      });
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
       return with_rot<TEAM>(d.rot, [&]<int R>() {
-        if constexpr (R == 0) return hipErrorInvalidValue;  // a rotation always has a block
-        hipLaunchKernelGGL((k_hadamard<DT, TEAM, UPL, R>), row_grid(d, TEAM), dim3(kBlock), 0, s,
-                           d.x, d.R, nunits, d.bs, d.rs, d.rot, (char*)out);
-        return hipGetLastError();
+        if constexpr (R == 1) return go.template operator()<TEAM, UPL, 1>();
+        else return hipErrorInvalidValue;  // a rotation always has a block; long ones go above
       });
     });
   });

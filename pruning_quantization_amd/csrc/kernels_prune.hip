@@ -444,7 +444,7 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   if (wanda && d.rot.n) return hipErrorInvalidValue;  // rotated calls take no norms
   return with_dtype(d.dtype, [&]<class DT>() {
-    // LONG: rotation blocks over 512 elements, which need one-wave teams
+    // LONG: rotation blocks over 512 elements, on whole-workgroup teams
     auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
       auto go = [&]<bool W, int P, int CF, int R>() {
         constexpr auto K = k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>;
@@ -458,11 +458,8 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
         return go.template operator()<W, P, CF_INT16, R>();
       };
       if constexpr (LONG) {
-        if constexpr (TEAM == 64)
-          return pat == PAT_48 ? fmt.template operator()<false, PAT_48, 2>()
-                               : fmt.template operator()<false, PAT_24, 2>();
-        else
-          return hipErrorInvalidValue;
+        return pat == PAT_48 ? fmt.template operator()<false, PAT_48, 3>()
+                             : fmt.template operator()<false, PAT_24, 3>();
       } else {
         if (wanda) return fmt.template operator()<true, PAT_24, 0>();
         if (pat == PAT_48)
@@ -473,7 +470,7 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
       }
     };
     if (d.rot.n > 512)
-      return with_row_variant<0>(nunits, [&]<int TEAM, int UPL>() {
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
         return body.template operator()<TEAM, UPL, true>();
       });
     return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {

@@ -375,17 +375,19 @@ hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   return with_dtype(d.dtype, [&]<class DT>() {
-    auto body = [&]<int TEAM, int UPL>() {
-      return with_rot<TEAM>(d.rot, [&]<int R>() {
-        constexpr auto K = k_quant_rows<DT, TEAM, UPL, R>;
-        hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
-                           s, g, cfmt, qmax, (char*)codes, scales);
-        return hipGetLastError();
-      });
+    auto go = [&]<int TEAM, int UPL, int R>() {
+      constexpr auto K = k_quant_rows<DT, TEAM, UPL, R>;
+      hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
+                         s, g, cfmt, qmax, (char*)codes, scales);
+      return hipGetLastError();
     };
-    if (d.rot.n > 512)  // rotation blocks over 512 elements need one-wave teams
-      return with_row_variant<0>(nunits, body);
-    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, body);
+    if (d.rot.n > 512)  // rotation blocks over 512 elements, on whole-workgroup teams
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return go.template operator()<TEAM, UPL, 3>();
+      });
+    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
+      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, R>(); });
+    });
   });
 }
 
