@@ -342,30 +342,53 @@ struct PartialSink {
   bool acc;
 };
 
+// Accumulator slots per column of a workgroup: one per team, or one per wave
+// for teams of several waves.
+template <int TEAM>
+constexpr int kSinkSlots = kBlock / (TEAM > 64 ? 64 : TEAM);
+
 template <int TEAM>
 __device__ inline void sink_put(const PartialSink& k, double* lacc, int64_t row, int col,
                                 double v) {
-  if (k.acc) lacc[col * (kBlock / TEAM) + threadIdx.x / TEAM] += v;
+  if (k.acc) lacc[col * kSinkSlots<TEAM> + (TEAM > 64 ? 0 : threadIdx.x / TEAM)] += v;
   else k.rowpart[(int64_t)col * k.stride + row] = v;
 }
 
-// One partial per workgroup: thread c adds column c over the teams in order.
+// A row's column value from every lane's share v.  Whole-operand partials of
+// multi-wave teams take each wave's sum into the wave's own slot (no
+// workgroup barrier per row; the flush adds the slots in order); otherwise
+// the team sum goes to the sink from the team's first lane.
+template <int TEAM>
+__device__ inline void sink_sum(const PartialSink& k, double* lacc, double* redd, int64_t row,
+                                int col, double v, bool live) {
+  if constexpr (TEAM > 64) {
+    if (k.acc) {
+      const double w = team_sum_f64<64>(v, redd);
+      if (live && (threadIdx.x & 63) == 0) lacc[col * kSinkSlots<TEAM> + (threadIdx.x >> 6)] += w;
+      return;
+    }
+  }
+  const double a = team_sum_f64<TEAM>(v, redd);
+  if (live && threadIdx.x % TEAM == 0) sink_put<TEAM>(k, lacc, row, col, a);
+}
+
+// One partial per workgroup: thread c adds column c over its slots in order.
 template <int TEAM>
 __device__ inline void sink_flush(const PartialSink& k, double* lacc, int ncols) {
   if (!k.acc) return;
-  constexpr int TPB = kBlock / TEAM;
+  constexpr int NS = kSinkSlots<TEAM>;
   __syncthreads();
   const int c = threadIdx.x;
   if (c < ncols) {
     double a = 0.0;
-    for (int i = 0; i < TPB; ++i) a += lacc[c * TPB + i];
+    for (int i = 0; i < NS; ++i) a += lacc[c * NS + i];
     k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
   }
 }
 
 template <int TEAM>
 __device__ inline void sink_init(double* lacc, int ncols) {
-  for (int i = threadIdx.x; i < ncols * (kBlock / TEAM); i += kBlock) lacc[i] = 0.0;
+  for (int i = threadIdx.x; i < ncols * kSinkSlots<TEAM>; i += kBlock) lacc[i] = 0.0;
   __syncthreads();
 }
 
@@ -407,7 +430,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
                         PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
-  __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
+  __shared__ double lacc[(2 + 2 * kMaxQ) * kSinkSlots<TEAM>];
   const int ncols = 2 + p.kept.n + p.dense.n;
   sink_init<TEAM>(lacc, ncols);
   bool any_nv = false;
@@ -426,7 +449,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   }
   const int64_t nrows = g.nrows;
   for_each_row_pipelined<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
-    const bool writer = row < nrows && t == 0;
+    const bool live = row < nrows;
     uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept (0, 1), dropped (2, 3)
     uint32_t am = 0;       // magnitude 2:4: max top key; otherwise packed kept max
     uint32_t amd2 = 0;     // packed dropped max (Wanda, pairwise 4:8)
@@ -465,12 +488,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
       amk = team_max_u32<TEAM>(unpack_max16(am) << 16, redu);
       amd = team_max_u32<TEAM>(unpack_max16(pk_max_u16(am, amd2)) << 16, redu);
     }
-    double x2 = team_sum_f64<TEAM>(kept2 + drop, redd);
-    drop = team_sum_f64<TEAM>(drop, redd);
-    if (writer) {
-      sink_put<TEAM>(sink, lacc, row, 0, x2);
-      sink_put<TEAM>(sink, lacc, row, 1, drop);
-    }
+    sink_sum<TEAM>(sink, lacc, redd, row, 0, kept2 + drop, live);
+    sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
     // INT quantizers run in chunks of up to kIntChunk per pass over the row:
     // each unit is unpacked once for the whole chunk.  A kept one with a
@@ -499,10 +518,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
       }
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const double a = team_sum_f64<TEAM>(acc[i], redd);
-        if (writer) sink_put<TEAM>(sink, lacc, row, 2 + idx[i], a);
-      }
+      for (int i = 0; i < NQ; ++i) sink_sum<TEAM>(sink, lacc, redd, row, 2 + idx[i], acc[i], live);
     };
     auto dense_ints = [&]<int NQ>(int c0) {
       pin_packed<UPL>(pk);
@@ -532,15 +548,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         if (SEL == SEL_MAG)
           for (int k = 0; k < p.kept.n; ++k)
             if (p.kept_twin[k] == idx[i]) twin = k;
-        double a;
-        if (twin >= 0) {
-          const double ak = team_sum_f64<TEAM>(acck[i], redd);
-          a = team_sum_f64<TEAM>(accd[i], redd) + ak;
-          if (writer) sink_put<TEAM>(sink, lacc, row, 2 + twin, ak);
-        } else {
-          a = team_sum_f64<TEAM>(acck[i] + accd[i], redd);
-        }
-        if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + idx[i], a);
+        if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck[i], live);
+        sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + idx[i], acck[i] + accd[i], live);
       }
     };
     auto chunks = [&](int n, auto&& run) {
@@ -585,8 +594,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           acc += (double)kept_block_err4<false>(v, 0.f, 0.f);
         }
       }
-      acc = team_sum_f64<TEAM>(acc, redd);
-      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
     }
     for (int q = 0; q < p.dense.n; ++q) {
       const int fmt = p.dense.fmt[q];
@@ -608,13 +616,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
           acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
         }
-        if (twin >= 0) {
-          acck = team_sum_f64<TEAM>(acck, redd);
-          acc = team_sum_f64<TEAM>(acc, redd) + acck;
-          if (writer) sink_put<TEAM>(sink, lacc, row, 2 + twin, acck);
-        } else {
-          acc = team_sum_f64<TEAM>(acc + acck, redd);
-        }
+        if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
+        acc += acck;
       } else if (fmt == CF_MX || fmt == CF_NV) {
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
@@ -637,9 +640,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
             acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv);
           }
         }
-        acc = team_sum_f64<TEAM>(acc, redd);
       }
-      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + q, acc);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   });
   sink_flush<TEAM>(sink, lacc, ncols);
@@ -650,7 +652,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
                                                         EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
-  __shared__ double lacc[(2 + 2 * kMaxQ) * (kBlock / TEAM)];
+  __shared__ double lacc[(2 + 2 * kMaxQ) * kSinkSlots<TEAM>];
   const int ncols0 = 2 + p.kept.n + p.dense.n;
   sink_init<TEAM>(lacc, ncols0);
 
