@@ -170,3 +170,26 @@ def test_rotation_raises_R_on_outlier_activations():
     r0 = raw_np(S.predict_R(x, kept, dense))[0]
     r1 = raw_np(S.predict_R_rot(x, 128, kept, dense))[0]
     assert (r1[:, 4] > 1.3 * r0[:, 4]).all()
+
+
+@pytest.mark.parametrize("k,n", [(3072, 1024), (6144, 2048), (8192, 4096), (1024, 1024)])
+def test_long_blocks_rows_not_filling_team_registers(k, n):
+    # long blocks on whole-workgroup teams: rows whose units do not fill the
+    # last register of 256 lanes (K = 3072, 6144), two 4096-element blocks
+    # per row, and a row of one 1024-element block (half the lanes idle)
+    raw = rot_inputs(k + n, 37, k, "bf16")
+    exact(raw, "bf16", n)
+    x = to_dev(raw, "bf16")
+    rot = O.rotate(raw, "bf16", n)
+    assert_same(raw_np(S.hadamard(x, n)), rot, f"rotate k={k} n={n}")
+    check_pq(S.prune_quantize_rot(x, n, ("fp8", 0)), O.prune_quantize(rot, "bf16", O.QSpec("fp8", 0)),
+             f"2:4 rot k={k} n={n}")
+    c, s = S.quantize_rot(x, n, ("int", 8))
+    wc, ws = O.quantize_rows(rot, "bf16", O.QSpec("int", 8))
+    assert_same(raw_np(c), wc, f"codes k={k} n={n}")
+    assert_same(raw_np(s), ws, f"scales k={k} n={n}")
+    kept, dense = ["fp8", ("int", 4)], [("int", 8), "fp8"]
+    ok, od = [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense]
+    for rpb in (0, 16):
+        got = S.predict_R_rot(x, n, kept, dense, rows_per_block=rpb)
+        rel_close(raw_np(got), O.predict_R(rot, "bf16", ok, od, rows_per_block=rpb))
