@@ -543,7 +543,7 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 // A block of n <= 8 * TEAM elements is n/8 units on adjacent lanes of one
 // register j (lane t owns units t, t + TEAM, ...), so the butterflies run
 // three stages inside a unit and log2(n/8) stages across lanes; longer blocks
-// add stages across a lane's consecutive units (hadamard_long).
+// run on whole-workgroup teams (hadamard_team).
 // ---------------------------------------------------------------------------
 template <class DT>
 __device__ inline void unit_store_f32(Unit<DT>& u, const float* f) {
@@ -641,42 +641,6 @@ __device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
   unit_store_rotated(u, v, c);
 }
 
-// Blocks longer than a wave's 512 elements (one-wave teams): lane t's unit j
-// holds elements 8 (64 j + t) .. 8 (64 j + t) + 7 of its row or chunk, so a
-// block of n = 512 NJ elements is NJ consecutive units of every lane.  After
-// the unit and lane stages, the remaining log2(NJ) stages pair units j and
-// j ^ d of the same lane; one block's NJ units are held in fp64 at a time.
-template <class DT, int UPL, int NJ>
-__device__ inline void hadamard_long(Unit<DT> (&u)[UPL], double c, int t) {
-#pragma unroll
-  for (int j0 = 0; j0 < UPL; j0 += NJ) {
-    double v[NJ][8];
-#pragma unroll
-    for (int k = 0; k < NJ; ++k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[k][e] = (double)u[j0 + k].f(e);
-      had_unit_lanes(v[k], 64, t);
-      // one unit's lane stages at a time: interleaving them would add a
-      // second set of fp64 temporaries per unit
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int d = 1; d < NJ; d <<= 1)
-#pragma unroll
-      for (int k = 0; k < NJ; ++k)
-        if (!(k & d))
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double a = v[k][e], b = v[k | d][e];
-            v[k][e] = a + b;
-            v[k | d][e] = a - b;
-          }
-#pragma unroll
-    for (int k = 0; k < NJ; ++k) unit_store_rotated(u[j0 + k], v[k], c);
-  }
-}
-
-// Every lane of the wave must call this (zero units rotate to zeros).
 // Blocks of 1024 .. 4096 elements on whole-workgroup teams (TEAM = kBlock =
 // 256 lanes; lane t's register j holds unit 256 j + t, so a 4096-element
 // block is 16 elements per lane).  After the unit and in-wave lane stages, a
@@ -731,28 +695,16 @@ __device__ inline void hadamard_team(Unit<DT> (&u)[UPL], const Rot& r, int t) {
   for (int j = 0; j < UPL; ++j) unit_store_rotated(u[j], v[j], r.c);
 }
 
-// ROT = 1: blocks of up to 8 * TEAM elements, rotated unit by unit.  ROT = 2:
-// blocks of 1024 .. 4096 elements (one-wave teams, n / 512 <= UPL); a variant
-// of its own, since holding a block's units in fp64 needs far more registers.
-// ROT = 3: the same blocks on whole-workgroup teams (hadamard_team).
+// ROT = 1: blocks of up to 512 elements (and at most 8 * TEAM), rotated unit
+// by unit.  ROT = 3: blocks of 1024 .. 4096 elements on whole-workgroup teams
+// (hadamard_team).
 template <class DT, int TEAM, int UPL, int ROT>
 __device__ inline void hadamard_units(Unit<DT> (&u)[UPL], const Rot& r, int t) {
+  static_assert(ROT == 1 || ROT == 3, "rotation variants 1 and 3");
   if constexpr (ROT == 1) {
 #pragma unroll
     for (int j = 0; j < UPL; ++j) hadamard_unit(u[j], r.n >> 3, r.c, t);
-  } else if constexpr (ROT == 2) {
-    static_assert(TEAM == 64, "long rotation blocks need one-wave teams");
-    const int nj = r.n >> 9;
-    if constexpr (UPL >= 2) {
-      if (nj == 2) hadamard_long<DT, UPL, 2>(u, r.c, t);
-    }
-    if constexpr (UPL >= 4) {
-      if (nj == 4) hadamard_long<DT, UPL, 4>(u, r.c, t);
-    }
-    if constexpr (UPL >= 8) {
-      if (nj == 8) hadamard_long<DT, UPL, 8>(u, r.c, t);
-    }
-  } else if constexpr (ROT == 3) {
+  } else {
     static_assert(TEAM == kBlock, "whole-workgroup teams only");
     hadamard_team<DT, UPL>(u, r, t);
   }

@@ -56,15 +56,13 @@ inline hipError_t with_loop_variant(int64_t nunits, F&& f) {
 }
 
 // Rotation variant of a launch on teams of TEAM lanes: 0 none, 1 blocks of
-// up to 512 elements (unit by unit), 2 longer blocks on one-wave teams
-// (callers pick one-wave teams for them, or launch variant 3 on the teams of
-// with_long_rot_variant).
+// up to 512 elements (unit by unit).  Longer blocks are launched as variant 3
+// on the teams of with_long_rot_variant.
 template <int TEAM, class F>
 inline hipError_t with_rot(const Rot& r, F&& f) {
   if (r.n == 0) return f.template operator()<0>();
   if (r.n <= 512) return f.template operator()<1>();
-  if constexpr (TEAM == 64) return f.template operator()<2>();
-  else return hipErrorInvalidValue;
+  return hipErrorInvalidValue;
 }
 
 // Team shape for rotation blocks of 1024 .. 4096 elements on whole-workgroup

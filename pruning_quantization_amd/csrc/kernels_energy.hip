@@ -915,17 +915,21 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   }
   // fp32 and fp16 operands
   auto generic = [&]<class DT>() {
+    auto go = [&]<int TEAM, int UPL, bool WANDA, int R>() {
+      constexpr auto K = k_energy_rows<DT, TEAM, UPL, WANDA, R>;
+      const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
+      PartialSink k;
+      geom(TEAM, grid, k);
+      hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
+      return hipGetLastError();
+    };
+    if (d.rot.n > 512)  // long rotation blocks: whole-workgroup teams
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return go.template operator()<TEAM, UPL, false, 3>();
+      });
     return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
-      auto go = [&]<bool WANDA, int R>() {
-        constexpr auto K = k_energy_rows<DT, TEAM, UPL, WANDA, R>;
-        const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
-        PartialSink k;
-        geom(TEAM, grid, k);
-        hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
-        return hipGetLastError();
-      };
-      if (wanda) return go.template operator()<true, 0>();  // rotated calls take no norms
-      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<false, R>(); });
+      if (wanda) return go.template operator()<TEAM, UPL, true, 0>();  // rotated calls take no norms
+      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, false, R>(); });
     });
   };
   if (d.dtype == 0) return generic.template operator()<F32T>();

@@ -141,12 +141,17 @@ hipError_t launch_absmax_partials(const RowDesc& d, uint32_t* partials, hipStrea
   const int64_t nunits = d.K / 8;
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      return with_rot<TEAM>(d.rot, [&]<int R>() {
-        hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, R>), dim3(nb), dim3(kBlock), 0, s,
-                           d.x, d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
-        return hipGetLastError();
+    auto go = [&]<int TEAM, int UPL, int R>() {
+      hipLaunchKernelGGL((k_absmax_partial<DT, TEAM, UPL, R>), dim3(nb), dim3(kBlock), 0, s, d.x,
+                         d.B, d.R, nunits, d.bs, d.rs, partials, d.rot);
+      return hipGetLastError();
+    };
+    if (d.rot.n > 512)  // long rotation blocks: whole-workgroup teams
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return go.template operator()<TEAM, UPL, 3>();
       });
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, R>(); });
     });
   });
 }
@@ -397,13 +402,18 @@ static hipError_t launch_quant_block(const RowDesc& d, const float* tamax_in,
                                      uint8_t* scales, float* ts_out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
-      return with_rot<TEAM>(d.rot, [&]<int R>() {
-        hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, R>), row_grid(d, TEAM),
-                           dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials,
-                           nparts, (uint32_t*)codes, scales, ts_out, d.rot);
-        return hipGetLastError();
+    auto go = [&]<int TEAM, int UPL, int R>() {
+      hipLaunchKernelGGL((k_quant_block<DT, TEAM, UPL, NV, R>), row_grid(d, TEAM), dim3(kBlock), 0,
+                         s, d.x, d.R, nunits, d.bs, d.rs, tamax_in, partials, nparts,
+                         (uint32_t*)codes, scales, ts_out, d.rot);
+      return hipGetLastError();
+    };
+    if (d.rot.n > 512)  // long rotation blocks: whole-workgroup teams
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return go.template operator()<TEAM, UPL, 3>();
       });
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, R>(); });
     });
   });
 }
@@ -426,8 +436,10 @@ hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const f
                                   float* ts_out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   if (wanda && d.rot.n) return hipErrorInvalidValue;
+  const bool nv = cfmt == CF_NV;
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+    // LONG: rotation blocks over 512 elements, on whole-workgroup teams
+    auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
       auto go = [&]<int P, bool W, bool NV, int R>() {
         hipLaunchKernelGGL((k_prune_quant_fp4<DT, TEAM, UPL, P, W, NV, R>), row_grid(d, TEAM),
                            dim3(kBlock), 0, s, d.x, d.R, nunits, d.bs, d.rs, norm, tamax_in,
@@ -435,15 +447,24 @@ hipError_t launch_prune_quant_fp4(const RowDesc& d, int pat, bool wanda, const f
         return hipGetLastError();
       };
       auto mag = [&]<int P, bool NV>() {
-        return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<P, false, NV, R>(); });
+        if constexpr (LONG) return go.template operator()<P, false, NV, 3>();
+        else return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<P, false, NV, R>(); });
       };
-      const bool nv = cfmt == CF_NV;
       if (pat == PAT_48)
         return nv ? mag.template operator()<PAT_48, true>() : mag.template operator()<PAT_48, false>();
-      if (wanda)
-        return nv ? go.template operator()<PAT_24, true, true, 0>()
-                  : go.template operator()<PAT_24, true, false, 0>();
+      if constexpr (!LONG) {
+        if (wanda)
+          return nv ? go.template operator()<PAT_24, true, true, 0>()
+                    : go.template operator()<PAT_24, true, false, 0>();
+      }
       return nv ? mag.template operator()<PAT_24, true>() : mag.template operator()<PAT_24, false>();
+    };
+    if (d.rot.n > 512)
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return body.template operator()<TEAM, UPL, true>();
+      });
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      return body.template operator()<TEAM, UPL, false>();
     });
   });
 }
@@ -455,16 +476,28 @@ hipError_t launch_kept_absmax_partials(const RowDesc& d, int pat, bool wanda, co
   const int64_t nunits = d.K / 8;
   const int nb = absmax_partial_count(d);
   return with_dtype(d.dtype, [&]<class DT>() {
-    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+    // LONG: rotation blocks over 512 elements, on whole-workgroup teams
+    auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
       auto go = [&]<int P, bool W, int R>() {
         hipLaunchKernelGGL((k_kept_absmax_partial<DT, TEAM, UPL, P, W, R>), dim3(nb),
                            dim3(kBlock), 0, s, d.x, d.B, d.R, nunits, d.bs, d.rs, norm, partials,
                            d.rot);
         return hipGetLastError();
       };
-      if (pat == PAT_48)
-        return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<PAT_48, false, R>(); });
-      return go.template operator()<PAT_24, true, 0>();
+      if constexpr (LONG) {
+        return go.template operator()<PAT_48, false, 3>();  // only pairwise 4:8 gets here rotated
+      } else {
+        if (pat == PAT_48)
+          return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<PAT_48, false, R>(); });
+        return go.template operator()<PAT_24, true, 0>();
+      }
+    };
+    if (d.rot.n > 512)
+      return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
+        return body.template operator()<TEAM, UPL, true>();
+      });
+    return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {
+      return body.template operator()<TEAM, UPL, false>();
     });
   });
 }
