@@ -462,12 +462,16 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
           acc[TH + ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
               __builtin_bit_cast(bf16x8_t, af[ii]), bfr[j], acc[TH + ii][j], (int)ix[ii], 0, 0);
     } else if constexpr (MODE == GM_FP8) {
-      // a lane's 32 codes of a row are chunks 2h and 2h + 1 (k 32h .. 32h + 31),
-      // the same k positions for A and B; rows in two halves (register budget)
-      const unsigned al = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + ((2 * h) ^ gemm_swz<8>(fr))) * 16);
-      const unsigned ah = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + ((2 * h + 1) ^ gemm_swz<8>(fr))) * 16);
-      const unsigned bl = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + ((2 * h) ^ gemm_swz<8>(fr))) * 16);
-      const unsigned bh = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + ((2 * h + 1) ^ gemm_swz<8>(fr))) * 16);
+      // a lane's 32 codes of a row are chunks h and 4 + h of the slab (k 16h ..
+      // 16h + 15 and 64 + 16h .. 64 + 16h + 15): any split of the 128 k among
+      // the lane groups gives the same product as long as A and B use the
+      // same one, and this one reads without bank conflicts (chunks 2h and
+      // 2h + 1 measured 4 conflict cycles per read); rows in two halves
+      // (register budget)
+      const unsigned al = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + (h ^ gemm_swz<8>(fr))) * 16);
+      const unsigned ah = lds0 + so + (unsigned)(((wm * WTM + fr) * 8 + ((4 + h) ^ gemm_swz<8>(fr))) * 16);
+      const unsigned bl = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + (h ^ gemm_swz<8>(fr))) * 16);
+      const unsigned bh = lds0 + so + A_BYTES + (unsigned)(((wn * WTN + fr) * 8 + ((4 + h) ^ gemm_swz<8>(fr))) * 16);
       u32x4_t b0[TJ], b1[TJ], x0[TH], x1[TH];
       asm volatile(
           "ds_read_b128 %0, %16\n\t"
