@@ -364,10 +364,17 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
       __builtin_amdgcn_global_load_lds(B + n * g.ldb + bk + c * 8,
                                        (lds_void_t*)(st + A_BYTES + (q * NT + w * 64) * 16), 16, 0, 0);
     }
-    if constexpr (SPARSE) {  // 8 metadata bytes per row: dword p is row p / 2, half p % 2
-      const int r = tid >> 1;
+    if constexpr (SPARSE) {
+      // Metadata (8 bytes per row and slab) laid out per reading lane: 16-byte
+      // chunk c = ((wr * 16 + f) * 2 + hp) * 2 + ih holds dword hp of rows
+      // wr * 128 + 16 (4 ih + 0..3) + f, i.e. the index halfwords lane f of
+      // wave row wr needs for 4 row tiles; chunks sit at c with its low two
+      // bits xor (f >> 1) & 3 (8 lanes of one read hit 8 bank groups).
+      // Dword p of the region is loaded by thread p.
+      const int C = tid >> 2, f = (C >> 2) & 15, c = C ^ ((f >> 1) & 3);
+      const int hp = (c >> 1) & 1, i = (c & 1) * 4 + (tid & 3), r = (c >> 6) * WTM + 16 * i + f;
       const int64_t m = m0 + r < M ? m0 + r : M - 1;
-      __builtin_amdgcn_global_load_lds(g.meta + m * g.ldm + k0 / 8 + (tid & 1) * 4,
+      __builtin_amdgcn_global_load_lds(g.meta + m * g.ldm + k0 / 8 + hp * 4,
                                        (lds_void_t*)(st + A_BYTES + B_BYTES + w * 64 * 4), 4, 0, 0);
     }
   };
@@ -379,7 +386,12 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
   const unsigned b_ad = lds0 + A_BYTES + (unsigned)(((wn * WTN + fr) * BCH + (h ^ gemm_swz<BCH>(fr))) * 16);
   // sparse: B's second chunk (k 32 + 8h) and the metadata halfword of lane group h
   const unsigned b2_ad = lds0 + A_BYTES + (unsigned)(((wn * WTN + fr) * BCH + ((4 + h) ^ gemm_swz<BCH>(fr))) * 16);
-  const unsigned m_ad = lds0 + A_BYTES + B_BYTES + (unsigned)((wm * WTM + fr) * 8 + 2 * h);
+  // the metadata chunk of row tiles 0..3 (that of 4..7 is its neighbour, xor 1)
+  const unsigned m_ad =
+      lds0 + A_BYTES + B_BYTES + (unsigned)(((((wm * 16 + fr) * 2 + (h >> 1)) * 2) ^ ((fr >> 1) & 3)) * 16);
+  const unsigned m_ad2 =
+      lds0 + A_BYTES + B_BYTES + (unsigned)(((((wm * 16 + fr) * 2 + (h >> 1)) * 2 + 1) ^ ((fr >> 1) & 3)) * 16);
+  const int m_sh = 16 * (h & 1);  // lane group h's halfword of the dword
   constexpr int AR = 16 * ACH * 16, BR = 16 * BCH * 16;  // bytes between 16-row tiles
 
   f32x4_t acc[TI][TJ];
@@ -403,33 +415,34 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
     }
     const unsigned so = (unsigned)(cur * STAGE);
     if constexpr (SPARSE) {
-      const unsigned aa = a_ad + so, ba = b_ad + so, b2 = b2_ad + so, ma = m_ad + so;
-      u32x4_t bl[TJ], bh[TJ], af[TH];
-      unsigned ix[TH];
+      const unsigned aa = a_ad + so, ba = b_ad + so, b2 = b2_ad + so, ma = m_ad + so, mb = m_ad2 + so;
+      u32x4_t bl[TJ], bh[TJ], af[TH], md;
+      // outputs %0..%12; inputs %13 B, %14 B second chunk, %15 A, %16 metadata,
+      // %17..%19 B row-tile offsets, %20..%22 A row-tile offsets
       asm volatile(
-          "ds_read_b128 %0, %16 offset:%c20\n\t"
-          "ds_read_b128 %1, %16 offset:%c21\n\t"
-          "ds_read_b128 %2, %16 offset:%c22\n\t"
-          "ds_read_b128 %3, %16 offset:%c23\n\t"
-          "ds_read_b128 %4, %17 offset:%c20\n\t"
-          "ds_read_b128 %5, %17 offset:%c21\n\t"
-          "ds_read_b128 %6, %17 offset:%c22\n\t"
-          "ds_read_b128 %7, %17 offset:%c23\n\t"
-          "ds_read_b128 %8, %18\n\t"
-          "ds_read_b128 %9, %18 offset:%c24\n\t"
-          "ds_read_b128 %10, %18 offset:%c25\n\t"
-          "ds_read_b128 %11, %18 offset:%c26\n\t"
-          "ds_read_u16 %12, %19\n\t"
-          "ds_read_u16 %13, %19 offset:128\n\t"
-          "ds_read_u16 %14, %19 offset:256\n\t"
-          "ds_read_u16 %15, %19 offset:384\n\t"
+          "ds_read_b128 %0, %13\n\t"
+          "ds_read_b128 %1, %13 offset:%c17\n\t"
+          "ds_read_b128 %2, %13 offset:%c18\n\t"
+          "ds_read_b128 %3, %13 offset:%c19\n\t"
+          "ds_read_b128 %4, %14\n\t"
+          "ds_read_b128 %5, %14 offset:%c17\n\t"
+          "ds_read_b128 %6, %14 offset:%c18\n\t"
+          "ds_read_b128 %7, %14 offset:%c19\n\t"
+          "ds_read_b128 %8, %15\n\t"
+          "ds_read_b128 %9, %15 offset:%c20\n\t"
+          "ds_read_b128 %10, %15 offset:%c21\n\t"
+          "ds_read_b128 %11, %15 offset:%c22\n\t"
+          "ds_read_b128 %12, %16\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(bl[0]), "=&v"(bl[1]), "=&v"(bl[2]), "=&v"(bl[3]), "=&v"(bh[0]), "=&v"(bh[1]),
             "=&v"(bh[2]), "=&v"(bh[3]), "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]),
-            "=&v"(ix[0]), "=&v"(ix[1]), "=&v"(ix[2]), "=&v"(ix[3])
-          : "v"(ba), "v"(b2), "v"(aa), "v"(ma), "i"(0), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR),
+            "=&v"(md)
+          : "v"(ba), "v"(b2), "v"(aa), "v"(ma), "i"(BR), "i"(2 * BR), "i"(3 * BR), "i"(AR),
             "i"(2 * AR), "i"(3 * AR)
           : "memory");
+      int ix[TH];
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii) ix[ii] = (int)((md[ii] >> m_sh) & 0xFFFFu);
       bf16x16_t bfr[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
@@ -440,27 +453,25 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8_t, af[ii]), bfr[j],
-                                                                 acc[ii][j], (int)ix[ii], 0, 0);
+                                                                 acc[ii][j], ix[ii], 0, 0);
       asm volatile(
-          "ds_read_b128 %0, %8 offset:%c10\n\t"
-          "ds_read_b128 %1, %8 offset:%c11\n\t"
-          "ds_read_b128 %2, %8 offset:%c12\n\t"
-          "ds_read_b128 %3, %8 offset:%c13\n\t"
-          "ds_read_u16 %4, %9 offset:512\n\t"
-          "ds_read_u16 %5, %9 offset:640\n\t"
-          "ds_read_u16 %6, %9 offset:768\n\t"
-          "ds_read_u16 %7, %9 offset:896\n\t"
+          "ds_read_b128 %0, %5 offset:%c7\n\t"
+          "ds_read_b128 %1, %5 offset:%c8\n\t"
+          "ds_read_b128 %2, %5 offset:%c9\n\t"
+          "ds_read_b128 %3, %5 offset:%c10\n\t"
+          "ds_read_b128 %4, %6\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(ix[0]), "=&v"(ix[1]),
-            "=&v"(ix[2]), "=&v"(ix[3])
-          : "v"(aa), "v"(ma), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
+          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(md)
+          : "v"(aa), "v"(mb), "i"(4 * AR), "i"(5 * AR), "i"(6 * AR), "i"(7 * AR)
           : "memory");
+#pragma unroll
+      for (int ii = 0; ii < TH; ++ii) ix[ii] = (int)((md[ii] >> m_sh) & 0xFFFFu);
 #pragma unroll
       for (int ii = 0; ii < TH; ++ii)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[TH + ii][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-              __builtin_bit_cast(bf16x8_t, af[ii]), bfr[j], acc[TH + ii][j], (int)ix[ii], 0, 0);
+              __builtin_bit_cast(bf16x8_t, af[ii]), bfr[j], acc[TH + ii][j], ix[ii], 0, 0);
     } else if constexpr (MODE == GM_FP8) {
       // a lane's 32 codes of a row are chunks h and 4 + h of the slab (k 16h ..
       // 16h + 15 and 64 + 16h .. 64 + 16h + 15): any split of the 128 k among
