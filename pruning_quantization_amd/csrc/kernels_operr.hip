@@ -184,14 +184,19 @@ SPARQ24_ROW_KERNEL void k_side_delta(RowGeom g, SideParams sp, uint16_t* __restr
 __global__ __launch_bounds__(kBlock) void k_rowsq_final(const float* __restrict__ part, int64_t M,
                                                         int64_t ntiles, int ncols,
                                                         double* __restrict__ out) {
-  const int64_t m = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (m >= M) return;
-  for (int c = 0; c < ncols; ++c) {
-    const float* p = part + ((int64_t)c * M + m) * ntiles;
-    double a = 0.0;
-    for (int64_t q = 0; q < ntiles; ++q) a += (double)p[q];
-    out[m * ncols + c] = a;
-  }
+  // one wave per (column, row): the lanes stride the row's tile partials
+  // (contiguous), then a fixed-order wave sum
+  const int64_t item = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (item >= M * ncols) return;  // whole waves
+  const int c = (int)(item / M);
+  const int64_t m = item % M;
+  const float* p = part + ((int64_t)c * M + m) * ntiles;
+  double a = 0.0;
+  for (int64_t q = lane; q < ntiles; q += 64) a += (double)p[q];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+  if (lane == 0) out[m * ncols + c] = a;
 }
 
 // ---------------------------------------------------------------------------
@@ -218,7 +223,8 @@ hipError_t launch_gemm_rowsq(const void* A, int64_t lda, const void* B, int64_t 
 
 hipError_t launch_rowsq_final(const float* part, int64_t M, int64_t ntiles, int ncols, double* out,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_rowsq_final, dim3((unsigned)((M + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+  const int64_t waves = M * ncols, per = kBlock / 64;
+  hipLaunchKernelGGL(k_rowsq_final, dim3((unsigned)((waves + per - 1) / per)), dim3(kBlock), 0, s,
                      part, M, ntiles, ncols, out);
   return hipGetLastError();
 }
