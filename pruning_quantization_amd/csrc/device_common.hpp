@@ -651,7 +651,8 @@ __device__ inline void hadamard_unit(Unit<DT>& u, int nb, double c, int t) {
 template <class DT, int UPL>
 __device__ inline void hadamard_team(Unit<DT> (&u)[UPL], const Rot& r, int t) {
   static_assert(UPL <= 4, "rows of up to 8192 elements (32 KB of LDS per 2 registers)");
-  __shared__ double xw[UPL * 8][kBlock];
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  __shared__ f64x2 xw[UPL * 4][kBlock];  // element pairs (e, e + 1): 16-byte LDS accesses
   double v[UPL][8];
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
@@ -673,22 +674,26 @@ __device__ inline void hadamard_team(Unit<DT> (&u)[UPL], const Rot& r, int t) {
 #pragma unroll
   for (int j = 0; j < UPL; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xw[j * 8 + e][t] = v[j][e];
+    for (int e = 0; e < 8; e += 2) xw[j * 4 + e / 2][t] = f64x2{v[j][e], v[j][e + 1]};
   __syncthreads();
   const int q = t >> 6, l = t & 63;
 #pragma unroll
   for (int j = 0; j < UPL; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double* col = xw[j * 8 + e];
+    for (int e = 0; e < 8; e += 2) {
+      const f64x2* col = xw[j * 4 + e / 2];
       if (r.n == 1024) {  // waves 2c, 2c + 1 hold one block: the lower keeps a + b, the upper a - b
-        const double p = col[t ^ 64];
-        v[j][e] = (q & 1) ? p - v[j][e] : v[j][e] + p;
+        const f64x2 p = col[t ^ 64];
+        v[j][e] = (q & 1) ? p.x - v[j][e] : v[j][e] + p.x;
+        v[j][e + 1] = (q & 1) ? p.y - v[j][e + 1] : v[j][e + 1] + p.y;
       } else {  // lane bits 6 and 7: the 4-point transform over the four waves
-        const double a0 = col[l], a1 = col[l + 64], a2 = col[l + 128], a3 = col[l + 192];
-        const double s01 = (q & 1) ? a0 - a1 : a0 + a1;
-        const double s23 = (q & 1) ? a2 - a3 : a2 + a3;
-        v[j][e] = (q & 2) ? s01 - s23 : s01 + s23;
+        const f64x2 a0 = col[l], a1 = col[l + 64], a2 = col[l + 128], a3 = col[l + 192];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const double s01 = (q & 1) ? a0[k] - a1[k] : a0[k] + a1[k];
+          const double s23 = (q & 1) ? a2[k] - a3[k] : a2[k] + a3[k];
+          v[j][e + k] = (q & 2) ? s01 - s23 : s01 + s23;
+        }
       }
     }
 #pragma unroll
