@@ -627,8 +627,10 @@ __device__ inline void had_unit_lanes(double (&v)[8], int nb, int t) {
 template <class DT>
 __device__ inline void unit_store_rotated(Unit<DT>& u, const double (&v)[8], double c) {
   float f[8];
+  // fma(v, c, +0) is (v + 0) * c in one rounding: a zero sum becomes +0, and
+  // any other sum is scaled exactly once
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = (float)((v[e] + 0.0) * c);
+  for (int e = 0; e < 8; ++e) f[e] = (float)__builtin_fma(v[e], c, 0.0);
   unit_store_f32(u, f);
 }
 
