@@ -32,7 +32,9 @@
  * Memory.  Every array pointer is DEVICE memory owned by the caller, which
  *   must keep it alive until the stream work completes.  Inputs and outputs
  *   must not overlap.  The library allocates nothing and keeps no state
- *   between calls; calls are safe from several host threads.
+ *   between calls apart from device properties it caches on first use (the
+ *   compute-unit count per device, each kernel's resident workgroups per CU);
+ *   calls are safe from several host threads.
  * Alignment.  data, outputs and workspace must be 16-byte aligned, and
  *   batch_stride/row_stride (K-contiguous) or k_stride/batch_stride
  *   (transposed) times the element size must be multiples of 16 bytes

@@ -4,24 +4,27 @@
 // summary), [PD §2]: Wanda ranks a weight by its magnitude times the size of
 // the activation on its input channel; here that size is the L2 norm of the
 // channel over all tokens.
+#include <atomic>
+
 #include "dispatch.hpp"
 
 namespace sparq24 {
 
 constexpr int kColStrips = 128;
 
-// Compute units of the current device, cached per device id.
+// Compute units of the current device, cached per device id (relaxed atomics:
+// host threads that race on the first query store the same value).
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
       v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 int col_strips(const RowDesc& d) {
