@@ -290,6 +290,29 @@ def test_predict_R_blocks_degenerate_and_deterministic():
     rel_close(raw_np(a), want)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k,rows", [(4096, 300), (16384, 40)])
+def test_predict_R_whole_operand_multi_wave_teams(dtype, k, rows):
+    """Whole-operand predict_R (one block, per-workgroup partial slots): rows
+    of 4096 and 16384 elements run on teams of two and four waves, and a
+    workgroup can hold two teams.  Regression for teams of several waves that
+    added into one shared slot: the sums must match the oracle and repeat bit
+    for bit."""
+    raw = inputs(k + rows, rows, k, dtype, "normal")
+    x = to_dev(raw, dtype)
+    kept = ["fp8", ("int", 4), "none"]
+    dense = [("int", 8), "fp8", "mxfp4"]
+    a = S.predict_R(x, kept, dense)
+    b = S.predict_R(x, kept, dense)
+    assert torch.equal(a.view(torch.int64), b.view(torch.int64))
+    want = O.predict_R(raw, dtype, [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense])
+    rel_close(raw_np(a), want)
+    got = S.predict_R_pairs48(x, ["fp8", "none"], [("int", 8), "nvfp4"])
+    want = O.predict_R(raw, dtype, [O.QSpec("fp8"), O.QSpec("none")],
+                       [O.QSpec("int", 8), O.QSpec("nvfp4")], pattern="pairs4:8")
+    rel_close(raw_np(got), want)
+
+
 def test_col_l2norm_within_one_ulp():
     import workloads as W
     raw = W.activation_x(3, 512, 1024)
