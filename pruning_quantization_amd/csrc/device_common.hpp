@@ -127,12 +127,23 @@ __device__ inline void zero_unit(Unit<DT>& u) {
 // ---------------------------------------------------------------------------
 template <class K>
 __device__ inline void top2(K a, K b, K c, K d, K& t1, K& t2) {
-  K m1 = a > b ? a : b, n1 = a > b ? b : a;
-  K m2 = c > d ? c : d, n2 = c > d ? d : c;
-  t1 = m1 > m2 ? m1 : m2;
-  K lo = m1 > m2 ? m2 : m1;
-  K nn = n1 > n2 ? n1 : n2;
-  t2 = lo > nn ? lo : nn;
+  if constexpr (sizeof(K) == 4) {
+    // M = max(a, b, c), m = median(a, b, c); then t1 = max(M, d) and the
+    // second largest of the four is median(m, M, d) (m <= M): 4 instructions
+    // (v_max3, v_med3, v_max, v_med3)
+    K M, m;
+    asm("v_max3_u32 %0, %1, %2, %3" : "=v"(M) : "v"(a), "v"(b), "v"(c));
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(a), "v"(b), "v"(c));
+    t1 = M > d ? M : d;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(t2) : "v"(m), "v"(M), "v"(d));
+  } else {
+    K m1 = a > b ? a : b, n1 = a > b ? b : a;
+    K m2 = c > d ? c : d, n2 = c > d ? d : c;
+    t1 = m1 > m2 ? m1 : m2;
+    K lo = m1 > m2 ? m2 : m1;
+    K nn = n1 > n2 ? n1 : n2;
+    t2 = lo > nn ? lo : nn;
+  }
 }
 
 // nibble = i0 | i1 << 2 with i0 < i1, from the low 2 bits (3 - position) of
