@@ -59,16 +59,41 @@ __device__ inline uint32_t unit_absmax_e(const Unit<DT>& u) {
 // ---------------------------------------------------------------------------
 // Kept and dropped magnitudes of one group as packed bf16 pairs: bits 0..15
 // and 16..31 each hold a |x| bf16 pattern.
+// The four keys in order, t1 > t2 > d2 > d1: with M, m and n the max, median
+// and min of k0..k2, t1 = max(M, k3), t2 = median(m, M, k3), d2 = median(n,
+// m, k3), d1 = min(n, k3) (7 instructions instead of a 10-instruction
+// network).
+__device__ inline uint32_t u32_max3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_max3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline uint32_t u32_min3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_min3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline uint32_t u32_med3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline void sort4_keys(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, uint32_t& t1,
+                                  uint32_t& t2, uint32_t& d2, uint32_t& d1) {
+  const uint32_t M = u32_max3(k0, k1, k2), m = u32_med3(k0, k1, k2), n = u32_min3(k0, k1, k2);
+  t1 = M > k3 ? M : k3;
+  t2 = u32_med3(m, M, k3);
+  d2 = u32_med3(n, m, k3);
+  d1 = n < k3 ? n : k3;
+}
+
 __device__ inline void sel16_mags_packed(uint32_t w0, uint32_t w1, uint32_t& kept, uint32_t& drop,
                                          uint32_t& top) {
   const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
   const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
   const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
-  const uint32_t m1 = k0 > k1 ? k0 : k1, n1 = k0 > k1 ? k1 : k0;
-  const uint32_t m2 = k2 > k3 ? k2 : k3, n2 = k2 > k3 ? k3 : k2;
-  const uint32_t t1 = m1 > m2 ? m1 : m2, lo = m1 > m2 ? m2 : m1;
-  const uint32_t nn = n1 > n2 ? n1 : n2, d1 = n1 > n2 ? n2 : n1;
-  const uint32_t t2 = lo > nn ? lo : nn, d2 = lo > nn ? nn : lo;
+  uint32_t t1, t2, d2, d1;
+  sort4_keys(k0, k1, k2, k3, t1, t2, d2, d1);
   kept = __builtin_amdgcn_perm(t2, t1, 0x07060302u);  // t1 high half low, t2 high half high
   drop = __builtin_amdgcn_perm(d2, d1, 0x07060302u);
   top = t1;
@@ -81,11 +106,8 @@ __device__ inline void sel16_mags(uint32_t w0, uint32_t w1, float* kept2, float*
   const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
   const uint32_t k0 = (a << 16) | 3u, k1 = (a & 0xFFFF0000u) | 2u;
   const uint32_t k2 = (b << 16) | 1u, k3 = b & 0xFFFF0000u;
-  const uint32_t m1 = k0 > k1 ? k0 : k1, n1 = k0 > k1 ? k1 : k0;
-  const uint32_t m2 = k2 > k3 ? k2 : k3, n2 = k2 > k3 ? k3 : k2;
-  const uint32_t t1 = m1 > m2 ? m1 : m2, lo = m1 > m2 ? m2 : m1;
-  const uint32_t nn = n1 > n2 ? n1 : n2, d1 = n1 > n2 ? n2 : n1;
-  const uint32_t t2 = lo > nn ? lo : nn, d2 = lo > nn ? nn : lo;
+  uint32_t t1, t2, d2, d1;
+  sort4_keys(k0, k1, k2, k3, t1, t2, d2, d1);
   kept2[0] = __uint_as_float(t1 & 0xFFFF0000u);
   kept2[1] = __uint_as_float(t2 & 0xFFFF0000u);
   drop2[0] = __uint_as_float(d1 & 0xFFFF0000u);
