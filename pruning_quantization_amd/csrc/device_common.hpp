@@ -122,8 +122,9 @@ __device__ inline void zero_unit(Unit<DT>& u) {
 // Top-2 of 4 with ties to the lower position [PD intro; PD §3].
 // Each element gets an integer key whose order is (score, -position): the
 // score's bit pattern (non-negative floats order like unsigned integers)
-// with (3 - position) in the low bits.  A 7-op max/min network finds the two
-// largest keys; their low bits give the positions.
+// with (3 - position) in the low bits.  The two largest keys (4 instructions
+// for 32-bit keys, a max/min network for 64-bit ones) give the positions in
+// their low bits.
 // ---------------------------------------------------------------------------
 template <class K>
 __device__ inline void top2(K a, K b, K c, K d, K& t1, K& t2) {
@@ -213,7 +214,8 @@ __device__ inline uint32_t unpack_max16(uint32_t acc2) {
 // Magnitude selection for a 16-bit unit, everything in 32-bit lanes:
 //  keys  = |x| in bits 16..30, (3 - position) in bits 0..1 (from the pair of
 //          elements in one dword: 3 ops per pair);
-//  top2  = 7-op max/min network;
+//  top2  = v_max3 / v_med3 of three keys, then a max and a median with the
+//          fourth (4 instructions);
 //  i0/i1 = 3 - max(j), 3 - min(j) with j the winners' low bits;
 //  kept  = byte permute with selector bytes (2*i0, 2*i0+1, 2*i1, 2*i1+1),
 //          i.e. 0x07060706 - (jmax | jmin << 16) * 0x0202;
