@@ -441,7 +441,7 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 #endif
 }
 
-// 4096-element rows under magnitude 2:4 without rotation fit 120 VGPRs
+// 4096-element rows under magnitude 2:4 without rotation fit 122 VGPRs
 // without spilling: four waves per SIMD keep a whole 4096-row operand
 // resident in one pass.
 #ifndef SPARQ24_E_WAVES
