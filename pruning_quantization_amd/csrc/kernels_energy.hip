@@ -284,7 +284,7 @@ __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t
                                      int64_t r0, int64_t r1, const FinalizeParams& f,
                                      double* __restrict__ out, int64_t blk) {
   constexpr int CB = 8;  // columns reduced together: CB independent loads per row
-  __shared__ double sh[CB][kBlock];
+  __shared__ double sh[CB][kBlock / 64];
   __shared__ double sb[2 + 2 * kMaxQ];
   for (int cb = 0; cb < f.ncols; cb += CB) {
     double a[CB];
@@ -316,16 +316,22 @@ __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t
 #pragma unroll
         for (int c = 0; c < CB; ++c) a[c] += v[u][c];
     }
+    // wave sums (xor shuffles, fixed order), then the waves' sums in order
 #pragma unroll
-    for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] = a[c];
-    __syncthreads();
-    for (int w = kBlock / 2; w > 0; w >>= 1) {
-      if ((int)threadIdx.x < w)
+    for (int c = 0; c < CB; ++c) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c) sh[c][threadIdx.x] += sh[c][threadIdx.x + w];
-      __syncthreads();
+      for (int o = 32; o > 0; o >>= 1) a[c] += __shfl_xor(a[c], o, 64);
     }
-    if (threadIdx.x < CB && cb + (int)threadIdx.x < f.ncols) sb[cb + threadIdx.x] = sh[threadIdx.x][0];
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) sh[c][threadIdx.x >> 6] = a[c];
+    __syncthreads();
+    if (threadIdx.x < CB && cb + (int)threadIdx.x < f.ncols) {
+      double r = sh[threadIdx.x][0];
+#pragma unroll
+      for (int w = 1; w < kBlock / 64; ++w) r += sh[threadIdx.x][w];
+      sb[cb + threadIdx.x] = r;
+    }
     __syncthreads();
   }
   if (threadIdx.x != 0) return;
