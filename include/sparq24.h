@@ -253,7 +253,9 @@ typedef enum {
  * out [B][R][K] in x's storage type, K-contiguous.  Workspace: a transposed
  * operand's staging copy, else none.  Errors: block not a power of two in
  * range -> INVALID; K % block -> SHAPE; block > 512 with K > 8192 ->
- * UNSUPPORTED (such blocks are rotated within one wave's registers). */
+ * UNSUPPORTED (such blocks are rotated by a whole 256-lane workgroup per
+ * row, each lane holding at most four 8-element units of the row in
+ * registers, so a row may span at most 256 * 4 * 8 = 8192 elements). */
 sparq24_status sparq24_hadamard(const sparq24_tensor* x, int32_t block, void* out, void* ws,
                                 size_t* ws_bytes, hipStream_t stream);
 
@@ -274,8 +276,10 @@ sparq24_status sparq24_prune_quantize_rot(const sparq24_tensor* x, int32_t block
                                           void* scales, float* tensor_scale_out, void* ws,
                                           size_t* ws_bytes, hipStream_t stream);
 
-/* Predicted R of the rotated operand [PD §4: rotation roughly doubles R for
- * Q, K and linear-layer inputs], magnitude selection with the given pattern:
+/* Predicted R of the rotated operand ("Is 2:4 Sparsity Still Worth It?",
+ * paper-daily.com English summary, §4: the pages report that a Hadamard
+ * rotation raises R by about a factor of two on attention Q, K and on
+ * linear-layer inputs), magnitude selection with the given pattern:
  * identical outputs to sparq24_hadamard followed by sparq24_predict_R (2:4)
  * or sparq24_predict_R_pairs48, up to the energy tolerance. */
 sparq24_status sparq24_predict_R_rot(const sparq24_tensor* x, int32_t block, int32_t pattern,

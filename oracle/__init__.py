@@ -56,6 +56,7 @@ from .reference import (  # noqa: F401
     dequantize_pruned,
     error_energy,
     predict_R,
+    energies_to_R,
     col_l2norm,
     tensor_absmax,
     bits_per_element,

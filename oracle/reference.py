@@ -715,15 +715,23 @@ def predict_R(raw: np.ndarray, dtype: str, kept_qs: Sequence[QSpec],
     outs = []
     for kq, dq in zip(kept_qs, dense_qs):
         s = error_energy(raw, dtype, kq, dq, score, col_norm, rows_per_block, pattern)
-        with np.errstate(divide="ignore", invalid="ignore"):
-            tot = s[:, 0]
-            e_prune = s[:, 1] / tot
-            e_qk = s[:, 2] / tot
-            e24 = e_prune + e_qk
-            e_d = s[:, 3] / tot
-            r = np.sqrt(e24 / e_d)
-        outs.append(np.stack([e_prune, e_qk, e24, e_d, r], axis=1))
+        outs.append(energies_to_R(s))
     return np.stack(outs, axis=1)
+
+
+def energies_to_R(s: np.ndarray) -> np.ndarray:
+    """The five outputs of one quantizer pair from the four absolute sums of
+    :func:`error_energy` ([PD §4]): fp64 ``[nblk, 4]`` -> ``[nblk, 5]`` =
+    (E_prune, E_qkept, E_2:4 = E_prune + E_qkept, E_dense, R), each energy
+    over the block's total sum of squares, R = sqrt(E_2:4 / E_dense)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        tot = s[:, 0]
+        e_prune = s[:, 1] / tot
+        e_qk = s[:, 2] / tot
+        e24 = e_prune + e_qk
+        e_d = s[:, 3] / tot
+        r = np.sqrt(e24 / e_d)
+    return np.stack([e_prune, e_qk, e24, e_d, r], axis=1)
 
 
 # ---------------------------------------------------------------------------

@@ -17,17 +17,7 @@ namespace sparq24 {
 
 constexpr int kBlock = 256;  // threads per workgroup for every row kernel
 
-// Occupancy hint for the row kernels (waves per SIMD the register budget
-// must allow); 0 leaves the choice to the compiler.
-#ifndef SPARQ24_WAVES_PER_EU
-#define SPARQ24_WAVES_PER_EU 0
-#endif
-#if SPARQ24_WAVES_PER_EU > 0
-#define SPARQ24_ROW_KERNEL __global__ __launch_bounds__(kBlock) \
-  __attribute__((amdgpu_waves_per_eu(SPARQ24_WAVES_PER_EU)))
-#else
 #define SPARQ24_ROW_KERNEL __global__ __launch_bounds__(kBlock)
-#endif
 
 // ---------------------------------------------------------------------------
 // Storage types.  W = dwords per 8-element unit.
@@ -70,19 +60,9 @@ struct Unit {
 
 // Streaming hints: operands are read once and outputs written once, so loads
 // and stores carry the nontemporal bit (measured 10-20% faster on MI355X).
-#ifndef SPARQ24_NT_LOAD
-#define SPARQ24_NT_LOAD 1
-#endif
-#ifndef SPARQ24_NT_STORE
-#define SPARQ24_NT_STORE 1
-#endif
 template <class T>
 __device__ inline void st(T* p, T v) {
-#if SPARQ24_NT_STORE
   __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 // 64/128-bit stores as vectors of 32-bit lanes (what the nontemporal builtin takes)
 __device__ inline void st2(void* p, uint32_t a, uint32_t b) {
@@ -101,13 +81,8 @@ __device__ inline void load_unit(Unit<DT>& u, const void* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
   for (int i = 0; i < DT::W / 4; ++i) {
-#if SPARQ24_NT_LOAD
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q) + i);
-    uint4 v = make_uint4(t.x, t.y, t.z, t.w);
-#else
-    uint4 v = q[i];
-#endif
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q) + i);
     u.w[4 * i + 0] = v.x; u.w[4 * i + 1] = v.y; u.w[4 * i + 2] = v.z; u.w[4 * i + 3] = v.w;
   }
 }
@@ -537,15 +512,6 @@ __device__ inline double team_sum_f64(double v, double* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent row driver.  Rows are flattened over (b, r); team k of the grid
-// takes rows k, k + nteams, k + 2*nteams, ...  With SPARQ24_PIPELINE=1 a team
-// keeps two rows in flight (the next row's loads are issued before the
-// current row is processed); the default single-buffered form measured
-// faster on MI355X because its lower register count admits more waves per
-// SIMD.  The trip count is the same for every team, so team reductions that
-// synchronise a workgroup are reached by all of its threads.
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // Block Hadamard rotation along K [PD §4: before low-bit quantization the
 // operand is multiplied by a rescaled +-1 orthogonal Hadamard matrix].  Each
 // aligned block of n elements becomes y = H_n x / sqrt(n) (Sylvester order),
@@ -742,14 +708,11 @@ __device__ inline const char* row_ptr(const RowGeom& g, int64_t row) {
   return g.x + b * g.bs + (row - b * g.R) * g.rs;
 }
 
-// Branch-free by default: every lane issues all UPL loads (a unit past the
-// row's end or a row past the last re-reads unit 0 of the operand, which
-// always exists when a kernel runs) and zeroes those units afterwards.  With
-// no load under a branch the compiler waits for each unit's load just before
-// its first use, so work on early units overlaps the arrival of later ones.
-#ifndef SPARQ24_LOAD_BRANCHFREE
-#define SPARQ24_LOAD_BRANCHFREE 1
-#endif
+// Every lane issues all UPL loads (a unit past the row's end or a row past
+// the last re-reads unit 0 of the operand, which always exists when a kernel
+// runs) and zeroes those units afterwards.  With no load under a branch the
+// compiler waits for each unit's load just before its first use, so work on
+// early units overlaps the arrival of later ones (2-6% on every row kernel).
 template <class DT, int TEAM, int UPL>
 __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t row, int t) {
   const bool act = row < g.nrows;
@@ -757,51 +720,32 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
     const int64_t i = (int64_t)j * TEAM + t;
-#if SPARQ24_LOAD_BRANCHFREE
     const bool ok = act && i < g.nunits;
     load_unit(u[j], ok ? xr + i * (8 * DT::ESIZE) : g.x);
     if (!ok) zero_unit(u[j]);
-#else
-    if (act && i < g.nunits) load_unit(u[j], xr + i * (8 * DT::ESIZE));
-    else zero_unit(u[j]);
-#endif
   }
 }
 
-#ifndef SPARQ24_PIPELINE
-#define SPARQ24_PIPELINE 0
-#endif
-
+// ---------------------------------------------------------------------------
+// Row driver.  Rows are flattened over (b, r); team k of the grid takes rows
+// k, k + nteams, k + 2*nteams, ...: one row per team when the grid covers
+// every row (the streaming kernels), several for a persistent grid (the
+// energy kernels).  The trip count is the same for every team, so team
+// reductions that synchronise a workgroup are reached by all of its threads.
+// ---------------------------------------------------------------------------
 template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
-__device__ inline void for_each_row_pipelined(const RowGeom& g, Body&& body) {
+__device__ inline void for_each_row(const RowGeom& g, Body&& body) {
   constexpr int TPB = kBlock / TEAM;
   const int t = threadIdx.x % TEAM;
   const int64_t first = (int64_t)blockIdx.x * TPB + threadIdx.x / TEAM;
   const int64_t stride = (int64_t)gridDim.x * TPB;
   const int64_t iters = (g.nrows + stride - 1) / stride;
-  if constexpr (!SPARQ24_PIPELINE) {
-    for (int64_t it = 0; it < iters; ++it) {
-      Unit<DT> A[UPL];
-      const int64_t ra = first + it * stride;
-      load_row<DT, TEAM, UPL>(A, g, ra, t);
-      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
-      body(A, ra, t);
-    }
-    return;
-  }
-  Unit<DT> A[UPL], B[UPL];
-  load_row<DT, TEAM, UPL>(A, g, first, t);
-  for (int64_t it = 0; it < iters; it += 2) {
+  for (int64_t it = 0; it < iters; ++it) {
+    Unit<DT> A[UPL];
     const int64_t ra = first + it * stride;
-    const int64_t rb = ra + stride;
-    load_row<DT, TEAM, UPL>(B, g, rb, t);
+    load_row<DT, TEAM, UPL>(A, g, ra, t);
     if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
     body(A, ra, t);
-    if (it + 1 < iters) {
-      load_row<DT, TEAM, UPL>(A, g, rb + stride, t);
-      if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(B, g.rot, t);
-      body(B, rb, t);
-    }
   }
 }
 

@@ -22,12 +22,10 @@ inline hipError_t with_dtype(int dtype, F&& f) {
 // (TEAM lanes, UPL units per lane) with TEAM * UPL >= units of the row.
 // WIDE = 1 uses two-wave teams (TEAM 128) for rows of 2049..4096 elements:
 // half the per-wave arithmetic at the end of a row, which measured faster for
-// the quantizers; the energy kernel, with many more team reductions, keeps
+// the quantizers (and for the fp32 / fp16 energy kernel, whose one-wave form
+// spills); the bf16 energy kernel, with many more team reductions, keeps
 // one-wave teams.
-#ifndef SPARQ24_WIDE_PQ
-#define SPARQ24_WIDE_PQ 1
-#endif
-template <int WIDE = 0, class F>
+template <int WIDE, class F>
 inline hipError_t with_row_variant(int64_t nunits, F&& f) {
   if (nunits <= 16) return f.template operator()<16, 1>();
   if (nunits <= 32) return f.template operator()<32, 1>();
@@ -81,12 +79,17 @@ inline dim3 row_grid(const RowDesc& d, int team) {
   return dim3((unsigned)((d.R + rpb - 1) / rpb), (unsigned)d.B, 1);
 }
 
-// Grid of a persistent row kernel: enough workgroups to fill every CU
-// kBlocksPerCU times (at most one team per row).
-#ifndef SPARQ24_BLOCKS_PER_CU
-#define SPARQ24_BLOCKS_PER_CU 4
-#endif
-constexpr int kBlocksPerCU = SPARQ24_BLOCKS_PER_CU;
+// Grid of a streaming row kernel: one team per row.  New workgroups start as
+// old ones retire, so loads of fresh rows overlap the arithmetic of others.
+inline dim3 stream_grid(int64_t nrows, int team) {
+  const int64_t rpb = kBlock / team;
+  const int64_t need = (nrows + rpb - 1) / rpb;
+  return dim3((unsigned)(need > 0 ? need : 1));
+}
+
+// Grid of a persistent row kernel (the VALU-bound energy kernels): enough
+// workgroups to fill every CU kBlocksPerCU times (at most one team per row).
+constexpr int kBlocksPerCU = 4;
 int device_cu_count();
 
 // Workgroups of kernel K resident per CU (register and LDS limits), from the

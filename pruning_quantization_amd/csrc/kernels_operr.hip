@@ -65,7 +65,7 @@ SPARQ24_ROW_KERNEL void k_side_delta(RowGeom g, SideParams sp, uint16_t* __restr
   if (sp.fmt == CF_NV) nv_tensor_scales(block_tensor_amax(sp.tamax_in, sp.partials, sp.nparts, redu),
                                         s_t, gnv);
   const int64_t K = g.nunits * 8;
-  for_each_row_pipelined<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+  for_each_row<BF16T, TEAM, UPL>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     uint32_t sel[UPL], km[UPL];
     uint32_t am = 0;  // largest |x| over what the quantizer sees, bf16 bits
 #pragma unroll

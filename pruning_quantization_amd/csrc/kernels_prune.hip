@@ -237,8 +237,9 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
 // Fused prune + compress + quantize of the kept values, one scale per row.
 // A team holds its whole row in registers: one read, then the kept absolute
 // maximum (team reduction), then codes, metadata and the scale are written.
-// Teams are persistent and keep the next row's loads in flight.  CF (the
-// code format) is a template parameter so each variant is straight-line code.
+// The grid covers every row (one row per team): at 16384 x 4096 this measured
+// 3.5% faster than persistent teams walking several rows.  CF (the code
+// format) is a template parameter so each variant is straight-line code.
 // ---------------------------------------------------------------------------
 template <int CF>
 __device__ inline void store_kept_codes(char* dst, const float* y, float qmax) {
@@ -265,21 +266,31 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
                                          float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
   constexpr int CB = CF == CF_INT16 ? 8 : 4;  // code bytes per unit
-  // 16-bit magnitude 2:4: the kept maximum of a row equals its plain maximum
-  // (every group keeps its largest element), so the scale comes from one
-  // packed-max pass over the raw row and selection + encode stream unit by
-  // unit afterwards.  Pairwise 4:8 can drop a row's largest element, so it
-  // takes the kept maximum like Wanda.
+  // 16-bit magnitude 2:4: every unit is selected first and only its kept
+  // pairs and metadata byte stay in registers.  The group's top key from the
+  // top-2 network carries the group's |max| in its high half, and every group
+  // keeps its largest element, so the row maximum of the top keys is the
+  // kept maximum that sets the scale (no separate max pass; 1.5% faster at
+  // 16384 x 4096).  Pairwise 4:8 can drop a row's largest element, so it
+  // takes the kept maximum of the gathered values like Wanda.
   constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA && PAT == PAT_24;
-  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
     uint32_t am = 0;
-    uint32_t mb[FAST16 ? 1 : UPL];
+    uint32_t mb[UPL];
+    uint32_t sk[FAST16 ? UPL : 1][2];      // kept pairs of each unit (16-bit magnitude 2:4)
     uint32_t mo[PAT == PAT_48 ? UPL : 1];  // neighbouring unit's nibble (4:8 meta bytes)
     if constexpr (FAST16) {
+      uint32_t top = 0;
 #pragma unroll
-      for (int j = 0; j < UPL; ++j) am = unit_absmax16_packed(u[j].w, am);
-      am = unpack_max16(am);
+      for (int j = 0; j < UPL; ++j) {  // zero units select zeros
+        const Sel16 r = select16(u[j].w);
+        sk[j][0] = r.k0;
+        sk[j][1] = r.k1;
+        mb[j] = r.mb;
+        top = top > r.topkey ? top : r.topkey;
+      }
+      am = top >> 16;
     } else {
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
@@ -308,10 +319,9 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
       Kept<DT> kp;
       uint32_t m;
       if constexpr (FAST16) {
-        const Sel16 r = select16(u[j].w);
-        kp.k[0] = r.k0;
-        kp.k[1] = r.k1;
-        m = r.mb;
+        kp.k[0] = sk[j][0];
+        kp.k[1] = sk[j][1];
+        m = mb[j];
       } else if constexpr (PAT == PAT_48) {
         kp = gather_pairs48(u[j], mb[j]);
         m = mb[j];
@@ -447,9 +457,8 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
     // LONG: rotation blocks over 512 elements, on whole-workgroup teams
     auto body = [&]<int TEAM, int UPL, bool LONG>() -> hipError_t {
       auto go = [&]<bool W, int P, int CF, int R>() {
-        constexpr auto K = k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>;
-        hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
-                           s, g, norm, qmax, (char*)codes, meta, scales);
+        hipLaunchKernelGGL((k_prune_quantize<DT, TEAM, UPL, W, CF, P, R>), stream_grid(g.nrows, TEAM),
+                           dim3(kBlock), 0, s, g, norm, qmax, (char*)codes, meta, scales);
         return hipGetLastError();
       };
       auto fmt = [&]<bool W, int P, int R>() {
@@ -473,7 +482,7 @@ hipError_t launch_prune_quantize(const RowDesc& d, int pat, bool wanda, const fl
       return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
         return body.template operator()<TEAM, UPL, true>();
       });
-    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<1>(nunits, [&]<int TEAM, int UPL>() {
       return body.template operator()<TEAM, UPL, false>();
     });
   });

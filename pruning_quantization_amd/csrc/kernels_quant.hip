@@ -11,7 +11,7 @@ namespace sparq24 {
 
 // ---------------------------------------------------------------------------
 // Per-row INT-b / FP8: the team holds its row, reduces |x|max, encodes.
-// Persistent teams keep the next row's loads in flight.
+// The grid covers every row (one row per team).
 // ---------------------------------------------------------------------------
 template <class DT>
 __device__ inline uint32_t unit_absmax(const Unit<DT>& u) {
@@ -41,12 +41,18 @@ SPARQ24_ROW_KERNEL void k_quant_rows(RowGeom g, int cfmt, float qmax,
                                                        char* __restrict__ codes,
                                                        float* __restrict__ scales) {
   __shared__ uint32_t red[kBlock / 64];
-  for_each_row_pipelined<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     uint32_t am = 0;
+    if constexpr (DT::ESIZE == 2) {  // packed 16-bit maxima of |x|, unpacked once
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const uint32_t a = unit_absmax(u[j]);
-      am = am > a ? am : a;
+      for (int j = 0; j < UPL; ++j) am = unit_absmax16_packed(u[j].w, am);
+      am = unpack_max16(am);
+    } else {
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const uint32_t a = unit_absmax(u[j]);
+        am = am > a ? am : a;
+      }
     }
     am = team_max_u32<TEAM>(am, red);
     if (row >= g.nrows) return;
@@ -381,16 +387,15 @@ hipError_t launch_quant_rows(const RowDesc& d, int cfmt, float qmax, void* codes
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   return with_dtype(d.dtype, [&]<class DT>() {
     auto go = [&]<int TEAM, int UPL, int R>() {
-      constexpr auto K = k_quant_rows<DT, TEAM, UPL, R>;
-      hipLaunchKernelGGL(K, persistent_grid(g.nrows, TEAM, resident_blocks<K>()), dim3(kBlock), 0,
-                         s, g, cfmt, qmax, (char*)codes, scales);
+      hipLaunchKernelGGL((k_quant_rows<DT, TEAM, UPL, R>), stream_grid(g.nrows, TEAM), dim3(kBlock),
+                         0, s, g, cfmt, qmax, (char*)codes, scales);
       return hipGetLastError();
     };
     if (d.rot.n > 512)  // rotation blocks over 512 elements, on whole-workgroup teams
       return with_long_rot_variant(nunits, [&]<int TEAM, int UPL>() {
         return go.template operator()<TEAM, UPL, 3>();
       });
-    return with_row_variant<SPARQ24_WIDE_PQ>(nunits, [&]<int TEAM, int UPL>() {
+    return with_row_variant<1>(nunits, [&]<int TEAM, int UPL>() {
       return with_rot<TEAM>(d.rot, [&]<int R>() { return go.template operator()<TEAM, UPL, R>(); });
     });
   });

@@ -209,7 +209,8 @@ def test_rotation_validation(L):
     assert fr(ctypes.byref(tensor(k=256)), 128, 1, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == OK
     assert n.value > 0
     assert fr(ctypes.byref(tensor(k=256)), 512, 0, arr, arr, 1, 0, FAKE, None, ctypes.byref(n), None) == SHAPE
-    # whole-row blocks up to 4096 elements, rotated inside one wave's registers
+    # whole-row blocks up to 4096 elements, rotated by a 256-lane workgroup per row
+    # (at most four 8-element units per lane: rows of up to 8192 elements)
     assert fq(ctypes.byref(tensor(k=4096)), 4096, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,
               ctypes.byref(n), None) == OK
     assert fq(ctypes.byref(tensor(k=8192)), 8192, ctypes.byref(q(B.Q_FP8)), FAKE, FAKE, FAKE, None,

@@ -543,3 +543,32 @@ def test_predict_R_block_kept_wanda():
     want = O.predict_R(raw, "bf16", [O.QSpec("nvfp4"), O.QSpec("mxfp4")],
                        [O.QSpec("nvfp4"), O.QSpec("fp8")], "wanda", norm)
     rel_close(raw_np(got), want)
+
+
+# ---------------------------------------------------------------------------
+# the hand-worked rows with inexact fp32 scales, through the library
+# ---------------------------------------------------------------------------
+
+
+def test_hand_rows_inexact_scales():
+    import json
+    import os
+    from conftest import GOLDEN
+    hand = json.load(open(os.path.join(GOLDEN, "hand_examples.json")))
+
+    def f32hex(xs):
+        return np.array([int(h, 16) for h in xs], dtype=np.uint32).view(np.float32)
+
+    for key, q in (("fp8_row_inexact_scale", "fp8"), ("int8_row_inexact_scale", ("int", 8))):
+        ex = hand[key]
+        x = to_dev(f32hex(ex["row_hex"])[None, :], "f32")
+        c, s = S.quantize(x, q)
+        assert int(raw_np(s).view(np.uint32)[0]) == int(ex["scale_hex"], 16), key
+        want = [int(h, 16) for h in ex["codes"]] if q == "fp8" else ex["codes"]
+        assert raw_np(c)[0].astype(np.int64).tolist() == want, key
+    ex = hand["nvfp4_inexact_tensor_scale"]
+    x = to_dev(np.stack([f32hex(r) for r in ex["rows_hex"]]), "f32")
+    c, bs, ts = S.quantize(x, "nvfp4")
+    assert int(raw_np(ts).view(np.uint32)[0]) == int(ex["tensor_scale_hex"], 16)
+    assert raw_np(bs)[:, 0].tolist() == [int(h, 16) for h in ex["block_scales"]]
+    assert raw_np(c).tolist() == [[int(h, 16) for h in r] for r in ex["packed"]]

@@ -101,6 +101,139 @@ def test_nvfp4_hand_example():
         assert np.array_equal(packed[r], hexs(ex["packed"][r]))
 
 
+def f32hex(xs):
+    return np.array([int(h, 16) for h in xs], dtype=np.uint32).view(np.float32)
+
+
+def test_fp8_row_inexact_scale_hand_example():
+    # [PD §3]: FP8 with one scale per row; the scale 448/amax is inexact in fp32
+    ex = HAND["fp8_row_inexact_scale"]
+    raw = f32hex(ex["row_hex"])[None, :]
+    codes, s = O.quantize_rows(raw, O.F32, O.QSpec("fp8"))
+    assert int(s.view(np.uint32)[0]) == int(ex["scale_hex"], 16)
+    assert np.array_equal(codes[0], hexs(ex["codes"]))
+
+
+def test_int8_row_inexact_scale_hand_example():
+    # [PD §3]: INT8 with one scale per row; qmax/amax inexact in fp32
+    ex = HAND["int8_row_inexact_scale"]
+    raw = f32hex(ex["row_hex"])[None, :]
+    codes, s = O.quantize_rows(raw, O.F32, O.QSpec("int", ex["bits"]))
+    assert int(s.view(np.uint32)[0]) == int(ex["scale_hex"], 16)
+    assert codes[0].tolist() == ex["codes"]
+
+
+def test_nvfp4_inexact_tensor_scale_hand_example():
+    # [PD §3]: NVFP4 = an FP8 scale per 16 elements plus one fp32 scale per
+    # tensor; here T/2688 is inexact, and so are 448/T, the block scale times
+    # s_t and its reciprocal
+    ex = HAND["nvfp4_inexact_tensor_scale"]
+    raw = np.stack([f32hex(r) for r in ex["rows_hex"]])
+    packed, bs, s_t = O.quantize_nvfp4(raw, O.F32)
+    assert int(np.float32(s_t).view(np.uint32)) == int(ex["tensor_scale_hex"], 16)
+    assert np.array_equal(bs[:, 0], hexs(ex["block_scales"]))
+    for r in range(2):
+        assert np.array_equal(packed[r], hexs(ex["packed"][r]))
+        got = np.empty(16, dtype=np.int64)
+        got[0::2] = packed[r] & 0xF
+        got[1::2] = packed[r] >> 4
+        assert got.tolist() == ex["codes"][r]
+
+
+def _e2m1_nearest(y):
+    """E2M1 code of each y: nearest of the 8 magnitudes, ties to the even code,
+    saturating, sign copied (a second, independent encoder for the check below)."""
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    a = np.minimum(np.abs(y).astype(np.float64), 6.0)
+    d = np.abs(a[..., None] - grid)
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    return code | np.where(np.signbit(y), 8, 0)
+
+
+def test_inexact_scale_examples_catch_precision_mistakes():
+    # The rows above are sensitive: forming any one fp32 step of the NVFP4
+    # chain in fp64 instead (or replacing a division by a reciprocal
+    # multiply) changes a stored value.  Each variant below plants one such
+    # mistake in a plain numpy rendering of the chain and must disagree with
+    # the hand-worked result.
+    ex = HAND["nvfp4_inexact_tensor_scale"]
+    x = np.stack([f32hex(r) for r in ex["rows_hex"]]).astype(np.float32)
+    T = np.float32(np.abs(x).max())
+    want_codes = np.array(ex["codes"])
+    want_bs = hexs(ex["block_scales"])
+    want_st = int(ex["tensor_scale_hex"], 16)
+
+    def chain(st_mode="ok", g_mode="ok", d_mode="ok", inv_mode="ok", y_mode="ok"):
+        st32 = np.float32(T / np.float32(2688.0))
+        st = {"ok": st32, "recip": np.float32(T * np.float32(1.0 / 2688.0))}[st_mode]
+        g = np.float32(448.0) / T if g_mode == "ok" else 448.0 / np.float64(T)
+        amax = np.abs(x).max(axis=1)
+        bs = O.e4m3_encode(np.float32(amax * g) if g_mode == "ok" else np.float32(amax.astype(np.float64) * g))
+        bval = O.e4m3_decode(bs)
+        if d_mode == "ok":
+            d = (bval.astype(np.float32) * st).astype(np.float32)
+        elif d_mode == "fp64":
+            d = bval * np.float64(st)                          # product left unrounded
+        else:                                                  # s_t unrounded inside d
+            d = np.float32(bval * (np.float64(T) / 2688.0))
+        if inv_mode == "ok":
+            y = np.float32(x * np.float32(1.0 / np.float64(np.float32(d))[:, None]).astype(np.float32)) \
+                if d_mode == "ok" else np.float32(x * np.float32(1.0 / d)[:, None])
+        else:                                                  # one rounding of x / d
+            y = np.float32(x.astype(np.float64) / np.float64(d)[:, None])
+        if y_mode == "fp64":
+            y = x.astype(np.float64) * np.float64(np.float32(1.0 / np.float64(np.float32(d))))[:, None]
+        return int(np.float32(st).view(np.uint32)), bs, _e2m1_nearest(y)
+
+    st, bs, codes = chain()
+    assert st == want_st and np.array_equal(bs, want_bs) and np.array_equal(codes, want_codes)
+    for variant in ({"st_mode": "recip"}, {"g_mode": "fp64"}, {"d_mode": "fp64"},
+                    {"d_mode": "st_fp64"}, {"inv_mode": "div"}, {"y_mode": "fp64"}):
+        st, bs, codes = chain(**variant)
+        assert (st != want_st or not np.array_equal(bs, want_bs)
+                or not np.array_equal(codes, want_codes)), variant
+
+
+def test_row_scale_examples_catch_precision_mistakes():
+    # Same for the per-row FP8 and INT8 examples: s = fp32(amax/qmax),
+    # inv = fp32(qmax/amax), y = fp32(x * inv); each variant plants one
+    # mistake (s from a reciprocal multiply, inv = 1/s, x / s, an unrounded
+    # inv or an unrounded y) and must change the scale bits or a code.
+    for key, q, enc in (("fp8_row_inexact_scale", 448.0, lambda y: O.e4m3_encode(y)),
+                        ("int8_row_inexact_scale", 127.0, lambda y: np.clip(np.rint(y), -127, 127))):
+        ex = HAND[key]
+        x = f32hex(ex["row_hex"]).astype(np.float32)
+        want_s = int(ex["scale_hex"], 16)
+        want = hexs(ex["codes"]) if key.startswith("fp8") else np.array(ex["codes"])
+        amax = np.float32(np.abs(x).max())
+
+        def chain(mode):
+            s = np.float32(amax / np.float32(q))
+            if mode == "s_recip":
+                s = np.float32(amax * np.float32(1.0 / q))
+            inv = np.float32(np.float32(q) / amax)
+            if mode == "inv_from_s":
+                y = np.float32(x * np.float32(np.float32(1.0) / s))
+            elif mode == "div":
+                y = np.float32(x / s)
+            elif mode == "inv_fp64":
+                y = np.float32(x.astype(np.float64) * (q / np.float64(amax)))
+            elif mode == "y_fp64":
+                y = x.astype(np.float64) * np.float64(inv)
+            else:
+                y = np.float32(x * inv)
+            return int(np.float32(s).view(np.uint32)), np.asarray(enc(y)).astype(np.int64)
+
+        s, c = chain("ok")
+        assert s == want_s and np.array_equal(c, want.astype(np.int64)), key
+        for mode in ("s_recip", "inv_from_s", "div", "inv_fp64", "y_fp64"):
+            s, c = chain(mode)
+            assert s != want_s or not np.array_equal(c, want.astype(np.int64)), (key, mode)
+
+
 def test_predict_R_hand_example():
     ex = HAND["predict_R_row"]
     raw = bf16([ex["row"]])
@@ -605,8 +738,9 @@ def test_sparse_bits_accounting():
 
 
 # ---------------------------------------------------------------------------
-# Hadamard rotation ([PD §4]: rescaled +-1 orthogonal matrix, spreads outliers;
-# rotation roughly doubles R for linear-layer inputs)
+# Hadamard rotation ([PD §4]: a rescaled orthogonal +-1 matrix mixes values and
+# spreads outliers; the pages measure R about twice as large after rotation on
+# Q, K and linear-layer inputs)
 # ---------------------------------------------------------------------------
 
 
@@ -670,7 +804,8 @@ def test_rotation_exactness_predicate():
 
 def test_rotation_flattens_outliers_and_raises_R():
     # [PD §4]: rotation spreads the outlier channels, so 2:4 drops more energy
-    # while the dense quantizer's range narrows; R roughly doubles for X
+    # while the dense quantizer's range narrows; the pages measure R about twice
+    # as large on linear-layer inputs
     raw = W.activation_x(0, 256, 4096)
     rot = O.rotate(raw, O.BF16, 128)
     assert O.rotation_exact(raw, O.BF16, 128).all()
