@@ -227,6 +227,55 @@ __device__ inline Sel16 select16(const uint32_t* w) {
   return r;
 }
 
+// Selection of a 16-bit unit through a table in LDS.  The keys carry
+// 8 * (3 - position) in their low byte, so one byte permute placing the low
+// bytes of the two winning keys side by side gives 8 * j1 + 2048 * j2, the
+// LDS byte offset of the table entry for that pair of positions.  The entry
+// holds the byte-permute selector that gathers the kept pair in position
+// order and the group's metadata nibble in both halves of a byte, so the
+// unit's metadata byte is one bit-field insert of its two groups' entries.
+struct SelLut {
+  uint32_t sel, nib;
+};
+constexpr int kSelLutEntries = 3 + 256 * 3 + 1;
+
+// Every thread of the workgroup calls this; the table is ready after the
+// next workgroup barrier.
+__device__ inline void sel_lut_fill(SelLut* lut) {
+  if (threadIdx.x < 16) {
+    const uint32_t j1 = threadIdx.x & 3u, j2 = threadIdx.x >> 2;  // j1 == j2 never occurs
+    const uint32_t jmax = j1 > j2 ? j1 : j2, jmin = j1 > j2 ? j2 : j1;
+    const uint32_t i0 = 3u - jmax, i1 = 3u - jmin, nib = i0 | (i1 << 2);
+    lut[j1 + 256u * j2] = SelLut{0x01000100u + i0 * 0x0202u + i1 * 0x02020000u, nib | (nib << 4)};
+  }
+}
+
+__device__ inline void sel16_group_lut(uint32_t w0, uint32_t w1, const SelLut* lut, uint32_t& kept,
+                                       uint32_t& nib, uint32_t& top) {
+  const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
+  const uint32_t k0 = (a << 16) | 24u, k1 = (a & 0xFFFF0000u) | 16u;
+  const uint32_t k2 = (b << 16) | 8u, k3 = b & 0xFFFF0000u;
+  uint32_t t1, t2;
+  top2(k0, k1, k2, k3, t1, t2);
+  const uint32_t off = __builtin_amdgcn_perm(t2, t1, 0x0c0c0400u);  // 8 * j1 + 2048 * j2
+  const SelLut e = *reinterpret_cast<const SelLut*>(reinterpret_cast<const char*>(lut) + off);
+  kept = __builtin_amdgcn_perm(w1, w0, e.sel);
+  nib = e.nib;
+  top = t1;
+}
+
+// Kept pairs, metadata byte and the larger top key (its high half is the
+// unit's |max|) of a 16-bit unit.
+__device__ inline Sel16 select16_lut(const uint32_t* w, const SelLut* lut) {
+  Sel16 r;
+  uint32_t n0, n1, t0, t1;
+  sel16_group_lut(w[0], w[1], lut, r.k0, n0, t0);
+  sel16_group_lut(w[2], w[3], lut, r.k1, n1, t1);
+  r.mb = (n0 & 0x0Fu) | (n1 & 0xF0u);
+  r.topkey = t0 > t1 ? t0 : t1;
+  return r;
+}
+
 // Both group selections of a unit -> metadata byte (group 0 in the low nibble).
 // Wanda reads the 8 channel norms of the unit (k0 = its first position).
 // ---------------------------------------------------------------------------
@@ -461,25 +510,80 @@ __device__ inline float enc_int(float y, float qmax) {
 }
 
 // ---------------------------------------------------------------------------
-// Team reductions (fixed order -> deterministic).  TEAM <= 64 stays inside a
-// wave; larger teams combine their waves through LDS (all threads of the
-// block must call these together).
+// Lane exchange and team reductions.
 // ---------------------------------------------------------------------------
+// Value of lane (lane ^ D) of the wave.  DPP row operations for D <= 8
+// (quad_perm [1,0,3,2] and [2,3,0,1]; D = 4 as a quad reverse followed by a
+// half-row mirror, i ^ 3 ^ 7 = i ^ 4; row_ror:8 on 16-lane rows), ds_swizzle
+// (xor mask 16 within 32 lanes) and ds_bpermute for 32.  Every lane of the
+// wave must be active.
+template <int CTRL>
+__device__ inline uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int D>
+__device__ inline uint32_t xor_lane32(uint32_t v) {
+  if constexpr (D == 1) return dpp32<0xB1>(v);
+  else if constexpr (D == 2) return dpp32<0x4E>(v);
+  else if constexpr (D == 4) return dpp32<0x141>(dpp32<0x1B>(v));
+  else if constexpr (D == 8) return dpp32<0x128>(v);
+  else if constexpr (D == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else return (uint32_t)__shfl_xor((int)v, D, 64);
+}
+template <int D>
+__device__ inline double xor_lane(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = xor_lane32<D>((uint32_t)b), hi = xor_lane32<D>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Xor butterflies over the TEAM (<= 64) adjacent lanes of a team: DPP row
+// operations for distances 1..8, ds_swizzle for 16, and for a whole wave the
+// two half-wave results read as scalars.  Every lane ends with the team's
+// result, combined in a fixed order (deterministic; commutative + and max give
+// all lanes the same bits).  Every lane of the wave must take part.
+template <int TEAM>
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  if constexpr (TEAM > 1) { const uint32_t w = xor_lane32<1>(v); v = v > w ? v : w; }
+  if constexpr (TEAM > 2) { const uint32_t w = xor_lane32<2>(v); v = v > w ? v : w; }
+  if constexpr (TEAM > 4) { const uint32_t w = xor_lane32<4>(v); v = v > w ? v : w; }
+  if constexpr (TEAM > 8) { const uint32_t w = xor_lane32<8>(v); v = v > w ? v : w; }
+  if constexpr (TEAM > 16) { const uint32_t w = xor_lane32<16>(v); v = v > w ? v : w; }
+  if constexpr (TEAM > 32) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    v = a > b ? a : b;
+  }
+  return v;
+}
+
+template <int TEAM>
+__device__ inline double wave_sum_f64(double v) {
+  if constexpr (TEAM > 1) v += xor_lane<1>(v);
+  if constexpr (TEAM > 2) v += xor_lane<2>(v);
+  if constexpr (TEAM > 4) v += xor_lane<4>(v);
+  if constexpr (TEAM > 8) v += xor_lane<8>(v);
+  if constexpr (TEAM > 16) v += xor_lane<16>(v);
+  if constexpr (TEAM > 32) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t l0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 0);
+    const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 0);
+    const uint32_t l1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 32);
+    const uint32_t h1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 32);
+    v = __builtin_bit_cast(double, (uint64_t)l0 | ((uint64_t)h0 << 32)) +
+        __builtin_bit_cast(double, (uint64_t)l1 | ((uint64_t)h1 << 32));
+  }
+  return v;
+}
+
+// Teams wider than a wave combine their waves through LDS (all threads of the
+// block must call these together).
 template <int TEAM>
 __device__ inline uint32_t team_max_u32(uint32_t v, uint32_t* lds) {
   if constexpr (TEAM <= 64) {
-#pragma unroll
-    for (int o = TEAM / 2; o > 0; o >>= 1) {
-      uint32_t w = (uint32_t)__shfl_xor((int)v, o, TEAM);
-      v = v > w ? v : w;
-    }
-    return v;
+    return wave_max_u32<TEAM>(v);
   } else {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
-      v = v > w ? v : w;
-    }
+    v = wave_max_u32<64>(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -494,12 +598,9 @@ __device__ inline uint32_t team_max_u32(uint32_t v, uint32_t* lds) {
 template <int TEAM>
 __device__ inline double team_sum_f64(double v, double* lds) {
   if constexpr (TEAM <= 64) {
-#pragma unroll
-    for (int o = TEAM / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, TEAM);
-    return v;
+    return wave_sum_f64<TEAM>(v);
   } else {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v = wave_sum_f64<64>(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -543,31 +644,6 @@ __device__ inline void unit_store_f32(Unit<DT>& u, const float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) u.w[i] = h[2 * i] | (h[2 * i + 1] << 16);
   }
-}
-
-// Value of lane (lane ^ D) of the wave.  DPP row operations for D <= 8
-// (quad_perm [1,0,3,2] and [2,3,0,1]; D = 4 as a quad reverse followed by a
-// half-row mirror, i ^ 3 ^ 7 = i ^ 4; row_ror:8 on 16-lane rows), ds_swizzle
-// (xor mask 16 within 32 lanes) and ds_bpermute for 32.  Every lane of the
-// wave must be active.
-template <int CTRL>
-__device__ inline uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
-}
-template <int D>
-__device__ inline uint32_t xor_lane32(uint32_t v) {
-  if constexpr (D == 1) return dpp32<0xB1>(v);
-  else if constexpr (D == 2) return dpp32<0x4E>(v);
-  else if constexpr (D == 4) return dpp32<0x141>(dpp32<0x1B>(v));
-  else if constexpr (D == 8) return dpp32<0x128>(v);
-  else if constexpr (D == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-  else return (uint32_t)__shfl_xor((int)v, D, 64);
-}
-template <int D>
-__device__ inline double xor_lane(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = xor_lane32<D>((uint32_t)b), hi = xor_lane32<D>((uint32_t)(b >> 32));
-  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
 }
 
 // One butterfly stage across lanes at unit distance D: the lower lane of a

@@ -207,7 +207,7 @@ int64_t gemm_col_tiles(int64_t N) { return (N + kGN - 1) / kGN; }
 hipError_t launch_side_delta(const RowDesc& d, const SideParams& sp, void* out, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
-  return with_row_variant(nunits, [&]<int TEAM, int UPL>() {
+  return with_row_variant<0>(nunits, [&]<int TEAM, int UPL>() {
     hipLaunchKernelGGL((k_side_delta<TEAM, UPL>), persistent_grid(g.nrows, TEAM), dim3(kBlock), 0,
                        s, g, sp, (uint16_t*)out);
     return hipGetLastError();

@@ -274,6 +274,11 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
   // 16384 x 4096).  Pairwise 4:8 can drop a row's largest element, so it
   // takes the kept maximum of the gathered values like Wanda.
   constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA && PAT == PAT_24;
+  __shared__ SelLut lut[FAST16 ? kSelLutEntries : 1];
+  if constexpr (FAST16) {
+    sel_lut_fill(lut);
+    __syncthreads();
+  }
   for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
     uint32_t am = 0;
@@ -284,7 +289,7 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
       uint32_t top = 0;
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {  // zero units select zeros
-        const Sel16 r = select16(u[j].w);
+        const Sel16 r = select16_lut(u[j].w, lut);
         sk[j][0] = r.k0;
         sk[j][1] = r.k1;
         mb[j] = r.mb;
