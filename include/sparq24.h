@@ -202,6 +202,23 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score,
                                  int64_t rows_per_block, double* out, void* ws,
                                  size_t* ws_bytes, hipStream_t stream);
 
+/* sparq24_predict_R without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs and errors as
+ * sparq24_predict_R, except that the workspace is a static device array of
+ * SPARQ24_NOALLOC_SCRATCH_BYTES inside the library: each GPU it runs on holds
+ * one copy until the process ends, and the call allocates nothing.  A call
+ * whose workspace would exceed that size (as sparq24_predict_R's size query
+ * reports it) returns SPARQ24_ERR_WORKSPACE and enqueues nothing.  Every call
+ * on one GPU uses that GPU's array, so calls that overlap on one GPU (from
+ * several host threads or on several streams) race; serialise them.  The
+ * array's contents need no initialisation (each call writes before it reads). */
+#define SPARQ24_NOALLOC_SCRATCH_BYTES (8u << 20)
+sparq24_status sparq24_predict_R_noalloc(const sparq24_tensor* x, int32_t score,
+                                         const float* col_norm, const sparq24_qspec* kept_q,
+                                         const sparq24_qspec* dense_q, int32_t npairs,
+                                         int64_t rows_per_block, double* out, hipStream_t stream);
+
 /* Pairwise 4:8 prune-and-compress [PD §6: Blackwell's sparse FP4 splits each
  * group of eight into four adjacent pairs and keeps two].  In every aligned
  * group of eight along K the two pairs (2p, 2p+1) with the largest energy

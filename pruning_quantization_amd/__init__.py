@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     lib,
     operator_error,
     predict_R,
+    predict_R_noalloc,
     prune_compress,
     prune_compress_pairs48,
     predict_R_pairs48,

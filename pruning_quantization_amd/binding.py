@@ -56,7 +56,8 @@ SYMBOLS = ("sparq24_prune_compress", "sparq24_quantize", "sparq24_prune_quantize
            "sparq24_predict_R_pairs48", "sparq24_hadamard", "sparq24_quantize_rot",
            "sparq24_prune_quantize_rot", "sparq24_predict_R_rot", "sparq24_operator_error",
            "sparq24_sparse_gemm", "sparq24_dense_gemm", "sparq24_fp8_gemm",
-           "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version")
+           "sparq24_bits_per_element", "sparq24_status_string", "sparq24_version",
+           "sparq24_predict_R_noalloc")
 
 _lib = None
 
@@ -82,6 +83,8 @@ def lib(path: Optional[str] = None):
                                  POINTER(c_size_t), c_void_p],
         "sparq24_predict_R": [T, c_int32, c_void_p, Q, Q, c_int32, c_int64, c_void_p, c_void_p,
                               POINTER(c_size_t), c_void_p],
+        "sparq24_predict_R_noalloc": [T, c_int32, c_void_p, Q, Q, c_int32, c_int64, c_void_p,
+                                      c_void_p],
         "sparq24_col_l2norm": [T, c_void_p, c_void_p, POINTER(c_size_t), c_void_p],
         "sparq24_copy": [c_void_p, c_void_p, c_size_t, c_void_p],
         "sparq24_prune_compress_pairs48": [T, c_void_p, c_void_p, c_void_p],
@@ -454,6 +457,28 @@ def predict_R(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QLike], ax
     st = L.sparq24_predict_R(ctypes.byref(c), _score(score), npt, ka, da, npairs, rows_per_block,
                              out.data_ptr(), _ptr(ws), _wsarg(n), s)
     _check("sparq24_predict_R", st)
+    return out
+
+
+def predict_R_noalloc(x: torch.Tensor, kept: Sequence[QLike], dense: Sequence[QLike],
+                      axis: int = -1, score: str = "magnitude",
+                      col_norm: Optional[torch.Tensor] = None, rows_per_block: int = 0,
+                      out: Optional[torch.Tensor] = None):
+    """:func:`predict_R` through the allocation-free entry point (its workspace
+    is the library's static device array); ``out`` may be preallocated."""
+    if len(kept) != len(dense):
+        raise ValueError("kept and dense must pair up")
+    c, _ = describe(x, axis)
+    ka, da = _qarray(kept), _qarray(dense)
+    nrows = int(c.batch) * int(c.rows)
+    rpb = rows_per_block or nrows
+    nblk = (nrows + rpb - 1) // rpb
+    if out is None:
+        out = torch.empty(nblk, len(kept), 5, dtype=torch.float64, device=x.device)
+    st = lib().sparq24_predict_R_noalloc(ctypes.byref(c), _score(score), _norm_ptr(score, col_norm),
+                                         ka, da, len(kept), rows_per_block, out.data_ptr(),
+                                         _stream(x))
+    _check("sparq24_predict_R_noalloc", st)
     return out
 
 

@@ -5,12 +5,18 @@
 // include/sparq24.h for the contract of each call.
 #include "sparq24.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "launch.hpp"
 
 using namespace sparq24;
+
+// Workspace of sparq24_predict_R_noalloc (see scratch_address below).
+static __device__ __align__(256) char scratch[SPARQ24_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -445,11 +451,11 @@ sparq24_status prune_quantize_any(const sparq24_tensor* x, int32_t rot_block, in
 }
 
 // mode 0: error_energy (one pair, raw sums); 1: predict_R
-sparq24_status energy_any(const sparq24_tensor* x, int32_t rot_block, int pat, int32_t score,
-                          const float* col_norm, const sparq24_qspec* kept_q,
-                          const sparq24_qspec* dense_q, int32_t npairs, int64_t rows_per_block,
-                          int mode, double* out, void* ws, size_t* ws_bytes, hipStream_t stream) {
-  RowDesc d;
+// Validation and planning shared by the energy calls.
+sparq24_status energy_plan(const sparq24_tensor* x, int32_t rot_block, int pat, int32_t score,
+                           const float* col_norm, const sparq24_qspec* kept_q,
+                           const sparq24_qspec* dense_q, int32_t npairs, int64_t rows_per_block,
+                           int mode, RowDesc& d, EnergyPlan& pl) {
   CHECK(check_tensor(x, true, d));
   if (rot_block) CHECK(check_rot(rot_block, d));
   CHECK(check_score(score, col_norm));
@@ -460,10 +466,20 @@ sparq24_status energy_any(const sparq24_tensor* x, int32_t rot_block, int pat, i
   if (pat == PAT_48 && d.K % 16) return SPARQ24_ERR_SHAPE;
   if (d.B * d.R == 0 || d.K == 0) return SPARQ24_ERR_SHAPE;
   if (d.K / 8 > kMaxRowUnits) return SPARQ24_ERR_SHAPE;
-  EnergyPlan pl;
   CHECK(plan_energy(d, kept_q, dense_q, npairs, rows_per_block, pl));
   pl.p.pairs48 = pat == PAT_48 ? 1 : 0;
   pl.f.mode = mode;
+  return SPARQ24_OK;
+}
+
+sparq24_status energy_any(const sparq24_tensor* x, int32_t rot_block, int pat, int32_t score,
+                          const float* col_norm, const sparq24_qspec* kept_q,
+                          const sparq24_qspec* dense_q, int32_t npairs, int64_t rows_per_block,
+                          int mode, double* out, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  RowDesc d;
+  EnergyPlan pl;
+  CHECK(energy_plan(x, rot_block, pat, score, col_norm, kept_q, dense_q, npairs, rows_per_block,
+                    mode, d, pl));
   bool query;
   CHECK(workspace(ws, ws_bytes, pl.need, query));
   if (query) return SPARQ24_OK;
@@ -471,6 +487,36 @@ sparq24_status energy_any(const sparq24_tensor* x, int32_t rot_block, int pat, i
   if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
   CHECK(device_ok());
   return run_energy(d, score, col_norm, pl, out, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free predict_R.  Its workspace is `scratch`, the static device
+// array at the top of this file: every GPU the library runs on holds one copy
+// until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory,
+// so the device address of the current device's copy is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept; kernels
+// and copies only ever receive that address.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+sparq24_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return SPARQ24_ERR_DEVICE;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {  // two threads racing here both store the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SPARQ24_ERR_DEVICE;
+    }
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return SPARQ24_OK;
 }
 
 int32_t pattern_code(int32_t pattern) {
@@ -517,6 +563,23 @@ sparq24_status sparq24_predict_R(const sparq24_tensor* x, int32_t score, const f
                                  size_t* ws_bytes, hipStream_t stream) {
   return energy_any(x, 0, PAT_24, score, col_norm, kept_q, dense_q, npairs, rows_per_block, 1, out,
                     ws, ws_bytes, stream);
+}
+
+sparq24_status sparq24_predict_R_noalloc(const sparq24_tensor* x, int32_t score,
+                                         const float* col_norm, const sparq24_qspec* kept_q,
+                                         const sparq24_qspec* dense_q, int32_t npairs,
+                                         int64_t rows_per_block, double* out, hipStream_t stream) {
+  RowDesc d;
+  EnergyPlan pl;
+  CHECK(energy_plan(x, 0, PAT_24, score, col_norm, kept_q, dense_q, npairs, rows_per_block, 1, d,
+                    pl));
+  if (pl.need > (size_t)SPARQ24_NOALLOC_SCRATCH_BYTES) return SPARQ24_ERR_WORKSPACE;
+  if (!out) return SPARQ24_ERR_INVALID;
+  if (!aligned16(out)) return SPARQ24_ERR_ALIGN;
+  CHECK(device_ok());
+  void* ws = nullptr;
+  CHECK(scratch_address(&ws));
+  return run_energy(d, score, col_norm, pl, out, ws, stream);
 }
 
 sparq24_status sparq24_prune_compress_pairs48(const sparq24_tensor* x, void* values,

@@ -145,6 +145,17 @@ def test_energy_validation(L):
     assert g(ctypes.byref(t), 0, None, None, ctypes.byref(q(B.Q_FP8)), 0, FAKE, None, ctypes.byref(n), None) == INVALID
 
 
+def test_predict_R_noalloc_size_limit(L):
+    # the static scratch holds SPARQ24_NOALLOC_SCRATCH_BYTES (8 MiB); a plan past
+    # it is rejected on the host, before the device is touched
+    arr = (B.CQSpec * 2)(q(B.Q_FP8), q(B.Q_INT, 4))
+    f = L.sparq24_predict_R_noalloc
+    assert f(ctypes.byref(tensor(rows=1 << 20, k=64)), 0, None, arr, arr, 2, 0, FAKE, None) == WORKSPACE
+    assert f(ctypes.byref(tensor(rows=4, k=64)), 0, None, arr, arr, 0, 0, FAKE, None) == INVALID
+    assert f(ctypes.byref(tensor(rows=4, k=64)), 0, None, arr, arr, 2, 0, None, None) == INVALID
+    assert f(ctypes.byref(tensor(rows=4, k=64)), 0, None, arr, arr, 2, 0, FAKE, None) == DEVICE
+
+
 def test_pairs48_validation(L):
     f = L.sparq24_prune_compress_pairs48
     assert f(ctypes.byref(tensor(k=24)), FAKE, FAKE, None) == SHAPE        # K % 16
