@@ -19,8 +19,12 @@
  *                   Q/K [heads*seq, head_dim], P [heads*q, keys]);
  *     transposed:   row_stride == 1 and k_stride >= R (e.g. V [heads, seq,
  *                   head_dim] pruned along seq: B = heads, R = head_dim,
- *                   K = seq, k_stride = head_dim).  sparq24_prune_compress
- *                   reads it directly through an LDS-tiled transpose; the
+ *                   K = seq, k_stride = head_dim), R <= 4194240 (65535
+ *                   tiles of 64 rows, else SPARQ24_ERR_UNSUPPORTED).
+ *                   sparq24_prune_compress reads it directly (16-bit
+ *                   magnitude with R % 64 == 0 and K % 256 == 0: 8 x 8
+ *                   blocks transposed in registers; otherwise an LDS-tiled
+ *                   transpose); the
  *                   other calls (except sparq24_col_l2norm, which rejects it
  *                   with SPARQ24_ERR_UNSUPPORTED) first stage it as dense
  *                   K-contiguous rows in their workspace, which then needs

@@ -74,6 +74,8 @@ sparq24_status check_tensor(const sparq24_tensor* x, bool allow_transposed, RowD
     if (d.B > 1 && x->batch_stride < (d.K - 1) * x->k_stride + d.R) return SPARQ24_ERR_UNSUPPORTED;
     if ((x->k_stride * es) % 16) return SPARQ24_ERR_ALIGN;
     if (d.B > 1 && (x->batch_stride * es) % 16) return SPARQ24_ERR_ALIGN;
+    // the transposed kernels tile rows by 64 on grid.y (at most 65535 tiles)
+    if ((d.R + 63) / 64 > 65535) return SPARQ24_ERR_UNSUPPORTED;
     d.kcontig = false;
     d.flat = false;
     d.rs = es;

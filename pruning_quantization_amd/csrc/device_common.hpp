@@ -140,20 +140,29 @@ __device__ inline uint32_t select_group(const Unit<DT>& u, int g, const float* n
     uint32_t t1, t2;
     top2(k0, k1, k2, k3, t1, t2);
     return nibble_from_j(t1 & 3u, t2 & 3u);
+  } else if constexpr (WANDA) {
+    // exact: <= 24-bit x 24-bit significands fit in fp64's 53, so the low
+    // mantissa bits of the product are zero and can carry the position.
+    // Non-negative finite doubles (fp64 subnormals are kept) order like their
+    // bit patterns, so the fp64 max / min (one instruction each) rank the
+    // keys exactly.
+    double k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double p = (double)__uint_as_float(__float_as_uint(u.f(4 * g + i)) & 0x7FFFFFFFu) *
+                       (double)n4[i];
+      k[i] = __longlong_as_double(__double_as_longlong(p) | (long long)(3u - i));
+    }
+    const double m1 = __builtin_fmax(k[0], k[1]), n1 = __builtin_fmin(k[0], k[1]);
+    const double m2 = __builtin_fmax(k[2], k[3]), n2 = __builtin_fmin(k[2], k[3]);
+    const double t1 = __builtin_fmax(m1, m2);
+    const double t2 = __builtin_fmax(__builtin_fmin(m1, m2), __builtin_fmax(n1, n2));
+    return nibble_from_j((uint32_t)__double_as_longlong(t1) & 3u,
+                         (uint32_t)__double_as_longlong(t2) & 3u);
   } else {
     uint64_t k[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (WANDA) {
-        // exact: <= 24-bit x 24-bit significands fit in fp64's 53, so the low
-        // mantissa bits of the product are zero and can carry the position
-        double p = (double)__uint_as_float(__float_as_uint(u.f(4 * g + i)) & 0x7FFFFFFFu) *
-                   (double)n4[i];
-        k[i] = (uint64_t)__double_as_longlong(p) | (uint64_t)(3u - i);
-      } else {
-        k[i] = ((uint64_t)u.absbits(4 * g + i) << 2) | (uint64_t)(3u - i);
-      }
-    }
+    for (int i = 0; i < 4; ++i) k[i] = ((uint64_t)u.absbits(4 * g + i) << 2) | (uint64_t)(3u - i);
     uint64_t t1, t2;
     top2(k[0], k[1], k[2], k[3], t1, t2);
     return nibble_from_j((uint32_t)t1 & 3u, (uint32_t)t2 & 3u);

@@ -92,20 +92,24 @@ inline dim3 stream_grid(int64_t nrows, int team) {
 constexpr int kBlocksPerCU = 4;
 int device_cu_count();
 
-// Workgroups of kernel K resident per CU (register and LDS limits), from the
-// runtime's occupancy calculator, queried once per kernel.
+// Workgroups of kernel K resident per CU (register and LDS limits) with
+// `shmem` bytes of dynamic LDS, from the runtime's occupancy calculator:
+// queried once per kernel without dynamic LDS, per launch with it.
 template <auto K>
-inline int resident_blocks() {
-  static const int n = [] {
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(K), kBlock,
-                                                     0) != hipSuccess ||
-        b < 1) {
-      (void)hipGetLastError();
-      b = kBlocksPerCU;
-    }
-    return b;
-  }();
+inline int occupancy_query(size_t shmem) {
+  int b = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(K), kBlock,
+                                                   shmem) != hipSuccess ||
+      b < 1) {
+    (void)hipGetLastError();
+    b = shmem ? 1 : kBlocksPerCU;
+  }
+  return b;
+}
+template <auto K>
+inline int resident_blocks(size_t shmem = 0) {
+  if (shmem) return occupancy_query<K>(shmem);
+  static const int n = occupancy_query<K>(0);
   return n;
 }
 

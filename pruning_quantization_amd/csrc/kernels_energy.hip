@@ -358,66 +358,50 @@ __global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restri
   finalize_rows(rowpart, nrows, r0, r1, f, out, blk);
 }
 
-// Row partial sums go either to rowpart[col][row] (blocked reductions) or,
-// when the whole operand is one block (ACC), into a per-team LDS accumulator
-// that each team writes once, to rowpart[col][team] (nparts = all teams).
+// Row partial sums go either to rowpart[col][row] (blocked reductions: the
+// team's sum of each row, from its first lane) or, when the whole operand is
+// one block (acc), into per-lane accumulators in LDS: every lane adds its own
+// share of each row into its own slot (one LDS add, no reduction per row),
+// and at the end the workgroup reduces each column's slots once, in a fixed
+// order, to rowpart[col][workgroup] (nparts = all workgroups).  Each slot is
+// written by one lane only, in program order, so the sums repeat bit for bit.
 struct PartialSink {
   double* rowpart;
   int64_t stride;  // elements per column
   bool acc;
 };
 
-// Accumulator slots per column of a workgroup: one per team, or one per wave
-// for teams of several waves.
-template <int TEAM>
-constexpr int kSinkSlots = kBlock / (TEAM > 64 ? 64 : TEAM);
-
-// Called by one lane per team.  Whole-operand partials go to the team's own
-// slot: its index for one-wave teams, the writing lane's wave for wider ones
-// (distinct per team, so teams of one workgroup never add into one slot).
-template <int TEAM>
-__device__ inline void sink_put(const PartialSink& k, double* lacc, int64_t row, int col,
-                                double v) {
-  if (k.acc) lacc[col * kSinkSlots<TEAM> + (TEAM > 64 ? threadIdx.x >> 6 : threadIdx.x / TEAM)] += v;
-  else k.rowpart[(int64_t)col * k.stride + row] = v;
+// Dynamic LDS of a launch: ncols x kBlock per-lane accumulators (acc only).
+inline size_t sink_lds_bytes(bool acc, int ncols) {
+  return acc ? (size_t)ncols * kBlock * sizeof(double) : 0;
 }
 
-// A row's column value from every lane's share v.  Whole-operand partials of
-// multi-wave teams take each wave's sum into the wave's own slot (no
-// workgroup barrier per row; the flush adds the slots in order); otherwise
-// the team sum goes to the sink from the team's first lane.
 template <int TEAM>
 __device__ inline void sink_sum(const PartialSink& k, double* lacc, double* redd, int64_t row,
                                 int col, double v, bool live) {
-  if constexpr (TEAM > 64) {
-    if (k.acc) {
-      const double w = team_sum_f64<64>(v, redd);
-      if (live && (threadIdx.x & 63) == 0) lacc[col * kSinkSlots<TEAM> + (threadIdx.x >> 6)] += w;
-      return;
-    }
+  if (k.acc) {
+    if (live)
+      __hip_atomic_fetch_add(&lacc[col * kBlock + threadIdx.x], v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
   }
   const double a = team_sum_f64<TEAM>(v, redd);
-  if (live && threadIdx.x % TEAM == 0) sink_put<TEAM>(k, lacc, row, col, a);
+  if (live && threadIdx.x % TEAM == 0) k.rowpart[(int64_t)col * k.stride + row] = a;
 }
 
-// One partial per workgroup: thread c adds column c over its slots in order.
-template <int TEAM>
-__device__ inline void sink_flush(const PartialSink& k, double* lacc, int ncols) {
+// One partial per workgroup and column (acc only; every thread calls this).
+__device__ inline void sink_flush(const PartialSink& k, double* lacc, double* redd, int ncols) {
   if (!k.acc) return;
-  constexpr int NS = kSinkSlots<TEAM>;
-  __syncthreads();
-  const int c = threadIdx.x;
-  if (c < ncols) {
-    double a = 0.0;
-    for (int i = 0; i < NS; ++i) a += lacc[c * NS + i];
-    k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
+  for (int c = 0; c < ncols; ++c) {
+    const double a = team_sum_f64<kBlock>(lacc[c * kBlock + threadIdx.x], redd);
+    if (threadIdx.x == 0) k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
   }
 }
 
-template <int TEAM>
-__device__ inline void sink_init(double* lacc, int ncols) {
-  for (int i = threadIdx.x; i < ncols * kSinkSlots<TEAM>; i += kBlock) lacc[i] = 0.0;
-  __syncthreads();
+// Each lane clears its own slots (acc only).
+__device__ inline void sink_init(const PartialSink& k, double* lacc, int ncols) {
+  if (!k.acc) return;
+  for (int c = 0; c < ncols; ++c) lacc[c * kBlock + threadIdx.x] = 0.0;
 }
 
 // Empty asm that claims to modify the packed magnitudes: values derived from
@@ -436,11 +420,10 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
 // without spilling at four waves per SIMD, so a whole 4096-row operand is
 // resident in one pass.
 constexpr int kEnergyWavesMag4096 = 4;
-// INT quantizers evaluated per unpacked unit in one pass of the bf16 kernel.
-// 1: chunks of 2 or 4 share each unit's unpacking but raise register use
-// past four waves per SIMD (magnitude 2:4, spills) or three (Wanda), which
-// costs more than the shared unpacking saves.
-constexpr int kIntChunk = 1;
+// INT quantizers of each side evaluated per unpacked unit in one pass of the
+// bf16 kernel (the equal-bits sweep 2:4 + INT-2m vs INT-(m+1), m = 2..8, is
+// two passes: 4 + 4 and 3 + 3; eight per side spilled registers).
+constexpr int kFusedInt = 4;
 
 template <int TEAM, int UPL, int ROT, int SEL>
 constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? kEnergyWavesMag4096 : 1;
@@ -451,9 +434,9 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
                         PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
-  __shared__ double lacc[(2 + 2 * kMaxQ) * kSinkSlots<TEAM>];
+  extern __shared__ double lacc[];  // per-lane accumulators (whole-operand sums)
   const int ncols = 2 + p.kept.n + p.dense.n;
-  sink_init<TEAM>(lacc, ncols);
+  sink_init(sink, lacc, ncols);
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
@@ -512,80 +495,95 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     sink_sum<TEAM>(sink, lacc, redd, row, 0, kept2 + drop, live);
     sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
-    // INT quantizers run in chunks of up to kIntChunk per pass over the row:
-    // each unit is unpacked once for the whole chunk.  A kept one with a
-    // dense twin (same format and qmax) under magnitude 2:4 is evaluated by
-    // the twin, since both take their scale from the same maximum and code
-    // each kept value identically: the dense pass accumulates kept and
-    // dropped positions apart and writes both columns.
-    // (quantizer indices are read from the kernel arguments by position:
-    // a pointer into them would force a private copy of the parameters)
-    auto kept_ints = [&]<int NQ>(int c0) {
-      pin_packed<UPL>(pk);
-      int idx[NQ];
-      float s[NQ], inv[NQ];
-      double acc[NQ];
+    // INT quantizers, up to kFusedInt of each side per pass over the row, so
+    // each unit is unpacked once for all of them.  One-wave teams compute a
+    // pass's per-row scales lane-parallel (lane i divides for kept quantizer
+    // i, lane 32 + i for dense quantizer i) and read them back as
+    // wave-uniform values: two divisions per pass instead of two per
+    // quantizer (lane kFusedInt + i takes dense quantizer i).  A kept quantizer with a dense twin (same format and qmax)
+    // under magnitude 2:4 is evaluated by the twin, since both take their
+    // scale from the same maximum and code each kept value identically: the
+    // dense side accumulates kept and dropped positions apart and writes both
+    // columns.  (Quantizer indices are read from the kernel arguments by
+    // position: a pointer into them would force a private copy.)
+    const int nki = SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int;
+    for (int c0 = 0; c0 < nki || c0 < p.n_dense_int; c0 += kFusedInt) {
+      const int nk = nki - c0 < 0 ? 0 : (nki - c0 < kFusedInt ? nki - c0 : kFusedInt);
+      const int nd = p.n_dense_int - c0 < 0 ? 0
+                                            : (p.n_dense_int - c0 < kFusedInt ? p.n_dense_int - c0 : kFusedInt);
+      int kidx[kFusedInt], didx[kFusedInt];
+      float ks[kFusedInt], kinv[kFusedInt], ds[kFusedInt], dinv[kFusedInt];
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        idx[i] = SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i];
-        row_scale(famk, p.kept.qmax[idx[i]], s[i], inv[i]);
-        acc[i] = 0.0;
+      for (int i = 0; i < kFusedInt; ++i) {
+        kidx[i] = i < nk ? (SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i]) : 0;
+        didx[i] = i < nd ? p.dense_int[c0 + i] : 0;
       }
+      if constexpr (TEAM == 64) {
+        const int lane = threadIdx.x & 63;
+        float q = 1.0f, a = famk;
+#pragma unroll
+        for (int i = 0; i < kFusedInt; ++i) {
+          if (i < nk && lane == i) q = p.kept.qmax[kidx[i]];
+          if (i < nd && lane == kFusedInt + i) {
+            q = p.dense.qmax[didx[i]];
+            a = famd;
+          }
+        }
+        float sl, il;
+        row_scale(a, q, sl, il);
+#pragma unroll
+        for (int i = 0; i < kFusedInt; ++i) {
+          ks[i] = __shfl(sl, i, 64);
+          kinv[i] = __shfl(il, i, 64);
+          ds[i] = __shfl(sl, kFusedInt + i, 64);
+          dinv[i] = __shfl(il, kFusedInt + i, 64);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kFusedInt; ++i) {
+          ks[i] = kinv[i] = ds[i] = dinv[i] = 0.0f;
+          if (i < nk) row_scale(famk, p.kept.qmax[kidx[i]], ks[i], kinv[i]);
+          if (i < nd) row_scale(famd, p.dense.qmax[didx[i]], ds[i], dinv[i]);
+        }
+      }
+      // dense sums over kept and dropped positions apart only where a kept
+      // twin can exist (magnitude 2:4); otherwise one sum over the unit
+      constexpr bool SPLIT = SEL == SEL_MAG;
+      pin_packed<UPL>(pk);
+      double ka[kFusedInt], dka[kFusedInt], dda[kFusedInt];
+#pragma unroll
+      for (int i = 0; i < kFusedInt; ++i) ka[i] = dka[i] = dda[i] = 0.0;
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
-        const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+        const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
+                            mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) acc[i] += (double)mag_sq_err_int<4>(s[i], inv[i], v);
-        __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
-      }
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) sink_sum<TEAM>(sink, lacc, redd, row, 2 + idx[i], acc[i], live);
-    };
-    auto dense_ints = [&]<int NQ>(int c0) {
-      pin_packed<UPL>(pk);
-      int idx[NQ];
-      float s[NQ], inv[NQ];
-      double acck[NQ], accd[NQ];
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        idx[i] = p.dense_int[c0 + i];
-        row_scale(famd, p.dense.qmax[idx[i]], s[i], inv[i]);
-        acck[i] = accd[i] = 0.0;
-      }
-#pragma unroll
-      for (int j = 0; j < UPL; ++j) {
-        const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-        const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          acck[i] += (double)mag_sq_err_int<4>(s[i], inv[i], vk);
-          accd[i] += (double)mag_sq_err_int<4>(s[i], inv[i], vd);
+        for (int i = 0; i < kFusedInt; ++i) {
+          if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
+          if (i < nd) {
+            if constexpr (SPLIT) {
+              dka[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v);
+              dda[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v + 4);
+            } else {
+              dda[i] += (double)mag_sq_err_int<8>(ds[i], dinv[i], v);
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
       }
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        int twin = -1;
-        if (SEL == SEL_MAG)
-          for (int k = 0; k < p.kept.n; ++k)
-            if (p.kept_twin[k] == idx[i]) twin = k;
-        if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck[i], live);
-        sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + idx[i], acck[i] + accd[i], live);
-      }
-    };
-    auto chunks = [&](int n, auto&& run) {
-      for (int c0 = 0; c0 < n; c0 += kIntChunk) {
-        const int nq = n - c0 < kIntChunk ? n - c0 : kIntChunk;
-        if constexpr (kIntChunk >= 4) {
-          if (nq == 4) { run.template operator()<4>(c0); continue; }
-          if (nq == 3) { run.template operator()<3>(c0); continue; }
+      for (int i = 0; i < kFusedInt; ++i) {
+        if (i < nk) sink_sum<TEAM>(sink, lacc, redd, row, 2 + kidx[i], ka[i], live);
+        if (i < nd) {
+          int twin = -1;
+          if (SEL == SEL_MAG)
+            for (int k = 0; k < p.kept.n; ++k)
+              if (p.kept_twin[k] == didx[i]) twin = k;
+          if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dka[i], live);
+          sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + didx[i], dka[i] + dda[i], live);
         }
-        if (nq == 2) run.template operator()<2>(c0);
-        else run.template operator()<1>(c0);
       }
-    };
-    chunks(SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int, kept_ints);
-    chunks(p.n_dense_int, dense_ints);
+    }
 
     // the other formats, one pass each
     for (int q = 0; q < p.kept.n; ++q) {
@@ -665,7 +663,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
       sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   });
-  sink_flush<TEAM>(sink, lacc, ncols);
+  sink_flush(sink, lacc, redd, ncols);
 }
 
 template <class DT, int TEAM, int UPL, bool WANDA, int ROT>
@@ -673,9 +671,9 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
                                                         EnergyParams p, PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
   __shared__ double redd[kBlock / 64];
-  __shared__ double lacc[(2 + 2 * kMaxQ) * kSinkSlots<TEAM>];
+  extern __shared__ double lacc[];  // per-lane accumulators (whole-operand sums)
   const int ncols0 = 2 + p.kept.n + p.dense.n;
-  sink_init<TEAM>(lacc, ncols0);
+  sink_init(sink, lacc, ncols0);
 
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
@@ -694,7 +692,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   const int64_t nrows = g.nrows;
 
   for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
-    const bool writer = row < nrows && t == 0;
+    const bool live = row < nrows;
     uint32_t km[UPL];  // 8-bit kept mask per unit
     uint32_t mbs[UPL];
     double x2 = 0.0, drop = 0.0;
@@ -729,12 +727,8 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
     }
     amd = team_max_u32<TEAM>(amd, redu);
     amk = team_max_u32<TEAM>(amk, redu);
-    x2 = team_sum_f64<TEAM>(x2, redd);
-    drop = team_sum_f64<TEAM>(drop, redd);
-    if (writer) {
-      sink_put<TEAM>(sink, lacc, row, 0, x2);
-      sink_put<TEAM>(sink, lacc, row, 1, drop);
-    }
+    sink_sum<TEAM>(sink, lacc, redd, row, 0, x2, live);
+    sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
     const float famk = DT::to_f32(amk), famd = DT::to_f32(amd);
 
     // kept-side quantizers: per-row scale from the kept maximum.  Every
@@ -773,8 +767,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
           }
         }
       }
-      acc = team_sum_f64<TEAM>(acc, redd);
-      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + q, acc);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
     }
 
     // dense quantizers
@@ -819,11 +812,10 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
           }
         }
       }
-      acc = team_sum_f64<TEAM>(acc, redd);
-      if (writer) sink_put<TEAM>(sink, lacc, row, 2 + p.kept.n + q, acc);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   });
-  sink_flush<TEAM>(sink, lacc, ncols0);
+  sink_flush(sink, lacc, redd, ncols0);
 }
 
 // Stage 1: sum of one column over one chunk of at most kChunk rows that lies
@@ -895,7 +887,8 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               int64_t* nparts, hipStream_t s) {
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
-  const bool acc = rows_per_block >= g.nrows;  // one block: per-team partials
+  const bool acc = rows_per_block >= g.nrows;  // one block: per-lane accumulators
+  const size_t shmem = sink_lds_bytes(acc, 2 + p.kept.n + p.dense.n);
   if (wanda && d.rot.n) return hipErrorInvalidValue;
   auto geom = [&](int, dim3 grid, PartialSink& k) {
     k.rowpart = rowpart;
@@ -909,10 +902,10 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
     auto body = [&]<int TEAM, int UPL, bool LONG>() {
       auto go = [&]<int R, int SEL>() {
         constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL>;
-        const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
+        const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>(shmem));
         PartialSink k;
         geom(TEAM, grid, k);
-        hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
+        hipLaunchKernelGGL(K, grid, dim3(kBlock), shmem, s, g, norm, p, k);
         return hipGetLastError();
       };
       if constexpr (LONG) {
@@ -938,10 +931,10 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   auto generic = [&]<class DT>() {
     auto go = [&]<int TEAM, int UPL, bool WANDA, int R>() {
       constexpr auto K = k_energy_rows<DT, TEAM, UPL, WANDA, R>;
-      const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>());
+      const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>(shmem));
       PartialSink k;
       geom(TEAM, grid, k);
-      hipLaunchKernelGGL(K, grid, dim3(kBlock), 0, s, g, norm, p, k);
+      hipLaunchKernelGGL(K, grid, dim3(kBlock), shmem, s, g, norm, p, k);
       return hipGetLastError();
     };
     if (d.rot.n > 512)  // long rotation blocks: whole-workgroup teams

@@ -66,6 +66,9 @@ def test_prune_compress_validation(L):
     assert pc(L, tensor(rows=4, k=64, rs=68)) == ALIGN                     # 136-byte rows
     assert pc(L, tensor(rows=4, k=64, rs=32)) == UNSUPPORTED               # overlapping rows
     assert pc(L, tensor(rows=4, k=64, rs=2, ks=4)) == UNSUPPORTED          # neither layout
+    # transposed rows are tiled by 64 on grid.y: 65535 tiles at most
+    big = 65535 * 64
+    assert pc(L, tensor(rows=big + 8, k=64, rs=1, ks=big + 8, bs=0)) == UNSUPPORTED
     # empty operands are a no-op, even with null outputs
     assert pc(L, tensor(rows=0), vals=None, meta=None) == OK
     assert pc(L, tensor(k=0), vals=None, meta=None) == OK

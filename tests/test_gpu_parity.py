@@ -108,6 +108,25 @@ def test_prune_compress_transposed(dtype, shape):
     assert_same(raw_np(v).reshape(-1, shape[1] // 2), wv, "values")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(1, 256, 128), (3, 512, 64), (2, 1024, 192), (8, 16384, 128)])
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_prune_compress_transposed_register_blocks(dtype, shape, kind):
+    # 16-bit V with dims % 64 == 0 and seq % 256 == 0: the kernel that transposes
+    # 8 x 8 blocks in registers (the V shape of 16K-token attention included)
+    rng = np.random.default_rng(sum(shape) + len(kind))
+    flat = (shape[0] * shape[1], shape[2])
+    raw = (tie_heavy_raw(rng, flat, dtype) if kind == "ties" else random_raw(rng, flat, dtype)).reshape(shape)
+    x = to_dev(raw, dtype)
+    v, m = S.prune_compress(x, axis=1)
+    rows = np.ascontiguousarray(np.swapaxes(raw, 1, 2)).reshape(-1, shape[1])
+    pick = np.unique(np.r_[0:9, rows.shape[0] - 9:rows.shape[0],
+                           rng.choice(rows.shape[0], size=min(40, rows.shape[0]), replace=False)])
+    wv, wm = O.prune_compress(rows[pick], dtype)
+    assert_same(raw_np(m).reshape(-1, shape[1] // 8)[pick], wm, "meta")
+    assert_same(raw_np(v).reshape(-1, shape[1] // 2)[pick], wv, "values")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_transposed_rows_not_filling_chunks(dtype):
     # rows along the contiguous axis padded to 72 (16-byte aligned positions)
