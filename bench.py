@@ -504,7 +504,8 @@ def side_calls(a, S, W, O, torch, dev, bf, capture, elapsed_us, hx_bits, hpool, 
             us = elapsed_us(lambda: [graphs[name].replay() for _ in range(reps)]) / (reps * m)
         else:
             us = elapsed_us(lambda: [f(k % n) for _ in range(reps) for k in range(m)]) / (reps * m)
-        per_call[name] = {"us": round(us, 3), "GBps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+        per_call[name] = {"us": round(us, 3), "GBps": round(alg[name] / (us * 1e-6) / 1e9, 1),
+                          "bytes": alg[name], "launches": reps * m}
         if name in flops:
             tf = flops[name] / (us * 1e-6) / 1e12
             pk = mfma_peak.get(name, 2500.0)
