@@ -129,6 +129,21 @@ __device__ inline uint32_t nibble_from_j(uint32_t j1, uint32_t j2) {
   return 15u - jmax - 4u * jmin;
 }
 
+// fp64 maximum / minimum of finite operands: one instruction each, without
+// the quieting of signalling NaNs that the IEEE maxNum / minNum lowering
+// adds for operands it cannot prove canonical (keys built with bit
+// operations), which no finite value needs.
+__device__ inline double max_f64_finite(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline double min_f64_finite(double a, double b) {
+  double r;
+  asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Selection for group g (0 or 1) of a unit.
 template <class DT, bool WANDA>
 __device__ inline uint32_t select_group(const Unit<DT>& u, int g, const float* n4) {
@@ -153,10 +168,10 @@ __device__ inline uint32_t select_group(const Unit<DT>& u, int g, const float* n
                        (double)n4[i];
       k[i] = __longlong_as_double(__double_as_longlong(p) | (long long)(3u - i));
     }
-    const double m1 = __builtin_fmax(k[0], k[1]), n1 = __builtin_fmin(k[0], k[1]);
-    const double m2 = __builtin_fmax(k[2], k[3]), n2 = __builtin_fmin(k[2], k[3]);
-    const double t1 = __builtin_fmax(m1, m2);
-    const double t2 = __builtin_fmax(__builtin_fmin(m1, m2), __builtin_fmax(n1, n2));
+    const double m1 = max_f64_finite(k[0], k[1]), n1 = min_f64_finite(k[0], k[1]);
+    const double m2 = max_f64_finite(k[2], k[3]), n2 = min_f64_finite(k[2], k[3]);
+    const double t1 = max_f64_finite(m1, m2);
+    const double t2 = max_f64_finite(min_f64_finite(m1, m2), max_f64_finite(n1, n2));
     return nibble_from_j((uint32_t)__double_as_longlong(t1) & 3u,
                          (uint32_t)__double_as_longlong(t2) & 3u);
   } else {

@@ -270,10 +270,14 @@ __device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
 // column) in a fixed order and write block blk's outputs: mode 0 = Sx2,
 // Sdropped, kept error, dense error; mode 1 = E_prune, E_qkept, E_2:4,
 // E_dense, R per pair.  Every thread of the workgroup must call this.
+// CB columns are reduced together (CB independent loads per row); the launch
+// picks the smallest of 4, 8, 16 that holds every column, so a call's
+// partials are read in one round where they fit (up to 4 rows x 16 columns
+// of loads in flight per thread).
+template <int CB>
 __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t nrows,
                                      int64_t r0, int64_t r1, const FinalizeParams& f,
                                      double* __restrict__ out, int64_t blk) {
-  constexpr int CB = 8;  // columns reduced together: CB independent loads per row
   __shared__ double sh[CB][kBlock / 64];
   __shared__ double sb[2 + 2 * kMaxQ];
   for (int cb = 0; cb < f.ncols; cb += CB) {
@@ -348,6 +352,7 @@ __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t
   }
 }
 
+template <int CB>
 __global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restrict__ rowpart,
                                                           int64_t nrows, int64_t rpb,
                                                           FinalizeParams f,
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restri
   const int64_t blk = blockIdx.x;
   const int64_t r0 = blk * rpb;
   const int64_t r1 = (r0 + rpb) < nrows ? (r0 + rpb) : nrows;
-  finalize_rows(rowpart, nrows, r0, r1, f, out, blk);
+  finalize_rows<CB>(rowpart, nrows, r0, r1, f, out, blk);
 }
 
 // Row partial sums go either to rowpart[col][row] (blocked reductions: the
@@ -425,11 +430,141 @@ constexpr int kEnergyWavesMag4096 = 4;
 // two passes: 4 + 4 and 3 + 3; eight per side spilled registers).
 constexpr int kFusedInt = 4;
 
-template <int TEAM, int UPL, int ROT, int SEL>
-constexpr int kEnergyWaves = (TEAM == 64 && UPL == 8 && !ROT && SEL == SEL_MAG) ? kEnergyWavesMag4096 : 1;
+// Wave-uniform copy of lane `i` of v (i uniform).
+__device__ inline float lane_value(float v, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
+}
 
-template <int TEAM, int UPL, int ROT, int SEL>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL>)))
+// INT and FP8 quantizers of a bf16 row whose units are held unpacked in
+// registers (UPL <= 8: 8 magnitudes per unit, kept 0..3 then dropped 4..7),
+// for calls without block formats: each element is unpacked once per row and
+// the quantizer loops are plain runtime loops over the row's quantizers.
+// One-wave teams compute the INT scales lane-parallel once per row (lane i:
+// kept quantizer i, lane kMaxQ + i: dense quantizer i) and read them back as
+// wave-uniform values.  Under magnitude 2:4 a kept quantizer with a dense
+// twin (same format and qmax) is evaluated by the twin, which codes each
+// kept value identically: the dense side then sums kept and dropped
+// positions apart and writes both columns.  Per-unit fp32 sums and their
+// fp64 accumulation follow the packed path's order, so both give the same
+// bits.
+template <int TEAM, int UPL, int SEL>
+__device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uint32_t (&pk)[UPL][4],
+                                                float famk, float famd, const PartialSink& sink,
+                                                double* lacc, double* redd, int64_t row,
+                                                bool live) {
+  float v[UPL][8];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[j][2 * h] = mag_lo(pk[j][h]);
+      v[j][2 * h + 1] = mag_hi(pk[j][h]);
+    }
+  constexpr bool SPLIT = SEL == SEL_MAG;
+  const int nki = SPLIT ? p.n_kept_int_solo : p.n_kept_int;
+  const int ndi = p.n_dense_int;
+  float sl = 0.0f, il = 0.0f;
+  if constexpr (TEAM == 64) {
+    const int lane = threadIdx.x & 63;
+    float q = 1.0f, a = famk;
+    for (int i = 0; i < nki || i < ndi; ++i) {
+      if (i < nki && lane == i) q = p.kept.qmax[SPLIT ? p.kept_int_solo[i] : p.kept_int[i]];
+      if (i < ndi && lane == kMaxQ + i) {
+        q = p.dense.qmax[p.dense_int[i]];
+        a = famd;
+      }
+    }
+    row_scale(a, q, sl, il);
+  }
+  for (int i = 0; i < nki; ++i) {
+    const int k = SPLIT ? p.kept_int_solo[i] : p.kept_int[i];
+    float s, inv;
+    if constexpr (TEAM == 64) {
+      s = lane_value(sl, i);
+      inv = lane_value(il, i);
+    } else {
+      row_scale(famk, p.kept.qmax[k], s, inv);
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_int<4>(s, inv, v[j]);
+    sink_sum<TEAM>(sink, lacc, redd, row, 2 + k, acc, live);
+  }
+  for (int i = 0; i < ndi; ++i) {
+    const int dq = p.dense_int[i];
+    float s, inv;
+    if constexpr (TEAM == 64) {
+      s = lane_value(sl, kMaxQ + i);
+      inv = lane_value(il, kMaxQ + i);
+    } else {
+      row_scale(famd, p.dense.qmax[dq], s, inv);
+    }
+    double dk = 0.0, dd = 0.0;
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      if constexpr (SPLIT) {
+        dk += (double)mag_sq_err_int<4>(s, inv, v[j]);
+        dd += (double)mag_sq_err_int<4>(s, inv, v[j] + 4);
+      } else {
+        dd += (double)mag_sq_err_int<8>(s, inv, v[j]);
+      }
+    }
+    if constexpr (SPLIT) {
+      int twin = -1;
+      for (int k = 0; k < p.kept.n; ++k)
+        if (p.kept_twin[k] == dq) twin = k;
+      if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dk, live);
+    }
+    sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + dq, dk + dd, live);
+  }
+  // FP8, one pass per quantizer (an unquantized side writes zero)
+  for (int q = 0; q < p.kept.n; ++q) {
+    const int fmt = p.kept.fmt[q];
+    if (fmt == CF_INT8 || fmt == CF_INT16 || (SPLIT && p.kept_twin[q] >= 0)) continue;
+    double acc = 0.0;
+    if (fmt == CF_FP8) {
+      float s, inv;
+      row_scale(famk, p.kept.qmax[q], s, inv);
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
+    }
+    sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
+  }
+  for (int q = 0; q < p.dense.n; ++q) {
+    const int fmt = p.dense.fmt[q];
+    if (fmt == CF_INT8 || fmt == CF_INT16) continue;
+    if (fmt != CF_FP8) {
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, 0.0, live);
+      continue;
+    }
+    int twin = -1;
+    if (SPLIT)
+      for (int k = 0; k < p.kept.n; ++k)
+        if (p.kept_twin[k] == q) twin = k;
+    float s, inv;
+    row_scale(famd, p.dense.qmax[q], s, inv);
+    double acck = 0.0, accd = 0.0;  // kept and dropped positions
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      acck += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
+      accd += (double)mag_sq_err_fp8<4>(s, inv, v[j] + 4);
+    }
+    if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
+    sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, accd + acck, live);
+  }
+}
+
+template <int TEAM, int UPL, int ROT, int SEL, bool HELD>
+constexpr int kEnergyWaves =
+    (TEAM == 64 && UPL == 8 && !ROT && (SEL == SEL_MAG || HELD)) ? kEnergyWavesMag4096 : 1;
+
+// HELD (UPL <= 8, no rotation, no block formats in the call, magnitude or
+// pairwise 4:8 selection): the row's magnitudes are unpacked once and held
+// for every quantizer; otherwise they stay packed and each quantizer pass
+// unpacks them.  (Held Wanda rows measured slower: its selection leaves too
+// few registers for four waves per SIMD.)
+template <int TEAM, int UPL, int ROT, int SEL, bool HELD>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL, HELD>)))
 void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams p,
                         PartialSink sink) {
   __shared__ uint32_t redu[kBlock / 64];
@@ -495,172 +630,176 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     sink_sum<TEAM>(sink, lacc, redd, row, 0, kept2 + drop, live);
     sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
-    // INT quantizers, up to kFusedInt of each side per pass over the row, so
-    // each unit is unpacked once for all of them.  One-wave teams compute a
-    // pass's per-row scales lane-parallel (lane i divides for kept quantizer
-    // i, lane 32 + i for dense quantizer i) and read them back as
-    // wave-uniform values: two divisions per pass instead of two per
-    // quantizer (lane kFusedInt + i takes dense quantizer i).  A kept quantizer with a dense twin (same format and qmax)
-    // under magnitude 2:4 is evaluated by the twin, since both take their
-    // scale from the same maximum and code each kept value identically: the
-    // dense side accumulates kept and dropped positions apart and writes both
-    // columns.  (Quantizer indices are read from the kernel arguments by
-    // position: a pointer into them would force a private copy.)
-    const int nki = SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int;
-    for (int c0 = 0; c0 < nki || c0 < p.n_dense_int; c0 += kFusedInt) {
-      const int nk = nki - c0 < 0 ? 0 : (nki - c0 < kFusedInt ? nki - c0 : kFusedInt);
-      const int nd = p.n_dense_int - c0 < 0 ? 0
-                                            : (p.n_dense_int - c0 < kFusedInt ? p.n_dense_int - c0 : kFusedInt);
-      int kidx[kFusedInt], didx[kFusedInt];
-      float ks[kFusedInt], kinv[kFusedInt], ds[kFusedInt], dinv[kFusedInt];
-#pragma unroll
-      for (int i = 0; i < kFusedInt; ++i) {
-        kidx[i] = i < nk ? (SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i]) : 0;
-        didx[i] = i < nd ? p.dense_int[c0 + i] : 0;
-      }
-      if constexpr (TEAM == 64) {
-        const int lane = threadIdx.x & 63;
-        float q = 1.0f, a = famk;
-#pragma unroll
+    if constexpr (HELD) {
+      quantizers_held<TEAM, UPL, SEL>(p, pk, famk, famd, sink, lacc, redd, row, live);
+    } else {
+      // INT quantizers, up to kFusedInt of each side per pass over the row, so
+      // each unit is unpacked once for all of them.  One-wave teams compute a
+      // pass's per-row scales lane-parallel (lane i divides for kept quantizer
+      // i, lane 32 + i for dense quantizer i) and read them back as
+      // wave-uniform values: two divisions per pass instead of two per
+      // quantizer (lane kFusedInt + i takes dense quantizer i).  A kept quantizer with a dense twin (same format and qmax)
+      // under magnitude 2:4 is evaluated by the twin, since both take their
+      // scale from the same maximum and code each kept value identically: the
+      // dense side accumulates kept and dropped positions apart and writes both
+      // columns.  (Quantizer indices are read from the kernel arguments by
+      // position: a pointer into them would force a private copy.)
+      const int nki = SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int;
+      for (int c0 = 0; c0 < nki || c0 < p.n_dense_int; c0 += kFusedInt) {
+        const int nk = nki - c0 < 0 ? 0 : (nki - c0 < kFusedInt ? nki - c0 : kFusedInt);
+        const int nd = p.n_dense_int - c0 < 0 ? 0
+                                              : (p.n_dense_int - c0 < kFusedInt ? p.n_dense_int - c0 : kFusedInt);
+        int kidx[kFusedInt], didx[kFusedInt];
+        float ks[kFusedInt], kinv[kFusedInt], ds[kFusedInt], dinv[kFusedInt];
+  #pragma unroll
         for (int i = 0; i < kFusedInt; ++i) {
-          if (i < nk && lane == i) q = p.kept.qmax[kidx[i]];
-          if (i < nd && lane == kFusedInt + i) {
-            q = p.dense.qmax[didx[i]];
-            a = famd;
-          }
+          kidx[i] = i < nk ? (SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i]) : 0;
+          didx[i] = i < nd ? p.dense_int[c0 + i] : 0;
         }
-        float sl, il;
-        row_scale(a, q, sl, il);
-#pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) {
-          ks[i] = __shfl(sl, i, 64);
-          kinv[i] = __shfl(il, i, 64);
-          ds[i] = __shfl(sl, kFusedInt + i, 64);
-          dinv[i] = __shfl(il, kFusedInt + i, 64);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) {
-          ks[i] = kinv[i] = ds[i] = dinv[i] = 0.0f;
-          if (i < nk) row_scale(famk, p.kept.qmax[kidx[i]], ks[i], kinv[i]);
-          if (i < nd) row_scale(famd, p.dense.qmax[didx[i]], ds[i], dinv[i]);
-        }
-      }
-      // dense sums over kept and dropped positions apart only where a kept
-      // twin can exist (magnitude 2:4); otherwise one sum over the unit
-      constexpr bool SPLIT = SEL == SEL_MAG;
-      pin_packed<UPL>(pk);
-      double ka[kFusedInt], dka[kFusedInt], dda[kFusedInt];
-#pragma unroll
-      for (int i = 0; i < kFusedInt; ++i) ka[i] = dka[i] = dda[i] = 0.0;
-#pragma unroll
-      for (int j = 0; j < UPL; ++j) {
-        const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
-                            mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-#pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) {
-          if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
-          if (i < nd) {
-            if constexpr (SPLIT) {
-              dka[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v);
-              dda[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v + 4);
-            } else {
-              dda[i] += (double)mag_sq_err_int<8>(ds[i], dinv[i], v);
+        if constexpr (TEAM == 64) {
+          const int lane = threadIdx.x & 63;
+          float q = 1.0f, a = famk;
+  #pragma unroll
+          for (int i = 0; i < kFusedInt; ++i) {
+            if (i < nk && lane == i) q = p.kept.qmax[kidx[i]];
+            if (i < nd && lane == kFusedInt + i) {
+              q = p.dense.qmax[didx[i]];
+              a = famd;
             }
           }
+          float sl, il;
+          row_scale(a, q, sl, il);
+  #pragma unroll
+          for (int i = 0; i < kFusedInt; ++i) {
+            ks[i] = __shfl(sl, i, 64);
+            kinv[i] = __shfl(il, i, 64);
+            ds[i] = __shfl(sl, kFusedInt + i, 64);
+            dinv[i] = __shfl(il, kFusedInt + i, 64);
+          }
+        } else {
+  #pragma unroll
+          for (int i = 0; i < kFusedInt; ++i) {
+            ks[i] = kinv[i] = ds[i] = dinv[i] = 0.0f;
+            if (i < nk) row_scale(famk, p.kept.qmax[kidx[i]], ks[i], kinv[i]);
+            if (i < nd) row_scale(famd, p.dense.qmax[didx[i]], ds[i], dinv[i]);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+        // dense sums over kept and dropped positions apart only where a kept
+        // twin can exist (magnitude 2:4); otherwise one sum over the unit
+        constexpr bool SPLIT = SEL == SEL_MAG;
+        pin_packed<UPL>(pk);
+        double ka[kFusedInt], dka[kFusedInt], dda[kFusedInt];
+  #pragma unroll
+        for (int i = 0; i < kFusedInt; ++i) ka[i] = dka[i] = dda[i] = 0.0;
+  #pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
+                              mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+  #pragma unroll
+          for (int i = 0; i < kFusedInt; ++i) {
+            if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
+            if (i < nd) {
+              if constexpr (SPLIT) {
+                dka[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v);
+                dda[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v + 4);
+              } else {
+                dda[i] += (double)mag_sq_err_int<8>(ds[i], dinv[i], v);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+        }
+  #pragma unroll
+        for (int i = 0; i < kFusedInt; ++i) {
+          if (i < nk) sink_sum<TEAM>(sink, lacc, redd, row, 2 + kidx[i], ka[i], live);
+          if (i < nd) {
+            int twin = -1;
+            if (SEL == SEL_MAG)
+              for (int k = 0; k < p.kept.n; ++k)
+                if (p.kept_twin[k] == didx[i]) twin = k;
+            if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dka[i], live);
+            sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + didx[i], dka[i] + dda[i], live);
+          }
+        }
       }
-#pragma unroll
-      for (int i = 0; i < kFusedInt; ++i) {
-        if (i < nk) sink_sum<TEAM>(sink, lacc, redd, row, 2 + kidx[i], ka[i], live);
-        if (i < nd) {
+
+      // the other formats, one pass each
+      for (int q = 0; q < p.kept.n; ++q) {
+        const int fmt = p.kept.fmt[q];
+        if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
+        if (SEL == SEL_MAG && p.kept_twin[q] >= 0) continue;
+        pin_packed<UPL>(pk);
+        double acc = 0.0;
+        if (fmt == CF_FP8) {
+          float s, inv;
+          row_scale(famk, p.kept.qmax[q], s, inv);
+  #pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            acc += (double)mag_sq_err_fp8<4>(s, inv, v);
+          }
+        } else if (fmt == CF_NV) {
+  #pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            acc += (double)kept_block_err4<true>(v, ks_t, kgnv);
+          }
+        } else if (fmt == CF_MX) {
+  #pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            acc += (double)kept_block_err4<false>(v, 0.f, 0.f);
+          }
+        }
+        sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
+      }
+      for (int q = 0; q < p.dense.n; ++q) {
+        const int fmt = p.dense.fmt[q];
+        if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
+        pin_packed<UPL>(pk);
+        double acc = 0.0;
+        if (fmt == CF_FP8) {
           int twin = -1;
           if (SEL == SEL_MAG)
             for (int k = 0; k < p.kept.n; ++k)
-              if (p.kept_twin[k] == didx[i]) twin = k;
-          if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dka[i], live);
-          sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + didx[i], dka[i] + dda[i], live);
-        }
-      }
-    }
-
-    // the other formats, one pass each
-    for (int q = 0; q < p.kept.n; ++q) {
-      const int fmt = p.kept.fmt[q];
-      if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
-      if (SEL == SEL_MAG && p.kept_twin[q] >= 0) continue;
-      pin_packed<UPL>(pk);
-      double acc = 0.0;
-      if (fmt == CF_FP8) {
-        float s, inv;
-        row_scale(famk, p.kept.qmax[q], s, inv);
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          acc += (double)mag_sq_err_fp8<4>(s, inv, v);
-        }
-      } else if (fmt == CF_NV) {
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          acc += (double)kept_block_err4<true>(v, ks_t, kgnv);
-        }
-      } else if (fmt == CF_MX) {
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          acc += (double)kept_block_err4<false>(v, 0.f, 0.f);
-        }
-      }
-      sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
-    }
-    for (int q = 0; q < p.dense.n; ++q) {
-      const int fmt = p.dense.fmt[q];
-      if (fmt == CF_INT8 || fmt == CF_INT16) continue;  // chunked above
-      pin_packed<UPL>(pk);
-      double acc = 0.0;
-      if (fmt == CF_FP8) {
-        int twin = -1;
-        if (SEL == SEL_MAG)
-          for (int k = 0; k < p.kept.n; ++k)
-            if (p.kept_twin[k] == q) twin = k;
-        float s, inv;
-        row_scale(famd, p.dense.qmax[q], s, inv);
-        double acck = 0.0;  // kept positions; acc holds the dropped ones
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-          const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-          acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
-          acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
-        }
-        if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
-        acc += acck;
-      } else if (fmt == CF_MX || fmt == CF_NV) {
-#pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          // the unit's |x| max (magnitude 2:4: its kept max, as each group
-          // keeps its largest)
-          const uint32_t km2 = SEL == SEL_MAG ? pk_max_u16(pk[j][0], pk[j][1])
-                                              : pk_max_u16(pk_max_u16(pk[j][0], pk[j][1]),
-                                                           pk_max_u16(pk[j][2], pk[j][3]));
-          const uint32_t kh = km2 >> 16, kl = km2 & 0xFFFFu;
-          uint32_t bm = (kh > kl ? kh : kl) << 16;  // fp32 bits of the unit's |x| max
-          uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
-          bm = bm > w ? bm : w;
-          const float vj[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
-                               mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
-          if (fmt == CF_MX) {
-            w = (uint32_t)__shfl_xor((int)bm, 2, 64);
+              if (p.kept_twin[k] == q) twin = k;
+          float s, inv;
+          row_scale(famd, p.dense.qmax[q], s, inv);
+          double acck = 0.0;  // kept positions; acc holds the dropped ones
+  #pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            const float vk[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
+            const float vd[4] = {mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+            acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
+            acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
+          }
+          if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
+          acc += acck;
+        } else if (fmt == CF_MX || fmt == CF_NV) {
+  #pragma unroll
+          for (int j = 0; j < UPL; ++j) {
+            // the unit's |x| max (magnitude 2:4: its kept max, as each group
+            // keeps its largest)
+            const uint32_t km2 = SEL == SEL_MAG ? pk_max_u16(pk[j][0], pk[j][1])
+                                                : pk_max_u16(pk_max_u16(pk[j][0], pk[j][1]),
+                                                             pk_max_u16(pk[j][2], pk[j][3]));
+            const uint32_t kh = km2 >> 16, kl = km2 & 0xFFFFu;
+            uint32_t bm = (kh > kl ? kh : kl) << 16;  // fp32 bits of the unit's |x| max
+            uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
             bm = bm > w ? bm : w;
-            acc += (double)unit_sq_err_mx8(vj, mx_exponent(bm));
-          } else {
-            acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv);
+            const float vj[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
+                                 mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+            if (fmt == CF_MX) {
+              w = (uint32_t)__shfl_xor((int)bm, 2, 64);
+              bm = bm > w ? bm : w;
+              acc += (double)unit_sq_err_mx8(vj, mx_exponent(bm));
+            } else {
+              acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv);
+            }
           }
         }
+        sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
       }
-      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   });
   sink_flush(sink, lacc, redd, ncols);
@@ -898,15 +1037,23 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   };
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
+    bool blockfmt = false;  // MXFP4 / NVFP4 on either side
+    for (int q = 0; q < p.kept.n; ++q) blockfmt |= p.kept.fmt[q] == CF_MX || p.kept.fmt[q] == CF_NV;
+    for (int q = 0; q < p.dense.n; ++q) blockfmt |= p.dense.fmt[q] == CF_MX || p.dense.fmt[q] == CF_NV;
     // LONG: rotation blocks over 512 elements, on whole-workgroup teams
     auto body = [&]<int TEAM, int UPL, bool LONG>() {
-      auto go = [&]<int R, int SEL>() {
-        constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL>;
+      auto go1 = [&]<int R, int SEL, bool HELD>() {
+        constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL, HELD>;
         const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>(shmem));
         PartialSink k;
         geom(TEAM, grid, k);
         hipLaunchKernelGGL(K, grid, dim3(kBlock), shmem, s, g, norm, p, k);
         return hipGetLastError();
+      };
+      auto go = [&]<int R, int SEL>() {
+        if constexpr (R == 0 && UPL <= 8 && SEL != SEL_WANDA)
+          if (!blockfmt) return go1.template operator()<0, SEL, true>();
+        return go1.template operator()<R, SEL, false>();
       };
       if constexpr (LONG) {
         return sel == SEL_P48 ? go.template operator()<3, SEL_P48>() : go.template operator()<3, SEL_MAG>();
@@ -963,8 +1110,16 @@ hipError_t launch_energy_finalize(const double* rowpart, int64_t nrows, int64_t 
                                   hipStream_t s) {
   const int64_t cpb = energy_chunks_per_block(rows_per_block);
   if (cpb == 1) {
-    hipLaunchKernelGGL(k_energy_final1, dim3((unsigned)nblk), dim3(kBlock), 0, s, rowpart, nrows,
-                       rows_per_block, f, out);
+    const dim3 grid((unsigned)nblk);
+    if (f.ncols <= 4)
+      hipLaunchKernelGGL(k_energy_final1<4>, grid, dim3(kBlock), 0, s, rowpart, nrows,
+                         rows_per_block, f, out);
+    else if (f.ncols <= 8)
+      hipLaunchKernelGGL(k_energy_final1<8>, grid, dim3(kBlock), 0, s, rowpart, nrows,
+                         rows_per_block, f, out);
+    else
+      hipLaunchKernelGGL(k_energy_final1<16>, grid, dim3(kBlock), 0, s, rowpart, nrows,
+                         rows_per_block, f, out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_energy_colsum, dim3((unsigned)(nblk * cpb), (unsigned)f.ncols),
