@@ -233,17 +233,19 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
   }
 }
 
-// Transposed 16-bit operand, magnitude score, R % 64 == 0 and K % 256 == 0
+// Transposed 16-bit operand, magnitude score, R % 64 == 0 and K % 512 == 0
 // (e.g. V [heads, seq, 128] pruned along seq): no LDS staging of the input.
-// A workgroup covers 256 positions x 64 rows.  Thread t owns the 8 x 8 block
-// of rows 8 * (t % 8) .. + 7 and positions 8 * ((t / 8) % 16) .. + 7 of its
-// 128-position half (t / 128): it loads one 16-byte chunk (8 adjacent rows)
-// per position, so each wave load instruction reads 8 whole 128-byte lines,
-// transposes the block in registers with byte permutes (one per output
-// dword), selects each row's unit through the LDS table and stores the kept
-// pairs directly (8 adjacent threads write 64 contiguous bytes of a row).
-// Metadata bytes go through a small LDS tile and leave as 16-byte chunks.
-constexpr int kT8_K = 256;  // positions per workgroup
+// A workgroup covers 512 positions x 64 rows as two 256-position tiles.  In
+// each tile thread t owns the 8 x 8 block of rows 8 * (t % 8) .. + 7 and
+// positions 8 * ((t / 8) % 16) .. + 7 of its 128-position half (t / 128):
+// it loads one 16-byte chunk (8 adjacent rows) per position, so each wave
+// load instruction reads 8 whole 128-byte lines; all 16 chunks of both tiles
+// are in flight together.  The block is transposed in registers with byte
+// permutes (one per output dword), each row's unit is selected through the
+// LDS table and the kept pairs are stored directly (8 adjacent threads write
+// 64 contiguous bytes of a row).  Metadata bytes go through a small LDS tile
+// and leave as 64-byte row segments.
+constexpr int kT8_K = 512;  // positions per workgroup
 constexpr int kT8_R = 64;   // rows per workgroup
 
 template <class DT>
@@ -251,43 +253,46 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T8(
     const char* __restrict__ x, int64_t R, int64_t K, int64_t bs, int64_t ks,
     char* __restrict__ vals, uint8_t* __restrict__ meta) {
   static_assert(DT::ESIZE == 2, "16-bit storage types");
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   __shared__ SelLut lut[kSelLutEntries];
   __shared__ __align__(16) uint8_t mtile[kT8_R][kT8_K / 8];  // [row][unit]
-  sel_lut_fill(lut);
-  __syncthreads();
   const int t = threadIdx.x;
   const int rg = t & 7, pg = (t >> 3) & 15, half = t >> 7;
-  const int64_t k0 = (int64_t)blockIdx.x * kT8_K + half * 128 + pg * 8;  // first position
-  const int64_t r0 = (int64_t)blockIdx.y * kT8_R + rg * 8;               // first row
+  const int64_t r0 = (int64_t)blockIdx.y * kT8_R + rg * 8;  // first row
   const int64_t b = blockIdx.z;
-  const char* src = x + b * bs + k0 * ks + r0 * 2;
-  uint4 c[8];  // chunk i: rows r0 .. r0 + 7 at position k0 + i
+  const int64_t kb = (int64_t)blockIdx.x * kT8_K + half * 128 + pg * 8;  // first position, tile 0
+  const char* src = x + b * bs + kb * ks + r0 * 2;
+  u32x4 c[2][8];  // chunk i of tile h: rows r0 .. r0 + 7 at position kb + 256 h + i
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * ks));
-    c[i] = make_uint4(v.x, v.y, v.z, v.w);
-  }
-  const int ucol = half * 16 + pg;  // unit column within the workgroup's 256 positions
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {  // row r0 + d: dword dp = d / 2 of each chunk, half d % 2
-    const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w[4];
+    for (int i = 0; i < 8; ++i)
+      c[h][i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(src + (int64_t)(256 * h + i) * ks));
+  sel_lut_fill(lut);
+  __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4& lo = c[2 * q];
-      const uint4& hi = c[2 * q + 1];
-      const uint32_t a = (d >> 1) == 0 ? lo.x : (d >> 1) == 1 ? lo.y : (d >> 1) == 2 ? lo.z : lo.w;
-      const uint32_t e = (d >> 1) == 0 ? hi.x : (d >> 1) == 1 ? hi.y : (d >> 1) == 2 ? hi.z : hi.w;
-      w[q] = __builtin_amdgcn_perm(e, a, sel);  // positions 2q, 2q + 1 of row r0 + d
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k0 = kb + 256 * h;
+    const int ucol = 32 * h + half * 16 + pg;  // unit column within the workgroup's positions
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {  // row r0 + d: dword d / 2 of each chunk, half d % 2
+      const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4& lo = c[h][2 * q];
+        const u32x4& hi = c[h][2 * q + 1];
+        w[q] = __builtin_amdgcn_perm(hi[d >> 1], lo[d >> 1], sel);  // positions 2q, 2q + 1
+      }
+      const Sel16 r = select16_lut(w, lut);
+      st2(vals + ((b * R + r0 + d) * (K / 2) + k0 / 2) * 2, r.k0, r.k1);
+      mtile[rg * 8 + d][ucol] = (uint8_t)r.mb;
     }
-    const Sel16 r = select16_lut(w, lut);
-    st2(vals + ((b * R + r0 + d) * (K / 2) + k0 / 2) * 2, r.k0, r.k1);
-    mtile[rg * 8 + d][ucol] = (uint8_t)r.mb;
   }
   __syncthreads();
-  if (t < kT8_R * 2) {  // 64 rows x 32 metadata bytes, in 16-byte chunks
-    const int row = t >> 1, part = t & 1;
+  {  // 64 rows x 64 metadata bytes: one 16-byte chunk per thread
+    const int row = t >> 2, part = t & 3;
     const uint4 v = *reinterpret_cast<const uint4*>(&mtile[row][part * 16]);
     st4(meta + (b * R + (int64_t)blockIdx.y * kT8_R + row) * (K / 8) +
             (int64_t)blockIdx.x * (kT8_K / 8) + part * 16,
