@@ -2,9 +2,9 @@
 more than one row into its partial slot.
 
 The energy kernels run on a persistent grid of at most 4 workgroups per CU;
-with more rows than resident teams, each team walks several rows and adds
-their sums into its own slot in LDS (per wave for teams wider than a wave),
-and the slots are added in a fixed order at the end.  These cases use more
+with more rows than resident teams, each team walks several rows, every lane
+adds its share of each row into its own fp64 slot in LDS, and each
+workgroup adds its slots in a fixed order at the end.  These cases use more
 rows than the teams a 256-CU MI355X holds, in the launch shapes the calls use
 at those sizes, and compare with the fp64 oracle to 1e-6 relative
 ("Is 2:4 Sparsity Still Worth It?", paper-daily.com English summary, §4:
