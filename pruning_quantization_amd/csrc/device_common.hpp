@@ -457,10 +457,19 @@ __device__ inline uint32_t enc_e4m3_x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // Value of an e4m3 code held in byte SEL of w (gfx950 v_cvt_f32_fp8).
 template <int SEL>
 __device__ inline float dec_e4m3_hw(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// Values of the two e4m3 codes in 16-bit half H of w, low byte first
+// (gfx950 v_cvt_pk_f32_fp8: one instruction for two codes).
+template <int H>
+__device__ inline f32x2 dec_e4m3_hw_x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, H != 0);
 }
 
 // E2M1 (values 0, .5, 1, 1.5, 2, 3, 4, 6), 4-bit code with sign in bit 3.
@@ -489,7 +498,6 @@ __device__ inline float dec_e2m1(uint32_t c) {
 // Bit pattern of dec_e2m1(c) (for the conversion check).
 __device__ inline uint32_t dec_e2m1_bits(uint32_t c) { return __float_as_uint(dec_e2m1(c)); }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Values of the two E2M1 codes in byte SEL of w (low nibble -> .x), with
 // gfx950's v_cvt_scalef32_pk_f32_fp4 at scale 1; equal to dec_e2m1 on every

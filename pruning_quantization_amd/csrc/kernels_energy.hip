@@ -150,10 +150,11 @@ __device__ inline float mag_sq_err_fp8(float s, float inv, const float* v) {
 #pragma unroll
   for (int q = 0; q < N; q += 4) {
     const uint32_t w = enc_e4m3_x4(v[q] * inv, v[q + 1] * inv, v[q + 2] * inv, v[q + 3] * inv);
-    const float e0 = __builtin_fmaf(dec_e4m3_hw<0>(w), s, -v[q + 0]);
-    const float e1 = __builtin_fmaf(dec_e4m3_hw<1>(w), s, -v[q + 1]);
-    const float e2 = __builtin_fmaf(dec_e4m3_hw<2>(w), s, -v[q + 2]);
-    const float e3 = __builtin_fmaf(dec_e4m3_hw<3>(w), s, -v[q + 3]);
+    const f32x2 c01 = dec_e4m3_hw_x2<0>(w), c23 = dec_e4m3_hw_x2<1>(w);
+    const float e0 = __builtin_fmaf(c01.x, s, -v[q + 0]);
+    const float e1 = __builtin_fmaf(c01.y, s, -v[q + 1]);
+    const float e2 = __builtin_fmaf(c23.x, s, -v[q + 2]);
+    const float e3 = __builtin_fmaf(c23.y, s, -v[q + 3]);
     a0 = __builtin_fmaf(e0, e0, a0);
     a1 = __builtin_fmaf(e1, e1, a1);
     a0 = __builtin_fmaf(e2, e2, a0);

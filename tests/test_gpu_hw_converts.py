@@ -1,7 +1,8 @@
 """The kernels encode FP8 and FP4 with gfx950 conversion instructions.  This
 runs the built check program, which compares those instructions with the
 exact round-to-nearest-even, saturating integer encoders over every finite
-fp32 input (and decoding over every e4m3 code), and expects no mismatch."""
+fp32 input (and decoding over every e4m3 code and code pair), and expects no
+mismatch."""
 import os
 import subprocess
 
@@ -22,4 +23,4 @@ def test_hw_conversions_match_exact_encoders():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=100)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count(": 0 mismatches") == 6
+    assert r.stdout.count(": 0 mismatches") == 7
