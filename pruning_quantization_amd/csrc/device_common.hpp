@@ -888,6 +888,26 @@ __device__ inline void nv_tensor_scales(float T, float& s_t, float& g) {
   }
 }
 
+// NVFP4 block scales.  The e4m3 code of a block's scale fp32(am * g) (am >= 0
+// the block's absolute maximum, g = fp32(448 / T)) comes from the hardware
+// convert of the product clamped to 448, where it equals enc_e4m3 (the
+// product can pass 448 when the caller's T is below the operand's maximum,
+// and enc_e4m3 saturates).  The
+// elements' multiplier fp32(1 / fp32(dec_e4m3(code) * s_t)) (0 for a zero
+// scale) comes from a table of the non-negative codes filled once per
+// workgroup: the same fp32 operations, done once per code instead of once
+// per block.  The table is ready after the next workgroup barrier.
+constexpr int kNvInvEntries = 128;
+__device__ inline void nv_inv_fill(float* tab, float s_t) {
+  for (int c = threadIdx.x; c < kNvInvEntries; c += blockDim.x) {
+    const float d = dec_e4m3((uint32_t)c) * s_t;
+    tab[c] = d > 0.0f ? 1.0f / d : 0.0f;
+  }
+}
+__device__ inline uint32_t nv_block_code(float am, float g) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(am * g, 448.0f), 0.0f, 0u, false) & 0xFFu;
+}
+
 __device__ inline int mx_exponent(uint32_t amax_bits) {
   // floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 -> -127
   if (amax_bits == 0) return -127;

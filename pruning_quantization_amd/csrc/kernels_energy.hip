@@ -213,10 +213,11 @@ __device__ inline float unit_sq_err_mx8(const float* v, int ex) {
 
 // Same under NVFP4: bm = fp32 bits of the 16-value block's absolute maximum,
 // s_t / gnv the tensor scale and block-scale multiplier.
-__device__ inline float unit_sq_err_nv8(const float* v, uint32_t bm, float s_t, float gnv) {
-  const float bval = dec_e4m3(enc_e4m3(__uint_as_float(bm) * gnv));
-  const float d = bval * s_t;
-  const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+__device__ inline float unit_sq_err_nv8(const float* v, uint32_t bm, float s_t, float gnv,
+                                       const float* nvinv) {
+  const uint32_t bc = nv_block_code(__uint_as_float(bm), gnv);
+  const float bval = dec_e4m3_hw<0>(bc);
+  const float inv = nvinv[bc];
   float y[8], e[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = v[k] * inv;
@@ -229,7 +230,7 @@ __device__ inline float unit_sq_err_nv8(const float* v, uint32_t bm, float s_t, 
 // every lane of the wave must call this.  Returns the fp32 sum of the four
 // squared fp32-rounded residuals.
 template <bool NV>
-__device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
+__device__ inline float kept_block_err4(const float* v, float s_t, float gnv, const float* nvinv) {
   uint32_t am = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -244,9 +245,9 @@ __device__ inline float kept_block_err4(const float* v, float s_t, float gnv) {
   uint32_t pk;
   float m, sc;
   if constexpr (NV) {
-    const float bval = dec_e4m3(enc_e4m3(__uint_as_float(am) * gnv));
-    const float d = bval * s_t;
-    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    const uint32_t bc = nv_block_code(__uint_as_float(am), gnv);
+    const float bval = dec_e4m3_hw<0>(bc);
+    const float inv = nvinv[bc];
     pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     m = bval;
     sc = s_t;
@@ -576,9 +577,11 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
+  __shared__ float nvinv_d[kNvInvEntries], nvinv_k[kNvInvEntries];
   if (any_nv) {
     const float T = block_tensor_amax(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
+    nv_inv_fill(nvinv_d, s_t);
   }
   bool any_knv = false;
   for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
@@ -586,7 +589,9 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   if (any_knv) {
     const float T = block_tensor_amax(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
+    nv_inv_fill(nvinv_k, ks_t);
   }
+  __syncthreads();  // NVFP4 reciprocal tables
   const int64_t nrows = g.nrows;
   for_each_row<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
@@ -743,13 +748,13 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   #pragma unroll
           for (int j = 0; j < UPL; ++j) {
             const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            acc += (double)kept_block_err4<true>(v, ks_t, kgnv);
+            acc += (double)kept_block_err4<true>(v, ks_t, kgnv, nvinv_k);
           }
         } else if (fmt == CF_MX) {
   #pragma unroll
           for (int j = 0; j < UPL; ++j) {
             const float v[4] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1])};
-            acc += (double)kept_block_err4<false>(v, 0.f, 0.f);
+            acc += (double)kept_block_err4<false>(v, 0.f, 0.f, nullptr);
           }
         }
         sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
@@ -795,7 +800,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
               bm = bm > w ? bm : w;
               acc += (double)unit_sq_err_mx8(vj, mx_exponent(bm));
             } else {
-              acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv);
+              acc += (double)unit_sq_err_nv8(vj, bm, s_t, gnv, nvinv_d);
             }
           }
         }
@@ -818,9 +823,11 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
+  __shared__ float nvinv_d[kNvInvEntries], nvinv_k[kNvInvEntries];
   if (any_nv) {
     const float T = block_tensor_amax(p.nv_tamax, p.nv_partials, p.n_partials, redu);
     if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
+    nv_inv_fill(nvinv_d, s_t);
   }
   bool any_knv = false;
   for (int q = 0; q < p.kept.n; ++q) any_knv |= (p.kept.fmt[q] == CF_NV);
@@ -828,7 +835,9 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   if (any_knv) {
     const float T = block_tensor_amax(p.kept_nv_tamax, p.kept_nv_partials, p.n_kept_partials, redu);
     if (T >= 0x1p-64f) { ks_t = T / 2688.0f; kgnv = 448.0f / T; }
+    nv_inv_fill(nvinv_k, ks_t);
   }
+  __syncthreads();  // NVFP4 reciprocal tables
   const int64_t nrows = g.nrows;
 
   for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
@@ -883,8 +892,8 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
         for (int j = 0; j < UPL; ++j) {
           const Kept<DT> kp = p.pairs48 ? gather_pairs48(u[j], mbs[j]) : gather_kept(u[j], mbs[j]);
           const float v[4] = {kp.f(0), kp.f(1), kp.f(2), kp.f(3)};
-          acc += (double)(fmt == CF_NV ? kept_block_err4<true>(v, ks_t, kgnv)
-                                       : kept_block_err4<false>(v, 0.f, 0.f));
+          acc += (double)(fmt == CF_NV ? kept_block_err4<true>(v, ks_t, kgnv, nvinv_k)
+                                       : kept_block_err4<false>(v, 0.f, 0.f, nullptr));
         }
       } else if (fmt != CF_NONE) {
         float s, inv;
@@ -948,7 +957,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
             am = am > w ? am : w;
             acc += (double)unit_sq_err_mx8(v, mx_exponent(am));
           } else {
-            acc += (double)unit_sq_err_nv8(v, am, s_t, gnv);
+            acc += (double)unit_sq_err_nv8(v, am, s_t, gnv, nvinv_d);
           }
         }
       }

@@ -174,11 +174,14 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
     Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
+  __shared__ float nvinv[NV ? kNvInvEntries : 1];
   float s_t = 0.f, g = 0.f;
   if constexpr (NV) {
     const float T = block_tensor_amax(tamax_in, partials, nparts, red);
     nv_tensor_scales(T, s_t, g);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+    nv_inv_fill(nvinv, s_t);
+    __syncthreads();
   }
   const int t = threadIdx.x % TEAM;
   const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
@@ -221,9 +224,8 @@ __global__ __launch_bounds__(kBlock) void k_quant_block(
           if ((i & 3) == 0) st(scales + orow * (nunits / 4) + (i >> 2), (uint8_t)(e + 127));
         }
       } else {
-        const uint32_t bc = enc_e4m3(__uint_as_float(am) * g);
-        const float d = dec_e4m3(bc) * s_t;
-        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        const uint32_t bc = nv_block_code(__uint_as_float(am), g);
+        const float inv = nvinv[bc];
         float y[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) y[q] = u[j].f(q) * inv;
@@ -267,11 +269,14 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
     uint8_t* __restrict__ meta, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
     Rot rot) {
   __shared__ uint32_t red[kBlock / 64];
+  __shared__ float nvinv[NV ? kNvInvEntries : 1];
   float s_t = 0.f, g = 0.f;
   if constexpr (NV) {
     const float T = block_tensor_amax(tamax_in, partials, nparts, red);
     nv_tensor_scales(T, s_t, g);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+    nv_inv_fill(nvinv, s_t);
+    __syncthreads();
   }
   const int t = threadIdx.x % TEAM;
   const int64_t r = (int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM;
@@ -308,9 +313,8 @@ __global__ __launch_bounds__(kBlock) void k_prune_quant_fp4(
       am = am > w ? am : w;
       uint32_t sc, pk;
       if constexpr (NV) {
-        sc = enc_e4m3(__uint_as_float(am) * g);
-        const float d = dec_e4m3(sc) * s_t;
-        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        sc = nv_block_code(__uint_as_float(am), g);
+        const float inv = nvinv[sc];
         pk = enc_e2m1_x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       } else {
         w = (uint32_t)__shfl_xor((int)am, 4, 64);
