@@ -446,10 +446,9 @@ __device__ inline float lane_value(float v, int i) {
 // wave-uniform values.  Under magnitude 2:4 a kept quantizer with a dense
 // twin (same format and qmax) is evaluated by the twin, which codes each
 // kept value identically: the dense side then sums kept and dropped
-// positions apart and writes both columns.  Per-unit fp32 sums and their
-// fp64 accumulation follow the packed path's order, so both give the same
-// bits.
-template <int TEAM, int UPL, int SEL>
+// positions apart and writes both columns (TWINS: the call has such a pair;
+// without one each unit's eight residuals go into one fp32 sum).
+template <int TEAM, int UPL, int SEL, bool TWINS>
 __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uint32_t (&pk)[UPL][4],
                                                 float famk, float famd, const PartialSink& sink,
                                                 double* lacc, double* redd, int64_t row,
@@ -462,15 +461,15 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
       v[j][2 * h] = mag_lo(pk[j][h]);
       v[j][2 * h + 1] = mag_hi(pk[j][h]);
     }
-  constexpr bool SPLIT = SEL == SEL_MAG;
-  const int nki = SPLIT ? p.n_kept_int_solo : p.n_kept_int;
+  constexpr bool SPLIT = SEL == SEL_MAG && TWINS;
+  const int nki = SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int;
   const int ndi = p.n_dense_int;
   float sl = 0.0f, il = 0.0f;
   if constexpr (TEAM == 64) {
     const int lane = threadIdx.x & 63;
     float q = 1.0f, a = famk;
     for (int i = 0; i < nki || i < ndi; ++i) {
-      if (i < nki && lane == i) q = p.kept.qmax[SPLIT ? p.kept_int_solo[i] : p.kept_int[i]];
+      if (i < nki && lane == i) q = p.kept.qmax[SEL == SEL_MAG ? p.kept_int_solo[i] : p.kept_int[i]];
       if (i < ndi && lane == kMaxQ + i) {
         q = p.dense.qmax[p.dense_int[i]];
         a = famd;
@@ -479,7 +478,7 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
     row_scale(a, q, sl, il);
   }
   for (int i = 0; i < nki; ++i) {
-    const int k = SPLIT ? p.kept_int_solo[i] : p.kept_int[i];
+    const int k = SEL == SEL_MAG ? p.kept_int_solo[i] : p.kept_int[i];
     float s, inv;
     if constexpr (TEAM == 64) {
       s = lane_value(sl, i);
@@ -522,7 +521,7 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
   // FP8, one pass per quantizer (an unquantized side writes zero)
   for (int q = 0; q < p.kept.n; ++q) {
     const int fmt = p.kept.fmt[q];
-    if (fmt == CF_INT8 || fmt == CF_INT16 || (SPLIT && p.kept_twin[q] >= 0)) continue;
+    if (fmt == CF_INT8 || fmt == CF_INT16 || (SEL == SEL_MAG && p.kept_twin[q] >= 0)) continue;
     double acc = 0.0;
     if (fmt == CF_FP8) {
       float s, inv;
@@ -539,33 +538,40 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
       sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, 0.0, live);
       continue;
     }
-    int twin = -1;
-    if (SPLIT)
-      for (int k = 0; k < p.kept.n; ++k)
-        if (p.kept_twin[k] == q) twin = k;
     float s, inv;
     row_scale(famd, p.dense.qmax[q], s, inv);
-    double acck = 0.0, accd = 0.0;  // kept and dropped positions
+    if constexpr (SPLIT) {
+      int twin = -1;
+      for (int k = 0; k < p.kept.n; ++k)
+        if (p.kept_twin[k] == q) twin = k;
+      double acck = 0.0, accd = 0.0;  // kept and dropped positions
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      acck += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
-      accd += (double)mag_sq_err_fp8<4>(s, inv, v[j] + 4);
+      for (int j = 0; j < UPL; ++j) {
+        acck += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
+        accd += (double)mag_sq_err_fp8<4>(s, inv, v[j] + 4);
+      }
+      if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, accd + acck, live);
+    } else {
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_fp8<8>(s, inv, v[j]);
+      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
-    if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
-    sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, accd + acck, live);
   }
 }
 
-template <int TEAM, int UPL, int ROT, int SEL, bool HELD>
+template <int TEAM, int UPL, int ROT, int SEL, int HELD>
 constexpr int kEnergyWaves =
     (TEAM == 64 && UPL == 8 && !ROT && (SEL == SEL_MAG || HELD)) ? kEnergyWavesMag4096 : 1;
 
 // HELD (UPL <= 8, no rotation, no block formats in the call, magnitude or
 // pairwise 4:8 selection): the row's magnitudes are unpacked once and held
-// for every quantizer; otherwise they stay packed and each quantizer pass
-// unpacks them.  (Held Wanda rows measured slower: its selection leaves too
-// few registers for four waves per SIMD.)
-template <int TEAM, int UPL, int ROT, int SEL, bool HELD>
+// for every quantizer (2: the call has a kept quantizer with a dense twin);
+// otherwise (0) they stay packed and each quantizer pass unpacks them.
+// (Held Wanda rows measured slower: its selection leaves too few registers
+// for four waves per SIMD.)
+template <int TEAM, int UPL, int ROT, int SEL, int HELD>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kEnergyWaves<TEAM, UPL, ROT, SEL, HELD>)))
 void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams p,
                         PartialSink sink) {
@@ -636,8 +642,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     sink_sum<TEAM>(sink, lacc, redd, row, 0, kept2 + drop, live);
     sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
-    if constexpr (HELD) {
-      quantizers_held<TEAM, UPL, SEL>(p, pk, famk, famd, sink, lacc, redd, row, live);
+    if constexpr (HELD != 0) {
+      quantizers_held<TEAM, UPL, SEL, HELD == 2>(p, pk, famk, famd, sink, lacc, redd, row, live);
     } else {
       // INT quantizers, up to kFusedInt of each side per pass over the row, so
       // each unit is unpacked once for all of them.  One-wave teams compute a
@@ -1047,12 +1053,14 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   };
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
+    bool twins = false;  // a kept quantizer evaluated by its dense twin
+    for (int q = 0; q < p.kept.n; ++q) twins |= p.kept_twin[q] >= 0;
     bool blockfmt = false;  // MXFP4 / NVFP4 on either side
     for (int q = 0; q < p.kept.n; ++q) blockfmt |= p.kept.fmt[q] == CF_MX || p.kept.fmt[q] == CF_NV;
     for (int q = 0; q < p.dense.n; ++q) blockfmt |= p.dense.fmt[q] == CF_MX || p.dense.fmt[q] == CF_NV;
     // LONG: rotation blocks over 512 elements, on whole-workgroup teams
     auto body = [&]<int TEAM, int UPL, bool LONG>() {
-      auto go1 = [&]<int R, int SEL, bool HELD>() {
+      auto go1 = [&]<int R, int SEL, int HELD>() {
         constexpr auto K = k_energy_rows_bf16<TEAM, UPL, R, SEL, HELD>;
         const dim3 grid = persistent_grid(g.nrows, TEAM, resident_blocks<K>(shmem));
         PartialSink k;
@@ -1061,9 +1069,14 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
         return hipGetLastError();
       };
       auto go = [&]<int R, int SEL>() {
-        if constexpr (R == 0 && UPL <= 8 && SEL != SEL_WANDA)
-          if (!blockfmt) return go1.template operator()<0, SEL, true>();
-        return go1.template operator()<R, SEL, false>();
+        if constexpr (R == 0 && UPL <= 8 && SEL != SEL_WANDA) {
+          if (!blockfmt) {
+            if constexpr (SEL == SEL_MAG)
+              if (twins) return go1.template operator()<0, SEL, 2>();
+            return go1.template operator()<0, SEL, 1>();
+          }
+        }
+        return go1.template operator()<R, SEL, 0>();
       };
       if constexpr (LONG) {
         return sel == SEL_P48 ? go.template operator()<3, SEL_P48>() : go.template operator()<3, SEL_MAG>();
