@@ -857,6 +857,34 @@ __device__ inline void for_each_row(const RowGeom& g, Body&& body) {
   }
 }
 
+// Same with contiguous rows per team: team k takes rows k * rpt .. k * rpt +
+// rpt - 1 (rpt = ceil(rows / teams)), so the rows a team sums lie in as few
+// row blocks as possible.  Every team runs rpt iterations; an iteration past
+// the team's last row (or the operand's) passes row = g.nrows and zero units.
+template <int TEAM>
+__device__ inline int64_t contig_rows_per_team(const RowGeom& g) {
+  const int64_t nteams = (int64_t)gridDim.x * (kBlock / TEAM);
+  return (g.nrows + nteams - 1) / nteams;
+}
+template <int TEAM>
+__device__ inline int64_t contig_first_row(const RowGeom& g) {
+  return ((int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM) * contig_rows_per_team<TEAM>(g);
+}
+template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
+__device__ inline void for_each_row_contig(const RowGeom& g, Body&& body) {
+  const int t = threadIdx.x % TEAM;
+  const int64_t rpt = contig_rows_per_team<TEAM>(g);
+  const int64_t r0 = contig_first_row<TEAM>(g);
+  const int64_t r1 = r0 + rpt < g.nrows ? r0 + rpt : g.nrows;
+  for (int64_t it = 0; it < rpt; ++it) {
+    Unit<DT> A[UPL];
+    const int64_t ra = r0 + it < r1 ? r0 + it : g.nrows;
+    load_row<DT, TEAM, UPL>(A, g, ra, t);
+    if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
+    body(A, ra, t);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Block-format and tensor-scale helpers shared by the quantizer, energy and
 // operator-error kernels.

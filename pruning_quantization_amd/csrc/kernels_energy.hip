@@ -365,49 +365,121 @@ __global__ __launch_bounds__(kBlock) void k_energy_final1(const double* __restri
   finalize_rows<CB>(rowpart, nrows, r0, r1, f, out, blk);
 }
 
-// Row partial sums go either to rowpart[col][row] (blocked reductions: the
-// team's sum of each row, from its first lane) or, when the whole operand is
-// one block (acc), into per-lane accumulators in LDS: every lane adds its own
-// share of each row into its own slot (one LDS add, no reduction per row),
-// and at the end the workgroup reduces each column's slots once, in a fixed
-// order, to rowpart[col][workgroup] (nparts = all workgroups).  Each slot is
+// Row partial sums.  Two forms of the blocked reduction (rows_per_block
+// rows per block), chosen per kernel (SEG):
+//  - SEG: every lane adds its own share of each row into its own fp64 slot
+//    in LDS (one LDS add per column, no reduction per row).  Teams walk
+//    contiguous rows (for_each_row_contig); after the last row of a block,
+//    and after its last row, a team reduces its slots once per column (fixed
+//    order) into rowpart[col][first row of that segment] and writes zeros to
+//    the segment's other rows, so a block's sum is the sum of its rows'
+//    entries, as the finalize reads them.
+//  - otherwise each row's sum is reduced over the team at once and written
+//    to rowpart[col][row] by the team's first lane.
+// Whole operand (acc), both forms: per-lane LDS slots as in SEG, and each
+// workgroup reduces each column's slots once at the end, in a fixed order,
+// to rowpart[col][workgroup] (nparts = all workgroups).  Every slot is
 // written by one lane only, in program order, so the sums repeat bit for bit.
 struct PartialSink {
   double* rowpart;
   int64_t stride;  // elements per column
+  int64_t rpb;     // rows per block (blocked)
   bool acc;
 };
 
-// Dynamic LDS of a launch: ncols x kBlock per-lane accumulators (acc only).
-inline size_t sink_lds_bytes(bool acc, int ncols) {
-  return acc ? (size_t)ncols * kBlock * sizeof(double) : 0;
-}
+// Dynamic LDS of a launch: ncols x kBlock per-lane accumulators.
+inline size_t sink_lds_bytes(int ncols) { return (size_t)ncols * kBlock * sizeof(double); }
 
-template <int TEAM>
+// In SEG kernels the empty asm and the scheduling barrier keep each
+// quantizer's work before its add: without them the scheduler interleaves
+// the quantizer loops of a row and the held kernels spill registers.
+template <int TEAM, bool SEG = false>
 __device__ inline void sink_sum(const PartialSink& k, double* lacc, double* redd, int64_t row,
                                 int col, double v, bool live) {
-  if (k.acc) {
+  if constexpr (SEG) {
+    asm volatile("" : "+v"(v));
     if (live)
       __hip_atomic_fetch_add(&lacc[col * kBlock + threadIdx.x], v, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
-    return;
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    if (k.acc) {
+      if (live)
+        __hip_atomic_fetch_add(&lacc[col * kBlock + threadIdx.x], v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+    const double a = team_sum_f64<TEAM>(v, redd);
+    if (live && threadIdx.x % TEAM == 0) k.rowpart[(int64_t)col * k.stride + row] = a;
   }
-  const double a = team_sum_f64<TEAM>(v, redd);
-  if (live && threadIdx.x % TEAM == 0) k.rowpart[(int64_t)col * k.stride + row] = a;
 }
 
-// One partial per workgroup and column (acc only; every thread calls this).
-__device__ inline void sink_flush(const PartialSink& k, double* lacc, double* redd, int ncols) {
-  if (!k.acc) return;
+// Rows first .. last of one block summed by one team (first < 0: none yet);
+// end = the first row of the next block.  A team's rows are contiguous, so
+// only its first segment's end takes a division (sink_segments).
+struct Segment {
+  int64_t first = -1, last = -1, end = 0;
+};
+template <int TEAM, bool SEG>
+__device__ inline Segment sink_segments(const PartialSink& k, const RowGeom& g) {
+  Segment s;
+  if (SEG && !k.acc) s.end = (contig_first_row<TEAM>(g) / k.rpb + 1) * k.rpb;
+  return s;
+}
+
+template <int TEAM>
+__device__ inline void sink_segment_flush(const PartialSink& k, double* lacc, double* redd,
+                                          int ncols, Segment& sg) {
+  const int t = threadIdx.x % TEAM;
+  for (int c = 0; c < ncols; ++c) {
+    double* slot = &lacc[c * kBlock + threadIdx.x];
+    const double a = team_sum_f64<TEAM>(*slot, redd);
+    *slot = 0.0;
+    double* col = k.rowpart + (int64_t)c * k.stride;
+    if (t == 0) col[sg.first] = a;
+    for (int64_t r = sg.first + 1 + t; r <= sg.last; r += TEAM) col[r] = 0.0;
+  }
+  sg.first = -1;
+  sg.end += k.rpb;
+}
+
+// Around each row's sums (SEG, blocked; every thread calls both, and the
+// conditions are uniform over a team, and over the workgroup for teams that
+// fill it, as the multi-wave team sums need).  A segment is flushed after
+// the last row of its block, when the row's own registers are free.
+template <bool SEG>
+__device__ inline void sink_row_begin(const PartialSink& k, int64_t row, bool live, Segment& sg) {
+  if (!SEG || k.acc || !live || sg.first >= 0) return;
+  sg.first = row;
+}
+template <int TEAM, bool SEG>
+__device__ inline void sink_row_end(const PartialSink& k, double* lacc, double* redd, int ncols,
+                                    int64_t row, bool live, Segment& sg) {
+  if constexpr (SEG) {
+    if (k.acc || !live) return;
+    sg.last = row;
+    if (row + 1 == sg.end) sink_segment_flush<TEAM>(k, lacc, redd, ncols, sg);
+  }
+}
+
+// After the last row: the open segment (SEG, blocked), or one partial per
+// workgroup and column (acc).  Every thread calls this.
+template <int TEAM, bool SEG>
+__device__ inline void sink_flush(const PartialSink& k, double* lacc, double* redd, int ncols,
+                                  Segment& sg) {
+  if (!k.acc) {
+    if constexpr (SEG)
+      if (sg.first >= 0) sink_segment_flush<TEAM>(k, lacc, redd, ncols, sg);
+    return;
+  }
   for (int c = 0; c < ncols; ++c) {
     const double a = team_sum_f64<kBlock>(lacc[c * kBlock + threadIdx.x], redd);
     if (threadIdx.x == 0) k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
   }
 }
 
-// Each lane clears its own slots (acc only).
-__device__ inline void sink_init(const PartialSink& k, double* lacc, int ncols) {
-  if (!k.acc) return;
+// Each lane clears its own slots.
+__device__ inline void sink_init(double* lacc, int ncols) {
   for (int c = 0; c < ncols; ++c) lacc[c * kBlock + threadIdx.x] = 0.0;
 }
 
@@ -489,7 +561,7 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_int<4>(s, inv, v[j]);
-    sink_sum<TEAM>(sink, lacc, redd, row, 2 + k, acc, live);
+    sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + k, acc, live);
   }
   for (int i = 0; i < ndi; ++i) {
     const int dq = p.dense_int[i];
@@ -514,9 +586,9 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
       int twin = -1;
       for (int k = 0; k < p.kept.n; ++k)
         if (p.kept_twin[k] == dq) twin = k;
-      if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dk, live);
+      if (twin >= 0) sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + twin, dk, live);
     }
-    sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + dq, dk + dd, live);
+    sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + p.kept.n + dq, dk + dd, live);
   }
   // FP8, one pass per quantizer (an unquantized side writes zero)
   for (int q = 0; q < p.kept.n; ++q) {
@@ -529,13 +601,13 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
 #pragma unroll
       for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
     }
-    sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
+    sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + q, acc, live);
   }
   for (int q = 0; q < p.dense.n; ++q) {
     const int fmt = p.dense.fmt[q];
     if (fmt == CF_INT8 || fmt == CF_INT16) continue;
     if (fmt != CF_FP8) {
-      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, 0.0, live);
+      sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + p.kept.n + q, 0.0, live);
       continue;
     }
     float s, inv;
@@ -550,13 +622,13 @@ __device__ __forceinline__ void quantizers_held(const EnergyParams& p, const uin
         acck += (double)mag_sq_err_fp8<4>(s, inv, v[j]);
         accd += (double)mag_sq_err_fp8<4>(s, inv, v[j] + 4);
       }
-      if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
-      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, accd + acck, live);
+      if (twin >= 0) sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + twin, acck, live);
+      sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + p.kept.n + q, accd + acck, live);
     } else {
       double acc = 0.0;
 #pragma unroll
       for (int j = 0; j < UPL; ++j) acc += (double)mag_sq_err_fp8<8>(s, inv, v[j]);
-      sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
+      sink_sum<TEAM, true>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   }
 }
@@ -579,7 +651,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   __shared__ double redd[kBlock / 64];
   extern __shared__ double lacc[];  // per-lane accumulators (whole-operand sums)
   const int ncols = 2 + p.kept.n + p.dense.n;
-  sink_init(sink, lacc, ncols);
+  sink_init(lacc, ncols);
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
   float s_t = 0.f, gnv = 0.f;
@@ -599,8 +671,11 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   }
   __syncthreads();  // NVFP4 reciprocal tables
   const int64_t nrows = g.nrows;
-  for_each_row<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+  constexpr bool SEG = HELD != 0;
+  Segment sg = sink_segments<TEAM, SEG>(sink, g);
+  for_each_row_contig<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
+    sink_row_begin<SEG>(sink, row, live, sg);
     uint32_t pk[UPL][4];   // packed |x| bf16 pairs: kept (0, 1), dropped (2, 3)
     uint32_t am = 0;       // magnitude 2:4: max top key; otherwise packed kept max
     uint32_t amd2 = 0;     // packed dropped max (Wanda, pairwise 4:8)
@@ -639,8 +714,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
       amk = team_max_u32<TEAM>(unpack_max16(am) << 16, redu);
       amd = team_max_u32<TEAM>(unpack_max16(pk_max_u16(am, amd2)) << 16, redu);
     }
-    sink_sum<TEAM>(sink, lacc, redd, row, 0, kept2 + drop, live);
-    sink_sum<TEAM>(sink, lacc, redd, row, 1, drop, live);
+    sink_sum<TEAM, SEG>(sink, lacc, redd, row, 0, kept2 + drop, live);
+    sink_sum<TEAM, SEG>(sink, lacc, redd, row, 1, drop, live);
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
     if constexpr (HELD != 0) {
       quantizers_held<TEAM, UPL, SEL, HELD == 2>(p, pk, famk, famd, sink, lacc, redd, row, live);
@@ -813,8 +888,9 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
       }
     }
+    sink_row_end<TEAM, SEG>(sink, lacc, redd, ncols, row, live, sg);
   });
-  sink_flush(sink, lacc, redd, ncols);
+  sink_flush<TEAM, SEG>(sink, lacc, redd, ncols, sg);
 }
 
 template <class DT, int TEAM, int UPL, bool WANDA, int ROT>
@@ -824,7 +900,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   __shared__ double redd[kBlock / 64];
   extern __shared__ double lacc[];  // per-lane accumulators (whole-operand sums)
   const int ncols0 = 2 + p.kept.n + p.dense.n;
-  sink_init(sink, lacc, ncols0);
+  sink_init(lacc, ncols0);
 
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
@@ -846,7 +922,8 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
   __syncthreads();  // NVFP4 reciprocal tables
   const int64_t nrows = g.nrows;
 
-  for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  Segment sg = sink_segments<TEAM, false>(sink, g);
+  for_each_row_contig<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
     uint32_t km[UPL];  // 8-bit kept mask per unit
     uint32_t mbs[UPL];
@@ -970,7 +1047,7 @@ SPARQ24_ROW_KERNEL void k_energy_rows(RowGeom g, const float* __restrict__ norm,
       sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
     }
   });
-  sink_flush(sink, lacc, redd, ncols0);
+  sink_flush<TEAM, false>(sink, lacc, redd, ncols0, sg);
 }
 
 // Stage 1: sum of one column over one chunk of at most kChunk rows that lies
@@ -1043,11 +1120,12 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   const bool acc = rows_per_block >= g.nrows;  // one block: per-lane accumulators
-  const size_t shmem = sink_lds_bytes(acc, 2 + p.kept.n + p.dense.n);
+  const size_t shmem = sink_lds_bytes(2 + p.kept.n + p.dense.n);
   if (wanda && d.rot.n) return hipErrorInvalidValue;
   auto geom = [&](int, dim3 grid, PartialSink& k) {
     k.rowpart = rowpart;
     k.acc = acc;
+    k.rpb = rows_per_block;
     k.stride = acc ? (int64_t)grid.x : g.nrows;
     *nparts = acc ? (int64_t)grid.x : g.nrows;
   };
