@@ -84,3 +84,26 @@ def test_whole_weight_wanda_sweep():
     whole = np.stack([raw_np(S.error_energy(w, kq, dq, score="wanda", col_norm=n))[0]
                       for kq, dq in zip(kept, dense)])
     rel_close(whole, raw_blocks, rtol=1e-12)
+
+
+@pytest.mark.parametrize("dtype,rows,k,team,kept,dense,rpb", [
+    ("bf16", 50000, 128, 16, "fp8", ("int", 8), 7),          # held rows, 4 teams per wave
+    ("bf16", 9000, 4096, 64, ("int", 4), "fp8", 100),        # held rows, one-wave teams
+    ("bf16", 9000, 4096, 64, "fp8", "mxfp4", 100),           # packed rows (block format)
+    ("f32", 20000, 256, 32, "fp8", ("int", 8), 33),          # fp32 operand
+])
+def test_blocked_sums_segments_straddle_blocks(dtype, rows, k, team, kept, dense, rpb):
+    """Blocked energies when each team walks several contiguous rows whose
+    blocks do not line up with the team's rows: a team's rows then fall in
+    two blocks, and each block's sums gather rows of several teams.  Every
+    block is compared with the fp64 oracle to 1e-6 relative, and the output
+    repeats bit for bit."""
+    assert rows > resident_teams(team)
+    raw = random_raw(np.random.default_rng(rows + k + rpb), (rows, k), dtype)
+    x = to_dev(raw, dtype)
+    print(f"blocked {dtype} [{rows}, {k}] rows_per_block {rpb} {kept} vs {dense}", flush=True)
+    a = S.predict_R(x, [kept], [dense], rows_per_block=rpb)
+    b = S.predict_R(x, [kept], [dense], rows_per_block=rpb)
+    assert torch.equal(a.view(torch.int64), b.view(torch.int64))
+    want = O.predict_R(raw, dtype, [qs_oracle(kept)], [qs_oracle(dense)], rows_per_block=rpb)
+    rel_close(raw_np(a), want)
