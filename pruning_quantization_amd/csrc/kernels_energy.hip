@@ -495,14 +495,17 @@ __device__ inline void pin_packed(uint32_t (&pk)[UPL][4]) {
     for (int h = 0; h < 4; ++h) asm volatile("" : "+v"(pk[j][h]));
 }
 
-// 4096-element rows under magnitude 2:4 without rotation fit 122 VGPRs
+// 4096-element rows under magnitude 2:4 without rotation fit 128 VGPRs
 // without spilling at four waves per SIMD, so a whole 4096-row operand is
 // resident in one pass.
 constexpr int kEnergyWavesMag4096 = 4;
 // INT quantizers of each side evaluated per unpacked unit in one pass of the
-// bf16 kernel (the equal-bits sweep 2:4 + INT-2m vs INT-(m+1), m = 2..8, is
-// two passes: 4 + 4 and 3 + 3; eight per side spilled registers).
-constexpr int kFusedInt = 4;
+// packed bf16 kernel: 4 for Wanda (the equal-bits sweep 2:4 + INT-2m vs
+// INT-(m+1), m = 2..8, is two passes: 4 + 4 and 3 + 3; eight per side
+// spilled registers), 3 for the others, which leaves the magnitude kernel
+// the registers its per-segment sums need at four waves per SIMD.
+template <int SEL>
+constexpr int kFusedInt = SEL == SEL_WANDA ? 4 : 3;
 
 // Wave-uniform copy of lane `i` of v (i uniform).
 __device__ inline float lane_value(float v, int i) {
@@ -671,7 +674,9 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   }
   __syncthreads();  // NVFP4 reciprocal tables
   const int64_t nrows = g.nrows;
-  constexpr bool SEG = HELD != 0;
+  // per-segment blocked sums (held kernels, and packed magnitude rows
+  // without rotation, which fit them in registers)
+  constexpr bool SEG = HELD != 0 || (SEL == SEL_MAG && ROT == 0);
   Segment sg = sink_segments<TEAM, SEG>(sink, g);
   for_each_row_contig<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
@@ -720,26 +725,26 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     if constexpr (HELD != 0) {
       quantizers_held<TEAM, UPL, SEL, HELD == 2>(p, pk, famk, famd, sink, lacc, redd, row, live);
     } else {
-      // INT quantizers, up to kFusedInt of each side per pass over the row, so
+      // INT quantizers, up to kFusedInt<SEL> of each side per pass over the row, so
       // each unit is unpacked once for all of them.  One-wave teams compute a
       // pass's per-row scales lane-parallel (lane i divides for kept quantizer
       // i, lane 32 + i for dense quantizer i) and read them back as
       // wave-uniform values: two divisions per pass instead of two per
-      // quantizer (lane kFusedInt + i takes dense quantizer i).  A kept quantizer with a dense twin (same format and qmax)
+      // quantizer (lane kFusedInt<SEL> + i takes dense quantizer i).  A kept quantizer with a dense twin (same format and qmax)
       // under magnitude 2:4 is evaluated by the twin, since both take their
       // scale from the same maximum and code each kept value identically: the
       // dense side accumulates kept and dropped positions apart and writes both
       // columns.  (Quantizer indices are read from the kernel arguments by
       // position: a pointer into them would force a private copy.)
       const int nki = SEL == SEL_MAG ? p.n_kept_int_solo : p.n_kept_int;
-      for (int c0 = 0; c0 < nki || c0 < p.n_dense_int; c0 += kFusedInt) {
-        const int nk = nki - c0 < 0 ? 0 : (nki - c0 < kFusedInt ? nki - c0 : kFusedInt);
+      for (int c0 = 0; c0 < nki || c0 < p.n_dense_int; c0 += kFusedInt<SEL>) {
+        const int nk = nki - c0 < 0 ? 0 : (nki - c0 < kFusedInt<SEL> ? nki - c0 : kFusedInt<SEL>);
         const int nd = p.n_dense_int - c0 < 0 ? 0
-                                              : (p.n_dense_int - c0 < kFusedInt ? p.n_dense_int - c0 : kFusedInt);
-        int kidx[kFusedInt], didx[kFusedInt];
-        float ks[kFusedInt], kinv[kFusedInt], ds[kFusedInt], dinv[kFusedInt];
+                                              : (p.n_dense_int - c0 < kFusedInt<SEL> ? p.n_dense_int - c0 : kFusedInt<SEL>);
+        int kidx[kFusedInt<SEL>], didx[kFusedInt<SEL>];
+        float ks[kFusedInt<SEL>], kinv[kFusedInt<SEL>], ds[kFusedInt<SEL>], dinv[kFusedInt<SEL>];
   #pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) {
+        for (int i = 0; i < kFusedInt<SEL>; ++i) {
           kidx[i] = i < nk ? (SEL == SEL_MAG ? p.kept_int_solo[c0 + i] : p.kept_int[c0 + i]) : 0;
           didx[i] = i < nd ? p.dense_int[c0 + i] : 0;
         }
@@ -747,9 +752,9 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           const int lane = threadIdx.x & 63;
           float q = 1.0f, a = famk;
   #pragma unroll
-          for (int i = 0; i < kFusedInt; ++i) {
+          for (int i = 0; i < kFusedInt<SEL>; ++i) {
             if (i < nk && lane == i) q = p.kept.qmax[kidx[i]];
-            if (i < nd && lane == kFusedInt + i) {
+            if (i < nd && lane == kFusedInt<SEL> + i) {
               q = p.dense.qmax[didx[i]];
               a = famd;
             }
@@ -757,15 +762,15 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           float sl, il;
           row_scale(a, q, sl, il);
   #pragma unroll
-          for (int i = 0; i < kFusedInt; ++i) {
+          for (int i = 0; i < kFusedInt<SEL>; ++i) {
             ks[i] = __shfl(sl, i, 64);
             kinv[i] = __shfl(il, i, 64);
-            ds[i] = __shfl(sl, kFusedInt + i, 64);
-            dinv[i] = __shfl(il, kFusedInt + i, 64);
+            ds[i] = __shfl(sl, kFusedInt<SEL> + i, 64);
+            dinv[i] = __shfl(il, kFusedInt<SEL> + i, 64);
           }
         } else {
   #pragma unroll
-          for (int i = 0; i < kFusedInt; ++i) {
+          for (int i = 0; i < kFusedInt<SEL>; ++i) {
             ks[i] = kinv[i] = ds[i] = dinv[i] = 0.0f;
             if (i < nk) row_scale(famk, p.kept.qmax[kidx[i]], ks[i], kinv[i]);
             if (i < nd) row_scale(famd, p.dense.qmax[didx[i]], ds[i], dinv[i]);
@@ -775,15 +780,15 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         // twin can exist (magnitude 2:4); otherwise one sum over the unit
         constexpr bool SPLIT = SEL == SEL_MAG;
         pin_packed<UPL>(pk);
-        double ka[kFusedInt], dka[kFusedInt], dda[kFusedInt];
+        double ka[kFusedInt<SEL>], dka[kFusedInt<SEL>], dda[kFusedInt<SEL>];
   #pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) ka[i] = dka[i] = dda[i] = 0.0;
+        for (int i = 0; i < kFusedInt<SEL>; ++i) ka[i] = dka[i] = dda[i] = 0.0;
   #pragma unroll
         for (int j = 0; j < UPL; ++j) {
           const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
                               mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
   #pragma unroll
-          for (int i = 0; i < kFusedInt; ++i) {
+          for (int i = 0; i < kFusedInt<SEL>; ++i) {
             if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
             if (i < nd) {
               if constexpr (SPLIT) {
@@ -797,15 +802,15 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
         }
   #pragma unroll
-        for (int i = 0; i < kFusedInt; ++i) {
-          if (i < nk) sink_sum<TEAM>(sink, lacc, redd, row, 2 + kidx[i], ka[i], live);
+        for (int i = 0; i < kFusedInt<SEL>; ++i) {
+          if (i < nk) sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + kidx[i], ka[i], live);
           if (i < nd) {
             int twin = -1;
             if (SEL == SEL_MAG)
               for (int k = 0; k < p.kept.n; ++k)
                 if (p.kept_twin[k] == didx[i]) twin = k;
-            if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, dka[i], live);
-            sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + didx[i], dka[i] + dda[i], live);
+            if (twin >= 0) sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + twin, dka[i], live);
+            sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + p.kept.n + didx[i], dka[i] + dda[i], live);
           }
         }
       }
@@ -838,7 +843,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
             acc += (double)kept_block_err4<false>(v, 0.f, 0.f, nullptr);
           }
         }
-        sink_sum<TEAM>(sink, lacc, redd, row, 2 + q, acc, live);
+        sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + q, acc, live);
       }
       for (int q = 0; q < p.dense.n; ++q) {
         const int fmt = p.dense.fmt[q];
@@ -860,7 +865,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
             acck += (double)mag_sq_err_fp8<4>(s, inv, vk);
             acc += (double)mag_sq_err_fp8<4>(s, inv, vd);
           }
-          if (twin >= 0) sink_sum<TEAM>(sink, lacc, redd, row, 2 + twin, acck, live);
+          if (twin >= 0) sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + twin, acck, live);
           acc += acck;
         } else if (fmt == CF_MX || fmt == CF_NV) {
   #pragma unroll
@@ -885,7 +890,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
             }
           }
         }
-        sink_sum<TEAM>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
+        sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + p.kept.n + q, acc, live);
       }
     }
     sink_row_end<TEAM, SEG>(sink, lacc, redd, ncols, row, live, sg);
