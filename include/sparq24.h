@@ -22,7 +22,7 @@
  *                   K = seq, k_stride = head_dim), R <= 4194240 (65535
  *                   tiles of 64 rows, else SPARQ24_ERR_UNSUPPORTED).
  *                   sparq24_prune_compress reads it directly (16-bit
- *                   magnitude with R % 64 == 0 and K % 512 == 0: 8 x 8
+ *                   magnitude with R % 64 == 0 and K % 256 == 0: 8 x 8
  *                   blocks transposed in registers; otherwise an LDS-tiled
  *                   transpose); the
  *                   other calls (except sparq24_col_l2norm, which rejects it

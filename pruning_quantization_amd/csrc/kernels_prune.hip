@@ -233,70 +233,82 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
   }
 }
 
-// Transposed 16-bit operand, magnitude score, R % 64 == 0 and K % 512 == 0
+// Transposed 16-bit operand, magnitude score, R % 64 == 0 and K % 256 == 0
 // (e.g. V [heads, seq, 128] pruned along seq): no LDS staging of the input.
-// A workgroup covers 512 positions x 64 rows as two 256-position tiles.  In
-// each tile thread t owns the 8 x 8 block of rows 8 * (t % 8) .. + 7 and
-// positions 8 * ((t / 8) % 16) .. + 7 of its 128-position half (t / 128):
-// it loads one 16-byte chunk (8 adjacent rows) per position, so each wave
-// load instruction reads 8 whole 128-byte lines; all 16 chunks of both tiles
-// are in flight together.  The block is transposed in registers with byte
-// permutes (one per output dword), each row's unit is selected through the
-// LDS table and the kept pairs are stored directly (8 adjacent threads write
-// 64 contiguous bytes of a row).  Metadata bytes go through a small LDS tile
-// and leave as 64-byte row segments.
-constexpr int kT8_K = 512;  // positions per workgroup
-constexpr int kT8_R = 64;   // rows per workgroup
+// A tile is 256 positions x 64 rows; each workgroup walks kT8_Tiles tiles
+// (tile index strided by the grid) with the next tile's loads in flight
+// while it selects and stores the current one.  In a tile thread t owns the
+// 8 x 8 block of rows 8 * (t % 8) .. + 7 and positions 8 * ((t / 8) % 16)
+// .. + 7 of its 128-position half (t / 128): it loads one 16-byte chunk (8
+// adjacent rows) per position, so each wave load instruction reads 8 whole
+// 128-byte lines.  The block is transposed in registers with byte permutes
+// (one per output dword), each row's unit is selected through the LDS table
+// and the kept pairs are stored directly (8 adjacent threads write 64
+// contiguous bytes of a row).  Metadata bytes go through a double-buffered
+// LDS tile (one barrier per tile) and leave as 32-byte row segments.
+constexpr int kT8_K = 256;     // positions per tile
+constexpr int kT8_R = 64;      // rows per tile
+constexpr int kT8_Tiles = 2;   // tiles per workgroup (grid = ceil(tiles / kT8_Tiles))
 
 template <class DT>
 __global__ __launch_bounds__(kBlock) void k_prune_compress_T8(
     const char* __restrict__ x, int64_t R, int64_t K, int64_t bs, int64_t ks,
-    char* __restrict__ vals, uint8_t* __restrict__ meta) {
+    char* __restrict__ vals, uint8_t* __restrict__ meta, int64_t ntiles) {
   static_assert(DT::ESIZE == 2, "16-bit storage types");
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   __shared__ SelLut lut[kSelLutEntries];
-  __shared__ __align__(16) uint8_t mtile[kT8_R][kT8_K / 8];  // [row][unit]
+  __shared__ __align__(16) uint8_t mtile[2][kT8_R][kT8_K / 8];  // [buffer][row][unit]
   const int t = threadIdx.x;
   const int rg = t & 7, pg = (t >> 3) & 15, half = t >> 7;
-  const int64_t r0 = (int64_t)blockIdx.y * kT8_R + rg * 8;  // first row
-  const int64_t b = blockIdx.z;
-  const int64_t kb = (int64_t)blockIdx.x * kT8_K + half * 128 + pg * 8;  // first position, tile 0
-  const char* src = x + b * bs + kb * ks + r0 * 2;
-  u32x4 c[2][8];  // chunk i of tile h: rows r0 .. r0 + 7 at position kb + 256 h + i
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
+  const int64_t ntk = K / kT8_K, ntr = R / kT8_R;
+  // tile -> (batch, row tile, position tile); first position and row of this thread
+  auto origin = [&](int64_t tile, int64_t& b, int64_t& r0, int64_t& k0) {
+    const int64_t kt = tile % ntk, q = tile / ntk;
+    b = q / ntr;
+    r0 = (q % ntr) * kT8_R + rg * 8;
+    k0 = kt * kT8_K + half * 128 + pg * 8;
+  };
+  auto load = [&](int64_t tile, u32x4 (&c)[8]) {
+    int64_t b, r0, k0;
+    origin(tile, b, r0, k0);
+    const char* src = x + b * bs + k0 * ks + r0 * 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      c[h][i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(src + (int64_t)(256 * h + i) * ks));
+      c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * ks));
+  };
+  u32x4 cur[8], nxt[8];
+  int64_t tile = blockIdx.x;
+  load(tile, cur);  // the grid never exceeds the tile count
   sel_lut_fill(lut);
   __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t k0 = kb + 256 * h;
-    const int ucol = 32 * h + half * 16 + pg;  // unit column within the workgroup's positions
+  for (int buf = 0; tile < ntiles; tile += gridDim.x, buf ^= 1) {
+    const int64_t next = tile + gridDim.x;
+    if (next < ntiles) load(next, nxt);
+    int64_t b, r0, k0;
+    origin(tile, b, r0, k0);
+    const int ucol = half * 16 + pg;  // unit column within the tile
 #pragma unroll
     for (int d = 0; d < 8; ++d) {  // row r0 + d: dword d / 2 of each chunk, half d % 2
       const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
       uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4& lo = c[h][2 * q];
-        const u32x4& hi = c[h][2 * q + 1];
-        w[q] = __builtin_amdgcn_perm(hi[d >> 1], lo[d >> 1], sel);  // positions 2q, 2q + 1
-      }
+      for (int q = 0; q < 4; ++q)  // positions 2q, 2q + 1
+        w[q] = __builtin_amdgcn_perm(cur[2 * q + 1][d >> 1], cur[2 * q][d >> 1], sel);
       const Sel16 r = select16_lut(w, lut);
       st2(vals + ((b * R + r0 + d) * (K / 2) + k0 / 2) * 2, r.k0, r.k1);
-      mtile[rg * 8 + d][ucol] = (uint8_t)r.mb;
+      mtile[buf][rg * 8 + d][ucol] = (uint8_t)r.mb;
     }
-  }
-  __syncthreads();
-  {  // 64 rows x 64 metadata bytes: one 16-byte chunk per thread
-    const int row = t >> 2, part = t & 3;
-    const uint4 v = *reinterpret_cast<const uint4*>(&mtile[row][part * 16]);
-    st4(meta + (b * R + (int64_t)blockIdx.y * kT8_R + row) * (K / 8) +
-            (int64_t)blockIdx.x * (kT8_K / 8) + part * 16,
-        v.x, v.y, v.z, v.w);
+    __syncthreads();
+    if (t < kT8_R * 2) {  // 64 rows x 32 metadata bytes, in 16-byte chunks
+      const int row = t >> 1, part = t & 1;
+      const uint4 v = *reinterpret_cast<const uint4*>(&mtile[buf][row][part * 16]);
+      const int64_t q = tile / ntk;
+      st4(meta + ((q / ntr) * R + (q % ntr) * kT8_R + row) * (K / 8) + (tile % ntk) * (kT8_K / 8) +
+              part * 16,
+          v.x, v.y, v.z, v.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
   }
 }
 
@@ -471,13 +483,14 @@ hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm
   const int64_t nunits = d.K / 8;
   if (!d.kcontig) {
     if (!wanda && d.dtype != 0 && d.R % kT8_R == 0 && d.K % kT8_K == 0) {
-      const dim3 grid((unsigned)(d.K / kT8_K), (unsigned)(d.R / kT8_R), (unsigned)d.B);
+      const int64_t ntiles = (d.K / kT8_K) * (d.R / kT8_R) * d.B;
+      const dim3 grid((unsigned)((ntiles + kT8_Tiles - 1) / kT8_Tiles));
       if (d.dtype == 1)
         hipLaunchKernelGGL((k_prune_compress_T8<BF16T>), grid, dim3(kBlock), 0, s, d.x, d.R, d.K,
-                           d.bs, d.ks, (char*)vals, meta);
+                           d.bs, d.ks, (char*)vals, meta, ntiles);
       else
         hipLaunchKernelGGL((k_prune_compress_T8<F16T>), grid, dim3(kBlock), 0, s, d.x, d.R, d.K,
-                           d.bs, d.ks, (char*)vals, meta);
+                           d.bs, d.ks, (char*)vals, meta, ntiles);
       return hipGetLastError();
     }
     return with_dtype(d.dtype, [&]<class DT>() {

@@ -112,9 +112,8 @@ def test_prune_compress_transposed(dtype, shape):
 @pytest.mark.parametrize("shape", [(1, 256, 128), (3, 512, 64), (2, 1024, 192), (8, 16384, 128)])
 @pytest.mark.parametrize("kind", ["normal", "ties"])
 def test_prune_compress_transposed_register_blocks(dtype, shape, kind):
-    # 16-bit V with dims % 64 == 0 and seq % 512 == 0: the kernel that transposes
-    # 8 x 8 blocks in registers (the V shape of 16K-token attention included);
-    # seq 256 takes the LDS-tiled kernel
+    # 16-bit V with dims % 64 == 0 and seq % 256 == 0: the kernel that transposes
+    # 8 x 8 blocks in registers (the V shape of 16K-token attention included)
     rng = np.random.default_rng(sum(shape) + len(kind))
     flat = (shape[0] * shape[1], shape[2])
     raw = (tie_heavy_raw(rng, flat, dtype) if kind == "ties" else random_raw(rng, flat, dtype)).reshape(shape)
