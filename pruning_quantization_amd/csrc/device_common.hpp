@@ -300,6 +300,46 @@ __device__ inline Sel16 select16_lut(const uint32_t* w, const SelLut* lut) {
   return r;
 }
 
+// Wanda selection of a bf16 group from fp32 products.  Rounding to fp32 is
+// monotone, so fp32(|w_a| n_a) > fp32(|w_b| n_b) implies the exact products
+// order the same way; only equal fp32 values leave the exact order open.  The
+// keys are the product's fp32 bits with the low byte replaced by 2 * position
+// (a further monotone truncation that keeps the four keys distinct).  When
+// the second and third largest keys differ above that byte, the top-2 set is
+// exactly the one the exact fp64 products give, ties included (no tie sits at
+// the boundary), and the order inside the low byte never decides anything;
+// otherwise the group is ambiguous and the caller ranks it exactly.  A
+// winner's low byte 2i is the first byte of element i in the group's two
+// dwords, so the byte-permute selector gathering a pair is two bytes of keys
+// placed side by side, plus one.
+// a, b: the group's two dwords with sign bits cleared; n: its four norms.
+// kept / drop: the kept and the dropped |x| as packed bf16 pairs (in rank
+// order, not position order).  Returns true when the group is ambiguous
+// (kept / drop are then not the exact selection).
+__device__ inline bool wanda_group_fp32(uint32_t a, uint32_t b, const float* n, uint32_t& kept,
+                                        uint32_t& drop) {
+  const float p0 = __uint_as_float(a << 16) * n[0], p1 = __uint_as_float(a & 0xFFFF0000u) * n[1];
+  const float p2 = __uint_as_float(b << 16) * n[2], p3 = __uint_as_float(b & 0xFFFF0000u) * n[3];
+  const uint32_t k0 = __float_as_uint(p0) & 0xFFFFFF00u;
+  const uint32_t k1 = (__float_as_uint(p1) & 0xFFFFFF00u) | 2u;
+  const uint32_t k2 = (__float_as_uint(p2) & 0xFFFFFF00u) | 4u;
+  const uint32_t k3 = (__float_as_uint(p3) & 0xFFFFFF00u) | 6u;
+  uint32_t M, m, l, t2, d2;
+  asm("v_max3_u32 %0, %1, %2, %3" : "=v"(M) : "v"(k0), "v"(k1), "v"(k2));
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(k0), "v"(k1), "v"(k2));
+  asm("v_min3_u32 %0, %1, %2, %3" : "=v"(l) : "v"(k0), "v"(k1), "v"(k2));
+  const uint32_t t1 = M > k3 ? M : k3;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(t2) : "v"(m), "v"(M), "v"(k3));
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(d2) : "v"(l), "v"(m), "v"(k3));
+  const uint32_t d1 = l < k3 ? l : k3;
+  // selector bytes (2i, 2i + 1, 2j, 2j + 1) for the pair (i, j)
+  const uint32_t ks = __builtin_amdgcn_perm(t2, t1, 0x04040000u) + 0x01000100u;
+  const uint32_t ds = __builtin_amdgcn_perm(d1, d2, 0x04040000u) + 0x01000100u;
+  kept = __builtin_amdgcn_perm(b, a, ks);
+  drop = __builtin_amdgcn_perm(b, a, ds);
+  return (t2 ^ d2) < 256u;
+}
+
 // Both group selections of a unit -> metadata byte (group 0 in the low nibble).
 // Wanda reads the 8 channel norms of the unit (k0 = its first position).
 // ---------------------------------------------------------------------------

@@ -118,17 +118,33 @@ enum { SEL_MAG = 0, SEL_WANDA = 1, SEL_P48 = 2 };
 // Kept and dropped |x| of one bf16 unit as packed pairs: pk[0], pk[1] the
 // four kept magnitudes, pk[2], pk[3] the four dropped ones (Wanda 2:4 or
 // pairwise 4:8; magnitude 2:4 has its own faster path).  Units past the
-// row's end (valid = false) are zeros and select anything.
+// row's end (valid = false) are zeros and select anything.  Wanda ranks by
+// fp32 products first (wanda_group_fp32) and takes the exact fp64 ranking
+// only for units with a group whose fp32 keys leave the kept set open.
 template <int SEL>
 __device__ inline void unit_mags_packed(const Unit<BF16T>& u, const float* __restrict__ norm,
                                         int64_t k0, bool valid, uint32_t (&pk)[4]) {
   if constexpr (SEL == SEL_WANDA) {
-    const uint32_t mb = valid ? select_unit<BF16T, true>(u, norm, k0) : 0x44u;
-    const uint32_t n0 = mb & 0xFu, n1 = mb >> 4;
-    pk[0] = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(n0)) & 0x7FFF7FFFu;
-    pk[1] = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(n1)) & 0x7FFF7FFFu;
-    pk[2] = __builtin_amdgcn_perm(u.w[1], u.w[0], perm_sel(other_pair(n0))) & 0x7FFF7FFFu;
-    pk[3] = __builtin_amdgcn_perm(u.w[3], u.w[2], perm_sel(other_pair(n1))) & 0x7FFF7FFFu;
+    // a unit past the row's end reads the first norms (its products are zero)
+    const float4* np = reinterpret_cast<const float4*>(norm + (valid ? k0 : 0));
+    const float4 na = np[0], nb = np[1];
+    const float n8[8] = {na.x, na.y, na.z, na.w, nb.x, nb.y, nb.z, nb.w};
+    const uint32_t a0 = u.w[0] & 0x7FFF7FFFu, b0 = u.w[1] & 0x7FFF7FFFu;
+    const uint32_t a1 = u.w[2] & 0x7FFF7FFFu, b1 = u.w[3] & 0x7FFF7FFFu;
+    bool amb = wanda_group_fp32(a0, b0, n8, pk[0], pk[2]);
+    amb |= wanda_group_fp32(a1, b1, n8 + 4, pk[1], pk[3]);
+    // rare: a wave-uniform branch around the exact ranking, so that it is
+    // not computed (and selected away) on every unit
+    if (__builtin_amdgcn_ballot_w64(amb && valid)) {
+      if (amb && valid) {
+        const uint32_t n0 = select_group<BF16T, true>(u, 0, n8);
+        const uint32_t n1 = select_group<BF16T, true>(u, 1, n8 + 4);
+        pk[0] = __builtin_amdgcn_perm(b0, a0, perm_sel(n0));
+        pk[1] = __builtin_amdgcn_perm(b1, a1, perm_sel(n1));
+        pk[2] = __builtin_amdgcn_perm(b0, a0, perm_sel(other_pair(n0)));
+        pk[3] = __builtin_amdgcn_perm(b1, a1, perm_sel(other_pair(n1)));
+      }
+    }
   } else {
     // a bf16 pair (2p, 2p+1) is dword p of the unit
     const uint32_t nb = select_pairs48(u), dn = other_pair(nb);

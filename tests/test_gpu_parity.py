@@ -294,6 +294,44 @@ def test_predict_R_sweep_and_wanda():
         rel_close(raw_np(got), want)
 
 
+def wanda_colliding_inputs(seed, rows, k):
+    """bf16 weights and fp32 norms whose Wanda products |w| * n often round to
+    the same fp32 value (or agree in all but their last 8 bits) while the exact
+    products differ or tie: |w| from {0, 0.5, 1, 1.5, 2, 3} (random signs),
+    norms from values such as fp32(1/3), fp32(2/3), 1 + 2^-23 and 1 + 2^-20,
+    so that e.g. 3 * fp32(1/3) and 1 * 1 fall on one fp32 but rank apart
+    exactly.  The selection must still be the exact one (ties to the lower
+    position)."""
+    rng = np.random.default_rng(seed)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0])
+    w = mags[rng.integers(0, len(mags), size=(rows, k))] * rng.choice([-1.0, 1.0], size=(rows, k))
+    import workloads as W
+    raw = W.to_bf16_bits(w)
+    cands = np.array([1.0, np.float32(1 / 3), np.float32(2 / 3), 1 + 2.0 ** -23, 1 + 2.0 ** -20,
+                      0.5, 2.0, 0.0, np.float32(1 / 3) * (1 + 2.0 ** -22)], dtype=np.float32)
+    norm = cands[rng.integers(0, len(cands), size=k)].astype(np.float32)
+    return raw, norm
+
+
+@pytest.mark.parametrize("k", [1088, 4096])
+def test_wanda_energies_with_colliding_fp32_products(k):
+    # the energy kernels rank Wanda scores by fp32 products and fall back to
+    # the exact fp64 ranking where those leave the kept set open
+    raw, norm = wanda_colliding_inputs(k, 70, k)
+    x = to_dev(raw, "bf16")
+    n = torch.from_numpy(norm).cuda()
+    for kept, dense, rpb in [([("int", 4), "fp8"], [("int", 3), ("int", 8)], 0),
+                             ([("int", 6), "mxfp4"], ["nvfp4", ("int", 4)], 16)]:
+        got = S.predict_R(x, kept, dense, score="wanda", col_norm=n, rows_per_block=rpb)
+        want = O.predict_R(raw, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
+                           "wanda", norm, rows_per_block=rpb)
+        rel_close(raw_np(got), want)
+    v, m = S.prune_compress(x, score="wanda", col_norm=n)
+    wv, wm = O.prune_compress(raw, "bf16", "wanda", norm)
+    assert_same(raw_np(m), wm, "meta")
+    assert_same(raw_np(v), wv, "values")
+
+
 def test_predict_R_blocks_degenerate_and_deterministic():
     raw = inputs(5, 300, 256, "bf16", "ties")
     raw[:128] = 0                                   # first block all zero -> NaN
