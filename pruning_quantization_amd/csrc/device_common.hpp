@@ -308,36 +308,54 @@ __device__ inline Sel16 select16_lut(const uint32_t* w, const SelLut* lut) {
 // the second and third largest keys differ above that byte, the top-2 set is
 // exactly the one the exact fp64 products give, ties included (no tie sits at
 // the boundary), and the order inside the low byte never decides anything;
-// otherwise the group is ambiguous and the caller ranks it exactly.  A
-// winner's low byte 2i is the first byte of element i in the group's two
-// dwords, so the byte-permute selector gathering a pair is two bytes of keys
-// placed side by side, plus one.
+// otherwise the group is ambiguous and the caller ranks it exactly.
 // a, b: the group's two dwords with sign bits cleared; n: its four norms.
-// kept / drop: the kept and the dropped |x| as packed bf16 pairs (in rank
-// order, not position order).  Returns true when the group is ambiguous
-// (kept / drop are then not the exact selection).
-__device__ inline bool wanda_group_fp32(uint32_t a, uint32_t b, const float* n, uint32_t& kept,
-                                        uint32_t& drop) {
+// t1 > t2 > d2 > d1: the four keys in order.  Returns true when ambiguous.
+__device__ inline bool wanda_rank_fp32(uint32_t a, uint32_t b, const float* n, uint32_t& t1,
+                                       uint32_t& t2, uint32_t& d2, uint32_t& d1) {
   const float p0 = __uint_as_float(a << 16) * n[0], p1 = __uint_as_float(a & 0xFFFF0000u) * n[1];
   const float p2 = __uint_as_float(b << 16) * n[2], p3 = __uint_as_float(b & 0xFFFF0000u) * n[3];
   const uint32_t k0 = __float_as_uint(p0) & 0xFFFFFF00u;
   const uint32_t k1 = (__float_as_uint(p1) & 0xFFFFFF00u) | 2u;
   const uint32_t k2 = (__float_as_uint(p2) & 0xFFFFFF00u) | 4u;
   const uint32_t k3 = (__float_as_uint(p3) & 0xFFFFFF00u) | 6u;
-  uint32_t M, m, l, t2, d2;
+  uint32_t M, m, l;
   asm("v_max3_u32 %0, %1, %2, %3" : "=v"(M) : "v"(k0), "v"(k1), "v"(k2));
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(k0), "v"(k1), "v"(k2));
   asm("v_min3_u32 %0, %1, %2, %3" : "=v"(l) : "v"(k0), "v"(k1), "v"(k2));
-  const uint32_t t1 = M > k3 ? M : k3;
+  t1 = M > k3 ? M : k3;
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(t2) : "v"(m), "v"(M), "v"(k3));
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(d2) : "v"(l), "v"(m), "v"(k3));
-  const uint32_t d1 = l < k3 ? l : k3;
+  d1 = l < k3 ? l : k3;
+  return (t2 ^ d2) < 256u;
+}
+
+// The kept and the dropped |x| of a group as packed bf16 pairs (in rank
+// order, not position order).  A key's low byte 2i is the first byte of
+// element i in the group's two dwords, so the byte-permute selector that
+// gathers a pair is two keys' low bytes placed side by side, plus one.
+// Returns true when the group is ambiguous (kept / drop are then not the
+// exact selection).
+__device__ inline bool wanda_group_fp32(uint32_t a, uint32_t b, const float* n, uint32_t& kept,
+                                        uint32_t& drop) {
+  uint32_t t1, t2, d2, d1;
+  const bool amb = wanda_rank_fp32(a, b, n, t1, t2, d2, d1);
   // selector bytes (2i, 2i + 1, 2j, 2j + 1) for the pair (i, j)
   const uint32_t ks = __builtin_amdgcn_perm(t2, t1, 0x04040000u) + 0x01000100u;
   const uint32_t ds = __builtin_amdgcn_perm(d1, d2, 0x04040000u) + 0x01000100u;
   kept = __builtin_amdgcn_perm(b, a, ks);
   drop = __builtin_amdgcn_perm(b, a, ds);
-  return (t2 ^ d2) < 256u;
+  return amb;
+}
+
+// The metadata nibble i0 | i1 << 2 (i0 < i1) of a group.  Returns true when
+// the group is ambiguous (the nibble is then not the exact selection).
+__device__ inline bool wanda_nibble_fp32(uint32_t a, uint32_t b, const float* n, uint32_t& nib) {
+  uint32_t t1, t2, d2, d1;
+  const bool amb = wanda_rank_fp32(a, b, n, t1, t2, d2, d1);
+  const uint32_t q1 = t1 & 6u, q2 = t2 & 6u;  // 2 * position
+  nib = ((q1 < q2 ? q1 : q2) >> 1) | ((q1 < q2 ? q2 : q1) << 1);
+  return amb;
 }
 
 // Both group selections of a unit -> metadata byte (group 0 in the low nibble).
@@ -352,6 +370,21 @@ __device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restric
     float4 a = np[0], b = np[1];
     n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
     n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
+  }
+  if constexpr (WANDA && DT::IS_BF16) {
+    // fp32 products first; the exact ranking (under a wave-uniform branch,
+    // so that it is skipped when no lane needs it) for units with an open
+    // group
+    uint32_t n0, n1;
+    bool amb = wanda_nibble_fp32(u.w[0] & 0x7FFF7FFFu, u.w[1] & 0x7FFF7FFFu, n8, n0);
+    amb |= wanda_nibble_fp32(u.w[2] & 0x7FFF7FFFu, u.w[3] & 0x7FFF7FFFu, n8 + 4, n1);
+    if (__builtin_amdgcn_ballot_w64(amb)) {
+      if (amb) {
+        n0 = select_group<DT, true>(u, 0, n8);
+        n1 = select_group<DT, true>(u, 1, n8 + 4);
+      }
+    }
+    return n0 | (n1 << 4);
   }
   uint32_t n0 = select_group<DT, WANDA>(u, 0, n8);
   uint32_t n1 = select_group<DT, WANDA>(u, 1, n8 + 4);

@@ -326,10 +326,17 @@ def test_wanda_energies_with_colliding_fp32_products(k):
         want = O.predict_R(raw, "bf16", [qs_oracle(q) for q in kept], [qs_oracle(q) for q in dense],
                            "wanda", norm, rows_per_block=rpb)
         rel_close(raw_np(got), want)
+    # the prune kernels rank the same way
     v, m = S.prune_compress(x, score="wanda", col_norm=n)
     wv, wm = O.prune_compress(raw, "bf16", "wanda", norm)
     assert_same(raw_np(m), wm, "meta")
     assert_same(raw_np(v), wv, "values")
+    for fmt, bits in (("fp8", 0), ("int", 4)):
+        c, m, s = S.prune_quantize(x, (fmt, bits), score="wanda", col_norm=n)
+        wc, wm, ws = O.prune_quantize(raw, "bf16", O.QSpec(fmt, bits), "wanda", norm)
+        assert_same(raw_np(m), wm, f"meta {fmt}")
+        assert_same(raw_np(s), ws, f"scales {fmt}")
+        assert_same(raw_np(c), wc, f"codes {fmt}")
 
 
 def test_predict_R_blocks_degenerate_and_deterministic():
