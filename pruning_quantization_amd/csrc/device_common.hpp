@@ -362,15 +362,7 @@ __device__ inline bool wanda_nibble_fp32(uint32_t a, uint32_t b, const float* n,
 // Wanda reads the 8 channel norms of the unit (k0 = its first position).
 // ---------------------------------------------------------------------------
 template <class DT, bool WANDA>
-__device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restrict__ norm,
-                                       int64_t k0) {
-  float n8[8];
-  if constexpr (WANDA) {
-    const float4* np = reinterpret_cast<const float4*>(norm + k0);
-    float4 a = np[0], b = np[1];
-    n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
-    n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
-  }
+__device__ inline uint32_t select_unit_norms(const Unit<DT>& u, const float* n8) {
   if constexpr (WANDA && DT::IS_BF16) {
     // fp32 products first; the exact ranking (under a wave-uniform branch,
     // so that it is skipped when no lane needs it) for units with an open
@@ -389,6 +381,19 @@ __device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restric
   uint32_t n0 = select_group<DT, WANDA>(u, 0, n8);
   uint32_t n1 = select_group<DT, WANDA>(u, 1, n8 + 4);
   return n0 | (n1 << 4);
+}
+
+template <class DT, bool WANDA>
+__device__ inline uint32_t select_unit(const Unit<DT>& u, const float* __restrict__ norm,
+                                       int64_t k0) {
+  float n8[8];
+  if constexpr (WANDA) {
+    const float4* np = reinterpret_cast<const float4*>(norm + k0);
+    float4 a = np[0], b = np[1];
+    n8[0] = a.x; n8[1] = a.y; n8[2] = a.z; n8[3] = a.w;
+    n8[4] = b.x; n8[5] = b.y; n8[6] = b.z; n8[7] = b.w;
+  }
+  return select_unit_norms<DT, WANDA>(u, n8);
 }
 
 // The four kept elements of a unit (two per group, in position order) as raw

@@ -90,6 +90,71 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_rows(
 }
 
 // ---------------------------------------------------------------------------
+// Wanda 2:4 of bf16 rows with K % 16 == 0 and K <= 16 * kBlock * UPP: a
+// whole workgroup is the team of one row, persistent over rows (row
+// blockIdx.x, then + gridDim.x, ...).  Lane t owns the unit pairs t, t +
+// kBlock, ... (16 positions each): their 16 channel norms are loaded once
+// and held in registers for every row, each pair leaves as one 16-byte store
+// of kept values and one 2-byte metadata store, and the next row's loads are
+// in flight while the current row is selected and stored (two rows ahead
+// measured slower).
+// ---------------------------------------------------------------------------
+template <int UPP>
+__global__ __launch_bounds__(kBlock) void k_prune_compress_wanda_rows(
+    const char* __restrict__ x, int64_t R, int64_t nrows, int64_t npairs, int64_t bs, int64_t rs,
+    const float* __restrict__ norm, char* __restrict__ vals, uint8_t* __restrict__ meta) {
+  const int t = threadIdx.x;
+  float n[UPP][16];
+  bool ok[UPP];
+#pragma unroll
+  for (int q = 0; q < UPP; ++q) {
+    const int64_t p = t + (int64_t)q * kBlock;
+    ok[q] = p < npairs;
+    const float4* np = reinterpret_cast<const float4*>(norm + (ok[q] ? p * 16 : 0));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v = np[c];
+      n[q][4 * c] = v.x; n[q][4 * c + 1] = v.y; n[q][4 * c + 2] = v.z; n[q][4 * c + 3] = v.w;
+    }
+  }
+  // (batch, row) of a flattened row index, stepped on the scalar unit
+  int64_t row = blockIdx.x, b = row / R, r = row % R;
+  auto load = [&](int64_t bb, int64_t rr, Unit<BF16T> (&u)[UPP][2]) {
+    const char* xr = x + bb * bs + rr * rs;
+#pragma unroll
+    for (int q = 0; q < UPP; ++q) {
+      const int64_t p = ok[q] ? t + (int64_t)q * kBlock : 0;
+      load_unit(u[q][0], xr + p * 32);
+      load_unit(u[q][1], xr + p * 32 + 16);
+    }
+  };
+  Unit<BF16T> cur[UPP][2], nxt[UPP][2];
+  load(b, r, cur);  // the grid never exceeds the row count
+  for (; row < nrows; row += gridDim.x) {
+    int64_t nb = b, nr = r + gridDim.x;
+    while (nr >= R) { nr -= R; ++nb; }
+    if (row + gridDim.x < nrows) load(nb, nr, nxt);
+#pragma unroll
+    for (int q = 0; q < UPP; ++q) {
+      if (!ok[q]) continue;
+      const int64_t p = t + (int64_t)q * kBlock;
+      const uint32_t m0 = select_unit_norms<BF16T, true>(cur[q][0], n[q]);
+      const uint32_t m1 = select_unit_norms<BF16T, true>(cur[q][1], n[q] + 8);
+      const Kept<BF16T> k0 = gather_kept(cur[q][0], m0), k1 = gather_kept(cur[q][1], m1);
+      st4(vals + (row * npairs + p) * 16, k0.k[0], k0.k[1], k1.k[0], k1.k[1]);
+      st(reinterpret_cast<uint16_t*>(meta) + row * npairs + p, (uint16_t)(m0 | (m1 << 8)));
+    }
+    b = nb;
+    r = nr;
+#pragma unroll
+    for (int q = 0; q < UPP; ++q) {
+      cur[q][0] = nxt[q][0];
+      cur[q][1] = nxt[q][1];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Transposed operand (row_stride == 1, the reduction axis strided), e.g. V
 // [heads, seq, head_dim] pruned along seq.  A workgroup stages a tile of
 // KT positions x RT rows through LDS: loads run along the contiguous row
@@ -514,6 +579,19 @@ hipError_t launch_prune_compress(const RowDesc& d, bool wanda, const float* norm
                          s, d.x, total, (char*)vals, meta);
       return hipGetLastError();
     });
+  }
+  if (wanda && d.dtype == 1 && d.K % 16 == 0 && d.K <= 32 * kBlock) {
+    // bf16 Wanda rows: persistent whole-workgroup teams with the norms in registers
+    auto go = [&]<int UPP>() {
+      constexpr auto Kn = k_prune_compress_wanda_rows<UPP>;
+      const int64_t nrows = d.B * d.R;
+      const int64_t cap = (int64_t)device_cu_count() * resident_blocks<Kn>();
+      const int64_t grid = nrows < cap ? nrows : cap;
+      hipLaunchKernelGGL(Kn, dim3((unsigned)grid), dim3(kBlock), 0, s, d.x, d.R, nrows,
+                         d.K / 16, d.bs, d.rs, norm, (char*)vals, meta);
+      return hipGetLastError();
+    };
+    return d.K <= 16 * kBlock ? go.template operator()<1>() : go.template operator()<2>();
   }
   return with_dtype(d.dtype, [&]<class DT>() {
     return with_loop_variant(nunits, [&]<int TEAM, int UPL>() {

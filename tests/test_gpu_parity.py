@@ -93,6 +93,35 @@ def test_prune_compress_wanda(dtype, k):
     assert_same(raw_np(v), wv, "values")
 
 
+@pytest.mark.parametrize("view", ["batch_strided", "row_strided", "k16", "k4112", "k8192"])
+def test_prune_compress_wanda_bf16_rows(view):
+    # bf16 Wanda rows with K % 16 == 0 run on persistent whole-workgroup teams
+    # (norms held per lane, several rows per workgroup when rows exceed the
+    # grid, batches stepped with the rows); ragged pair counts and strided views
+    rng = np.random.default_rng(len(view))
+    if view == "batch_strided":
+        full = tie_heavy_raw(rng, (2 * 1600, 528), "bf16").reshape(2, 1600, 528)
+        raw = np.ascontiguousarray(full[:, :1500, :])
+        x = to_dev(full, "bf16")[:, :1500, :]
+    elif view == "row_strided":
+        full = random_raw(rng, (3000, 544), "bf16")
+        raw = np.ascontiguousarray(full[:, :528])
+        x = to_dev(full, "bf16")[:, :528]
+    else:
+        k = int(view[1:])
+        raw = random_raw(rng, (37 if k > 16 else 3000, k), "bf16")
+        x = to_dev(raw, "bf16")
+    k = raw.shape[-1]
+    norm = (rng.integers(0, 5, size=k) * 0.75).astype(np.float32)
+    norm[: k // 2] = rng.random(k // 2).astype(np.float32) * 3
+    n = torch.from_numpy(norm).cuda()
+    v, m = S.prune_compress(x, score="wanda", col_norm=n)
+    flat = raw.reshape(-1, k)
+    wv, wm = O.prune_compress(flat, "bf16", "wanda", norm)
+    assert_same(raw_np(m).reshape(-1, k // 8), wm, "meta")
+    assert_same(raw_np(v).reshape(-1, k // 2), wv, "values")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 136, 72), (1, 256, 128), (3, 40, 8), (2, 16392, 128)])
 def test_prune_compress_transposed(dtype, shape):
