@@ -346,28 +346,37 @@ __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t
     }
     __syncthreads();
   }
-  if (threadIdx.x != 0) return;
   if (f.mode == 0) {
+    if (threadIdx.x != 0) return;
     double* o = out + blk * 4;
     o[0] = sb[0];
     o[1] = sb[1];
     o[2] = sb[f.kcol[0]];
     o[3] = sb[f.dcol[0]];
-  } else {
-    const double tot = sb[0];
-    for (int p = 0; p < f.npairs; ++p) {
-      double* o = out + (blk * f.npairs + p) * 5;
-      const double ep = sb[1] / tot;
-      const double eq = sb[f.kcol[p]] / tot;
-      const double e24 = ep + eq;
-      const double ed = sb[f.dcol[p]] / tot;
-      o[0] = ep;
-      o[1] = eq;
-      o[2] = e24;
-      o[3] = ed;
-      o[4] = __builtin_sqrt(e24 / ed);
-    }
+    return;
   }
+  // thread p forms pair p (the fp64 divisions and square roots of the pairs
+  // run side by side); its two columns are picked with a uniform loop, so the
+  // kernel arguments are never indexed per lane
+  const int tp = threadIdx.x;
+  int kc = 0, dc = 0;
+  for (int p = 0; p < f.npairs; ++p)
+    if (tp == p) {
+      kc = f.kcol[p];
+      dc = f.dcol[p];
+    }
+  if (tp >= f.npairs) return;
+  const double tot = sb[0];
+  double* o = out + (blk * f.npairs + tp) * 5;
+  const double ep = sb[1] / tot;
+  const double eq = sb[kc] / tot;
+  const double e24 = ep + eq;
+  const double ed = sb[dc] / tot;
+  o[0] = ep;
+  o[1] = eq;
+  o[2] = e24;
+  o[3] = ed;
+  o[4] = __builtin_sqrt(e24 / ed);
 }
 
 template <int CB>
