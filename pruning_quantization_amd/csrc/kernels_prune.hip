@@ -307,10 +307,10 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T(
 // .. + 7 of its 128-position half (t / 128): it loads one 16-byte chunk (8
 // adjacent rows) per position, so each wave load instruction reads 8 whole
 // 128-byte lines.  The block is transposed in registers with byte permutes
-// (one per output dword), each row's unit is selected through the LDS table
-// and the kept pairs are stored directly (8 adjacent threads write 64
-// contiguous bytes of a row).  Metadata bytes go through a double-buffered
-// LDS tile (one barrier per tile) and leave as 32-byte row segments.
+// (one per output dword) and each row's unit is selected through the LDS
+// table.  Kept pairs and metadata bytes go through double-buffered LDS tiles
+// (one barrier per tile) and leave in 16-byte chunks: a wave stores four
+// whole 256-byte rows of kept values, metadata as 32-byte row segments.
 constexpr int kT8_K = 256;     // positions per tile
 constexpr int kT8_R = 64;      // rows per tile
 constexpr int kT8_Tiles = 2;   // tiles per workgroup (grid = ceil(tiles / kT8_Tiles))
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T8(
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   __shared__ SelLut lut[kSelLutEntries];
   __shared__ __align__(16) uint8_t mtile[2][kT8_R][kT8_K / 8];  // [buffer][row][unit]
+  __shared__ __align__(16) char ktile[2][kT8_R][kT8_K];         // [buffer][row][kept bytes]
   const int t = threadIdx.x;
   const int rg = t & 7, pg = (t >> 3) & 15, half = t >> 7;
   const int64_t ntk = K / kT8_K, ntr = R / kT8_R;
@@ -349,8 +350,6 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T8(
   for (int buf = 0; tile < ntiles; tile += gridDim.x, buf ^= 1) {
     const int64_t next = tile + gridDim.x;
     if (next < ntiles) load(next, nxt);
-    int64_t b, r0, k0;
-    origin(tile, b, r0, k0);
     const int ucol = half * 16 + pg;  // unit column within the tile
 #pragma unroll
     for (int d = 0; d < 8; ++d) {  // row r0 + d: dword d / 2 of each chunk, half d % 2
@@ -360,17 +359,25 @@ __global__ __launch_bounds__(kBlock) void k_prune_compress_T8(
       for (int q = 0; q < 4; ++q)  // positions 2q, 2q + 1
         w[q] = __builtin_amdgcn_perm(cur[2 * q + 1][d >> 1], cur[2 * q][d >> 1], sel);
       const Sel16 r = select16_lut(w, lut);
-      st2(vals + ((b * R + r0 + d) * (K / 2) + k0 / 2) * 2, r.k0, r.k1);
+      *reinterpret_cast<uint2*>(&ktile[buf][rg * 8 + d][(half * 64 + pg * 4) * 2]) =
+          make_uint2(r.k0, r.k1);
       mtile[buf][rg * 8 + d][ucol] = (uint8_t)r.mb;
     }
     __syncthreads();
+    const int64_t qt = tile / ntk, kt = tile % ntk;
+    const int64_t orow0 = (qt / ntr) * R + (qt % ntr) * kT8_R;  // the tile's first output row
+#pragma unroll
+    for (int i = 0; i < kT8_R * kT8_K / 16 / kBlock; ++i) {
+      // 64 rows x 256 bytes of kept values in 16-byte chunks: a wave stores
+      // four whole rows of the tile (whole 128-byte lines)
+      const int c = t + kBlock * i, row = c >> 4, part = c & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(&ktile[buf][row][part * 16]);
+      st4(vals + (orow0 + row) * K + kt * kT8_K + part * 16, v.x, v.y, v.z, v.w);
+    }
     if (t < kT8_R * 2) {  // 64 rows x 32 metadata bytes, in 16-byte chunks
       const int row = t >> 1, part = t & 1;
       const uint4 v = *reinterpret_cast<const uint4*>(&mtile[buf][row][part * 16]);
-      const int64_t q = tile / ntk;
-      st4(meta + ((q / ntr) * R + (q % ntr) * kT8_R + row) * (K / 8) + (tile % ntk) * (kT8_K / 8) +
-              part * 16,
-          v.x, v.y, v.z, v.w);
+      st4(meta + (orow0 + row) * (K / 8) + kt * (kT8_K / 8) + part * 16, v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
