@@ -195,6 +195,20 @@ __device__ inline float mag_sq_err_int(float s, float inv, const float* v) {
   return a0 + a1;
 }
 
+// Same, as one chain of fused multiply-adds continuing acc: the packed
+// kernel's INT passes chain the four kept values of two units (8 terms) or
+// the eight values of one unit before each fp64 add, at most 8 roundings
+// after the residual's (< 6e-7 relative), with one register per quantizer.
+template <int N>
+__device__ inline float mag_sq_err_int_chain(float s, float inv, const float* v, float acc) {
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const float e = __builtin_fmaf(__builtin_rintf(v[q] * inv), s, -v[q]);
+    acc = __builtin_fmaf(e, e, acc);
+  }
+  return acc;
+}
+
 // fp32 sum of the squares of 8 residuals: four chains of two fused
 // multiply-adds, added pairwise (4 roundings after the residuals').
 __device__ inline float sq_sum8(const float* e) {
@@ -806,22 +820,37 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
         constexpr bool SPLIT = SEL == SEL_MAG;
         pin_packed<UPL>(pk);
         double ka[kFusedInt<SEL>], dka[kFusedInt<SEL>], dda[kFusedInt<SEL>];
+        // without the kept / dropped split the kept sums chain in fp32 over
+        // two units (the split's extra chains would spill the magnitude
+        // kernel at four waves per SIMD)
+        float fk[kFusedInt<SEL>];
   #pragma unroll
-        for (int i = 0; i < kFusedInt<SEL>; ++i) ka[i] = dka[i] = dda[i] = 0.0;
+        for (int i = 0; i < kFusedInt<SEL>; ++i) {
+          ka[i] = dka[i] = dda[i] = 0.0;
+          fk[i] = 0.0f;
+        }
   #pragma unroll
         for (int j = 0; j < UPL; ++j) {
           const float v[8] = {mag_lo(pk[j][0]), mag_hi(pk[j][0]), mag_lo(pk[j][1]), mag_hi(pk[j][1]),
                               mag_lo(pk[j][2]), mag_hi(pk[j][2]), mag_lo(pk[j][3]), mag_hi(pk[j][3])};
+          const bool pair_end = (j & 1) || j == UPL - 1;
   #pragma unroll
           for (int i = 0; i < kFusedInt<SEL>; ++i) {
-            if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
-            if (i < nd) {
-              if constexpr (SPLIT) {
+            if constexpr (SPLIT) {
+              if (i < nk) ka[i] += (double)mag_sq_err_int<4>(ks[i], kinv[i], v);
+              if (i < nd) {
                 dka[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v);
                 dda[i] += (double)mag_sq_err_int<4>(ds[i], dinv[i], v + 4);
-              } else {
-                dda[i] += (double)mag_sq_err_int<8>(ds[i], dinv[i], v);
               }
+            } else {
+              if (i < nk) {
+                fk[i] = mag_sq_err_int_chain<4>(ks[i], kinv[i], v, fk[i]);
+                if (pair_end) {
+                  ka[i] += (double)fk[i];
+                  fk[i] = 0.0f;
+                }
+              }
+              if (i < nd) dda[i] += (double)mag_sq_err_int_chain<8>(ds[i], dinv[i], v, 0.0f);
             }
           }
           __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
