@@ -342,12 +342,10 @@ __device__ inline void finalize_rows(const double* __restrict__ rowpart, int64_t
 #pragma unroll
         for (int c = 0; c < CB; ++c) a[c] += v[u][c];
     }
-    // wave sums (xor shuffles, fixed order), then the waves' sums in order
+    // wave sums (DPP butterflies and lane reads, fixed order), then the
+    // waves' sums in order
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) a[c] += __shfl_xor(a[c], o, 64);
-    }
+    for (int c = 0; c < CB; ++c) a[c] = wave_sum_f64<64>(a[c]);
     if ((threadIdx.x & 63) == 0)
 #pragma unroll
       for (int c = 0; c < CB; ++c) sh[c][threadIdx.x >> 6] = a[c];
@@ -511,9 +509,21 @@ __device__ inline void sink_flush(const PartialSink& k, double* lacc, double* re
       if (sg.first >= 0) sink_segment_flush<TEAM>(k, lacc, redd, ncols, sg);
     return;
   }
+  // every column's wave sums first (independent, no barrier between them),
+  // then thread c adds column c's wave sums in wave order: the same
+  // additions as a workgroup sum per column, with one barrier in all
+  __shared__ double wsum[2 + 2 * kMaxQ][kBlock / 64];
+#pragma unroll 4
   for (int c = 0; c < ncols; ++c) {
-    const double a = team_sum_f64<kBlock>(lacc[c * kBlock + threadIdx.x], redd);
-    if (threadIdx.x == 0) k.rowpart[(int64_t)c * k.stride + blockIdx.x] = a;
+    const double w = wave_sum_f64<64>(lacc[c * kBlock + threadIdx.x]);
+    if ((threadIdx.x & 63) == 0) wsum[c][threadIdx.x >> 6] = w;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < ncols) {
+    double r = wsum[threadIdx.x][0];
+#pragma unroll
+    for (int i = 1; i < kBlock / 64; ++i) r += wsum[threadIdx.x][i];
+    k.rowpart[(int64_t)threadIdx.x * k.stride + blockIdx.x] = r;
   }
 }
 
