@@ -935,24 +935,37 @@ __device__ inline void for_each_row(const RowGeom& g, Body&& body) {
   }
 }
 
-// Same with contiguous rows per team: team k takes rows k * rpt .. k * rpt +
-// rpt - 1 (rpt = ceil(rows / teams)), so the rows a team sums lie in as few
-// row blocks as possible.  Every team runs rpt iterations; an iteration past
-// the team's last row (or the operand's) passes row = g.nrows and zero units.
+// Same with contiguous rows per team, so the rows a team sums lie in as few
+// row blocks as possible.  With q = rows / teams (rounded down), the teams of
+// the first workgroups take q + 1 rows each and the others q, just enough
+// workgroups taking q + 1 to cover the rows, so a SIMD's teams share the rows
+// evenly instead of every team running ceil(rows / teams) iterations.  The
+// count is uniform over a workgroup (its team reductions may synchronise the
+// workgroup); an iteration past the operand's last row passes row = g.nrows
+// and zero units.
+struct ContigRows {
+  int64_t first, count;
+};
 template <int TEAM>
-__device__ inline int64_t contig_rows_per_team(const RowGeom& g) {
-  const int64_t nteams = (int64_t)gridDim.x * (kBlock / TEAM);
-  return (g.nrows + nteams - 1) / nteams;
+__device__ inline ContigRows contig_rows(const RowGeom& g) {
+  constexpr int64_t TPB = kBlock / TEAM;
+  const int64_t nw = gridDim.x, w = blockIdx.x;
+  const int64_t q = g.nrows / (nw * TPB);
+  const int64_t rem = g.nrows - q * nw * TPB;
+  const int64_t e = (rem + TPB - 1) / TPB;  // workgroups whose teams take q + 1 rows
+  const int64_t n = w < e ? q + 1 : q;
+  const int64_t base = w < e ? w * TPB * (q + 1) : e * TPB * (q + 1) + (w - e) * TPB * q;
+  return ContigRows{base + (int64_t)(threadIdx.x / TEAM) * n, n};
 }
 template <int TEAM>
 __device__ inline int64_t contig_first_row(const RowGeom& g) {
-  return ((int64_t)blockIdx.x * (kBlock / TEAM) + threadIdx.x / TEAM) * contig_rows_per_team<TEAM>(g);
+  return contig_rows<TEAM>(g).first;
 }
 template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
 __device__ inline void for_each_row_contig(const RowGeom& g, Body&& body) {
   const int t = threadIdx.x % TEAM;
-  const int64_t rpt = contig_rows_per_team<TEAM>(g);
-  const int64_t r0 = contig_first_row<TEAM>(g);
+  const ContigRows cr = contig_rows<TEAM>(g);
+  const int64_t rpt = cr.count, r0 = cr.first;
   const int64_t r1 = r0 + rpt < g.nrows ? r0 + rpt : g.nrows;
   for (int64_t it = 0; it < rpt; ++it) {
     Unit<DT> A[UPL];
