@@ -919,8 +919,11 @@ __device__ inline void load_row(Unit<DT> (&u)[UPL], const RowGeom& g, int64_t ro
 // energy kernels).  The trip count is the same for every team, so team
 // reductions that synchronise a workgroup are reached by all of its threads.
 // ---------------------------------------------------------------------------
-template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
-__device__ inline void for_each_row(const RowGeom& g, Body&& body) {
+// pre() runs once, after the first row's loads are issued and before they
+// are used (set-up such as an LDS table then overlaps the loads' latency);
+// every thread of the workgroup calls it.
+template <class DT, int TEAM, int UPL, int ROT = 0, class Pre, class Body>
+__device__ inline void for_each_row(const RowGeom& g, Pre&& pre, Body&& body) {
   constexpr int TPB = kBlock / TEAM;
   const int t = threadIdx.x % TEAM;
   const int64_t first = (int64_t)blockIdx.x * TPB + threadIdx.x / TEAM;
@@ -930,9 +933,14 @@ __device__ inline void for_each_row(const RowGeom& g, Body&& body) {
     Unit<DT> A[UPL];
     const int64_t ra = first + it * stride;
     load_row<DT, TEAM, UPL>(A, g, ra, t);
+    if (it == 0) pre();
     if constexpr (ROT) hadamard_units<DT, TEAM, UPL, ROT>(A, g.rot, t);
     body(A, ra, t);
   }
+}
+template <class DT, int TEAM, int UPL, int ROT = 0, class Body>
+__device__ inline void for_each_row(const RowGeom& g, Body&& body) {
+  for_each_row<DT, TEAM, UPL, ROT>(g, [] {}, body);
 }
 
 // Same with contiguous rows per team, so the rows a team sums lie in as few

@@ -426,11 +426,14 @@ SPARQ24_ROW_KERNEL void k_prune_quantize(RowGeom g, const float* __restrict__ no
   // takes the kept maximum of the gathered values like Wanda.
   constexpr bool FAST16 = DT::ESIZE == 2 && !WANDA && PAT == PAT_24;
   __shared__ SelLut lut[FAST16 ? kSelLutEntries : 1];
-  if constexpr (FAST16) {
-    sel_lut_fill(lut);
-    __syncthreads();
-  }
-  for_each_row<DT, TEAM, UPL, ROT>(g, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
+  // the table is filled while the first row's loads are in flight
+  auto pre = [&] {
+    if constexpr (FAST16) {
+      sel_lut_fill(lut);
+      __syncthreads();
+    }
+  };
+  for_each_row<DT, TEAM, UPL, ROT>(g, pre, [&](Unit<DT>(&u)[UPL], int64_t row, int t) {
     const bool active = row < g.nrows;
     uint32_t am = 0;
     uint32_t mb[UPL];

@@ -197,6 +197,29 @@ def test_prune_quantize_fp8_int8(dtype, k):
             assert_same(raw_np(c), wc, f"codes {fmt}")
 
 
+@pytest.mark.parametrize("dtype,rows,k,q,sample", [
+    ("bf16", 16384, 4096, ("fp8", 0), False),    # the 16384-token activation, every row
+    ("bf16", 16384, 4096, ("int", 8), False),
+    ("f16", 20000, 512, ("fp8", 0), False),      # one-wave teams, four rows per workgroup
+    ("bf16", 6000, 16384, ("int", 16), True),    # whole-workgroup teams
+])
+def test_prune_quantize_many_rows(dtype, rows, k, q, sample):
+    # 16-bit magnitude 2:4 + INT/FP8 at full operand sizes (the grid's last
+    # workgroups, ragged team counts, whole-workgroup teams): every row, or a
+    # spread sample of rows, against the oracle, bit for bit
+    rng = np.random.default_rng(rows + k)
+    raw = random_raw(rng, (rows, k), dtype, scale=3.0)
+    raw[rows // 3] = 0                                # an all-zero row
+    x = to_dev(raw, dtype)
+    c, m, s = S.prune_quantize(x, q)
+    pick = (np.unique(np.r_[0:8, rows - 8:rows, rng.choice(rows, 300, replace=False)])
+            if sample else np.arange(rows))
+    wc, wm, ws = O.prune_quantize(raw[pick], dtype, O.QSpec(*q))
+    assert_same(raw_np(m)[pick], wm, "meta")
+    assert_same(raw_np(s)[pick], ws, "scales")
+    assert_same(raw_np(c)[pick], wc, "codes")
+
+
 @pytest.mark.parametrize("fmt,bits", QS)
 @pytest.mark.parametrize("score", ["magnitude", "wanda"])
 def test_prune_quantize_formats(fmt, bits, score):
