@@ -64,7 +64,54 @@ def parse():
     ap.add_argument("--markers", action="store_true",
                     help="launch a one-workgroup copy before each measured phase, so that a "
                          "profile's dispatches can be split by phase")
+    ap.add_argument("--ops-jsonl", default=None,
+                    help="also write one JSON line per (config, op) to this file")
     return ap.parse_args()
+
+
+# (config, operand shape) of each timed call, by name prefix; the configs are
+# the five workloads: C0 tiny fp32 (a parity case only, not timed), C1 the
+# linear-layer activation, C2 the MLP weight, C3 the attention operands, C4
+# the heavy-tailed activation
+OP_SHAPES = [
+    ("headline", "C4", [16384, 4096]), ("act_", "C1", [4096, 4096]),
+    ("weight_", "C2", [14336, 4096]), ("heavy_", "C4", [16384, 4096]),
+    ("attn_prune_compress_Q", "C3", [32, 16384, 128]), ("attn_prune_compress_K", "C3", [8, 16384, 128]),
+    ("attn_prune_compress_V_seq", "C3", [8, 16384, 128]), ("attn_prune_compress_P", "C3", [32, 4096, 4096]),
+    ("attn_predict_R_P", "C3", [32, 4096, 4096]), ("operator_error", "C1 x C2", [4096, 4096]),
+    ("gemm_", "C1 x C2", [4096, 4096]),
+]
+
+
+def op_records(line, gpu, rocm):
+    """One record per (config, op) from a bench line: the metrics the line
+    holds for that call, in one flat object."""
+    copy = line["copy_GBps"]
+    calls = [("headline_prune_quantize_fp8", {"us": line["roofline"]["avg_launch_us"],
+                                              "bytes": line["roofline"]["algorithmic_bytes_per_launch"],
+                                              "launches": line["steps"]})]
+    calls += list(line["per_call"].items())
+    out = []
+    for name, c in calls:
+        cfg, shape = next((cf, sh) for pre, cf, sh in OP_SHAPES if name.startswith(pre))
+        elems = int(np.prod(shape))
+        gbps = c["bytes"] / (c["us"] * 1e-6) / 1e9
+        rec = {"config": cfg, "op": name, "dtype": "bf16", "shape": shape,
+               "algorithmic_bytes": c["bytes"], "us": c["us"], "GBps": round(gbps, 1),
+               "Gelem_per_s": round(elems / (c["us"] * 1e-6) / 1e9, 2),
+               "pct_copy": round(100 * gbps / copy, 2), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+               "launches": c["launches"], "gpu": gpu, "rocm": rocm}
+        if "predict_R" in name:
+            rec["tensors_per_s"] = round(1e6 / c["us"], 1)
+        if "TFLOPs" in c:
+            rec.update({"TFLOPs": c["TFLOPs"], "mfma_frac": c["mfma_frac"]})
+        if name.startswith("headline"):
+            rec["parity_sampled_rows"] = line["parity_sampled_rows"]
+            if line.get("cpu_baseline"):
+                rec["oracle_seconds"] = line["cpu_baseline"]["seconds"]
+                rec["host_cpus"] = line["cpu_baseline"]["host_cpus"]
+        out.append(rec)
+    return out
 
 
 def source_hash(names) -> str:
@@ -304,6 +351,12 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+    if a.ops_jsonl:
+        with open(a.ops_jsonl, "w") as fh:
+            props = torch.cuda.get_device_properties(dev)
+            gpu = f"{props.name} ({getattr(props, 'gcnArchName', '')})"
+            for rec in op_records(line, gpu, torch.version.hip):
+                fh.write(json.dumps(rec) + "\n")
 
 
 def side_calls(a, S, W, O, torch, dev, bf, capture, elapsed_us, hx_bits, hpool, use_graphs, marker):
