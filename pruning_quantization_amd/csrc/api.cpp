@@ -182,6 +182,7 @@ struct EnergyPlan {
   const float* nv_in = nullptr;
   const float* knv_in = nullptr;  // NVFP4 on kept values
   bool need_nv_partials = false, need_knv_partials = false;
+  bool nv_second_pass = false;
   int nparts = 0, nkparts = 0;
   int64_t nrows = 0, rpb = 0, nblk = 0;
   size_t off_rowpart = 0, off_csum = 0, off_parts = 0, off_kparts = 0, need = 0;
@@ -274,7 +275,14 @@ sparq24_status plan_energy(const RowDesc& d, const sparq24_qspec* kept_q,
   pl.rpb = rows_per_block == 0 ? pl.nrows : rows_per_block;
   pl.nblk = (pl.nrows + pl.rpb - 1) / pl.rpb;
   pl.need_nv_partials = n_nv == 1 && pl.nv_in == nullptr;
-  pl.nparts = pl.need_nv_partials ? absmax_partial_count(d) : 0;
+  // bf16 rows of up to 4096 elements without rotation: the energy pass
+  // itself leaves the tensor maximum's partials (one per workgroup of its
+  // grid, at most energy_max_workgroups()) and a second pass evaluates the dense
+  // NVFP4 quantizer; otherwise a maximum pass runs first
+  pl.nv_second_pass = pl.need_nv_partials && d.dtype == 1 && d.rot.n == 0 && d.K <= 4096;
+  pl.nparts = !pl.need_nv_partials ? 0
+              : pl.nv_second_pass ? energy_max_workgroups()
+                                  : absmax_partial_count(d);
   pl.need_knv_partials = n_knv == 1 && pl.knv_in == nullptr;
   pl.nkparts = pl.need_knv_partials ? absmax_partial_count(d) : 0;
   const size_t rowpart = (size_t)pl.f.ncols * (size_t)energy_partial_rows(pl.nrows) * sizeof(double);
@@ -297,7 +305,10 @@ sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, Energ
   }
   double* rowpart = (double*)(w + pl.off_rowpart);
   uint32_t* parts = (uint32_t*)(w + pl.off_parts);
-  if (pl.need_nv_partials) {
+  if (pl.nv_second_pass) {
+    pl.p.defer_nv = 1;
+    pl.p.max_out = parts;
+  } else if (pl.need_nv_partials) {
     CHECK(launched(launch_absmax_partials(d, parts, stream)));
     pl.p.nv_partials = parts;
     pl.p.n_partials = pl.nparts;
@@ -312,9 +323,17 @@ sparq24_status run_energy(RowDesc d, int32_t score, const float* col_norm, Energ
     pl.p.n_kept_partials = pl.nkparts;
   }
   pl.p.kept_nv_tamax = pl.knv_in;
-  int64_t nparts = 0;
+  int64_t nparts = 0, grid = 0;
   CHECK(launched(launch_energy_rows(d, score == SPARQ24_SCORE_WANDA, col_norm, pl.p, rowpart,
-                                    pl.rpb, &nparts, stream)));
+                                    pl.rpb, &nparts, stream, &grid)));
+  if (pl.nv_second_pass) {
+    int qnv = 0;
+    for (int q = 0; q < pl.p.dense.n; ++q)
+      if (pl.p.dense.fmt[q] == CF_NV) qnv = q;
+    if (grid > pl.nparts) return SPARQ24_ERR_LAUNCH;  // the maxima buffer holds one per workgroup
+    CHECK(launched(launch_energy_nv_dense(d, parts, (int)grid, 2 + pl.p.kept.n + qnv, rowpart,
+                                          pl.rpb, grid, stream)));
+  }
   double* csum = (double*)(w + pl.off_csum);
   if (pl.rpb >= pl.nrows)  // one block: reduce the per-workgroup partials
     return launched(launch_energy_finalize(rowpart, nparts, nparts, 1, pl.f, csum, out, stream));

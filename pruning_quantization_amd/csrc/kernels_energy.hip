@@ -706,6 +706,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   sink_init(lacc, ncols);
   bool any_nv = false;
   for (int q = 0; q < p.dense.n; ++q) any_nv |= (p.dense.fmt[q] == CF_NV);
+  any_nv = any_nv && !p.defer_nv;
   float s_t = 0.f, gnv = 0.f;
   __shared__ float nvinv_d[kNvInvEntries], nvinv_k[kNvInvEntries];
   if (any_nv) {
@@ -727,6 +728,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
   // without rotation, which fit them in registers)
   constexpr bool SEG = HELD != 0 || (SEL == SEL_MAG && ROT == 0);
   Segment sg = sink_segments<TEAM, SEG>(sink, g);
+  uint32_t rows_max = 0;  // fp32 bits of the largest |x| of this team's rows (defer_nv)
   for_each_row_contig<BF16T, TEAM, UPL, ROT>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
     const bool live = row < nrows;
     sink_row_begin<SEG>(sink, row, live, sg);
@@ -770,6 +772,7 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     }
     sink_sum<TEAM, SEG>(sink, lacc, redd, row, 0, kept2 + drop, live);
     sink_sum<TEAM, SEG>(sink, lacc, redd, row, 1, drop, live);
+    rows_max = rows_max > amd ? rows_max : amd;  // zero for rows past the end
     const float famk = __uint_as_float(amk), famd = __uint_as_float(amd);
     if constexpr (HELD != 0) {
       quantizers_held<TEAM, UPL, SEL, HELD == 2>(p, pk, famk, famd, sink, lacc, redd, row, live);
@@ -931,6 +934,8 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
           }
           if (twin >= 0) sink_sum<TEAM, SEG>(sink, lacc, redd, row, 2 + twin, acck, live);
           acc += acck;
+        } else if (fmt == CF_NV && p.defer_nv) {
+          // evaluated by k_energy_nv_dense once the tensor maximum is known
         } else if (fmt == CF_MX || fmt == CF_NV) {
   #pragma unroll
           for (int j = 0; j < UPL; ++j) {
@@ -960,6 +965,85 @@ void k_energy_rows_bf16(RowGeom g, const float* __restrict__ norm, EnergyParams 
     sink_row_end<TEAM, SEG>(sink, lacc, redd, ncols, row, live, sg);
   });
   sink_flush<TEAM, SEG>(sink, lacc, redd, ncols, sg);
+  if (p.max_out) {  // uniform over the launch
+    const uint32_t m = team_max_u32<kBlock>(rows_max, redu);
+    if (threadIdx.x == 0) p.max_out[blockIdx.x] = m;
+  }
+}
+
+// Dense NVFP4 error energy of bf16 rows (no selection, no rotation), the
+// second pass of a predict_R whose NVFP4 tensor maximum comes from the first
+// pass's per-workgroup maxima.  Each unit is coded as in the energy kernel
+// (16-value blocks over two adjacent lanes' units); its squared residuals
+// go into the partial column col: per row (blocked sums: the finalize adds a
+// block's rows) or per workgroup (the whole operand as one block, on the same
+// grid as the first pass).
+template <int TEAM, int UPL>
+__global__ __launch_bounds__(kBlock) void k_energy_nv_dense(RowGeom g, const uint32_t* __restrict__ parts,
+                                                            int nparts, int col, PartialSink sink) {
+  __shared__ uint32_t redu[kBlock / 64];
+  __shared__ double redd[kBlock / 64];
+  __shared__ double wsum[kBlock / 64];
+  __shared__ float nvinv[kNvInvEntries];
+  const float T = block_tensor_amax(nullptr, parts, nparts, redu);
+  float s_t = 0.f, gnv = 0.f;
+  if (T >= 0x1p-64f) { s_t = T / 2688.0f; gnv = 448.0f / T; }
+  nv_inv_fill(nvinv, s_t);
+  __syncthreads();
+  double lane_acc = 0.0;
+  for_each_row_contig<BF16T, TEAM, UPL, 0>(g, [&](Unit<BF16T>(&u)[UPL], int64_t row, int t) {
+    double acc = 0.0;  // zero units (past the row or the operand) add +0
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      uint32_t a[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) a[h] = u[j].w[h] & 0x7FFF7FFFu;
+      uint32_t bm = unpack_max16(pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]))) << 16;
+      const uint32_t w = (uint32_t)__shfl_xor((int)bm, 1, 64);
+      bm = bm > w ? bm : w;  // the 16-value block of units 2k, 2k + 1
+      const float v[8] = {mag_lo(a[0]), mag_hi(a[0]), mag_lo(a[1]), mag_hi(a[1]),
+                          mag_lo(a[2]), mag_hi(a[2]), mag_lo(a[3]), mag_hi(a[3])};
+      acc += (double)unit_sq_err_nv8(v, bm, s_t, gnv, nvinv);
+    }
+    if (sink.acc) {
+      lane_acc += acc;
+    } else {
+      const double r = team_sum_f64<TEAM>(acc, redd);
+      if (row < g.nrows && t == 0) sink.rowpart[(int64_t)col * sink.stride + row] = r;
+    }
+  });
+  if (sink.acc) {
+    const double w = wave_sum_f64<64>(lane_acc);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double r = wsum[0];
+#pragma unroll
+      for (int i = 1; i < kBlock / 64; ++i) r += wsum[i];
+      sink.rowpart[(int64_t)col * sink.stride + blockIdx.x] = r;
+    }
+  }
+}
+
+hipError_t launch_energy_nv_dense(const RowDesc& d, const uint32_t* parts, int nparts, int col,
+                                  double* rowpart, int64_t rows_per_block, int64_t grid,
+                                  hipStream_t s) {
+  const int64_t nunits = d.K / 8;
+  const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
+  PartialSink k;
+  k.rowpart = rowpart;
+  k.acc = rows_per_block >= g.nrows;
+  k.rpb = rows_per_block;
+  k.stride = k.acc ? grid : g.nrows;
+  return with_row_variant<0>(nunits, [&]<int TEAM, int UPL>() {
+    if constexpr (UPL > 8) {
+      return hipErrorInvalidValue;  // rows of up to 4096 elements
+    } else {
+      hipLaunchKernelGGL((k_energy_nv_dense<TEAM, UPL>), dim3((unsigned)grid), dim3(kBlock), 0, s, g,
+                         parts, nparts, col, k);
+      return hipGetLastError();
+    }
+  });
 }
 
 template <class DT, int TEAM, int UPL, bool WANDA, int ROT>
@@ -1185,7 +1269,7 @@ __global__ __launch_bounds__(kBlock) void k_energy_combine(const double* __restr
 // b sums each column over its rows (fixed order) and forms the outputs.
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               const EnergyParams& p, double* rowpart, int64_t rows_per_block,
-                              int64_t* nparts, hipStream_t s) {
+                              int64_t* nparts, hipStream_t s, int64_t* grid_out) {
   const int64_t nunits = d.K / 8;
   const RowGeom g{d.x, d.R, d.B * d.R, nunits, d.bs, d.rs, d.rot};
   const bool acc = rows_per_block >= g.nrows;  // one block: per-lane accumulators
@@ -1197,6 +1281,7 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
     k.rpb = rows_per_block;
     k.stride = acc ? (int64_t)grid.x : g.nrows;
     *nparts = acc ? (int64_t)grid.x : g.nrows;
+    if (grid_out) *grid_out = grid.x;
   };
   if (d.dtype == 1) {  // bf16: packed-magnitude kernel
     const int sel = wanda ? SEL_WANDA : (p.pairs48 ? SEL_P48 : SEL_MAG);
@@ -1267,6 +1352,9 @@ hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
   if (d.dtype == 2) return generic.template operator()<F16T>();
   return hipErrorInvalidValue;
 }
+
+// Most workgroups an energy launch has (the persistent grids' cap).
+int energy_max_workgroups() { return device_cu_count() * kBlocksPerCU; }
 
 // Upper bound of the partial rows launch_energy_rows writes per column.
 int64_t energy_partial_rows(int64_t nrows) { return nrows + kBlock; }

@@ -71,6 +71,11 @@ struct EnergyParams {
   const float* kept_nv_tamax;
   const uint32_t* kept_nv_partials;
   int n_kept_partials;
+  // Dense NVFP4 deferred to launch_energy_nv_dense: its column is written as
+  // zero, and each workgroup writes the fp32 bits of the largest |x| of its
+  // rows to max_out[workgroup] (the tensor maximum's partials).
+  int defer_nv;
+  uint32_t* max_out;
 };
 
 // Row kernels that hold a whole row in registers support up to this many units.
@@ -103,8 +108,15 @@ hipError_t launch_quant_nv(const RowDesc& d, const float* tamax_in, const uint32
 // one partial per team; *nparts receives the partial rows per column.
 hipError_t launch_energy_rows(const RowDesc& d, bool wanda, const float* norm,
                               const EnergyParams& p, double* rowpart, int64_t rows_per_block,
-                              int64_t* nparts, hipStream_t s);
+                              int64_t* nparts, hipStream_t s, int64_t* grid_out = nullptr);
+// The dense NVFP4 error energy of a bf16 operand (no rotation) into partial
+// column col of rowpart, in the layout launch_energy_rows used with grid
+// workgroups; the tensor maximum from the nparts partial maxima at parts.
+hipError_t launch_energy_nv_dense(const RowDesc& d, const uint32_t* parts, int nparts, int col,
+                                  double* rowpart, int64_t rows_per_block, int64_t grid,
+                                  hipStream_t s);
 int64_t energy_partial_rows(int64_t nrows);
+int energy_max_workgroups();
 // mode 0: out[blk][4] raw sums for pair 0; mode 1: out[blk][npairs][5] E's and R
 struct FinalizeParams {
   int ncols;            // 2 + nkept + ndense
